@@ -1,0 +1,202 @@
+"""The oracle: plain, slow, obviously correct CPU versions of what the GPU path computes.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  It shares no code with the HIP library (``gated_deltanet_delta_amd``) and never
+imports it; the library never imports this.
+
+Contents
+--------
+``forward``  the gated delta rule token by token in fp64 (``gdn_oracle.c``, compiled with gcc).  It
+             serves both entry points: a prefill is one call over whole sequences, a decode step is
+             the same call over length-1 sequences.
+``gates``    the gate formulas of the Qwen3.5 Gated DeltaNet flowchart (wanger-sjtu.github.io,
+             "Qwen3.5 Gated DeltaNet core-mechanism" page, flowchart nodes "Sigmoid -> beta",
+             "Softplus + dt_bias", "Exp and Neg", "Mul -> g") and of the Qwen3-Next architecture
+             write-up (intelliparadigm.com, section 2.2 "linear attention module", step 2 "gate
+             generation"), in fp64.
+``chunked``  the chunk-parallel (WY/UT) form of the same rule in fp64 numpy.  It is not the
+             definition: it exists to show, against ``forward``, that the block algebra a chunked
+             kernel uses reaches the token-by-token result exactly (up to rounding order).
+
+Every function here is pinned by ``tests/test_oracle.py`` against closed forms, a hand-worked example
+(``tests/golden/``), brute-force transition products and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "gdn_oracle.c")
+LIBRARY = os.path.join(HERE, "libgdn_oracle.so")
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the C oracle with gcc (plain -O2, OpenMP, no target-specific flags)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", source, "-o", output, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library (the real one, or a test's mutant)."""
+
+    def __init__(self, path: str = LIBRARY):
+        if path == LIBRARY and (
+            not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SOURCE)
+        ):
+            build()
+        self.path = path
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.gdn_oracle_forward.restype = ctypes.c_int
+        lib.gdn_oracle_forward.argtypes = [
+            dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.POINTER(ctypes.c_ubyte), ctypes.c_int, dp, dp,
+        ]
+        lib.gdn_oracle_default_threads.restype = ctypes.c_int
+        self._lib = lib
+
+    def default_threads(self) -> int:
+        return int(self._lib.gdn_oracle_default_threads())
+
+    def forward(
+        self,
+        q: np.ndarray,
+        k: np.ndarray,
+        v: np.ndarray,
+        g: np.ndarray,
+        beta: np.ndarray,
+        initial_state: Optional[np.ndarray] = None,
+        cu_seqlens: Optional[np.ndarray] = None,
+        unit_mask: Optional[np.ndarray] = None,
+        threads: int = 0,
+    ) -> Tuple[np.ndarray, np.ndarray]:
+        """(o, final_state) in fp64 for q,k [B,T,Hk,dk], v [B,T,Hv,dv], g,beta [B,T,Hv].
+
+        ``initial_state`` is [N,Hv,dk,dv] or None (zeros).  ``cu_seqlens`` (int32 [N+1], B == 1)
+        packs N sequences along T; without it N == B.  ``unit_mask`` (bool [N,Hv]) restricts the run
+        to a sample of (sequence, v-head) units; o rows and states of skipped units are NaN.
+        """
+        B, T, Hk, dk = q.shape
+        Hv, dv = v.shape[2], v.shape[3]
+        if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) or beta.shape != g.shape:
+            raise ValueError("inconsistent shapes")
+        N = B if cu_seqlens is None else len(cu_seqlens) - 1
+        arrs = [np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, g, beta)]
+        s0 = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float64)
+        if s0 is not None and s0.shape != (N, Hv, dk, dv):
+            raise ValueError("initial_state shape")
+        cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        mask = None if unit_mask is None else np.ascontiguousarray(unit_mask, dtype=np.uint8).reshape(N * Hv)
+        o = np.full((B, T, Hv, dv), np.nan)
+        fs = np.full((N, Hv, dk, dv), np.nan)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ptr = lambda a: a.ctypes.data_as(dp)  # noqa: E731
+        rc = self._lib.gdn_oracle_forward(
+            *(ptr(a) for a in arrs),
+            None if s0 is None else ptr(s0),
+            None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            B, T, Hk, Hv, dk, dv, N,
+            None if mask is None else mask.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)),
+            int(threads), ptr(o), ptr(fs),
+        )
+        if rc != 0:
+            raise ValueError(f"gdn_oracle_forward returned {rc}")
+        return o, fs
+
+
+_default: Optional[Oracle] = None
+
+
+def _oracle() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def forward(*args, **kwargs) -> Tuple[np.ndarray, np.ndarray]:
+    """Token-by-token fp64 gated delta rule; see ``Oracle.forward``."""
+    return _oracle().forward(*args, **kwargs)
+
+
+def default_threads() -> int:
+    return _oracle().default_threads()
+
+
+def gates(a: np.ndarray, b: np.ndarray, A_log: np.ndarray, dt_bias: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(g, beta) in fp64 from the raw per-token projections a, b [..., H] and per-head A_log, dt_bias [H].
+
+    Qwen3.5 flowchart (wanger-sjtu.github.io) and the Qwen3-Next write-up (intelliparadigm.com §2.2):
+    beta = sigmoid(b) is the write strength; g = -exp(A_log) * softplus(a + dt_bias) is the log-decay,
+    always <= 0, so the per-token decay factor exp(g) lies in (0, 1].  (The jsqmd.com article's §2.1
+    swaps the two names; its "beta" is negative and cannot be a strength in (0,1), so its labels are
+    not followed.)
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    x = a + np.asarray(dt_bias, dtype=np.float64)
+    softplus = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+    g = -np.exp(np.asarray(A_log, dtype=np.float64)) * softplus
+    beta = 1.0 / (1.0 + np.exp(-b))
+    return g, beta
+
+
+def chunked(
+    q: np.ndarray,
+    k: np.ndarray,
+    v: np.ndarray,
+    g: np.ndarray,
+    beta: np.ndarray,
+    initial_state: Optional[np.ndarray],
+    chunk: int,
+) -> Tuple[np.ndarray, np.ndarray]:
+    """The chunk-parallel form, fp64, for one sequence: q,k [T,Hk,dk], v [T,Hv,dv], g,beta [T,Hv].
+
+    Within a chunk of C tokens starting from state S0, with G_t the running sum of g inside the chunk,
+    unrolling the per-token rule gives (rows are tokens):
+
+        (I + A) U = diag(beta) V - diag(beta e^G) K S0,   A_tj = beta_t (k_t.k_j) e^(G_t - G_j), j < t
+        O   = diag(e^G) Q S0 + P U,                         P_tj = (q_t.k_j) e^(G_t - G_j), j <= t
+        S_C = e^(G_C) S0 + K^T diag(e^(G_C - G)) U
+
+    so U = W~ - W S0 with W = (I+A)^-1 diag(beta e^G) K and W~ = (I+A)^-1 diag(beta) V.  Every decay
+    factor is exp of a non-positive number.  The last chunk may be shorter than C.
+    """
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    grp = Hv // Hk
+    o = np.zeros((T, Hv, dv))
+    fs = np.zeros((Hv, dk, dv))
+    for h in range(Hv):
+        kh = h // grp
+        S = np.zeros((dk, dv)) if initial_state is None else np.array(initial_state[h], dtype=np.float64)
+        for c0 in range(0, T, chunk):
+            c1 = min(T, c0 + chunk)
+            Q = np.asarray(q[c0:c1, kh], dtype=np.float64)
+            K = np.asarray(k[c0:c1, kh], dtype=np.float64)
+            V = np.asarray(v[c0:c1, h], dtype=np.float64)
+            bt = np.asarray(beta[c0:c1, h], dtype=np.float64)
+            G = np.cumsum(np.asarray(g[c0:c1, h], dtype=np.float64))
+            L = c1 - c0
+            diff = G[:, None] - G[None, :]
+            lower_strict = np.tril(np.ones((L, L)), -1)
+            lower = np.tril(np.ones((L, L)))
+            decay_strict = np.exp(np.where(lower_strict > 0, diff, -np.inf))
+            decay = np.exp(np.where(lower > 0, diff, -np.inf))
+            A = bt[:, None] * (K @ K.T) * decay_strict
+            Tinv = np.linalg.solve(np.eye(L) + A, np.eye(L))
+            W = Tinv @ ((bt * np.exp(G))[:, None] * K)
+            Wt = Tinv @ (bt[:, None] * V)
+            U = Wt - W @ S
+            P = (Q @ K.T) * decay
+            o[c0:c1, h] = np.exp(G)[:, None] * (Q @ S) + P @ U
+            S = np.exp(G[-1]) * S + K.T @ (np.exp(G[-1] - G)[:, None] * U)
+        fs[h] = S
+    return o, fs

@@ -1,0 +1,358 @@
+"""Pins for the CPU oracle: closed forms, a hand-worked example, brute force and invariants.
+
+None of these re-types the oracle's own loop.  Each pin fixes the answer by other means: a value
+worked by hand, a closed form of a special case, the explicit product of per-token transition
+matrices, or an identity the rule must satisfy.  ``test_pins_catch_planted_mistakes`` plants typical
+mistakes in a copy of the oracle's C source and shows that every one of them fails some pin.
+"""
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------------------------
+# input helpers (plain random draws; nothing here evaluates the rule)
+
+def rand_inputs(rng, B=1, T=16, Hk=1, Hv=1, dk=8, dv=8, init=True, gscale=1.0):
+    q = rng.standard_normal((B, T, Hk, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((B, T, Hk, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, Hv, dv))
+    g = -gscale * rng.uniform(0.0, 1.0, (B, T, Hv))
+    beta = rng.uniform(0.05, 0.95, (B, T, Hv))
+    s0 = rng.standard_normal((B, Hv, dk, dv)) if init else None
+    return q, k, v, g, beta, s0
+
+
+def rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(1e-300, np.sqrt(np.mean(np.square(b)))))
+
+
+# ----------------------------------------------------------------------------------------------
+# pins, written against an oracle object so the mutation test can reuse them
+
+def pin_golden(orc):
+    d = json.load(open(os.path.join(GOLDEN, "hand_worked_two_tokens.json")))
+    x = d["inputs"]
+    q = np.array(x["q"])[None, :, None, :]
+    k = np.array(x["k"])[None, :, None, :]
+    v = np.array(x["v"])[None, :, None, :]
+    g = np.array(x["g"])[None, :, None]
+    beta = np.array(x["beta"])[None, :, None]
+    s0 = np.array(x["initial_state"])[None, None]
+    o, fs = orc.forward(q, k, v, g, beta, s0)
+    tol = d["tolerance"]
+    assert np.allclose(o[0, :, 0, :], np.array(d["expected"]["o"]), atol=tol, rtol=0)
+    assert np.allclose(fs[0, 0], np.array(d["expected"]["final_state"]), atol=tol, rtol=0)
+
+
+def pin_pure_decay(orc):
+    """beta = 0: nothing is written, S_t = exp(G_t) S0 and o_t = exp(G_t) S0^T q_t."""
+    rng = np.random.default_rng(1)
+    q, k, v, g, beta, s0 = rand_inputs(rng, T=12, dk=6, dv=5)
+    beta[:] = 0.0
+    o, fs = orc.forward(q, k, v, g, beta, s0)
+    G = np.cumsum(g[0, :, 0])
+    expect_o = np.exp(G)[:, None] * (q[0, :, 0, :] @ s0[0, 0])
+    assert np.allclose(o[0, :, 0, :], expect_o, atol=1e-12)
+    assert np.allclose(fs[0, 0], np.exp(G[-1]) * s0[0, 0], atol=1e-12)
+
+
+def pin_retrieval_overwrite(orc):
+    """g = 0, beta = 1, orthonormal keys, S0 = 0: the state stores each (key, value) pair exactly;
+    a query equal to a stored key returns its value; writing a key again keeps only the later value."""
+    rng = np.random.default_rng(2)
+    dk, dv = 8, 5
+    basis, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = basis.T  # orthonormal rows
+    order = [0, 3, 5, 3, 7]  # key 3 is written twice
+    T = len(order)
+    k = keys[order][None, :, None, :]
+    v = rng.standard_normal((1, T, 1, dv))
+    q = keys[[0, 0, 5, 3, 3]][None, :, None, :]
+    g = np.zeros((1, T, 1))
+    beta = np.ones((1, T, 1))
+    o, fs = orc.forward(q, k, v, g, beta, None)
+    S = fs[0, 0]
+    assert np.allclose(keys[0] @ S, v[0, 0, 0], atol=1e-12)
+    assert np.allclose(keys[5] @ S, v[0, 2, 0], atol=1e-12)
+    assert np.allclose(keys[3] @ S, v[0, 3, 0], atol=1e-12)  # the later write wins
+    assert np.allclose(keys[7] @ S, v[0, 4, 0], atol=1e-12)
+    assert np.allclose(keys[1] @ S, 0.0, atol=1e-12)         # never written
+    assert np.allclose(o[0, 0, 0], v[0, 0, 0], atol=1e-12)   # read-out includes the current token
+    assert np.allclose(o[0, 1, 0], v[0, 0, 0], atol=1e-12)
+    assert np.allclose(o[0, 2, 0], v[0, 2, 0], atol=1e-12)
+    assert np.allclose(o[0, 3, 0], v[0, 3, 0], atol=1e-12)   # overwritten on this very token
+    assert np.allclose(o[0, 4, 0], v[0, 3, 0], atol=1e-12)
+    # S equals the sum of outer products of the surviving pairs
+    expect = np.outer(keys[0], v[0, 0, 0]) + np.outer(keys[5], v[0, 2, 0]) + \
+        np.outer(keys[3], v[0, 3, 0]) + np.outer(keys[7], v[0, 4, 0])
+    assert np.allclose(S, expect, atol=1e-12)
+
+
+def pin_single_direction(orc):
+    """k_t = e_0 for all t: row 0 of S follows the scalar EMA s <- e^g (1 - beta) s + beta v,
+    every other row only decays by e^(sum g); o_t = S_t^T q_t reads those rows."""
+    rng = np.random.default_rng(3)
+    T, dk, dv = 10, 4, 3
+    q, k, v, g, beta, s0 = rand_inputs(rng, T=T, dk=dk, dv=dv)
+    k[:] = 0.0
+    k[..., 0] = 1.0
+    o, fs = orc.forward(q, k, v, g, beta, s0)
+    s = s0[0, 0].copy()
+    for t in range(T):
+        a, b = np.exp(g[0, t, 0]), beta[0, t, 0]
+        s[0] = a * (1 - b) * s[0] + b * v[0, t, 0]
+        s[1:] = a * s[1:]
+        assert np.allclose(o[0, t, 0], q[0, t, 0] @ s, atol=1e-12)
+    assert np.allclose(fs[0, 0], s, atol=1e-12)
+
+
+def pin_brute_force(orc):
+    """T <= 8: S_T = A_T...A_1 S0 + sum_j A_T...A_{j+1} beta_j k_j v_j^T with the explicit dk x dk
+    transitions A_t = e^{g_t} (I - beta_t k_t k_t^T); o_t from the same unrolled products."""
+    rng = np.random.default_rng(4)
+    for T in (1, 2, 5, 8):
+        dk, dv = 5, 4
+        q, k, v, g, beta, s0 = rand_inputs(rng, T=T, dk=dk, dv=dv, gscale=2.0)
+        o, fs = orc.forward(q, k, v, g, beta, s0)
+        A = [np.exp(g[0, t, 0]) * (np.eye(dk) - beta[0, t, 0] * np.outer(k[0, t, 0], k[0, t, 0]))
+             for t in range(T)]
+        Bt = [beta[0, t, 0] * np.outer(k[0, t, 0], v[0, t, 0]) for t in range(T)]
+
+        def prod(lo, hi):  # A_hi ... A_lo (inclusive, 0-based), identity if empty
+            P = np.eye(dk)
+            for t in range(lo, hi + 1):
+                P = A[t] @ P
+            return P
+
+        for t in range(T):
+            St = prod(0, t) @ s0[0, 0] + sum(prod(j + 1, t) @ Bt[j] for j in range(t + 1))
+            assert np.allclose(o[0, t, 0], St.T @ q[0, t, 0], atol=1e-12)
+        assert np.allclose(fs[0, 0], St, atol=1e-12)
+
+
+def pin_split_and_carry(orc):
+    """Running T1 tokens, then T2 tokens from the carried state, equals running T1+T2 at once
+    (the jsqmd.com article's segment loop, §2.2)."""
+    rng = np.random.default_rng(5)
+    q, k, v, g, beta, s0 = rand_inputs(rng, B=2, T=23, Hk=2, Hv=4, dk=6, dv=7)
+    o, fs = orc.forward(q, k, v, g, beta, s0)
+    T1 = 9
+    o1, s1 = orc.forward(q[:, :T1], k[:, :T1], v[:, :T1], g[:, :T1], beta[:, :T1], s0)
+    o2, s2 = orc.forward(q[:, T1:], k[:, T1:], v[:, T1:], g[:, T1:], beta[:, T1:], s1)
+    assert np.allclose(np.concatenate([o1, o2], axis=1), o, atol=1e-12)
+    assert np.allclose(s2, fs, atol=1e-12)
+
+
+def pin_varlen_is_separate(orc):
+    """Packed sequences (cu_seqlens) give the same results as separate calls; a zero-length sequence
+    returns its initial state."""
+    rng = np.random.default_rng(6)
+    lens = [5, 0, 11, 1, 7]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, k, v, g, beta, _ = rand_inputs(rng, T=T, Hk=1, Hv=2, dk=4, dv=3)
+    s0 = rng.standard_normal((len(lens), 2, 4, 3))
+    o, fs = orc.forward(q, k, v, g, beta, s0, cu_seqlens=cu)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        if b == a:
+            assert np.array_equal(fs[n], s0[n])
+            continue
+        on, sn = orc.forward(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], beta[:, a:b], s0[n:n + 1])
+        assert np.allclose(o[:, a:b], on, atol=1e-12)
+        assert np.allclose(fs[n], sn[0], atol=1e-12)
+
+
+def pin_padding_neutral(orc):
+    """Tokens with g = 0 and beta = 0 leave the state exactly unchanged."""
+    rng = np.random.default_rng(7)
+    q, k, v, g, beta, s0 = rand_inputs(rng, T=9, dk=5, dv=4)
+    _, fs = orc.forward(q, k, v, g, beta, s0)
+    q2, k2, v2, _, _, _ = rand_inputs(rng, T=6, dk=5, dv=4)
+    cat = lambda a, b: np.concatenate([a, b], axis=1)  # noqa: E731
+    _, fs2 = orc.forward(cat(q, q2), cat(k, k2), cat(v, v2), cat(g, np.zeros((1, 6, 1))),
+                         cat(beta, np.zeros((1, 6, 1))), s0)
+    assert np.array_equal(fs2, fs)
+
+
+def pin_linearity(orc):
+    """For fixed q, k, g, beta the map (S0, V) -> (o, S_T) is linear."""
+    rng = np.random.default_rng(8)
+    q, k, v1, g, beta, sa = rand_inputs(rng, T=14, Hk=1, Hv=2, dk=5, dv=4)
+    v2 = rng.standard_normal(v1.shape)
+    sb = rng.standard_normal(sa.shape)
+    a, b = 0.7, -1.3
+    o1, f1 = orc.forward(q, k, v1, g, beta, sa)
+    o2, f2 = orc.forward(q, k, v2, g, beta, sb)
+    o3, f3 = orc.forward(q, k, a * v1 + b * v2, g, beta, a * sa + b * sb)
+    assert np.allclose(o3, a * o1 + b * o2, atol=1e-11)
+    assert np.allclose(f3, a * f1 + b * f2, atol=1e-11)
+
+
+def pin_norm_bound(orc):
+    """With |k| = 1 and beta in [0,1], (I - beta k k^T) is a contraction, so
+    ||S_t||_2 <= e^{g_t} ||S_{t-1}||_2 + beta_t ||v_t||; checked along every prefix."""
+    rng = np.random.default_rng(9)
+    T = 20
+    q, k, v, g, beta, s0 = rand_inputs(rng, T=T, dk=6, dv=6)
+    prev = np.linalg.norm(s0[0, 0], 2)
+    for t in range(1, T + 1):
+        _, fs = orc.forward(q[:, :t], k[:, :t], v[:, :t], g[:, :t], beta[:, :t], s0)
+        cur = np.linalg.norm(fs[0, 0], 2)
+        assert cur <= np.exp(g[0, t - 1, 0]) * prev + beta[0, t - 1, 0] * np.linalg.norm(v[0, t - 1, 0]) + 1e-12
+        prev = cur
+
+
+def pin_head_grouping(orc):
+    """v-head h reads q/k head h // (Hv/Hk): a grouped call equals per-v-head calls that are handed
+    that q/k head explicitly."""
+    rng = np.random.default_rng(10)
+    Hk, Hv = 2, 6
+    q, k, v, g, beta, s0 = rand_inputs(rng, T=7, Hk=Hk, Hv=Hv, dk=4, dv=3)
+    o, fs = orc.forward(q, k, v, g, beta, s0)
+    for h in range(Hv):
+        kh = h // (Hv // Hk)
+        oh, sh = orc.forward(q[:, :, kh:kh + 1], k[:, :, kh:kh + 1], v[:, :, h:h + 1],
+                             g[:, :, h:h + 1], beta[:, :, h:h + 1], s0[:, h:h + 1])
+        assert np.allclose(o[:, :, h:h + 1], oh, atol=1e-12)
+        assert np.allclose(fs[:, h:h + 1], sh, atol=1e-12)
+
+
+def pin_chunked_form(orc):
+    """The chunk-parallel (WY/UT) form reaches the token-by-token result for every chunk length,
+    including a ragged last chunk, with and without an initial state."""
+    rng = np.random.default_rng(11)
+    for T, C, init, gscale in ((37, 1, True, 1.0), (37, 5, True, 1.0), (64, 16, False, 4.0),
+                               (100, 64, True, 6.0), (37, 37, True, 0.01), (130, 64, True, 0.0)):
+        q, k, v, g, beta, s0 = rand_inputs(rng, T=T, Hk=1, Hv=2, dk=8, dv=6, init=init, gscale=gscale)
+        o, fs = orc.forward(q, k, v, g, beta, s0)
+        oc, fc = O.chunked(q[0], k[0], v[0], g[0], beta[0], None if s0 is None else s0[0], C)
+        assert rel(oc, o[0]) < 1e-11, (T, C)
+        assert rel(fc, fs[0]) < 1e-11, (T, C)
+
+
+PINS = [pin_golden, pin_pure_decay, pin_retrieval_overwrite, pin_single_direction, pin_brute_force,
+        pin_split_and_carry, pin_varlen_is_separate, pin_padding_neutral, pin_linearity,
+        pin_norm_bound, pin_head_grouping, pin_chunked_form]
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return O.Oracle()
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(orc, pin):
+    pin(orc)
+
+
+# ----------------------------------------------------------------------------------------------
+# gates
+
+def test_gates_closed_forms():
+    g, beta = O.gates(np.zeros(3), np.zeros(3), np.zeros(3), np.zeros(3))
+    assert np.allclose(beta, 0.5, atol=0, rtol=1e-15)
+    assert np.allclose(g, -np.log(2.0), atol=0, rtol=1e-15)   # softplus(0) = ln 2, exp(A_log=0) = 1
+    # A_log = log 3, a = large: softplus(a) -> a, so g -> -3a
+    g, _ = O.gates(np.array([40.0]), np.array([0.0]), np.log(np.array([3.0])), np.zeros(1))
+    assert np.isclose(g[0], -120.0, rtol=1e-15)
+    # a very negative: softplus(a) ~ e^a (tiny but positive), g stays < 0
+    g, _ = O.gates(np.array([-30.0]), np.array([0.0]), np.zeros(1), np.zeros(1))
+    assert g[0] < 0 and np.isclose(g[0], -np.exp(-30.0), rtol=1e-12)
+    # beta = sigmoid(b): symmetric, limits 0 and 1
+    _, bb = O.gates(np.zeros(3), np.array([-50.0, 2.0, 50.0]), np.zeros(3), np.zeros(3))
+    assert bb[0] < 1e-20 and np.isclose(bb[1], 1 / (1 + np.exp(-2.0))) and bb[2] == 1.0
+    # dt_bias shifts a
+    ga, _ = O.gates(np.array([0.3]), np.zeros(1), np.array([0.5]), np.array([0.2]))
+    gb, _ = O.gates(np.array([0.5]), np.zeros(1), np.array([0.5]), np.zeros(1))
+    assert np.isclose(ga[0], gb[0], rtol=1e-15)
+
+
+def test_synth_gates_follow_oracle_gates():
+    """The workload generator's fp32 g and beta agree with the oracle's fp64 gate formula."""
+    from gated_deltanet_delta_amd import synth
+    wl = synth.WORKLOADS["prefill"]
+    x = synth.make(wl, T=64)
+    raw = x["raw"]
+    g, beta = O.gates(raw["a"], raw["b"], raw["A_log"], raw["dt_bias"])
+    assert np.max(np.abs(raw["g"] - g) / np.abs(g)) < 1e-6
+    assert np.max(np.abs(raw["beta"] - beta)) < 1e-6
+    assert np.all(raw["g"] < 0)
+
+
+# ----------------------------------------------------------------------------------------------
+# sampling and threading do not change results
+
+def test_unit_mask_and_threads(orc):
+    rng = np.random.default_rng(12)
+    q, k, v, g, beta, s0 = rand_inputs(rng, B=3, T=11, Hk=2, Hv=4, dk=5, dv=3)
+    o, fs = orc.forward(q, k, v, g, beta, s0, threads=1)
+    mask = np.zeros((3, 4), bool)
+    mask[1, 2] = mask[2, 0] = True
+    om, fm = orc.forward(q, k, v, g, beta, s0, unit_mask=mask, threads=3)
+    for n, h in zip(*np.nonzero(mask)):
+        assert np.array_equal(om[n, :, h], o[n, :, h])
+        assert np.array_equal(fm[n, h], fs[n, h])
+    assert np.isnan(om[0, :, 0]).all()
+
+
+def test_rejects_bad_arguments(orc):
+    rng = np.random.default_rng(13)
+    q, k, v, g, beta, s0 = rand_inputs(rng, T=4, Hk=2, Hv=3)
+    with pytest.raises(ValueError):
+        orc.forward(q, k, v, g, beta, None)  # Hv % Hk != 0
+    q, k, v, g, beta, s0 = rand_inputs(rng, T=4)
+    with pytest.raises(ValueError):
+        orc.forward(q, k, v, g, beta, None, cu_seqlens=np.array([0, 3, 2], np.int32))
+
+
+# ----------------------------------------------------------------------------------------------
+# the pins are strong enough: planted mistakes in the C oracle each fail at least one of them
+
+MUTANTS = {
+    "no_decay": ("for (size_t e = 0; e < SS; ++e) S[e] *= a;", ";"),
+    "decay_sign": ("const double a = exp(gt);", "const double a = exp(-gt);"),
+    "delta_sign": ("u[j] = bt * (vt[j] - p[j]);", "u[j] = bt * (vt[j] + p[j]);"),
+    "no_beta": ("u[j] = bt * (vt[j] - p[j]);", "u[j] = (vt[j] - p[j]);"),
+    "predict_with_q": ("p[j] += Si[j] * ki;", "p[j] += Si[j] * qt[i];"),
+    "correct_with_q": ("Si[j] += ki * u[j];", "Si[j] += qt[i] * u[j];"),
+    "read_transposed": ("ot[j] += Si[j] * qi;", "ot[j] += S[(size_t)j * dv + i] * qi;"),
+    "read_with_k": ("ot[j] += Si[j] * qi;", "ot[j] += Si[j] * kt[i];"),
+    "interleaved_heads": ("const int kh = h / (Hv / Hk);", "const int kh = h % Hk;"),
+    "ignore_initial_state": ("if (s0) memcpy", "if (0) memcpy"),
+    "gate_of_head0": ("const double gt = g[row * Hv + h];", "const double gt = g[row * Hv];"),
+    "drop_last_token": ("const int t1 = cu_seqlens ? cu_seqlens[n + 1] : T;",
+                        "const int t1 = cu_seqlens ? cu_seqlens[n + 1] : T - 1;"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistakes(tmp_path, name):
+    src = open(O.SOURCE).read()
+    find, repl = MUTANTS[name]
+    assert src.count(find) == 1, f"mutation site for {name} no longer in the oracle source"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(find, repl))
+    lib = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-std=c99", str(path), "-o", lib, "-lm"],
+                   check=True)
+    mutant = O.Oracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
