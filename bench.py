@@ -1,0 +1,194 @@
+"""Benchmark: prefill tokens/s and decode state GB/s of the gated delta rule on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The timed step is one gdn_chunk_fwd call over the Qwen3-Next-shaped prefill
+workload (B=1, T=4096, 16 q/k heads, 32 v heads, head dim 128, bf16 inputs, fp32 state and output),
+inputs resident in HBM.  ``value`` is prefill tokens/s over K back-to-back steps.  The same run also
+times the decode workload (256 sequences, 2 MiB fp32 state each, D one-token steps of
+gdn_recurrent_step) and reports its state GB/s under ``decode``.
+
+Roofline figures use algorithmic work only:
+  prefill, per (token, v-head): bytes  = q,k (bf16, shared by Hv/Hk v-heads) + v (bf16) + g, beta
+                                         (bf16) + o (fp32) = 1028 B at d = 128, G = 2;
+                                         plus the fp32 initial/final state per (sequence, v-head).
+                                 flops = 6 dk dv + C (3 dk + 2 dv)  (C = 64; the three d x d
+                                         contractions per token and the lower-triangular intra-chunk
+                                         products, the triangular solve not counted).
+  decode, per step:              bytes = state read + write (2 B Hv dk dv 4) + q, k, v, g, beta, o.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MI355X_HBM_GBS = 8000.0        # HBM3E peak, GB/s
+MI355X_BF16_TFLOPS = 2500.0    # dense bf16 matrix peak, TFLOP/s
+CHUNK = 64
+
+METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next shape, 1 GPU"
+
+
+def prefill_algorithmic(wl, T: int, B: int, N: int, init_state: bool):
+    el = 2 if str(wl.dtype).endswith("bfloat16") else 4
+    gel = 2 if str(wl.gate_dtype).endswith("bfloat16") else 4
+    G = wl.Hv // wl.Hk
+    per_tok_head = (2 * wl.dk * el) / G + wl.dv * el + 2 * gel + wl.dv * 4
+    state = wl.dk * wl.dv * 4 * (2 if init_state else 1)
+    nbytes = B * T * wl.Hv * per_tok_head + N * wl.Hv * state
+    flops = B * T * wl.Hv * (6 * wl.dk * wl.dv + CHUNK * (3 * wl.dk + 2 * wl.dv))
+    return nbytes, flops, per_tok_head
+
+
+def decode_algorithmic(wl):
+    el = 2
+    gel = 4
+    state = 2 * wl.B * wl.Hv * wl.dk * wl.dv * 4
+    io = wl.B * (2 * wl.Hk * wl.dk * el + wl.Hv * wl.dv * el + 2 * wl.Hv * gel + wl.Hv * wl.dv * 4)
+    return state, state + io
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the gated delta "
+              "rule path here is a single-GPU build)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from gated_deltanet_delta_amd import gdn_chunk_fwd, gdn_recurrent_step, synth, workspace_size
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # ---------------- prefill -----------------------------------------------------------------
+    wl = synth.WORKLOADS["prefill"]
+    x = synth.make(wl)
+    d = {key: (None if x[key] is None else x[key].to(dev).contiguous())
+         for key in ("q", "k", "v", "g", "beta", "initial_state", "cu_seqlens")}
+    B, T = wl.B, wl.T
+    N = B
+    o = torch.empty((B, T, wl.Hv, wl.dv), dtype=torch.float32, device=dev)
+    fs = torch.empty((N, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+    ws_bytes = workspace_size(B, T, wl.Hk, wl.Hv, wl.dk, wl.dv, N, wl.dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def prefill_step():
+        gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], None,
+                      o=o, final_state=fs, workspace=ws)
+
+    for _ in range(args.warmup):
+        prefill_step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        prefill_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    ms_events = ev0.elapsed_time(ev1) / args.steps
+    ms_wall = (wall1 - wall0) * 1e3 / args.steps
+    tokens = B * T
+    value = tokens / (ms_wall / 1e3)
+    nbytes, flops, per_tok_head = prefill_algorithmic(wl, T, B, N, wl.init_state)
+    achieved_gbs = nbytes / (ms_events / 1e3) / 1e9
+    useful_tflops = flops / (ms_events / 1e3) / 1e12
+
+    # ---------------- decode ------------------------------------------------------------------
+    wd = synth.WORKLOADS["decode"]
+    x0 = synth.make(wd)
+    A_log = x0["raw"]["A_log"]
+    nd = args.decode_steps
+    steps = [x0] + [synth.decode_step(wd, s, A_log) for s in range(1, nd)]
+    dsteps = [{key: s[key].to(dev).contiguous() for key in ("q", "k", "v", "g", "beta")} for s in steps]
+    state = x0["initial_state"].to(dev).contiguous()
+    od = torch.empty((wd.B, 1, wd.Hv, wd.dv), dtype=torch.float32, device=dev)
+
+    def decode_pass():
+        for s in dsteps:
+            gdn_recurrent_step(s["q"], s["k"], s["v"], s["g"], s["beta"], state, o=od)
+
+    decode_pass()  # warm-up pass (advances the state; values stay bounded by the decay)
+    torch.cuda.synchronize()
+    ev0.record()
+    decode_pass()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_decode = ev0.elapsed_time(ev1) / nd
+    state_bytes, total_bytes = decode_algorithmic(wd)
+    state_gbs = state_bytes / (ms_decode / 1e3) / 1e9
+    total_gbs = total_bytes / (ms_decode / 1e3) / 1e9
+
+    # ---------------- CPU baseline: the oracle on the host cores --------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        f = synth.to_f64
+        arrs = [f(x[key]) for key in ("q", "k", "v", "g", "beta")]
+        threads = O.default_threads()
+        c0 = time.perf_counter()
+        O.forward(*arrs, None, None, threads=threads)
+        c1 = time.perf_counter()
+        cpu = {"value": round(tokens / (c1 - c0), 1), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the whole prefill workload (T={T}, {wl.Hv} v-heads), fp64 token-by-token, "
+                         f"{c1 - c0:.2f} s"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill B={B} T={T} Hk={wl.Hk} Hv={wl.Hv} dk=dv={wl.dk} bf16 in, fp32 "
+                               f"state/out, zero initial state",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": MI355X_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / MI355X_HBM_GBS, 4), "traffic": None,
+                     "kernel": "gdn_chunk_fwd (all kernels of one call)",
+                     "ms_per_launch_events": round(ms_events, 5),
+                     "algorithmic_bytes_per_launch": int(nbytes),
+                     "bytes_per_token_vhead": per_tok_head,
+                     "useful_tflops": round(useful_tflops, 2),
+                     "mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+        "decode": {"metric": "decode state GB/s", "value": round(state_gbs, 1), "unit": "GB/s",
+                   "workload": f"decode B={wd.B} Hk={wd.Hk} Hv={wd.Hv} dk=dv={wd.dk}, {nd} one-token "
+                               f"steps, fp32 state {wd.B * wd.Hv * wd.dk * wd.dv * 4 / 2**20:.0f} MiB",
+                   "ms_per_step": round(ms_decode, 5),
+                   "roofline": {"bound": "hbm", "achieved": round(total_gbs, 1), "peak": MI355X_HBM_GBS,
+                                "unit": "GB/s", "frac": round(total_gbs / MI355X_HBM_GBS, 4),
+                                "traffic": None, "kernel": "recurrent_kernel<128,128,bf16,f32>",
+                                "algorithmic_bytes_per_launch": int(total_bytes)}},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,1 +1,11 @@
-"""Gated delta rule on AMD Instinct MI355X (gfx950): a C-ABI HIP library and its Python binding."""
+"""Gated delta rule on AMD Instinct MI355X (gfx950): a C-ABI HIP library (libgdn.so) and its
+Python binding.
+
+    from gated_deltanet_delta_amd import gdn_chunk_fwd, gdn_recurrent_step
+
+The binding only marshals torch tensors into the C ABI declared in include/gdn.h; the library must
+be built (``python -m gated_deltanet_delta_amd.build``) and there is no CPU fallback.
+"""
+from .api import (chunk_gated_delta_rule, gdn_chunk_fwd, gdn_recurrent_step,  # noqa: F401
+                  recurrent_gated_delta_rule, workspace_size)
+from ._lib import GdnError  # noqa: F401

@@ -1,0 +1,56 @@
+"""ctypes declarations of libgdn's C ABI (include/gdn.h).  Loading fails loudly if the library
+has not been built: there is no fallback path."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+GDN_SUCCESS = 0
+GDN_ERROR_INVALID_VALUE = 1
+GDN_ERROR_NOT_SUPPORTED = 2
+GDN_ERROR_WORKSPACE = 3
+GDN_ERROR_LAUNCH_FAILURE = 4
+
+GDN_F32 = 0
+GDN_BF16 = 1
+
+EXPORTED = ("gdn_status_string", "gdn_version", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
+            "gdn_recurrent_step")
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(
+            f"libgdn.so is not built ({LIBRARY} missing); build it with "
+            "`python -m gated_deltanet_delta_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIBRARY)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [i32]
+    lib.gdn_version.restype = i32
+    lib.gdn_version.argtypes = []
+    lib.gdn_chunk_fwd_workspace_size.restype = sz
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [i32] * 7 + [i32]
+    lib.gdn_chunk_fwd.restype = i32
+    lib.gdn_chunk_fwd.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp, vp, sz, vp]
+    lib.gdn_recurrent_step.restype = i32
+    lib.gdn_recurrent_step.argtypes = [vp] * 6 + [i32] * 6 + [i32, i32] + [vp, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gdn_status_string(int(status)).decode()

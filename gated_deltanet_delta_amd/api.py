@@ -1,0 +1,141 @@
+"""Python binding of libgdn: argument marshalling only.
+
+Every function here checks that the torch tensors it is handed have the shapes, dtypes, devices and
+layouts the C ABI expects (the C library sees only pointers), allocates outputs and workspace with
+torch when the caller does not pass them, and calls the library on torch's current stream.  All
+arithmetic runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.GDN_F32, torch.bfloat16: _lib.GDN_BF16}
+
+
+def _code(t: torch.Tensor, what: str) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"{what}: dtype {t.dtype} not supported (bfloat16 or float32)") from None
+
+
+def _check(t: torch.Tensor, shape, what: str, device: torch.device, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{what}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_size(B: int, T: int, Hk: int, Hv: int, dk: int, dv: int, N: int,
+                   qkv_dtype: torch.dtype) -> int:
+    """Bytes of workspace gdn_chunk_fwd needs (0 if none)."""
+    return int(_lib.load().gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, _DTYPES[qkv_dtype]))
+
+
+def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, *, o: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunk-parallel prefill.  q,k [B,T,Hk,dk]; v [B,T,Hv,dv]; g,beta [B,T,Hv];
+    initial_state [N,Hv,dk,dv] fp32 or None; cu_seqlens int32 [N+1] (B == 1) or None.
+    Returns (o [B,T,Hv,dv] fp32, final_state [N,Hv,dk,dv] fp32)."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_chunk_fwd runs on a GPU; tensors must be on a cuda device")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(g, (B, T, Hv), "g", dev)
+    _check(beta, (B, T, Hv), "beta", dev, g.dtype)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
+    if initial_state is not None:
+        _check(initial_state, (N, Hv, dk, dv), "initial_state", dev, torch.float32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
+    if final_state is None:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    _check(final_state, (N, Hv, dk, dv), "final_state", dev, torch.float32)
+    qkv, gate = _code(q, "q"), _code(g, "g")
+    ws_bytes = int(lib.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    st = lib.gdn_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+        B, T, Hk, Hv, dk, dv, N, qkv, gate, _ptr(o), _ptr(final_state), _ptr(workspace),
+        ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
+        _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                       beta: torch.Tensor, state: torch.Tensor, *,
+                       o: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode step(s) against a cached state, updated in place.  q,k [B,T,Hk,dk]; v [B,T,Hv,dv];
+    g,beta [B,T,Hv]; state [B,Hv,dk,dv] fp32.  Returns (o [B,T,Hv,dv] fp32, state)."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_recurrent_step runs on a GPU; tensors must be on a cuda device")
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(g, (B, T, Hv), "g", dev)
+    _check(beta, (B, T, Hv), "beta", dev, g.dtype)
+    _check(state, (B, Hv, dk, dv), "state", dev, torch.float32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
+    st = lib.gdn_recurrent_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, T, Hk, Hv, dk, dv,
+        _code(q, "q"), _code(g, "g"), _ptr(o), _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_recurrent_step")
+    return o, state
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None):
+    """The prefill entry point under its model-side name; see gdn_chunk_fwd."""
+    return gdn_chunk_fwd(q, k, v, g, beta, initial_state, cu_seqlens)
+
+
+def recurrent_gated_delta_rule(q, k, v, g, beta, initial_state):
+    """The decode entry point under its model-side name: advances ``initial_state`` in place and
+    returns (o, the same state tensor); see gdn_recurrent_step."""
+    return gdn_recurrent_step(q, k, v, g, beta, initial_state)

@@ -1,0 +1,43 @@
+// common.h -- small device helpers shared by the libgdn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kWave = 64;
+
+// bf16 values travel as raw 16-bit patterns; widening to fp32 is exact (shift into the top half).
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+
+// Row/offset helpers with 64-bit arithmetic (packed sequences reach ~1e9 elements).
+__device__ __forceinline__ size_t idx3(size_t a, size_t b, size_t B_, size_t c, size_t C_) {
+    return (a * B_ + b) * C_ + c;
+}
+
+// Sequence n's token range [t0, t1) inside batch row `row`, clamped to [0, T] so that a malformed
+// cu_seqlens array can only produce wrong numbers, never an access outside the buffers.
+__device__ __forceinline__ void sequence_range(const int32_t* cu_seqlens, int n, int T, int& row,
+                                               int& t0, int& t1) {
+    if (cu_seqlens) {
+        int a = cu_seqlens[n], b = cu_seqlens[n + 1];
+        a = a < 0 ? 0 : (a > T ? T : a);
+        b = b < a ? a : (b > T ? T : b);
+        row = 0;
+        t0 = a;
+        t1 = b;
+    } else {
+        row = n;
+        t0 = 0;
+        t1 = T;
+    }
+}
+
+}  // namespace gdn

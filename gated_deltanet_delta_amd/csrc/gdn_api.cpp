@@ -1,0 +1,114 @@
+// gdn_api.cpp -- the C ABI of libgdn: argument checks, workspace sizing and kernel dispatch.
+//
+// Every check happens on the host before anything is enqueued, so a rejected call has no effect
+// on device memory.  Device memory is never read here (no synchronisation on the call path).
+
+#include <stdint.h>
+
+#include "gdn.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
+
+size_t dtype_bytes(gdn_dtype t) { return t == GDN_BF16 ? 2 : 4; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+bool dtype_ok(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
+
+bool use_mfma(int dk, int dv, gdn_dtype qkv) { return gdn::chunk_mfma_supported(dk, dv, qkv); }
+
+// Largest element count any tensor of a call may have (indices inside kernels are 64-bit, but
+// per-dimension arithmetic on ints must not overflow).
+bool sizes_fit(long long B, long long T, long long H, long long d) {
+    const long long lim = (1LL << 40);
+    return B * T < (1LL << 31) && B * T * H * d < lim;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status status) {
+    switch (status) {
+        case GDN_SUCCESS: return "GDN_SUCCESS";
+        case GDN_ERROR_INVALID_VALUE: return "GDN_ERROR_INVALID_VALUE";
+        case GDN_ERROR_NOT_SUPPORTED: return "GDN_ERROR_NOT_SUPPORTED";
+        case GDN_ERROR_WORKSPACE: return "GDN_ERROR_WORKSPACE";
+        case GDN_ERROR_LAUNCH_FAILURE: return "GDN_ERROR_LAUNCH_FAILURE";
+    }
+    return "GDN_ERROR_UNKNOWN";
+}
+
+int gdn_version(void) { return 100; }
+
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                    gdn_dtype qkv_dtype) {
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return 0;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || !dtype_ok(qkv_dtype)) return 0;
+    if (!use_mfma(dk, dv, qkv_dtype)) return 0;
+    return gdn::chunk_mfma_workspace_size(B, T, Hv, dk, dv, N);
+}
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                         int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                         gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!final_state) return GDN_ERROR_INVALID_VALUE;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERROR_INVALID_VALUE;
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
+    if (!dtype_ok(qkv_dtype) || !dtype_ok(gate_dtype)) return GDN_ERROR_INVALID_VALUE;
+    if (cu_seqlens ? B != 1 : N != B) return GDN_ERROR_INVALID_VALUE;
+    if (dk < 1 || dv < 1) return GDN_ERROR_INVALID_VALUE;
+    if (!sizes_fit(B, T, Hv, dv > dk ? dv : dk) || !sizes_fit(N, 1, Hv, (long long)dk * dv))
+        return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {q, k, v, (const void*)initial_state, (const void*)o, (const void*)final_state})
+        if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {g, beta})
+        if (p && !aligned(p, dtype_bytes(gate_dtype))) return GDN_ERROR_INVALID_VALUE;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return GDN_ERROR_INVALID_VALUE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
+
+    const gdn::ChunkArgs a{q, k, v, g, beta, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+                           qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes,
+                           stream};
+    hipError_t e;
+    if (use_mfma(dk, dv, qkv_dtype)) {
+        const size_t need = gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype);
+        if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+            return GDN_ERROR_WORKSPACE;
+        e = gdn::launch_chunk_mfma(a);
+    } else {
+        e = gdn::launch_chunk_f32(a);
+    }
+    return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+}
+
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, float* state, int B, int T, int Hk, int Hv,
+                              int dk, int dv, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
+                              hipStream_t stream) {
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERROR_INVALID_VALUE;
+    if (B < 1 || T < 1 || Hk < 1 || Hv < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
+    if (!dtype_ok(qkv_dtype) || !dtype_ok(gate_dtype)) return GDN_ERROR_INVALID_VALUE;
+    if (dk < 1 || dv < 1) return GDN_ERROR_INVALID_VALUE;
+    if (!sizes_fit(B, T, Hv, dv > dk ? dv : dk) || !sizes_fit(B, 1, Hv, (long long)dk * dv))
+        return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {(const void*)state, (const void*)o})
+        if (!aligned16(p)) return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {q, k, v})
+        if (!aligned(p, dtype_bytes(qkv_dtype))) return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {g, beta})
+        if (!aligned(p, dtype_bytes(gate_dtype))) return GDN_ERROR_INVALID_VALUE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
+
+    const gdn::RecurrentArgs a{q, k, v, g, beta, state, B, T, Hk, Hv, dk, dv,
+                               qkv_dtype, gate_dtype, o, stream};
+    return gdn::launch_recurrent(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// launch.h -- host-side launchers behind the C ABI (one per kernel family).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* initial_state;
+    const int32_t* cu_seqlens;
+    int B, T, Hk, Hv, dk, dv, N;
+    gdn_dtype qkv_dtype, gate_dtype;
+    float* o;
+    float* final_state;
+    void* workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+};
+
+struct RecurrentArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    float* state;
+    int B, T, Hk, Hv, dk, dv;
+    gdn_dtype qkv_dtype, gate_dtype;
+    float* o;
+    hipStream_t stream;
+};
+
+// Token-serial kernel: the state stays in registers for all T tokens of a call.
+hipError_t launch_recurrent(const RecurrentArgs& a);
+
+// Chunked kernel with fp32 arithmetic throughout (used for fp32 inputs; no workspace).
+hipError_t launch_chunk_f32(const ChunkArgs& a);
+
+// Chunked kernels on bf16 matrix cores (bf16 inputs).
+bool chunk_mfma_supported(int dk, int dv, gdn_dtype qkv_dtype);
+size_t chunk_mfma_workspace_size(int B, int T, int Hv, int dk, int dv, int N);
+hipError_t launch_chunk_mfma(const ChunkArgs& a);
+
+}  // namespace gdn

@@ -1,0 +1,146 @@
+/*
+ * gdn.h -- C ABI of libgdn, the gated delta rule on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Per (sequence, v-head) the library keeps a dk x dv fp32 state S and, for each
+ * token t of the sequence in order, applies
+ *
+ *     S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,      o_t = S_t^T q_t
+ *
+ * i.e. decay the state, then correct it along the current key towards the current value with
+ * strength beta, then read it out with the query (no query scale; the read-out includes token t).
+ * This is the "delta rule state update and retrieval" of the Qwen3.5 Gated DeltaNet write-up
+ * (wanger-sjtu.github.io, flowchart and section "Core mechanism: Gated DeltaNet": the state is
+ * corrected along the current key instead of being accumulated), with the gates of the same
+ * flowchart and of the Qwen3-Next architecture write-up (intelliparadigm.com, section 2.2):
+ * beta = sigmoid(b) in (0,1) is the write strength and g = -exp(A_log) softplus(a + dt_bias) <= 0
+ * is the log-decay.  Callers compute g and beta; the library takes them as inputs.
+ *
+ * The two entry points are the two modes of the Qwen3-Next Gated DeltaNet article (jsqmd.com,
+ * section 2.2 "chunked parallel computation"): chunk_gated_delta_rule processes whole segments in
+ * parallel chunks and returns the state to carry into the next segment; recurrent_gated_delta_rule
+ * advances a cached state by one token at decode time.  The Qwen3.5 flowchart's "cache valid and
+ * L = 1" switch picks between them; here the caller picks.
+ *
+ * Conventions shared by every call:
+ *   - All tensor arguments are DEVICE pointers to contiguous row-major memory (innermost index
+ *     last).  States, outputs and (for gdn_chunk_fwd) q, k, v must be 16-byte aligned; every other
+ *     pointer needs only the alignment of its element type.  The caller owns every buffer; the
+ *     library never allocates, frees or retains a pointer after the call returns.
+ *   - q/k head sharing (grouped heads): v-head h reads q/k head h / (Hv / Hk) (v-heads 0..G-1 share
+ *     q/k head 0, and so on, G = Hv / Hk).
+ *   - Work is enqueued on `stream` and runs asynchronously; nothing synchronises.  A device fault
+ *     surfaces at the caller's next synchronisation.  Calls on different streams are independent.
+ *   - Arguments are checked on the host before anything is enqueued.  On any error the call
+ *     returns a non-zero status and writes nothing.  Device memory is never read for validation:
+ *     a cu_seqlens array that is not non-decreasing from 0 to T is a caller error with undefined
+ *     results (but every kernel still stays inside the buffers the shapes describe).
+ *   - NaN and Inf in inputs propagate to the outputs; they never stop a kernel.
+ *   - Inputs are expected to satisfy g <= 0 and 0 <= beta <= 1 (the gates' ranges); q and k are
+ *     used exactly as given (callers normalise them if their model does).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_SUCCESS = 0,
+    GDN_ERROR_INVALID_VALUE = 1,    /* a null required pointer, a bad size or a bad combination */
+    GDN_ERROR_NOT_SUPPORTED = 2,    /* valid, but a head size or dtype this build has no kernel for */
+    GDN_ERROR_WORKSPACE = 3,        /* workspace pointer null or smaller than the size query says */
+    GDN_ERROR_LAUNCH_FAILURE = 4    /* the HIP runtime refused a launch (hipGetLastError) */
+} gdn_status;
+
+typedef enum {
+    GDN_F32 = 0,                    /* IEEE binary32 */
+    GDN_BF16 = 1                    /* bfloat16 (upper half of binary32) */
+} gdn_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gdn_status_string(gdn_status status);
+
+/* Library version as an integer: major * 10000 + minor * 100 + patch. */
+int gdn_version(void);
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 if none).  Pure host
+ * arithmetic; never fails (returns 0 for sizes gdn_chunk_fwd would reject).
+ */
+size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                    gdn_dtype qkv_dtype);
+
+/*
+ * gdn_chunk_fwd -- chunk-parallel prefill (chunk_gated_delta_rule).
+ *
+ * Runs the rule above over every sequence and v-head and returns every token's output and every
+ * sequence's final state.  Internally each sequence is cut into 64-token chunks (the last one may
+ * be shorter); the result does not depend on the cut (up to rounding order).
+ *
+ * Inputs (device):
+ *   q, k           [B, T, Hk, dk]  dtype qkv_dtype
+ *   v              [B, T, Hv, dv]  dtype qkv_dtype
+ *   g, beta        [B, T, Hv]      dtype gate_dtype
+ *   initial_state  [N, Hv, dk, dv] fp32, or NULL for a zero initial state
+ *   cu_seqlens     NULL: N == B and sequence n is batch row n (T tokens each).
+ *                  Otherwise int32 [N+1] with B == 1: sequence n is tokens
+ *                  [cu_seqlens[n], cu_seqlens[n+1]) of the packed T axis; cu_seqlens[0] == 0,
+ *                  non-decreasing, cu_seqlens[N] == T.  Zero-length sequences are allowed (their
+ *                  final state equals their initial state).  No chunk spans two sequences.
+ *   (With T == 0 there are no tokens: q, k, v, g, beta and o may then be NULL.)
+ * Outputs (device):
+ *   o              [B, T, Hv, dv]  fp32; must not overlap any input
+ *   final_state    [N, Hv, dk, dv] fp32; may be the same pointer as initial_state (the state is
+ *                  then advanced in place), must not partially overlap it
+ * Workspace (device): at least gdn_chunk_fwd_workspace_size(...) bytes, 256-byte aligned; may be
+ *   NULL when that size is 0.  Its contents on entry do not matter; on return they are garbage.
+ *   Two calls in flight at once need two workspaces.
+ * Sizes: B >= 1, T >= 0, Hk >= 1, Hv >= 1 with Hv % Hk == 0, N >= 1; dk and dv each 64 or 128
+ *   (other sizes: GDN_ERROR_NOT_SUPPORTED).  qkv_dtype and gate_dtype are GDN_BF16 or GDN_F32.
+ * Precision: states and outputs are fp32 throughout.  bf16 inputs take the bf16 matrix-core path
+ *   (fp32 accumulation, products that feed the output split into two bf16 terms); fp32 inputs take
+ *   an fp32 path.
+ */
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                         const void* g, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                         gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                         float* o, float* final_state,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * gdn_recurrent_step -- decode against a cached state (recurrent_gated_delta_rule).
+ *
+ * Advances B independent cached states by T tokens each (T == 1 is the usual decode step),
+ * token by token, and writes each token's output.  The state is read once and written once per
+ * call, in place.
+ *
+ * Inputs (device):
+ *   q, k           [B, T, Hk, dk]  dtype qkv_dtype
+ *   v              [B, T, Hv, dv]  dtype qkv_dtype
+ *   g, beta        [B, T, Hv]      dtype gate_dtype
+ * In/out (device):
+ *   state          [B, Hv, dk, dv] fp32, updated in place
+ * Output (device):
+ *   o              [B, T, Hv, dv]  fp32; must not overlap any input or the state
+ * Sizes: B >= 1, T >= 1, Hk >= 1, Hv >= 1 with Hv % Hk == 0; dk and dv each 64 or 128.
+ */
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
+                              const void* g, const void* beta,
+                              float* state,
+                              int B, int T, int Hk, int Hv, int dk, int dv,
+                              gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                              float* o, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,118 @@
+"""Host-side tests of the C ABI: the library loads, exports every function include/gdn.h declares,
+and rejects bad arguments on the host before anything reaches a GPU.  No kernel runs here: every
+call below fails validation, which happens before the first HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_delta_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+F32, BF16 = _lib.GDN_F32, _lib.GDN_BF16
+INVALID, UNSUPPORTED, WORKSPACE = (_lib.GDN_ERROR_INVALID_VALUE, _lib.GDN_ERROR_NOT_SUPPORTED,
+                                   _lib.GDN_ERROR_WORKSPACE)
+P = 0x10000  # stand-in device address; never dereferenced because every call here is rejected
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in gdn.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    for code, name in [(0, "GDN_SUCCESS"), (1, "GDN_ERROR_INVALID_VALUE"), (2, "GDN_ERROR_NOT_SUPPORTED"),
+                       (3, "GDN_ERROR_WORKSPACE"), (4, "GDN_ERROR_LAUNCH_FAILURE")]:
+        assert _lib.status_string(code) == name
+    assert _lib.status_string(77) == "GDN_ERROR_UNKNOWN"
+    assert lib.gdn_version() >= 100
+
+
+def chunk(lib, q=P, k=P, v=P, g=P, beta=P, s0=None, cu=None, B=1, T=64, Hk=1, Hv=1, dk=64, dv=64,
+          N=1, qkv=F32, gate=F32, o=P, fs=P, ws=None, ws_bytes=0):
+    return lib.gdn_chunk_fwd(q, k, v, g, beta, s0, cu, B, T, Hk, Hv, dk, dv, N, qkv, gate, o, fs, ws,
+                             ctypes.c_size_t(ws_bytes), None)
+
+
+def rec(lib, q=P, k=P, v=P, g=P, beta=P, state=P, B=1, T=1, Hk=1, Hv=1, dk=64, dv=64, qkv=F32,
+        gate=F32, o=P):
+    return lib.gdn_recurrent_step(q, k, v, g, beta, state, B, T, Hk, Hv, dk, dv, qkv, gate, o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(g=None), INVALID), (dict(beta=None), INVALID), (dict(o=None), INVALID),
+    (dict(fs=None), INVALID), (dict(fs=None, T=0), INVALID),
+    (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(Hk=0), INVALID), (dict(Hv=3, Hk=2), INVALID),
+    (dict(N=0), INVALID), (dict(N=2), INVALID),                       # N must equal B without cu_seqlens
+    (dict(cu=P, B=2, N=2), INVALID),                                  # cu_seqlens needs B == 1
+    (dict(qkv=7), INVALID), (dict(gate=-1), INVALID),
+    (dict(q=P + 4), INVALID), (dict(s0=P + 8), INVALID), (dict(fs=P + 4), INVALID),  # 16-byte
+    (dict(g=P + 2), INVALID), (dict(cu=P + 2, N=1), INVALID),        # element alignment
+    (dict(dk=96), UNSUPPORTED), (dict(dv=32), UNSUPPORTED), (dict(dk=256, dv=256), UNSUPPORTED),
+    (dict(dk=0), INVALID),
+])
+def test_chunk_rejects(lib, kw, status):
+    assert chunk(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(state=None), INVALID), (dict(o=None), INVALID),
+    (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(Hv=4, Hk=3), INVALID),
+    (dict(qkv=2), INVALID), (dict(state=P + 4), INVALID), (dict(o=P + 8), INVALID),
+    (dict(q=P + 2), INVALID), (dict(q=P + 2, qkv=BF16, gate=BF16, g=P + 1), INVALID),
+    (dict(dk=32), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
+])
+def test_recurrent_rejects(lib, kw, status):
+    assert rec(lib, **kw) == status
+
+
+def test_workspace_query_is_host_only(lib):
+    # fp32 inputs take the fp32 chunk kernel, which needs no workspace
+    assert lib.gdn_chunk_fwd_workspace_size(1, 256, 2, 2, 64, 64, 1, F32) == 0
+    # invalid sizes report 0 rather than failing
+    assert lib.gdn_chunk_fwd_workspace_size(1, 256, 2, 3, 64, 64, 1, BF16) == 0
+    assert lib.gdn_chunk_fwd_workspace_size(0, 256, 2, 2, 64, 64, 1, BF16) == 0
+    # the bf16 path's workspace grows with the token count and never shrinks below the small case
+    small = lib.gdn_chunk_fwd_workspace_size(1, 4096, 16, 32, 128, 128, 1, BF16)
+    big = lib.gdn_chunk_fwd_workspace_size(1, 32768, 16, 32, 128, 128, 1, BF16)
+    assert big >= small
+
+
+def test_too_small_workspace_is_rejected(lib):
+    need = lib.gdn_chunk_fwd_workspace_size(1, 4096, 16, 32, 128, 128, 1, BF16)
+    if need == 0:
+        pytest.skip("this build's bf16 path needs no workspace")
+    assert chunk(lib, T=4096, Hk=16, Hv=32, dk=128, dv=128, qkv=BF16, gate=BF16,
+                 ws=None, ws_bytes=0) == WORKSPACE
+    assert chunk(lib, T=4096, Hk=16, Hv=32, dk=128, dv=128, qkv=BF16, gate=BF16,
+                 ws=P, ws_bytes=need - 1) == WORKSPACE
+    assert chunk(lib, T=4096, Hk=16, Hv=32, dk=128, dv=128, qkv=BF16, gate=BF16,
+                 ws=P + 16, ws_bytes=need) == WORKSPACE               # 256-byte alignment
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from gated_deltanet_delta_amd import gdn_chunk_fwd, gdn_recurrent_step
+    x = torch.zeros(1, 4, 1, 64)
+    gg = torch.zeros(1, 4, 1)
+    with pytest.raises(ValueError):
+        gdn_chunk_fwd(x, x, x, gg, gg)
+    with pytest.raises(ValueError):
+        gdn_recurrent_step(x, x, x, gg, gg, torch.zeros(1, 1, 64, 64))
