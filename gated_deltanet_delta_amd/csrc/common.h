@@ -22,6 +22,16 @@ __device__ __forceinline__ size_t idx3(size_t a, size_t b, size_t B_, size_t c, 
     return (a * B_ + b) * C_ + c;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global memory at
+// workgroup scope, which on gfx950 waits for every outstanding global load and store of the wave
+// (vmcnt(0)); that would stall register prefetches of the next chunk at every barrier.  The kernels
+// here never exchange data through global memory within a launch, so an LDS-scoped fence suffices.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sequence n's token range [t0, t1) inside batch row `row`, clamped to [0, T] so that a malformed
 // cu_seqlens array can only produce wrong numbers, never an access outside the buffers.
 __device__ __forceinline__ void sequence_range(const int32_t* cu_seqlens, int n, int T, int& row,

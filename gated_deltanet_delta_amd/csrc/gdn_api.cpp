@@ -50,7 +50,7 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
     if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return 0;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || !dtype_ok(qkv_dtype)) return 0;
     if (!use_mfma(dk, dv, qkv_dtype)) return 0;
-    return gdn::chunk_mfma_workspace_size(B, T, Hv, dk, dv, N);
+    return gdn::chunk_mfma_workspace_size(B, T, Hk, Hv, dk, dv, N);
 }
 
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* g,

@@ -45,7 +45,7 @@ hipError_t launch_chunk_f32(const ChunkArgs& a);
 
 // Chunked kernels on bf16 matrix cores (bf16 inputs).
 bool chunk_mfma_supported(int dk, int dv, gdn_dtype qkv_dtype);
-size_t chunk_mfma_workspace_size(int B, int T, int Hv, int dk, int dv, int N);
+size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N);
 hipError_t launch_chunk_mfma(const ChunkArgs& a);
 
 }  // namespace gdn
