@@ -3,8 +3,8 @@
 // Notation (one chunk of C = 64 tokens of one sequence and v-head, start state S (dk x dv), G_t the
 // running sum of g inside the chunk, Gam_tj = e^(G_t - G_j) for j <= t):
 //
-//   A  = diag(beta) (K K^T o Gam), strictly lower        T  = (I + A)^-1
-//   W  = T diag(beta e^G) K                               Ut = T diag(beta) V
+//   A  = diag(beta) (K K^T o Gam), strictly lower        T  = (I + A)^-1,   M = T diag(beta)
+//   W  = M diag(e^G) K                                    Ut = M V
 //   P  = (Q K^T) o Gam, lower with diagonal
 //   U  = Ut - W S                                         (the chunk's per-token deltas)
 //   O  = diag(e^G) Q S + P U
@@ -14,24 +14,29 @@
 // o_t = S_t^T q_t unrolled over the chunk.  Every decay factor is exp of a non-positive number.
 //
 // Two kernels:
-//   chunk_prep_kernel   one workgroup per (chunk, v-head), all chunks in parallel: cumsum, A on
-//                       the matrix cores, T by a blocked forward substitution (16 x 16 diagonal
-//                       blocks by substitution, off-diagonal blocks by fp32 matrix-core products),
-//                       then -W (bf16) and Ut (fp32) into the workspace.
-//   chunk_state_kernel  one workgroup per (sequence, v-head, slice of WS state columns), walking
-//                       the chunks in order.  Columns of S never interact, so slices are
-//                       independent.  The slice of S stays in matrix-core accumulators for the
-//                       whole sequence; each of the 4 waves owns 32 of the 128 key rows.
+//   chunk_solve_kernel  one workgroup per (chunk, v-head), all chunks in parallel: the part with a
+//                       serial dependence inside a chunk.  Cumsum, A on the matrix cores, T by a
+//                       blocked forward substitution (16 x 16 diagonal blocks by substitution,
+//                       off-diagonal blocks by fp32 matrix-core products), M = T diag(beta) as
+//                       hi + lo bf16 into the workspace (16 KiB per chunk and v-head).
+//   chunk_fused_kernel  one workgroup per (sequence, v-head, 16-column slice of S), walking the
+//                       chunks in order with three wave roles (see there).  Everything else is
+//                       formed on the fly from q, k, v, M and G; nothing else round-trips memory.
 //
 // Precision: q, k, v enter the matrix cores as exact bf16 values.  Quantities that feed the output
-// with full weight (S, U, P, T diag(beta)) enter as two bf16 terms hi + lo (hi = bf16(x),
-// lo = bf16(x - hi)), so their products carry ~16 significant bits; W enters as one bf16 term.
-// Accumulation is fp32 everywhere; decay factors are applied on the fp32 side.
+// with full weight (S, U, P, M) enter as two bf16 terms hi + lo (hi = bf16(x), lo = bf16(x - hi)),
+// so their products carry ~16 significant bits; W enters as one bf16 term.  Accumulation is fp32
+// everywhere; decay factors are applied on the fp32 side.
 //
-// MFMA lane layouts used (wave64, v_mfma_f32_16x16x32_bf16): lane l = 16 g + c holds A[c][8g..8g+7]
-// and B[8g..8g+7][c]; the 16 x 16 result D[4g + r][c], r = 0..3, sits in lane l, element r.  The
-// reduction index of one instruction may be permuted freely as long as A and B agree; the kernels
-// use that to feed an accumulator tile straight back in as an operand without a transpose.
+// Lane layouts used (wave64, checked on the device):
+//   v_mfma_f32_16x16x32_bf16: lane l = 16 g + c holds A[c][8g..8g+7] and B[8g..8g+7][c]; the 16x16
+//     result D[4g + r][c], r = 0..3, sits in lane l, element r.  The reduction index of one
+//     instruction may be permuted freely as long as A and B agree; the kernels use that to feed
+//     an accumulator tile straight back in as an operand.
+//   ds_read_b64_tr_b16: within each 16-lane group, if lane j addresses four 16-bit values
+//     X[j][0..3], lane i receives X[4m + i/4][i%4], m = 0..3.  Pointing lane c of group g at row
+//     8g + c/4, columns c0 + 4(c%4) of a row-major tile therefore hands lane (g, c) the column
+//     segment X[8g .. 8g+3][c0 + c]: a row-major tile serves directly as a transposed operand.
 
 #include "common.h"
 #include "launch.h"
@@ -154,89 +159,56 @@ __device__ __forceinline__ bool locate_chunk(int slot, const int32_t* cu_seqlens
 }
 
 // ------------------------------------------------------------------------------------------------
-// Staging helpers.
+// Shared helpers.
 constexpr int kKP = kDK + 8;   // row pitch (elements) of 128-wide bf16 rows in LDS
-constexpr int kTP = kC + 8;    // row pitch of transposed (token-contiguous) bf16 tiles
+constexpr int kTP = kC + 8;    // row pitch of token-contiguous bf16 tiles [column][token]
 constexpr int kFP = kC + 4;    // row pitch of 64 x 64 fp32 tiles
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Two rows of eight bf16 (rows t and t+1) -> eight 32-bit words, word e = (row t [e], row t+1 [e]).
-__device__ __forceinline__ uint32_t pair_word(const uint4& x0, const uint4& x1, int e) {
-    const uint32_t a = (&x0.x)[e >> 1], b = (&x1.x)[e >> 1];
-    return (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-}
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// Writes the 16 x 8 block held as (rows 2m, 2m+1) x (columns 8p..8p+7) transposed into a
-// token-contiguous tile tr[col][token] (pitch kTP): for each column one 32-bit word holds the two
-// tokens.  Lanes m = 0..31 of a half-wave cover 32 consecutive words of one row.
-__device__ __forceinline__ void store_pair_transposed(__bf16* tr, int m, int p, const uint4& x0,
-                                                      const uint4& x1) {
-    uint32_t* tr32 = reinterpret_cast<uint32_t*>(tr);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tr32[((8 * p + e) * kTP) / 2 + m] = pair_word(x0, x1, e);
+// MFMA operand from a row-major bf16 tile X (pitch in elements) read transposed: lane (g, c)
+// receives X[r0 + 8g + e][c0 + c], e = 0..7, i.e. rows are the reduction index.
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* X, int pitch, int r0, int c0, int g, int c) {
+    const __bf16* p0 = X + (r0 + 8 * g + (c >> 2)) * pitch + c0 + 4 * (c & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 4 * pitch));
+    return cat44(lo, hi);
 }
 
 // ------------------------------------------------------------------------------------------------
-// chunk_prep_kernel: one workgroup per (chunk slot, v-head).
+// chunk_solve_kernel: one workgroup per (chunk slot, v-head).
 //
-// LDS: sK  [64][kKP] bf16 (K rows)             sA [64][kFP] fp32
-//      sKt [128][kTP] bf16 (K^T), later V^T     sT [64][kFP] fp32
-// The log-decay is kept in log2 units (G2 = G log2 e) so every decay factor is one exp2.
-template <int DV, typename TG>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const TG* __restrict__ g, const TG* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ chunk_start, int N, int T, int Hk, int Hv, int nct,
-    __bf16* __restrict__ ws_Wn, float* __restrict__ ws_U, float* __restrict__ ws_G,
-    __bf16* __restrict__ ws_Kt, __bf16* __restrict__ ws_P) {
-    static_assert(DV == 64 || DV == 128, "dv");
-    static_assert(kC * kKP * 2 == kC * kFP * 4, "Q rows and A share one buffer");
+// Writes G2 = running sum of g log2(e) (64 floats) and M = T diag(beta) as hi and lo bf16 tiles
+// [64][64] (row-major, zero above the diagonal and in rows/columns past the chunk's length).
+template <typename TG>
+__global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
+    const __bf16* __restrict__ k, const TG* __restrict__ g, const TG* __restrict__ beta,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start, int N, int T,
+    int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M) {
     __shared__ __attribute__((aligned(16))) __bf16 sK[kC * kKP];
-    __shared__ __attribute__((aligned(16))) __bf16 sKt[kDK * kTP];
     __shared__ __attribute__((aligned(16))) float sA[kC * kFP];
     __shared__ __attribute__((aligned(16))) float sT[kC * kFP];
-    __shared__ float sG[kC], sB[kC], sBE[kC];
-    __bf16* sVt = sKt;                            // V^T [DV][kTP] once K^T is dead
-    __bf16* sQ = reinterpret_cast<__bf16*>(sA);   // Q rows [64][kKP] until A is formed
+    __shared__ float sG[kC], sB[kC];
 
     const int slot = blockIdx.x, h = blockIdx.y;
     ChunkLoc loc;
     if (!locate_chunk(slot, cu_seqlens, chunk_start, N, T, nct, loc)) return;
-    const int G = Hv / Hk, kh = h / G;
+    const int kh = h / (Hv / Hk);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, gq = lane >> 4;
-    const int m = tid & 31, pg = tid >> 5;  // token pair (2m, 2m+1), column group
     const size_t tok0 = (size_t)loc.row * T + loc.t0;
     const int L = loc.len;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
 
-    // ---- stage K (rows and transposed); V stays in registers until K^T is dead -----------------
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int p = pg + 8 * it;
-        uint4 x0 = zero, x1 = zero;
-        if (2 * m < L) x0 = *reinterpret_cast<const uint4*>(k + ((tok0 + 2 * m) * Hk + kh) * kDK + 8 * p);
-        if (2 * m + 1 < L) x1 = *reinterpret_cast<const uint4*>(k + ((tok0 + 2 * m + 1) * Hk + kh) * kDK + 8 * p);
-        *reinterpret_cast<uint4*>(sK + (2 * m) * kKP + 8 * p) = x0;
-        *reinterpret_cast<uint4*>(sK + (2 * m + 1) * kKP + 8 * p) = x1;
-        store_pair_transposed(sKt, m, p, x0, x1);
-        uint4 y0 = zero, y1 = zero;
-        if (2 * m < L) y0 = *reinterpret_cast<const uint4*>(q + ((tok0 + 2 * m) * Hk + kh) * kDK + 8 * p);
-        if (2 * m + 1 < L) y1 = *reinterpret_cast<const uint4*>(q + ((tok0 + 2 * m + 1) * Hk + kh) * kDK + 8 * p);
-        *reinterpret_cast<uint4*>(sQ + (2 * m) * kKP + 8 * p) = y0;
-        *reinterpret_cast<uint4*>(sQ + (2 * m + 1) * kKP + 8 * p) = y1;
-    }
-    constexpr int kVIt = DV / 64;
-    uint4 v0[kVIt], v1[kVIt];
-#pragma unroll
-    for (int it = 0; it < kVIt; ++it) {
-        const int p = pg + 8 * it;
-        v0[it] = zero;
-        v1[it] = zero;
-        if (2 * m < L) v0[it] = *reinterpret_cast<const uint4*>(v + ((tok0 + 2 * m) * Hv + h) * DV + 8 * p);
-        if (2 * m + 1 < L) v1[it] = *reinterpret_cast<const uint4*>(v + ((tok0 + 2 * m + 1) * Hv + h) * DV + 8 * p);
+    for (int it = 0; it < 4; ++it) {
+        const int e = tid + kThreads * it;  // 1024 pieces: row e/16, columns 8 (e%16) .. +7
+        const int t = e >> 4, p = e & 15;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (t < L) x = *reinterpret_cast<const uint4*>(k + ((tok0 + t) * Hk + kh) * kDK + 8 * p);
+        *reinterpret_cast<uint4*>(sK + t * kKP + 8 * p) = x;
     }
     const size_t ws_row = ((size_t)slot * Hv + h) * kC;
     if (wave == 0) {
@@ -250,34 +222,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
         }
         sG[lane] = G2;
         sB[lane] = bt;
-        sBE[lane] = bt * exp2_fast(G2);
         ws_G[ws_row + lane] = G2;
     }
     for (int e = tid; e < kC * kFP; e += kThreads) sT[e] = 0.f;
-    // P's strictly-upper 16x16 tiles are zero
-    __bf16* Ph = ws_P + ((size_t)slot * Hv + h) * 2 * kC * kC;
-    __bf16* Pl = Ph + kC * kC;
-    for (int e = tid; e < kC * kC; e += kThreads) {
-        const int t = e >> 6, tp = e & 63;
-        if ((tp >> 4) > (t >> 4)) {
-            Ph[e] = hi_of(0.f);
-            Pl[e] = hi_of(0.f);
-        }
-    }
     lds_barrier();
 
-    // K^T for the state kernel: written once per q/k head (by the group's first v-head)
-    if (h % G == 0) {
-        __bf16* dst = ws_Kt + ((size_t)slot * Hk + kh) * kDK * kC;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int e = tid + kThreads * it;  // 128 rows x 8 pieces
-            const int i = e >> 3, p = e & 7;
-            *reinterpret_cast<uint4*>(dst + i * kC + 8 * p) = *reinterpret_cast<const uint4*>(sKt + i * kTP + 8 * p);
-        }
-    }
-
-    // ---- A = diag(beta) (K K^T o Gam), strictly lower: 10 lower 16x16 tiles over 4 waves ----------
+    // A = diag(beta) (K K^T o Gam), strictly lower: 10 lower 16x16 tiles over 4 waves
     // wave 0: (0,0) (3,3) (3,0); wave 1: (1,1) (3,1) (1,0); wave 2: (2,2) (3,2); wave 3: (2,0) (2,1)
     auto tile_a = [](int w, int s) {
         return s == 0 ? (w == 3 ? 2 : w) : s == 1 ? (w == 3 ? 2 : 3) : (w < 2 ? (w == 0 ? 3 : 1) : -1);
@@ -285,44 +235,24 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
     auto tile_b = [](int w, int s) {
         return s == 0 ? (w == 3 ? 0 : w) : s == 1 ? (w == 3 ? 1 : w == 0 ? 3 : w) : 0;
     };
-    f32x4 accA[3], accP[3];
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        const int ta = tile_a(wave, s), tb = tile_b(wave, s);
-        accA[s] = zero4();
-        accP[s] = zero4();
-        if (ta < 0) continue;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 b = lds8(sK + (16 * tb + c) * kKP + 32 * kb + 8 * gq);
-            accA[s] = mma(lds8(sK + (16 * ta + c) * kKP + 32 * kb + 8 * gq), b, accA[s]);
-            accP[s] = mma(lds8(sQ + (16 * ta + c) * kKP + 32 * kb + 8 * gq), b, accP[s]);
-        }
-        // P = (Q K^T) o Gam (lower with diagonal) as hi + lo, row-major [t][t']
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * ta + 4 * gq + r, j = 16 * tb + c;
-            const float pv = j <= t ? accP[s][r] * exp2_fast(sG[t] - sG[j]) : 0.f;
-            const __bf16 ph = hi_of(pv);
-            Ph[t * kC + j] = ph;
-            Pl[t * kC + j] = lo_of(pv, ph);
-        }
-    }
-    lds_barrier();  // Q rows dead: A overwrites them
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
         const int ta = tile_a(wave, s), tb = tile_b(wave, s);
         if (ta < 0) continue;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            acc = mma(lds8(sK + (16 * ta + c) * kKP + 32 * kb + 8 * gq),
+                      lds8(sK + (16 * tb + c) * kKP + 32 * kb + 8 * gq), acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * ta + 4 * gq + r, j = 16 * tb + c;
-            sA[t * kFP + j] = j < t ? sB[t] * accA[s][r] * exp2_fast(sG[t] - sG[j]) : 0.f;
+            sA[t * kFP + j] = j < t ? sB[t] * acc[r] * exp2_fast(sG[t] - sG[j]) : 0.f;
         }
     }
     lds_barrier();
 
-    // ---- T = (I + A)^-1 ---------------------------------------------------------------------------
-    // diagonal blocks: wave w inverts block w, lane c < 16 computes column c by substitution
+    // T = (I + A)^-1: diagonal blocks, wave w inverts block w (lane c < 16 computes column c)
     if (c == lane) {
         const int base = 16 * wave;
         float x[16];
@@ -364,182 +294,89 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(
         lds_barrier();
     }
 
-    // ---- -W = -T diag(beta e^G) K  (bf16) ---------------------------------------------------------
-    // wave w computes key-dim tiles 2w, 2w+1 for all four token tiles
+    // M = T diag(beta) as hi and lo rows: 64 rows x 8 pieces of 8 columns
+    __bf16* Mh = ws_M + ((size_t)slot * Hv + h) * 2 * kC * kC;
+    __bf16* Ml = Mh + kC * kC;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        f32x4 acc0 = zero4(), acc1 = zero4();
+    for (int it = 0; it < 2; ++it) {
+        const int e = tid + kThreads * it;
+        const int t = e >> 3, p = e & 7;
+        const float4 a0 = *reinterpret_cast<const float4*>(sT + t * kFP + 8 * p);
+        const float4 a1 = *reinterpret_cast<const float4*>(sT + t * kFP + 8 * p + 4);
+        const float tv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        bf16x8 hv, lv;
 #pragma unroll
-        for (int kb = 0; kb <= a / 2; ++kb) {
-            const int t = 16 * a + c, j0 = 32 * kb + 8 * gq;
-            const float4 t0 = *reinterpret_cast<const float4*>(sT + t * kFP + j0);
-            const float4 t1 = *reinterpret_cast<const float4*>(sT + t * kFP + j0 + 4);
-            const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-            bf16x8 af;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) af[e] = hi_of(tv[e] * sBE[j0 + e]);
-            const bf16x8 b0 = lds8(sKt + (16 * (2 * wave) + c) * kTP + j0);
-            const bf16x8 b1 = lds8(sKt + (16 * (2 * wave + 1) + c) * kTP + j0);
-            acc0 = mma(af, b0, acc0);
-            acc1 = mma(af, b1, acc1);
+        for (int j = 0; j < 8; ++j) {
+            const float x = tv[j] * sB[8 * p + j];
+            hv[j] = hi_of(x);
+            lv[j] = lo_of(x, hv[j]);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * a + 4 * gq + r;
-            ws_Wn[(ws_row + t) * kDK + 16 * (2 * wave) + c] = hi_of(-acc0[r]);
-            ws_Wn[(ws_row + t) * kDK + 16 * (2 * wave + 1) + c] = hi_of(-acc1[r]);
-        }
-    }
-    lds_barrier();  // K^T dead: V^T overwrites it
-
-    // ---- Ut = T diag(beta) V  (fp32) --------------------------------------------------------------
-#pragma unroll
-    for (int it = 0; it < kVIt; ++it) store_pair_transposed(sVt, m, pg + 8 * it, v0[it], v1[it]);
-    lds_barrier();
-    constexpr int kTilesPerWave = DV / 16 / 4;  // value-dim tiles per wave
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        f32x4 acc[kTilesPerWave];
-#pragma unroll
-        for (int q2 = 0; q2 < kTilesPerWave; ++q2) acc[q2] = zero4();
-#pragma unroll
-        for (int kb = 0; kb <= a / 2; ++kb) {
-            const int t = 16 * a + c, j0 = 32 * kb + 8 * gq;
-            const float4 t0 = *reinterpret_cast<const float4*>(sT + t * kFP + j0);
-            const float4 t1 = *reinterpret_cast<const float4*>(sT + t * kFP + j0 + 4);
-            const float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-            bf16x8 ah, al;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = tv[e] * sB[j0 + e];
-                ah[e] = hi_of(x);
-                al[e] = lo_of(x, ah[e]);
-            }
-#pragma unroll
-            for (int q2 = 0; q2 < kTilesPerWave; ++q2) {
-                const int ct = wave * kTilesPerWave + q2;
-                const bf16x8 bv = lds8(sVt + (16 * ct + c) * kTP + j0);
-                acc[q2] = mma(ah, bv, acc[q2]);
-                acc[q2] = mma(al, bv, acc[q2]);
-            }
-        }
-#pragma unroll
-        for (int q2 = 0; q2 < kTilesPerWave; ++q2) {
-            const int ct = wave * kTilesPerWave + q2;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * a + 4 * gq + r;
-                ws_U[(ws_row + t) * DV + 16 * ct + c] = acc[q2][r];
-            }
-        }
+        *reinterpret_cast<bf16x8*>(Mh + t * kC + 8 * p) = hv;
+        *reinterpret_cast<bf16x8*>(Ml + t * kC + 8 * p) = lv;
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// chunk_state_kernel: one workgroup per (sequence, v-head, 16-column slice of S), chunks in order.
+// chunk_fused_kernel: one workgroup per (sequence, v-head, 16-column slice of S).
 //
-// Eight waves in two roles, both walking the sequence's chunks:
-//   chain waves 0..3   carry the recurrence.  Chain wave w owns key rows [32w, 32w+32) of the
-//                      slice of S as two 16 x 16 accumulator tiles.  For chunk i:
-//                        - S (hi+lo) -> LDS, for the output waves
-//                        - partial U_w = (-W)[:, rows_w] S[rows_w, :] -> LDS
-//                        - (barrier) token tile w: U = Ut + sum_w U_w; U (hi+lo) and
-//                          e^(G_C - G) U (hi+lo) -> LDS, token-contiguous
-//                        - (barrier) S <- e^(G_C) S + K^T (e^(G_C - G) U)
-//   output waves 4..7  one chunk behind: for chunk i-1, output wave w' forms token tile w' of
-//                      O = e^G Q S + P U from the S and U the chain waves left in LDS.
-// Every wave loads its own matrix-core operand fragments straight from memory into registers, one
-// chunk ahead; LDS only carries what the waves exchange.  Two barriers per chunk.
-constexpr int kStateThreads = 512;
+// With M = T diag(beta) from chunk_solve_kernel, the chunk's deltas are
+//     U = Ut - W S = M (V - diag(e^G) K S)
+// so no W is formed: the chain needs K S (K exact bf16, S as hi + lo), one elementwise step and one
+// 64 x 64 product with M.  Eight waves step through the chunks together, three barriers per chunk:
+//
+//   chain waves 0..3 (wave w owns key rows [32w, 32w+32) of S as two 16x16 accumulator tiles)
+//     phase 1  S (hi + lo) -> LDS for the output waves; partial (K S)_w over its 32 key rows
+//     phase 2  token tile w: X = V - e^G sum_w (K S)_w  -> LDS as hi + lo
+//     phase 3  token tile w: U = M X; U (hi + lo) and e^(G_C - G) U (hi + lo) -> LDS
+//     phase 4  S <- e^(G_C) S + K^T (e^(G_C - G) U), K^T read transposed from the K rows
+//   output waves 4..7 (wave w' owns token tile w' of O)
+//     phase 1  P^T tiles (a, w') = K Q^T for a < 2 (masked, decayed)
+//     phase 2  O = e^G Q S from the chain's S copy
+//     phase 3  P^T tiles for a >= 2
+//     phase 4  O += P U from the chain's U copy; store
+// Both roles stage the next chunk's K rows and log-decay into a three-chunk LDS ring at phase 1.
+// All global operands (K, G for staging; M and V for the chain; q for the output waves) are
+// fetched into registers one chunk ahead, alternating between two register sets.
+constexpr int kFusedThreads = 512;
 constexpr int kWS = 16;          // state columns per workgroup
-constexpr int kRP = kC + 4;      // pitch of the column-major fp32 partial tiles [16][64]
-constexpr int kSP = kDK + 8;     // pitch of the key-contiguous state copies [16][128]
+constexpr int kRP = kC + 4;      // pitch of the column-major fp32 tiles [16][64]
+constexpr int kSP = kDK + 8;     // pitch of the key-contiguous state copy [16][128]
 
-struct StateLds {
-    float red[4][kWS * kRP];                     // chain waves' partial U, [column][token]
-    __bf16 Dh[kWS * kTP], Dl[kWS * kTP];         // e^(G_C - G) U, [column][token]
-    __bf16 Uh[2][kWS * kTP], Ul[2][kWS * kTP];   // U of the last two chunks, [column][token]
-    __bf16 Sh[2][kWS * kSP], Sl[2][kWS * kSP];   // chunk-start S of the last two chunks, [column][key]
+struct FusedLds {
+    __bf16 Kr[3][kC * kKP];        // K rows (ring of three chunks)
+    float G2[3][kC];               // running log2-decay (ring of three chunks)
+    float EG[3][kC];               // exp2(G2)
+    __bf16 Sh[kWS * kSP], Sl[kWS * kSP];   // chunk-start S, [column][key]
+    __bf16 Xh[kWS * kTP], Xl[kWS * kTP];   // V - e^G K S, [column][token]
+    __bf16 Uh[kWS * kTP], Ul[kWS * kTP];   // U, [column][token]
+    __bf16 Dh[kWS * kTP], Dl[kWS * kTP];   // e^(G_C - G) U, [column][token]
+    float red[4][kWS * kRP];       // chain waves' partial K S, [column][token]
+};
+
+struct StageFrag {                 // one thread's share of the next chunk's K rows and G
+    uint4 k[2];                    // K pieces e = tid + 512 it: row e/16, columns 8 (e%16) .. +7
+    float g2;                      // G2 row tid (tid < 64)
 };
 
 struct ChainFrag {
-    bf16x4 wn[4][2];  // -W rows 16a + c, key columns 32w + 4g .. +3 and 32w + 16 + 4g .. +3
-    bf16x8 kt[2][2];  // K^T rows 32w + 16it + c, tokens 32kb + 8g .. +7
-    float ut[4];      // Ut rows 16w + 4g + r, column c0 + c
-    float g2[4];      // G2 rows 16w + 4g + r
-    float g2c;        // G2 of the chunk's last row
+    bf16x8 mh[2], ml[2];           // M rows 16w + c, columns 32 kb + 8 g .. +7
+    __bf16 vv[4];                  // V rows 16w + 4g + r, column c0 + c (zero past the chunk)
 };
 
 struct OutFrag {
-    bf16x8 q[4];         // Q rows 16w' + c, key columns 32kb + 8g .. +7 (zero past the sequence)
-    bf16x8 ph[2], pl[2]; // P rows 16w' + c, tokens 32kb + 8g .. +7
-    float g2[4];         // G2 rows 16w' + 4g + r
+    bf16x8 q[4];                   // Q rows 16w' + c, key columns 32 kb + 8 g .. +7 (zero past L)
 };
 
 template <int DV>
-__device__ __forceinline__ void fetch_chain(ChainFrag& f, const __bf16* ws_Wn, const float* ws_U,
-                                           const float* ws_G, const __bf16* ws_Kt, size_t ws_row,
-                                           size_t kt_base, int w, int c0, int c, int gq) {
-    const __bf16* wn = ws_Wn + ws_row * kDK;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int off = (16 * a + c) * kDK + 32 * w + 4 * gq;
-        f.wn[a][0] = *reinterpret_cast<const bf16x4*>(wn + off);
-        f.wn[a][1] = *reinterpret_cast<const bf16x4*>(wn + off + 16);
-    }
-    const __bf16* kt = ws_Kt + kt_base;
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            f.kt[it][kb] = *reinterpret_cast<const bf16x8*>(kt + (32 * w + 16 * it + c) * kC + 32 * kb + 8 * gq);
-    const float* ut = ws_U + ws_row * DV + c0 + c;
-    const float* g2 = ws_G + ws_row;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        f.ut[r] = ut[(16 * w + 4 * gq + r) * DV];
-        f.g2[r] = g2[16 * w + 4 * gq + r];
-    }
-    f.g2c = g2[kC - 1];
-}
-
-__device__ __forceinline__ void fetch_out_q(OutFrag& f, const __bf16* q, const float* ws_G,
-                                            size_t tok0, int L, int Hk, int kh, size_t ws_row,
-                                            int w, int c, int gq) {
-    // rows past the sequence's end read its last row and are then zeroed (no branch)
-    const int t = 16 * w + c;
-    const bool live = t < L;
-    const __bf16* qr = q + ((tok0 + (live ? t : L - 1)) * Hk + kh) * kDK + 8 * gq;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const uint4 x = *reinterpret_cast<const uint4*>(qr + 32 * kb);
-        const uint4 y = live ? x : make_uint4(0, 0, 0, 0);
-        f.q[kb] = *reinterpret_cast<const bf16x8*>(&y);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) f.g2[r] = ws_G[ws_row + 16 * w + 4 * gq + r];
-}
-
-__device__ __forceinline__ void fetch_out_p(OutFrag& f, const __bf16* ws_P, size_t p_base, int w,
-                                            int c, int gq) {
-    const __bf16* ph = ws_P + p_base + (16 * w + c) * kC + 8 * gq;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        f.ph[kb] = *reinterpret_cast<const bf16x8*>(ph + 32 * kb);
-        f.pl[kb] = *reinterpret_cast<const bf16x8*>(ph + kC * kC + 32 * kb);
-    }
-}
-
-template <int DV>
-__global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
-    const __bf16* __restrict__ q, const float* initial_state,
-    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start,
-    const int32_t* __restrict__ order, int N, int T, int Hk, int Hv, int nct, int max_slots,
-    const __bf16* __restrict__ ws_Wn, const float* __restrict__ ws_U,
-    const float* __restrict__ ws_G, const __bf16* __restrict__ ws_Kt,
-    const __bf16* __restrict__ ws_P, float* __restrict__ o, float* final_state) {
+__global__ __launch_bounds__(kFusedThreads) void chunk_fused_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* initial_state, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ order, int N, int T,
+    int Hk, int Hv, int nct, int max_slots, const float* __restrict__ ws_G,
+    const __bf16* __restrict__ ws_M, float* __restrict__ o, float* final_state) {
     constexpr int S_SL = DV / kWS;  // slices per head
-    __shared__ __attribute__((aligned(16))) StateLds sm;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    FusedLds& sm = *reinterpret_cast<FusedLds*>(smem_raw);
 
     // blockIdx -> (unit, slice); all slices of a unit share blockIdx % 8 (the same XCD / L2)
     const int bid = blockIdx.x;
@@ -555,41 +392,94 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
     // (a malformed cu_seqlens can claim more chunks than the workspace holds: stop at its end)
     const int nchunks = min((t1 - t0 + kC - 1) / kC, max(0, max_slots - slot0));
     const int c0 = sl * kWS;
+    const size_t sbase = ((size_t)n * Hv + h) * kDK * DV;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, gq = lane >> 4;
     const bool chain = wave < 4;
-    const int w = chain ? wave : wave - 4;  // chain: key-row block; output: token tile
+    const int w = wave & 3;
 
     auto tok0_of = [&](int ci) { return (size_t)row * T + t0 + (size_t)ci * kC; };
     auto len_of = [&](int ci) { return min(kC, t1 - t0 - ci * kC); };
     auto ws_row_of = [&](int ci) { return ((size_t)(slot0 + ci) * Hv + h) * kC; };
-    auto kt_base_of = [&](int ci) { return ((size_t)(slot0 + ci) * Hk + kh) * kDK * kC; };
-    auto p_base_of = [&](int ci) { return ((size_t)(slot0 + ci) * Hv + h) * 2 * kC * kC; };
 
-    // chain waves: S slice rows 32w + 16it + 4g + r, column c0 + c
-    f32x4 S[2] = {zero4(), zero4()};
-    const size_t sbase = ((size_t)n * Hv + h) * kDK * DV;
-    if (chain && initial_state) {
+    if (nchunks == 0) {  // zero-length sequence: the state passes through
+        if (chain) {
 #pragma unroll
-        for (int it = 0; it < 2; ++it)
+            for (int it = 0; it < 2; ++it)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[it][r] = initial_state[sbase + (size_t)(32 * w + 16 * it + 4 * gq + r) * DV + c0 + c];
+                for (int r = 0; r < 4; ++r) {
+                    const size_t idx = sbase + (size_t)(32 * w + 16 * it + 4 * gq + r) * DV + c0 + c;
+                    final_state[idx] = initial_state ? initial_state[idx] : 0.f;
+                }
+        }
+        return;
     }
 
-    // The two roles run separate loops (wave-uniform branch) so that neither role's in-flight
-    // prefetches are drained at control-flow joins with the other's code.  Both loops execute the
-    // same barriers: two per chunk, plus one pair for the output waves' one-chunk lag.
+    // ---- staging of K rows and G (both roles, one chunk ahead) -------------------------------
+    auto fetch_stage = [&](StageFrag& f, int ci) {
+        const size_t tok0 = tok0_of(ci);
+        const int L = len_of(ci);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int e = tid + kFusedThreads * it, t = e >> 4, p = e & 15;
+            const bool live = t < L;
+            const uint4 x = *reinterpret_cast<const uint4*>(k + ((tok0 + (live ? t : L - 1)) * Hk + kh) * kDK + 8 * p);
+            f.k[it] = live ? x : make_uint4(0, 0, 0, 0);
+        }
+        f.g2 = ws_G[ws_row_of(ci) + (tid & 63)];
+    };
+    auto store_stage = [&](const StageFrag& f, int ci) {
+        __bf16* kr = sm.Kr[ci % 3];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int e = tid + kFusedThreads * it, t = e >> 4, p = e & 15;
+            *reinterpret_cast<uint4*>(kr + t * kKP + 8 * p) = f.k[it];
+        }
+        if (tid < kC) {
+            sm.G2[ci % 3][tid] = f.g2;
+            sm.EG[ci % 3][tid] = exp2_fast(f.g2);
+        }
+    };
+    StageFrag sa, sb;
+    fetch_stage(sa, 0);
+    store_stage(sa, 0);  // chunk 0 is staged before the loop; chunk i+1 at phase 1 of chunk i
+
     if (chain) {
-        // Chunk i with operands `cur`, prefetching chunk i+1 into `nxt` (the two sets alternate, so
-        // no register copy has to wait for the prefetch to land).
-        auto chain_step = [&](int i, const ChainFrag& cur, ChainFrag& nxt) {
-            const int nx = min(i + 1, nchunks - 1);  // (the last prefetch repeats the last chunk)
-            fetch_chain<DV>(nxt, ws_Wn, ws_U, ws_G, ws_Kt, ws_row_of(nx), kt_base_of(nx), w, c0, c, gq);
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a whole chunk ahead of its use
-            // S (hi + lo): B operand here, and the output waves' copy
+        // ------------------------------------------------ chain waves -------------------------
+        auto fetch_chain = [&](ChainFrag& f, int ci) {
+            const __bf16* mb = ws_M + ((size_t)(slot0 + ci) * Hv + h) * 2 * kC * kC + (16 * w + c) * kC + 8 * gq;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                f.mh[kb] = *reinterpret_cast<const bf16x8*>(mb + 32 * kb);
+                f.ml[kb] = *reinterpret_cast<const bf16x8*>(mb + kC * kC + 32 * kb);
+            }
+            const size_t tok0 = tok0_of(ci);
+            const int L = len_of(ci);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * w + 4 * gq + r;
+                const bool live = t < L;
+                const __bf16 x = v[((tok0 + (live ? t : L - 1)) * Hv + h) * DV + c0 + c];
+                f.vv[r] = live ? x : (__bf16)0.f;
+            }
+        };
+        f32x4 S[2] = {zero4(), zero4()};
+        if (initial_state) {
+#pragma unroll
+            for (int it = 0; it < 2; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[it][r] = initial_state[sbase + (size_t)(32 * w + 16 * it + 4 * gq + r) * DV + c0 + c];
+        }
+        auto step = [&](int i, const ChainFrag& cur, ChainFrag& nxt, const StageFrag& st, StageFrag& stn) {
+            store_stage(st, i + 1);  // (the last step stages a repeat of the last chunk: unread)
+            fetch_stage(stn, min(i + 2, nchunks - 1));
+            fetch_chain(nxt, min(i + 1, nchunks - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            const __bf16* kr = sm.Kr[i % 3];
+            // phase 1: S (hi + lo) -> LDS; partial K S over this wave's 32 key rows
             bf16x8 sh, sl8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -600,215 +490,253 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
                 const int off = c * kSP + 32 * w + 16 * it + 4 * gq;
-                *reinterpret_cast<bf16x4*>(sm.Sh[i & 1] + off) =
-                    bf16x4{sh[4 * it], sh[4 * it + 1], sh[4 * it + 2], sh[4 * it + 3]};
-                *reinterpret_cast<bf16x4*>(sm.Sl[i & 1] + off) =
-                    bf16x4{sl8[4 * it], sl8[4 * it + 1], sl8[4 * it + 2], sl8[4 * it + 3]};
+                *reinterpret_cast<bf16x4*>(sm.Sh + off) = bf16x4{sh[4 * it], sh[4 * it + 1], sh[4 * it + 2], sh[4 * it + 3]};
+                *reinterpret_cast<bf16x4*>(sm.Sl + off) = bf16x4{sl8[4 * it], sl8[4 * it + 1], sl8[4 * it + 2], sl8[4 * it + 3]};
             }
-            // partial U over this wave's 32 key rows, all 64 tokens
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const bf16x8 aw = cat44(cur.wn[a][0], cur.wn[a][1]);
-                const f32x4 uh = mma(aw, sh, zero4());
-                const f32x4 ul = mma(aw, sl8, zero4());
-                *reinterpret_cast<f32x4*>(&sm.red[w][c * kRP + 16 * a + 4 * gq]) = uh + ul;
+                const __bf16* kk = kr + (16 * a + c) * kKP + 32 * w + 4 * gq;
+                const bf16x8 ak = cat44(lds4(kk), lds4(kk + 16));
+                const f32x4 ph = mma(ak, sh, zero4());
+                const f32x4 pl = mma(ak, sl8, zero4());
+                *reinterpret_cast<f32x4*>(&sm.red[w][c * kRP + 16 * a + 4 * gq]) = ph + pl;
             }
             lds_barrier();
 
-            // token tile w: U = Ut + sum of the four partials
-            f32x4 uu = {cur.ut[0], cur.ut[1], cur.ut[2], cur.ut[3]};
+            // phase 2: token tile w: X = V - e^G K S  (hi + lo)
+            const int tr0 = 16 * w + 4 * gq;
+            f32x4 ks = *reinterpret_cast<const f32x4*>(&sm.red[0][c * kRP + tr0]);
 #pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2)
-                uu += *reinterpret_cast<const f32x4*>(&sm.red[w2][c * kRP + 16 * w + 4 * gq]);
+            for (int w2 = 1; w2 < 4; ++w2) ks += *reinterpret_cast<const f32x4*>(&sm.red[w2][c * kRP + tr0]);
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(&sm.EG[i % 3][tr0]);
+            bf16x4 xh4, xl4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = (float)cur.vv[r] - eg[r] * ks[r];
+                xh4[r] = hi_of(x);
+                xl4[r] = lo_of(x, xh4[r]);
+            }
+            *reinterpret_cast<bf16x4*>(sm.Xh + c * kTP + tr0) = xh4;
+            *reinterpret_cast<bf16x4*>(sm.Xl + c * kTP + tr0) = xl4;
+            lds_barrier();
+
+            // phase 3: token tile w: U = M X; U and e^(G_C - G) U (hi + lo) -> LDS
+            f32x4 uu = zero4(), uu2 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (2 * kb > w) continue;
+                const int off = c * kTP + 32 * kb + 8 * gq;
+                const bf16x8 xh = lds8(sm.Xh + off), xl = lds8(sm.Xl + off);
+                uu = mma(cur.mh[kb], xh, uu);
+                uu2 = mma(cur.mh[kb], xl, uu2);
+                uu2 = mma(cur.ml[kb], xh, uu2);
+            }
+            uu += uu2;
+            const f32x4 g2 = *reinterpret_cast<const f32x4*>(&sm.G2[i % 3][tr0]);
+            const float g2c = sm.G2[i % 3][kC - 1];
             bf16x4 uh4, ul4, dh4, dl4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uh4[r] = hi_of(uu[r]);
                 ul4[r] = lo_of(uu[r], uh4[r]);
-                const float dd = exp2_fast(cur.g2c - cur.g2[r]) * uu[r];
+                const float dd = exp2_fast(g2c - g2[r]) * uu[r];
                 dh4[r] = hi_of(dd);
                 dl4[r] = lo_of(dd, dh4[r]);
             }
-            const int off = c * kTP + 16 * w + 4 * gq;
-            *reinterpret_cast<bf16x4*>(sm.Uh[i & 1] + off) = uh4;
-            *reinterpret_cast<bf16x4*>(sm.Ul[i & 1] + off) = ul4;
+            const int off = c * kTP + tr0;
+            *reinterpret_cast<bf16x4*>(sm.Uh + off) = uh4;
+            *reinterpret_cast<bf16x4*>(sm.Ul + off) = ul4;
             *reinterpret_cast<bf16x4*>(sm.Dh + off) = dh4;
             *reinterpret_cast<bf16x4*>(sm.Dl + off) = dl4;
             lds_barrier();
 
-            // S <- e^(G_C) S + K^T (e^(G_C - G) U)
-            const float eC = exp2_fast(cur.g2c);
+            // phase 4: S <- e^(G_C) S + K^T (e^(G_C - G) U)
+            const float eC = sm.EG[i % 3][kC - 1];
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
                 f32x4 a0 = S[it] * eC, a1 = zero4();
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 kt = tr_frag(kr, kKP, 32 * kb, 32 * w + 16 * it, gq, c);
                     const int o2 = c * kTP + 32 * kb + 8 * gq;
-                    a0 = mma(cur.kt[it][kb], lds8(sm.Dh + o2), a0);
-                    a1 = mma(cur.kt[it][kb], lds8(sm.Dl + o2), a1);
+                    a0 = mma(kt, lds8(sm.Dh + o2), a0);
+                    a1 = mma(kt, lds8(sm.Dl + o2), a1);
                 }
                 S[it] = a0 + a1;
             }
         };
-        // Both steps of the unrolled loop are unconditional (an odd count peels the first chunk),
-        // so the compiler has no conditional block to sink a prefetch into.
-        ChainFrag fa, fb;
-        int i0 = 0;
-        if (nchunks & 1) {
-            fetch_chain<DV>(fb, ws_Wn, ws_U, ws_G, ws_Kt, ws_row_of(0), kt_base_of(0), w, c0, c, gq);
-            chain_step(0, fb, fa);
-            i0 = 1;
-        } else if (nchunks > 0) {
-            fetch_chain<DV>(fa, ws_Wn, ws_U, ws_G, ws_Kt, ws_row_of(0), kt_base_of(0), w, c0, c, gq);
+        ChainFrag ca, cb;
+        fetch_chain(ca, 0);
+        fetch_stage(sb, min(1, nchunks - 1));
+        lds_barrier();  // chunk 0 staged
+        int i = 0;
+        for (; i + 1 < nchunks; i += 2) {
+            step(i, ca, cb, sb, sa);
+            step(i + 1, cb, ca, sa, sb);
         }
-        for (int i = i0; i < nchunks; i += 2) {
-            chain_step(i, fa, fb);
-            chain_step(i + 1, fb, fa);
-        }
-        if (nchunks > 0) {  // the output waves' last chunk
-            lds_barrier();
-            lds_barrier();
-        }
+        if (i < nchunks) step(i, ca, cb, sb, sa);
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 final_state[sbase + (size_t)(32 * w + 16 * it + 4 * gq + r) * DV + c0 + c] = S[it][r];
     } else {
-        // Chunk i-1 with operands `cur`, prefetching chunk i into `nxt`.
-        auto out_step = [&](int i, const OutFrag& cur, OutFrag& nxt) {
-            const int pb = (i - 1) & 1;
-            const int nx = min(i, nchunks - 1);
-            fetch_out_q(nxt, q, ws_G, tok0_of(nx), len_of(nx), Hk, kh, ws_row_of(nx), w, c, gq);
-            fetch_out_p(nxt, ws_P, p_base_of(nx), w, c, gq);
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch here, a whole chunk ahead of its use
-            // O = e^G Q S for token tile w of chunk i-1
+        // ------------------------------------------------ output waves ------------------------
+        auto fetch_out = [&](OutFrag& f, int ci) {
+            // rows past the sequence's end read its last row and are then zeroed (no branch)
+            const int t = 16 * w + c, L = len_of(ci);
+            const bool live = t < L;
+            const __bf16* qr = q + ((tok0_of(ci) + (live ? t : L - 1)) * Hk + kh) * kDK + 8 * gq;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint4 x = *reinterpret_cast<const uint4*>(qr + 32 * kb);
+                const uint4 y = live ? x : make_uint4(0, 0, 0, 0);
+                f.q[kb] = *reinterpret_cast<const bf16x8*>(&y);
+            }
+        };
+        const int tq = 16 * w + c;
+        // P^T tile (a, w): rows t' = 16a + 4g + r, column t = tq; masked and decayed
+        auto ptile = [&](const OutFrag& cur, const __bf16* kr, const float* g2, float gt, int a) {
+            f32x4 pt = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                pt = mma(lds8(kr + (16 * a + c) * kKP + 32 * kb + 8 * gq), cur.q[kb], pt);
+            const f32x4 gp = *reinterpret_cast<const f32x4*>(g2 + 16 * a + 4 * gq);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tp = 16 * a + 4 * gq + r;
+                pt[r] = tp <= tq ? pt[r] * exp2_fast(gt - gp[r]) : 0.f;
+            }
+            return pt;
+        };
+        auto step = [&](int i, const OutFrag& cur, OutFrag& nxt, const StageFrag& st, StageFrag& stn) {
+            store_stage(st, i + 1);
+            fetch_stage(stn, min(i + 2, nchunks - 1));
+            fetch_out(nxt, min(i + 1, nchunks - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            const __bf16* kr = sm.Kr[i % 3];
+            const float* g2 = sm.G2[i % 3];
+            const float gt = g2[tq];
+            // phase 1: P^T tiles a = 0, 1
+            f32x4 PT[4] = {zero4(), zero4(), zero4(), zero4()};
+            PT[0] = ptile(cur, kr, g2, gt, 0);
+            if (w >= 1) PT[1] = ptile(cur, kr, g2, gt, 1);
+            lds_barrier();
+            // phase 2: O = e^G Q S
             f32x4 qs = zero4(), qs2 = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int off = c * kSP + 32 * kb + 8 * gq;
-                qs = mma(cur.q[kb], lds8(sm.Sh[pb] + off), qs);
-                qs2 = mma(cur.q[kb], lds8(sm.Sl[pb] + off), qs2);
+                qs = mma(cur.q[kb], lds8(sm.Sh + off), qs);
+                qs2 = mma(cur.q[kb], lds8(sm.Sl + off), qs2);
             }
-            f32x4 Ox;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ox[r] = exp2_fast(cur.g2[r]) * (qs[r] + qs2[r]);
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(&sm.EG[i % 3][16 * w + 4 * gq]);
+            f32x4 Ox = eg * (qs + qs2);
             lds_barrier();
-
-            // O += P U for token tile w of chunk i-1, then store
+            // phase 3: P^T tiles a = 2, 3
+            if (w >= 2) PT[2] = ptile(cur, kr, g2, gt, 2);
+            if (w >= 3) PT[3] = ptile(cur, kr, g2, gt, 3);
+            lds_barrier();
+            // phase 4: O += P U, then store
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (2 * kb > w) continue;
-                const int off = c * kTP + 32 * kb + 8 * gq;
-                const bf16x8 uh = lds8(sm.Uh[pb] + off), ul = lds8(sm.Ul[pb] + off);
-                Ox = mma(cur.ph[kb], uh, Ox);
-                Ox = mma(cur.ph[kb], ul, Ox);
-                Ox = mma(cur.pl[kb], uh, Ox);
+                bf16x8 ph, pl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = PT[2 * kb + (e >> 2)][e & 3];
+                    ph[e] = hi_of(x);
+                    pl[e] = lo_of(x, ph[e]);
+                }
+                const int j0 = c * kTP + 32 * kb + 4 * gq;  // token slots j..j+3 and j+16..j+19
+                const bf16x8 uh = cat44(lds4(sm.Uh + j0), lds4(sm.Uh + j0 + 16));
+                const bf16x8 ul = cat44(lds4(sm.Ul + j0), lds4(sm.Ul + j0 + 16));
+                Ox = mma(ph, uh, Ox);
+                Ox = mma(ph, ul, Ox);
+                Ox = mma(pl, uh, Ox);
             }
-            const size_t tok0 = tok0_of(i - 1);
-            const int L = len_of(i - 1);
+            const size_t tok0 = tok0_of(i);
+            const int L = len_of(i);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * w + 4 * gq + r;
                 if (t < L) o[((tok0 + t) * Hv + h) * DV + c0 + c] = Ox[r];
             }
-            lds_barrier();
         };
         OutFrag fa, fb;
-        int i0 = 1;
-        if (nchunks > 0) {
-            OutFrag& first = (nchunks & 1) ? fb : fa;
-            fetch_out_q(first, q, ws_G, tok0_of(0), len_of(0), Hk, kh, ws_row_of(0), w, c, gq);
-            fetch_out_p(first, ws_P, p_base_of(0), w, c, gq);
-            lds_barrier();  // the chain waves' first chunk
-            lds_barrier();
-            if (nchunks & 1) {
-                out_step(1, fb, fa);
-                i0 = 2;
-            }
+        fetch_out(fa, 0);
+        fetch_stage(sb, min(1, nchunks - 1));
+        lds_barrier();  // chunk 0 staged
+        int i = 0;
+        for (; i + 1 < nchunks; i += 2) {
+            step(i, fa, fb, sb, sa);
+            step(i + 1, fb, fa, sa, sb);
         }
-        for (int i = i0; i <= nchunks; i += 2) {
-            out_step(i, fa, fb);
-            out_step(i + 1, fb, fa);
-        }
+        if (i < nchunks) step(i, fa, fb, sb, sa);
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // workspace layout (each region 256-byte aligned):
 //   chunk_start [N+1] int32 | order [N] int32 | G2 [slots][Hv][64] f32
-//   | -W [slots][Hv][64][128] bf16 | Ut [slots][Hv][64][dv] f32 | K^T [slots][Hk][128][64] bf16
-//   | P [slots][Hv][hi, lo][64][64] bf16
+//   | M [slots][Hv][hi, lo][64][64] bf16
 struct Layout {
-    size_t chunk_start, order, G, Wn, U, Kt, P, total;
+    size_t chunk_start, order, G, M, total;
     int slots;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout layout(int B, int T, int Hk, int Hv, int dv, int N) {
+Layout layout(int B, int T, int Hv, int N) {
     Layout l;
     l.slots = (int)(((long long)B * T) / kC) + N;  // bounds B*ceil(T/64) and T/64 + N (packed)
     size_t off = 0;
     l.chunk_start = off; off = align256(off + sizeof(int32_t) * (size_t)(N + 1));
     l.order = off;       off = align256(off + sizeof(int32_t) * (size_t)N);
     l.G = off;           off = align256(off + sizeof(float) * (size_t)l.slots * Hv * kC);
-    l.Wn = off;          off = align256(off + 2 * (size_t)l.slots * Hv * kC * kDK);
-    l.U = off;           off = align256(off + sizeof(float) * (size_t)l.slots * Hv * kC * dv);
-    l.Kt = off;          off = align256(off + 2 * (size_t)l.slots * Hk * kDK * kC);
-    l.P = off;           off = align256(off + 2 * (size_t)l.slots * Hv * 2 * kC * kC);
+    l.M = off;           off = align256(off + 2 * (size_t)l.slots * Hv * 2 * kC * kC);
     l.total = off;
     return l;
 }
 
-template <int DV>
-hipError_t launch_state(const ChunkArgs& a, const Layout& lay, char* ws, int nct) {
-    const int units = a.N * a.Hv;
-    const int groups = (units + 7) / 8;
-    const dim3 grid((unsigned)(groups * 8 * (DV / kWS))), block(kStateThreads);
-    const bool packed = a.cu_seqlens != nullptr;
-    hipLaunchKernelGGL((chunk_state_kernel<DV>), grid, block, 0, a.stream,
-                       static_cast<const __bf16*>(a.q), a.initial_state, a.cu_seqlens,
-                       packed ? reinterpret_cast<const int32_t*>(ws + lay.chunk_start) : nullptr,
-                       packed ? reinterpret_cast<const int32_t*>(ws + lay.order) : nullptr,
-                       a.N, a.T, a.Hk, a.Hv, nct, packed ? lay.slots : a.B * nct,
-                       reinterpret_cast<const __bf16*>(ws + lay.Wn),
-                       reinterpret_cast<const float*>(ws + lay.U),
-                       reinterpret_cast<const float*>(ws + lay.G),
-                       reinterpret_cast<const __bf16*>(ws + lay.Kt),
-                       reinterpret_cast<const __bf16*>(ws + lay.P), a.o, a.final_state);
-    return hipGetLastError();
-}
-
 template <int DV, typename TG>
 hipError_t launch_dv(const ChunkArgs& a) {
-    const Layout lay = layout(a.B, a.T, a.Hk, a.Hv, DV, a.N);
+    const Layout lay = layout(a.B, a.T, a.Hv, a.N);
     char* ws = static_cast<char*>(a.workspace);
     const bool packed = a.cu_seqlens != nullptr;
     const int nct = (a.T + kC - 1) / kC;
     const int slots = packed ? lay.slots : a.B * nct;
+    const int32_t* chunk_start = packed ? reinterpret_cast<const int32_t*>(ws + lay.chunk_start) : nullptr;
+    const int32_t* order = packed ? reinterpret_cast<const int32_t*>(ws + lay.order) : nullptr;
+    float* ws_G = reinterpret_cast<float*>(ws + lay.G);
+    __bf16* ws_M = reinterpret_cast<__bf16*>(ws + lay.M);
+    hipError_t e;
     if (packed) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, a.stream, a.cu_seqlens, a.N,
                            a.T, reinterpret_cast<int32_t*>(ws + lay.chunk_start),
                            reinterpret_cast<int32_t*>(ws + lay.order));
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (slots > 0) {
-        hipLaunchKernelGGL((chunk_prep_kernel<DV, TG>), dim3((unsigned)slots, (unsigned)a.Hv),
-                           dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.q),
-                           static_cast<const __bf16*>(a.k),
-                           static_cast<const __bf16*>(a.v), static_cast<const TG*>(a.g),
-                           static_cast<const TG*>(a.beta), a.cu_seqlens,
-                           packed ? reinterpret_cast<const int32_t*>(ws + lay.chunk_start) : nullptr,
-                           a.N, a.T, a.Hk, a.Hv, nct,
-                           reinterpret_cast<__bf16*>(ws + lay.Wn), reinterpret_cast<float*>(ws + lay.U),
-                           reinterpret_cast<float*>(ws + lay.G), reinterpret_cast<__bf16*>(ws + lay.Kt),
-                           reinterpret_cast<__bf16*>(ws + lay.P));
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((chunk_solve_kernel<TG>), dim3((unsigned)slots, (unsigned)a.Hv),
+                           dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.k),
+                           static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta),
+                           a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    return launch_state<DV>(a, lay, ws, nct);
+    const auto kern = chunk_fused_kernel<DV>;
+    const size_t bytes = sizeof(FusedLds);
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)) != hipSuccess)
+        return e;
+    const int units = a.N * a.Hv;
+    const int groups = (units + 7) / 8;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(groups * 8 * (DV / kWS))), dim3(kFusedThreads), bytes,
+                       a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), a.initial_state, a.cu_seqlens, chunk_start,
+                       order, a.N, a.T, a.Hk, a.Hv, nct, packed ? lay.slots : a.B * nct, ws_G, ws_M,
+                       a.o, a.final_state);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -818,8 +746,10 @@ bool chunk_mfma_supported(int dk, int dv, gdn_dtype qkv_dtype) {
 }
 
 size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N) {
+    (void)Hk;
     (void)dk;
-    return layout(B, T, Hk, Hv, dv, N).total;
+    (void)dv;
+    return layout(B, T, Hv, N).total;
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a) {
