@@ -1,17 +1,22 @@
 """Benchmark: prefill tokens/s and decode state GB/s of the gated delta rule on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
+    python bench.py --copy-calibration      (a plain 256 MiB device copy, for HBM counter scaling)
 
 Prints ONE JSON line.  The timed step is one gdn_chunk_fwd call over the Qwen3-Next-shaped prefill
 workload (B=1, T=4096, 16 q/k heads, 32 v heads, head dim 128, bf16 inputs, fp32 state and output),
-inputs resident in HBM.  ``value`` is prefill tokens/s over K back-to-back steps.  The same run also
-times the decode workload (256 sequences, 2 MiB fp32 state each, D one-token steps of
-gdn_recurrent_step) and reports its state GB/s under ``decode``.
+inputs resident in HBM.  ``value`` is prefill tokens/s over K back-to-back steps.  The same run then
+times the call's two halves on their own (gdn_chunk_fwd_prepare: every chunk's triangular solve;
+gdn_chunk_fwd_scan: the in-order pass, the dominant kernel, which ``roofline`` describes), and the
+decode workload (256 sequences, 2 MiB fp32 state each, D one-token steps of gdn_recurrent_step),
+reported under ``decode``.
 
 Roofline figures use algorithmic work only:
   prefill, per (token, v-head): bytes  = q,k (bf16, shared by Hv/Hk v-heads) + v (bf16) + g, beta
                                          (bf16) + o (fp32) = 1028 B at d = 128, G = 2;
                                          plus the fp32 initial/final state per (sequence, v-head).
+                                         The scan kernel's share is the same without g and beta
+                                         (1024 B), which its roofline uses.
                                  flops = 6 dk dv + C (3 dk + 2 dv)  (C = 64; the three d x d
                                          contractions per token and the lower-triangular intra-chunk
                                          products, the triangular solve not counted).
@@ -34,6 +39,11 @@ MI355X_BF16_TFLOPS = 2500.0    # dense bf16 matrix peak, TFLOP/s
 CHUNK = 64
 
 METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next shape, 1 GPU"
+
+# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
+# reads on a plain copy of known size (profiles/); None whenever the kernel changed since.
+TRAFFIC_SCAN = 204.2e6
+TRAFFIC_DECODE = 1084.9e6
 
 
 def prefill_algorithmic(wl, T: int, B: int, N: int, init_state: bool):
@@ -62,6 +72,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the gated delta "
@@ -76,6 +88,17 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                          "launches": 4}), flush=True)
+        return 0
+
     # ---------------- prefill -----------------------------------------------------------------
     wl = synth.WORKLOADS["prefill"]
     x = synth.make(wl)
@@ -88,9 +111,9 @@ def main() -> int:
     ws_bytes = workspace_size(B, T, wl.Hk, wl.Hv, wl.dk, wl.dv, N, wl.dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
-    def prefill_step():
+    def prefill_step(stage="all"):
         gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], None,
-                      o=o, final_state=fs, workspace=ws)
+                      o=o, final_state=fs, workspace=ws, stage=stage)
 
     for _ in range(args.warmup):
         prefill_step()
@@ -109,7 +132,25 @@ def main() -> int:
     tokens = B * T
     value = tokens / (ms_wall / 1e3)
     nbytes, flops, per_tok_head = prefill_algorithmic(wl, T, B, N, wl.init_state)
-    achieved_gbs = nbytes / (ms_events / 1e3) / 1e9
+    gate_bytes = B * T * wl.Hv * 2 * (2 if str(wl.gate_dtype).endswith("bfloat16") else 4)
+    scan_bytes = nbytes - gate_bytes
+
+    # the two halves on their own, each timed with events on the stream the kernels run on
+    # (torch's current stream, which the binding passes to the library)
+    def time_stage(stage):
+        prefill_step("prepare")     # scan reads what prepare left in the workspace
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            prefill_step(stage)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_prepare = time_stage("prepare")
+    ms_scan = time_stage("scan")
+    achieved_gbs = scan_bytes / (ms_scan / 1e3) / 1e9
     useful_tflops = flops / (ms_events / 1e3) / 1e12
 
     # ---------------- decode ------------------------------------------------------------------
@@ -169,11 +210,15 @@ def main() -> int:
                                f"state/out, zero initial state",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": MI355X_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved_gbs / MI355X_HBM_GBS, 4), "traffic": None,
-                     "kernel": "gdn_chunk_fwd (all kernels of one call)",
-                     "ms_per_launch_events": round(ms_events, 5),
-                     "algorithmic_bytes_per_launch": int(nbytes),
-                     "bytes_per_token_vhead": per_tok_head,
+                     "unit": "GB/s", "frac": round(achieved_gbs / MI355X_HBM_GBS, 4),
+                     "traffic": TRAFFIC_SCAN,
+                     "kernel": "chunk_fused_kernel (gdn_chunk_fwd_scan)",
+                     "ms_per_launch_events": round(ms_scan, 5),
+                     "algorithmic_bytes_per_launch": int(scan_bytes),
+                     "bytes_per_token_vhead": per_tok_head - 2 * (2 if str(wl.gate_dtype).endswith("bfloat16") else 4),
+                     "prepare_ms_per_launch_events": round(ms_prepare, 5),
+                     "call_ms_per_launch_events": round(ms_events, 5),
+                     "call_achieved_gbs": round(nbytes / (ms_events / 1e3) / 1e9, 1),
                      "useful_tflops": round(useful_tflops, 2),
                      "mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4)},
         "cpu_baseline": cpu,
@@ -183,7 +228,7 @@ def main() -> int:
                    "ms_per_step": round(ms_decode, 5),
                    "roofline": {"bound": "hbm", "achieved": round(total_gbs, 1), "peak": MI355X_HBM_GBS,
                                 "unit": "GB/s", "frac": round(total_gbs / MI355X_HBM_GBS, 4),
-                                "traffic": None, "kernel": "recurrent_kernel<128,128,bf16,f32>",
+                                "traffic": TRAFFIC_DECODE, "kernel": "recurrent_kernel<128,128,bf16,f32>",
                                 "algorithmic_bytes_per_launch": int(total_bytes)}},
     }
     print(json.dumps(line), flush=True)

@@ -17,7 +17,7 @@ GDN_F32 = 0
 GDN_BF16 = 1
 
 EXPORTED = ("gdn_status_string", "gdn_version", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
-            "gdn_recurrent_step")
+            "gdn_chunk_fwd_prepare", "gdn_chunk_fwd_scan", "gdn_recurrent_step")
 
 _lib = None
 
@@ -44,8 +44,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_version.argtypes = []
     lib.gdn_chunk_fwd_workspace_size.restype = sz
     lib.gdn_chunk_fwd_workspace_size.argtypes = [i32] * 7 + [i32]
-    lib.gdn_chunk_fwd.restype = i32
-    lib.gdn_chunk_fwd.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp, vp, sz, vp]
+    for name in ("gdn_chunk_fwd", "gdn_chunk_fwd_prepare", "gdn_chunk_fwd_scan"):
+        fn = getattr(lib, name)
+        fn.restype = i32
+        fn.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp, vp, sz, vp]
     lib.gdn_recurrent_step.restype = i32
     lib.gdn_recurrent_step.argtypes = [vp] * 6 + [i32] * 6 + [i32, i32] + [vp, vp]
     _lib = lib

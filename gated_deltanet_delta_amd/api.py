@@ -55,11 +55,21 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, *, o: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  workspace: Optional[torch.Tensor] = None,
+                  stage: str = "all") -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunk-parallel prefill.  q,k [B,T,Hk,dk]; v [B,T,Hv,dv]; g,beta [B,T,Hv];
     initial_state [N,Hv,dk,dv] fp32 or None; cu_seqlens int32 [N+1] (B == 1) or None.
-    Returns (o [B,T,Hv,dv] fp32, final_state [N,Hv,dk,dv] fp32)."""
+    Returns (o [B,T,Hv,dv] fp32, final_state [N,Hv,dk,dv] fp32).
+
+    ``stage`` selects gdn_chunk_fwd ("all"), gdn_chunk_fwd_prepare ("prepare") or
+    gdn_chunk_fwd_scan ("scan"); the halves must be called in that order with the same tensors
+    and workspace."""
     lib = _lib.load()
+    try:
+        fn = {"all": lib.gdn_chunk_fwd, "prepare": lib.gdn_chunk_fwd_prepare,
+              "scan": lib.gdn_chunk_fwd_scan}[stage]
+    except KeyError:
+        raise ValueError(f"stage must be 'all', 'prepare' or 'scan', not {stage!r}") from None
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, T, H, d]")
     B, T, Hk, dk = q.shape
@@ -90,13 +100,13 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     if workspace is not None:
         if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
             raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
-    st = lib.gdn_chunk_fwd(
+    st = fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
         B, T, Hk, Hv, dk, dv, N, qkv, gate, _ptr(o), _ptr(final_state), _ptr(workspace),
         ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
         _stream(dev))
     if st != _lib.GDN_SUCCESS:
-        raise _lib.GdnError(st, "gdn_chunk_fwd")
+        raise _lib.GdnError(st, fn.__name__)
     return o, final_state
 
 

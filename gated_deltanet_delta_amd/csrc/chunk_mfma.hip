@@ -700,7 +700,7 @@ Layout layout(int B, int T, int Hv, int N) {
 }
 
 template <int DV, typename TG>
-hipError_t launch_dv(const ChunkArgs& a) {
+hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
     const Layout lay = layout(a.B, a.T, a.Hv, a.N);
     char* ws = static_cast<char*>(a.workspace);
     const bool packed = a.cu_seqlens != nullptr;
@@ -711,19 +711,20 @@ hipError_t launch_dv(const ChunkArgs& a) {
     float* ws_G = reinterpret_cast<float*>(ws + lay.G);
     __bf16* ws_M = reinterpret_cast<__bf16*>(ws + lay.M);
     hipError_t e;
-    if (packed) {
+    if ((stages & kStagePrepare) && packed) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, a.stream, a.cu_seqlens, a.N,
                            a.T, reinterpret_cast<int32_t*>(ws + lay.chunk_start),
                            reinterpret_cast<int32_t*>(ws + lay.order));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (slots > 0) {
+    if ((stages & kStagePrepare) && slots > 0) {
         hipLaunchKernelGGL((chunk_solve_kernel<TG>), dim3((unsigned)slots, (unsigned)a.Hv),
                            dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.k),
                            static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta),
                            a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    if (!(stages & kStageScan)) return hipSuccess;
     const auto kern = chunk_fused_kernel<DV>;
     const size_t bytes = sizeof(FusedLds);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -752,10 +753,10 @@ size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, i
     return layout(B, T, Hv, N).total;
 }
 
-hipError_t launch_chunk_mfma(const ChunkArgs& a) {
+hipError_t launch_chunk_mfma(const ChunkArgs& a, unsigned stages) {
     const bool g_bf16 = a.gate_dtype == GDN_BF16;
-    if (a.dv == 128) return g_bf16 ? launch_dv<128, bf16_t>(a) : launch_dv<128, float>(a);
-    return g_bf16 ? launch_dv<64, bf16_t>(a) : launch_dv<64, float>(a);
+    if (a.dv == 128) return g_bf16 ? launch_dv<128, bf16_t>(a, stages) : launch_dv<128, float>(a, stages);
+    return g_bf16 ? launch_dv<64, bf16_t>(a, stages) : launch_dv<64, float>(a, stages);
 }
 
 }  // namespace gdn

@@ -53,11 +53,16 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
     return gdn::chunk_mfma_workspace_size(B, T, Hk, Hv, dk, dv, N);
 }
 
-gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
-                         const void* beta, const float* initial_state, const int32_t* cu_seqlens,
-                         int B, int T, int Hk, int Hv, int dk, int dv, int N,
-                         gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o, float* final_state,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of gdn_chunk_fwd and its two halves: checks, then the selected stages.
+gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                      const float* initial_state, const int32_t* cu_seqlens, int B, int T, int Hk,
+                      int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                      float* o, float* final_state, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream, unsigned stages) {
     if (!final_state) return GDN_ERROR_INVALID_VALUE;
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERROR_INVALID_VALUE;
     if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
@@ -81,11 +86,47 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void
         const size_t need = gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype);
         if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
             return GDN_ERROR_WORKSPACE;
-        e = gdn::launch_chunk_mfma(a);
+        e = gdn::launch_chunk_mfma(a, stages);
     } else {
-        e = gdn::launch_chunk_f32(a);
+        e = (stages & gdn::kStageScan) ? gdn::launch_chunk_f32(a) : hipSuccess;
     }
     return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                         int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                         gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return chunk_call(q, k, v, g, beta, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+                      qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
+                      gdn::kStagePrepare | gdn::kStageScan);
+}
+
+gdn_status gdn_chunk_fwd_prepare(const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, int B, int T, int Hk, int Hv, int dk,
+                                 int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
+                                 float* final_state, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    return chunk_call(q, k, v, g, beta, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+                      qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
+                      gdn::kStagePrepare);
+}
+
+gdn_status gdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, const float* initial_state,
+                              const int32_t* cu_seqlens, int B, int T, int Hk, int Hv, int dk,
+                              int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
+                              float* final_state, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    return chunk_call(q, k, v, g, beta, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+                      qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
+                      gdn::kStageScan);
 }
 
 gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const void* g,

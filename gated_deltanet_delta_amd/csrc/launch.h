@@ -46,6 +46,9 @@ hipError_t launch_chunk_f32(const ChunkArgs& a);
 // Chunked kernels on bf16 matrix cores (bf16 inputs).
 bool chunk_mfma_supported(int dk, int dv, gdn_dtype qkv_dtype);
 size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N);
-hipError_t launch_chunk_mfma(const ChunkArgs& a);
+// Stages of a chunked call: prepare (every chunk in parallel: log-decay sums and the per-chunk
+// triangular solve, into the workspace) and scan (the chunks in order).  A full call runs both.
+constexpr unsigned kStagePrepare = 1u, kStageScan = 2u;
+hipError_t launch_chunk_mfma(const ChunkArgs& a, unsigned stages);
 
 }  // namespace gdn

@@ -116,6 +116,36 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          hipStream_t stream);
 
 /*
+ * gdn_chunk_fwd_prepare, gdn_chunk_fwd_scan -- the two halves of gdn_chunk_fwd.
+ *
+ * gdn_chunk_fwd(args) is exactly gdn_chunk_fwd_prepare(args) followed by gdn_chunk_fwd_scan(args)
+ * on the same stream, with the same arguments and the same workspace.  prepare does the work that
+ * is independent across chunks, every chunk at once (per-chunk log-decay sums and the chunk's
+ * triangular solve, the UT/WY step of the jsqmd.com article's section 2.2 chunk form), and leaves
+ * it in the workspace; scan walks each sequence's chunks in order and writes o and final_state.
+ * The split exists so that a caller can time or schedule the two phases separately; between the
+ * two calls the workspace must not be touched, and scan must not run before prepare has finished
+ * on its stream.  Arguments, checks and status codes are those of gdn_chunk_fwd (both halves check
+ * all of them).  For fp32 inputs prepare enqueues nothing and scan does the whole call.
+ */
+gdn_status gdn_chunk_fwd_prepare(const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 const float* initial_state, const int32_t* cu_seqlens,
+                                 int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                 gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                                 float* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+gdn_status gdn_chunk_fwd_scan(const void* q, const void* k, const void* v,
+                              const void* g, const void* beta,
+                              const float* initial_state, const int32_t* cu_seqlens,
+                              int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                              gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                              float* o, float* final_state,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * gdn_recurrent_step -- decode against a cached state (recurrent_gated_delta_rule).
  *
  * Advances B independent cached states by T tokens each (T == 1 is the usual decode step),

@@ -44,10 +44,13 @@ def test_status_strings_and_version(lib):
     assert lib.gdn_version() >= 100
 
 
+CHUNK_CALLS = ("gdn_chunk_fwd", "gdn_chunk_fwd_prepare", "gdn_chunk_fwd_scan")
+
+
 def chunk(lib, q=P, k=P, v=P, g=P, beta=P, s0=None, cu=None, B=1, T=64, Hk=1, Hv=1, dk=64, dv=64,
-          N=1, qkv=F32, gate=F32, o=P, fs=P, ws=None, ws_bytes=0):
-    return lib.gdn_chunk_fwd(q, k, v, g, beta, s0, cu, B, T, Hk, Hv, dk, dv, N, qkv, gate, o, fs, ws,
-                             ctypes.c_size_t(ws_bytes), None)
+          N=1, qkv=F32, gate=F32, o=P, fs=P, ws=None, ws_bytes=0, fn="gdn_chunk_fwd"):
+    return getattr(lib, fn)(q, k, v, g, beta, s0, cu, B, T, Hk, Hv, dk, dv, N, qkv, gate, o, fs, ws,
+                            ctypes.c_size_t(ws_bytes), None)
 
 
 def rec(lib, q=P, k=P, v=P, g=P, beta=P, state=P, B=1, T=1, Hk=1, Hv=1, dk=64, dv=64, qkv=F32,
@@ -68,8 +71,10 @@ def rec(lib, q=P, k=P, v=P, g=P, beta=P, state=P, B=1, T=1, Hk=1, Hv=1, dk=64, d
     (dict(dk=96), UNSUPPORTED), (dict(dv=32), UNSUPPORTED), (dict(dk=256, dv=256), UNSUPPORTED),
     (dict(dk=0), INVALID),
 ])
-def test_chunk_rejects(lib, kw, status):
-    assert chunk(lib, **kw) == status
+@pytest.mark.parametrize("fn", CHUNK_CALLS)
+def test_chunk_rejects(lib, kw, status, fn):
+    # the two halves of gdn_chunk_fwd check exactly what the whole call checks
+    assert chunk(lib, fn=fn, **kw) == status
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -95,16 +100,15 @@ def test_workspace_query_is_host_only(lib):
     assert big >= small
 
 
-def test_too_small_workspace_is_rejected(lib):
+@pytest.mark.parametrize("fn", CHUNK_CALLS)
+def test_too_small_workspace_is_rejected(lib, fn):
     need = lib.gdn_chunk_fwd_workspace_size(1, 4096, 16, 32, 128, 128, 1, BF16)
     if need == 0:
         pytest.skip("this build's bf16 path needs no workspace")
-    assert chunk(lib, T=4096, Hk=16, Hv=32, dk=128, dv=128, qkv=BF16, gate=BF16,
-                 ws=None, ws_bytes=0) == WORKSPACE
-    assert chunk(lib, T=4096, Hk=16, Hv=32, dk=128, dv=128, qkv=BF16, gate=BF16,
-                 ws=P, ws_bytes=need - 1) == WORKSPACE
-    assert chunk(lib, T=4096, Hk=16, Hv=32, dk=128, dv=128, qkv=BF16, gate=BF16,
-                 ws=P + 16, ws_bytes=need) == WORKSPACE               # 256-byte alignment
+    kw = dict(T=4096, Hk=16, Hv=32, dk=128, dv=128, qkv=BF16, gate=BF16, fn=fn)
+    assert chunk(lib, ws=None, ws_bytes=0, **kw) == WORKSPACE
+    assert chunk(lib, ws=P, ws_bytes=need - 1, **kw) == WORKSPACE
+    assert chunk(lib, ws=P + 16, ws_bytes=need, **kw) == WORKSPACE    # 256-byte alignment
 
 
 def test_binding_refuses_cpu_tensors():

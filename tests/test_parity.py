@@ -120,6 +120,26 @@ def test_packed_matches_separate_calls_bitwise_per_sequence():
         assert torch.equal(sn.cpu(), fs[n:n + 1].cpu()), n
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_prepare_then_scan_equals_full_call_bitwise(packed):
+    # gdn_chunk_fwd is gdn_chunk_fwd_prepare followed by gdn_chunk_fwd_scan on one stream
+    if packed:
+        wl = with_dims(WL["varlen"], n_seqs=3, Hk=2, Hv=4)
+        x = synth.make(wl, lengths=np.array([130, 0, 64]), seed=43)
+    else:
+        x = synth.make(with_dims(WL["long"], Hk=2, Hv=4), T=200, seed=44)
+    d = to_gpu(x)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], d["cu_seqlens"])
+    o1, s1 = gdn_chunk_fwd(*args)
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    o2 = torch.full_like(o1, float("nan"))
+    s2 = torch.full_like(s1, float("nan"))
+    gdn_chunk_fwd(*args, o=o2, final_state=s2, workspace=ws, stage="prepare")
+    gdn_chunk_fwd(*args, o=o2, final_state=s2, workspace=ws, stage="scan")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
 def test_final_state_in_place():
     wl = with_dims(WL["long"], Hk=2, Hv=4)
     x = synth.make(wl, T=300, seed=51)
