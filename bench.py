@@ -42,7 +42,7 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
 # reads on a plain copy of known size (profiles/); None whenever the kernel changed since.
-TRAFFIC_SCAN = 204.2e6
+TRAFFIC_SCAN = None
 TRAFFIC_DECODE = 1084.9e6
 
 
@@ -212,7 +212,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": MI355X_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / MI355X_HBM_GBS, 4),
                      "traffic": TRAFFIC_SCAN,
-                     "kernel": "chunk_fused_kernel (gdn_chunk_fwd_scan)",
+                     "kernel": "chunk_scan_kernel<128> (gdn_chunk_fwd_scan)",
                      "ms_per_launch_events": round(ms_scan, 5),
                      "algorithmic_bytes_per_launch": int(scan_bytes),
                      "bytes_per_token_vhead": per_tok_head - 2 * (2 if str(wl.gate_dtype).endswith("bfloat16") else 4),

@@ -29,10 +29,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}", f"-I{
 
 SOURCES = ["gdn_api.cpp", "recurrent.hip", "chunk_f32.hip", "chunk_mfma.hip"]
 
+# Per-source code-generation options.  chunk_mfma.hip: matrix-core results go to ordinary VGPRs
+# (not AGPRs), because every product there is post-processed on the vector ALU (splits, decays),
+# and an AGPR result would cost one copy instruction per element.
+EXTRA = {"chunk_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "hip", *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
