@@ -341,49 +341,56 @@ __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------
-// chunk_scan_kernel: one workgroup of four waves per (sequence, v-head, 32 columns of S).
+// chunk_scan_kernel: one workgroup of five waves per (sequence, v-head, 16-column slice of S).
 //
-// Waves 0 and 1 are chain waves.  Each owns one 16-column slice of S whole (128 keys x 16 columns,
-// eight 16 x 16 fp32 accumulator tiles), so the chunk step
-//     KS = K S,   X = V - diag(e^G) KS,   U = M X,   D = diag(e^(G_C - G)) U,
-//     S <- e^(G_C) S + K^T D
-// runs inside one wave with no reduction across waves: every product's result stays in registers
-// and is fed straight back as the next product's B operand.  For that the accumulator rows are
-// given a fixed permutation of keys and tokens: row m (m = 4g + r) of tile a stands for index
+// The slice (128 keys x 16 columns) is carried by two chain waves, one per half of the keys (four
+// 16 x 16 fp32 accumulator tiles each).  Per chunk:
+//     KS = K S                     each half forms its partial over its 64 keys; the partials meet
+//                                  in LDS (barrier B1) and both halves add them in the same order
+//     X = V - diag(e^G) KS,  U = M X,  D = diag(e^(G_C - G)) U      (both halves, identically)
+//     S <- e^(G_C) S + K^T D       each half updates its own keys
+// Every product's result stays in registers and feeds the next product as its B operand.  For that
+// accumulator rows stand for a fixed permutation of keys or tokens: row m (m = 4g + r) of tile a
+// stands for index
 //     rho(a, m) = 32 (a / 2) + 8 (m / 4) + 4 (a % 2) + m % 4,
 // so that tiles 2j and 2j + 1 together hand lane (g, c) the eight consecutive indices
-// 32 j + 8 g .. + 7: exactly the B-operand fragment of a 32-deep product.  The A operands are then
-// plain 16-byte rows (K rows from LDS, M rows from memory), and K^T for the state update comes from
-// the same K rows through ds_read_b64_tr_b16.
+// 32 j + 8 g .. + 7, exactly the B-operand fragment of a 32-deep product.  (K S tiles use natural
+// token rows instead; the solve kernel stores M's columns in the matching order.)  A operands are
+// plain 16-byte rows (K from LDS, M from memory); K^T for the state update comes from the same K
+// rows through ds_read_b64_tr_b16.
 //
-// Waves 2 and 3 are output waves, running one chunk behind the chain.  Output wave w' owns token
-// tiles {0, 3} (w' = 0) or {1, 2} (w' = 1) of O^T = S^T Q^T diag(e^G) + U^T P^T for both slices
-// (tokens in natural order here): P^T tiles = K Q^T (masked, decayed) in registers, S^T and U^T
-// from the copies the chain waves leave in LDS.  They also stage the next chunk's K rows, V columns
-// and gate block into a three-chunk LDS ring.
+// Two output waves run one chunk behind: output wave w' owns token tiles {w', 3 - w'} of
+// O^T = S^T Q^T diag(e^G) + U^T P^T, with P^T tiles = K Q^T (masked, decayed) in registers and S^T,
+// U^T from the copies the chain waves leave in LDS.  A staging wave copies each chunk's K rows, V
+// columns and gate block straight from memory into a four-chunk LDS ring (global_load_lds), two
+// chunks ahead of their use.
 //
-// One LDS barrier per chunk step.  At step s: chain waves do chunk s (read ring slot s % 3, write
-// S/U copies to buffer s % 2); output waves finish chunk s - 1 (ring slot (s - 1) % 3, buffer
-// (s - 1) % 2) and store chunk s + 1 into ring slot (s + 1) % 3.
-constexpr int kScanThreads = 256;
-constexpr int kWS = 16;          // state columns per chain wave
-constexpr int kSlices = 2;       // chain waves (16-column slices) per workgroup
+// Waves 0 and 1 (chain) and 2 and 3 (output) have a SIMD each; the staging wave shares SIMD 0 at
+// the lowest priority (the chain waves raise theirs).  Two LDS barriers per chunk step: B1 for the
+// K S partials and B2 at the end.  At step s chain waves do chunk s (ring slot s % 4, copy buffer
+// s % 2); output waves finish chunk s - 1 (slot (s - 1) % 4, buffer (s - 1) % 2); the staging wave
+// starts chunk s + 2's copy into slot (s + 2) % 4 after B1 and waits for chunk s + 1's before B2.
+constexpr int kScanThreads = 320;
+constexpr int kWS = 16;          // state columns per workgroup
 constexpr int kSP = kDK + 8;     // row pitch of the S^T copies [column][key]
 constexpr int kUP = kC + 8;      // row pitch of the U^T copies [column][token]
-constexpr int kVP = 48;          // row pitch of the staged V columns [token][32 columns]
-// K ring rows: pitch kKR elements (320 bytes, 20 sixteen-byte chunks), and the 16-byte chunk q of
-// row t stored at chunk q ^ ((t >> 2) & 3).  With 64 four-byte banks, both ways the rows are read
-// then touch 16 different chunk positions per 16 lanes: a row fragment (16 rows, one chunk each,
-// rows t..t+15) and a transposed fragment (4 consecutive rows x 4 consecutive chunks).
+constexpr int kRing = 4;         // chunks in the staging ring
+// K ring rows: pitch kKR elements (320 bytes, 20 sixteen-byte chunks, the last 4 unused), and the
+// 16-byte chunk q of row t stored at chunk q ^ ((t >> 2) & 3).  With 64 four-byte banks, both ways
+// the rows are read then touch 16 different chunk positions per 16 lanes: a row fragment (16
+// rows, one chunk each) and a transposed fragment (4 consecutive rows x 4 consecutive chunks).
 constexpr int kKR = 160;
+constexpr int kKDma = kC * kKR * 2 / 1024;   // 1 KiB copy instructions per K slot (20)
+constexpr int kDmaOps = kKDma + 2 + 1;      // per chunk: K, V (2 KiB), gate block (768 bytes)
 __host__ __device__ constexpr int kswz(int t) { return (t >> 2) & 3; }
 
 struct ScanLds {
-    __bf16 Kr[3][kC * kKR];                    // K rows [token][key], ring of three chunks
-    float Gt[3][3 * kC];                       // gate block: G2, 2^G2, 2^(G2_C - G2)
-    __bf16 Vr[3][kC * kVP];                    // V [token][this workgroup's 32 columns]
-    __bf16 Ut[kSlices][2][2][kWS * kUP];       // U^T [slice][buffer][hi, lo]
-    __bf16 St[kSlices][2][2][kWS * kSP];       // S^T at chunk start [slice][buffer][hi, lo]
+    __bf16 Kr[kRing][kC * kKR];                // K rows [token][key]
+    __bf16 Vr[kRing][kC * kWS];                // V [token][this slice's 16 columns]
+    float Gt[kRing][256];                      // gate block: G2, 2^G2, 2^(G2_C - G2) (+ unused)
+    __bf16 St[2][2][kWS * kSP];                // S^T at chunk start [buffer][hi, lo]
+    __bf16 Ut[2][2][kWS * kUP];                // U^T [buffer][hi, lo]
+    f32x4 Ex[2][4][64];                        // partial K S [key half][token tile][lane]
 };
 
 // index (token or key) that accumulator row m of tile a stands for
@@ -403,6 +410,8 @@ __device__ __forceinline__ bf16x8 kt_frag(lds_u8* k0, lds_u8* k1, int kt, int kb
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) void glb_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // two floats -> two RNE bf16 values packed in one register (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ unsigned pack_bf16x2(float x0, float x1) {
@@ -424,8 +433,20 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
     l = __builtin_bit_cast(bf16x8, lp);
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes dst + 16 l
+__device__ __forceinline__ void copy_to_lds(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)dst, 16, 0, 0);
+}
+
 struct ChainIn {                   // one chunk's M fragments for a chain wave
-    bf16x8 mh[6], ml[6];           // M rows rho(a', c), columns 32 kb + 8 g ..: (a', kb) =
+    bf16x8 mh[6], ml[6];           // M rows rho(a', c), stored columns 32 kb + 8 g ..: (a', kb) =
                                    // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 };
 
@@ -433,36 +454,29 @@ struct OutIn {                     // one chunk's Q fragments for an output wave
     bf16x8 q[2][4];                // Q rows 16 a + c of its two tiles, columns 32 kb + 8 g ..
 };
 
-struct StageIn {                   // an output wave's half of one chunk's staged inputs
-    u32x4 k[8];                    // K piece e = lane + 64 (2 it + w'): row e / 16, columns 8 (e % 16)
-    u32x4 v[2];                    // V piece e = lane + 64 (2 it + w'): row e / 4, columns 8 (e % 4)
-    f32x4 gt;                      // gate piece lane (lanes < 24), 4 floats each per output wave
-};
-
 template <int DV>
-__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void chunk_scan_kernel(
+__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ order, int N, int T,
     int Hk, int Hv, int nct, int max_slots, const float* __restrict__ ws_G,
     const __bf16* __restrict__ ws_M, float* __restrict__ o, float* final_state) {
-    constexpr int NP = DV / (kWS * kSlices);  // column pairs per v-head
+    constexpr int NS = DV / kWS;  // slices per v-head
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     ScanLds& sm = *reinterpret_cast<ScanLds*>(smem_raw);
 
     // blockIdx -> (group, member): a group is one (sequence, q/k head); its members are the
-    // (v-head, column pair) workgroups that read the same q and k.  All members of a group share
+    // (v-head, slice) workgroups that read the same q and k.  All members of a group share
     // blockIdx % 8, hence one XCD and its L2.
-    const int Gq = Hv / Hk, MB = Gq * NP;
+    const int Gq = Hv / Hk, MB = Gq * NS;
     const int bid = blockIdx.x;
     const int xr = bid >> 3;
     const int member = xr % MB;
     const int grp = (xr / MB) * 8 + (bid & 7);
     if (grp >= N * Hk) return;
     const int rank = grp / Hk, kh = grp % Hk;
-    const int h = kh * Gq + member / NP;
-    const int pair = member % NP;
+    const int h = kh * Gq + member / NS;
+    const int c0 = (member % NS) * kWS;
     const int n = order ? order[rank] : rank;
     int row, t0, t1;
     sequence_range(cu_seqlens, n, T, row, t0, t1);
@@ -478,276 +492,235 @@ void chunk_scan_kernel(
     auto tok0_of = [&](int ci) { return (size_t)row * T + t0 + (size_t)ci * kC; };
     auto len_of = [&](int ci) { return min(kC, t1 - t0 - ci * kC); };
 
-    if (wave < kSlices) {
+    if (wave < 2) {
         // ------------------------------------------------ chain waves -------------------------
-        const int c0 = (pair * kSlices + wave) * kWS;
-        auto state_idx = [&](int kt, int r) {
-            return sbase + (size_t)rho(kt, 4 * g + r) * DV + c0 + c;
-        };
-        if (nchunks == 0) {  // zero-length sequence: the state passes through
+        auto chain = [&](auto hc) {
+            constexpr int hh = decltype(hc)::value;   // key half: state tiles 4 hh .. 4 hh + 3
+            auto state_idx = [&](int t, int r) {
+                return sbase + (size_t)rho(4 * hh + t, 4 * g + r) * DV + c0 + c;
+            };
+            if (nchunks == 0) {  // zero-length sequence: the state passes through
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    final_state[state_idx(kt, r)] = initial_state ? initial_state[state_idx(kt, r)] : 0.f;
-            return;
-        }
-        constexpr int ta[6] = {0, 1, 2, 2, 3, 3}, tb[6] = {0, 0, 0, 1, 0, 1};
-        auto fetch = [&](ChainIn& f, int ci) {
-            const __bf16* mb = ws_M + ((size_t)(slot0 + ci) * Hv + h) * 2 * kC * kC;
-#pragma unroll
-            for (int p = 0; p < 6; ++p) {
-                const __bf16* mp = mb + rho(ta[p], c) * kC + 32 * tb[p] + 8 * g;
-                f.mh[p] = *reinterpret_cast<const bf16x8*>(mp);
-                f.ml[p] = *reinterpret_cast<const bf16x8*>(mp + kC * kC);
+                    for (int r = 0; r < 4; ++r)
+                        final_state[state_idx(t, r)] = initial_state ? initial_state[state_idx(t, r)] : 0.f;
+                return;
             }
-        };
-
-        f32x4 S[8];
+            __builtin_amdgcn_s_setprio(2);
+            constexpr int ta[6] = {0, 1, 2, 2, 3, 3}, tb[6] = {0, 0, 0, 1, 0, 1};
+            auto fetch = [&](ChainIn& f, int ci) {
+                const __bf16* mb = ws_M + ((size_t)(slot0 + ci) * Hv + h) * 2 * kC * kC;
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[kt][r] = initial_state ? initial_state[state_idx(kt, r)] : 0.f;
-        // lane parts of the LDS addresses (the rest are compile-time offsets)
-        const int l_kf = c * kKR + 8 * (g ^ kswz(c));                     // K row c, logical chunk g
-        const int l_kt0 = (8 * g + (c >> 2)) * kKR + 8 * ((c & 3) ^ kswz(8 * g));
-        const int l_kt1 = (8 * g + 4 + (c >> 2)) * kKR + 8 * ((c & 3) ^ kswz(8 * g + 4));
-        const int l_v = (4 * g + (c >> 2)) * kVP + kWS * wave + 4 * (c & 3);
-        const int l_st = c * kSP + 8 * g, l_ut = c * kUP + 8 * g;
-
-        // one set of M registers: chunk i's fragments are consumed by U = M X, then the same
-        // registers are refilled with chunk i + 1's, a whole step ahead of their use
-        ChainIn mc;
-        auto step = [&](int i) {
-            const __bf16* kr = sm.Kr[i % 3];
-            const __bf16* vr = sm.Vr[i % 3];
-            const float* gt = sm.Gt[i % 3];
-            // K rows for K S, all issued before the first product
-            bf16x8 kf[4][4];                             // K rows 16 a + c, keys 32 j + 8 g ..
-            lds_u8* kfl = lds_at(kr + l_kf);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int a = 0; a < 4; ++a) kf[j][a] = ld<bf16x8>(kfl, 2 * (16 * a * kKR + 32 * j));
-            __builtin_amdgcn_sched_barrier(0);
-            // S as hi + lo B fragments (keys 32 j + 8 g + e)
-            bf16x8 sh[4], sl[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) split8(S[2 * j], S[2 * j + 1], sh[j], sl[j]);
-            // KS: token tile a, rows 16 a + m
-            f32x4 ks[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    ks[a] = mma(kf[j][a], sh[j], ks[a]);
-                    ks[a] = mma(kf[j][a], sl[j], ks[a]);
+                for (int p = 0; p < 6; ++p) {
+                    const __bf16* mp = mb + rho(ta[p], c) * kC + 32 * tb[p] + 8 * g;
+                    f.mh[p] = *reinterpret_cast<const bf16x8*>(mp);
+                    f.ml[p] = *reinterpret_cast<const bf16x8*>(mp + kC * kC);
                 }
-            __builtin_amdgcn_sched_barrier(0);
-            // V[16 a + 4 g + r][c0 + c], r = 0..3 (one transposed read of four consecutive rows),
-            // the decay factors, the first half of the K^T fragments; the S copy for the output
-            lds_u8* vl = lds_at(vr + l_v);
-            lds_u8* kt0 = lds_at(kr + l_kt0);
-            lds_u8* kt1 = lds_at(kr + l_kt1);
-            lds_u8* gl = lds_at(gt + 4 * g);
-            lds_u8* gd = lds_at(gt + 8 * g);
-            bf16x4 vv[4];
-            f32x4 eg[4], dg[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                vv[a] = read_tr(vl, 2 * 16 * a * kVP);
-                eg[a] = ld<f32x4>(gl, 4 * (kC + 16 * a));                   // 2^G2 at 16 a + 4 g + r
-                dg[a] = ld<f32x4>(gd, 4 * (2 * kC + 32 * (a >> 1) + 4 * (a & 1)));  // at rho(a, 4 g + r)
-            }
-            const float ec = gt[2 * kC - 1];
-            bf16x8 kt[8][2];
+            };
+
+            f32x4 S[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) kt[t][kb] = kt_frag(kt0, kt1, t, kb);
-            lds_u8* stb = lds_at(sm.St[wave][i & 1][0] + l_st);
+                for (int r = 0; r < 4; ++r) S[t][r] = initial_state ? initial_state[state_idx(t, r)] : 0.f;
+            // lane parts of the LDS addresses (the rest are compile-time offsets)
+            const int l_kf = c * kKR + 8 * (g ^ kswz(c));                 // K row c, logical chunk g
+            const int l_kt0 = (8 * g + (c >> 2)) * kKR + 8 * ((c & 3) ^ kswz(8 * g));
+            const int l_kt1 = (8 * g + 4 + (c >> 2)) * kKR + 8 * ((c & 3) ^ kswz(8 * g + 4));
+            const int l_v = (4 * g + (c >> 2)) * kWS + 4 * (c & 3);
+            const int l_st = c * kSP + 8 * g, l_ut = c * kUP + 8 * g;
+
+            // one set of M registers: chunk i's fragments are consumed by U = M X, then the same
+            // registers are refilled with chunk i + 1's, a whole step ahead of their use
+            ChainIn mc;
+            auto step = [&](int i) {
+                const int slot = i % kRing;
+                const __bf16* kr = sm.Kr[slot];
+                const float* gt = sm.Gt[slot];
+                // LDS operands that do not depend on B1, all issued up front: K rows 16 a + c at this
+                // half's keys (logical chunks 4 jj + g, jj = 2 hh + u); V[16 a + 4 g + r][c0 + c]
+                // (one transposed read of four consecutive rows); the decay factors; the K^T
+                // fragments of this half's keys
+                bf16x8 kf[2][4];
+                lds_u8* kfl = lds_at(kr + l_kf);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                st(stb, 2 * 32 * j, sh[j]);
-                st(stb, 2 * (kWS * kSP + 32 * j), sl[j]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // X = V - e^G KS as hi + lo B fragments (tokens 32 kb + 4 g + e for e < 4 and
-            // 32 kb + 16 + 4 g + e - 4 for e >= 4: the stored column order of M)
-            f32x4 xs[4];
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+                    for (int a = 0; a < 4; ++a)
+                        kf[u][a] = ld<bf16x8>(kfl, 2 * (16 * a * kKR + 32 * (2 * hh + u)));
+                lds_u8* vl = lds_at(sm.Vr[slot] + l_v);
+                lds_u8* gl = lds_at(gt + 4 * g);
+                lds_u8* gd = lds_at(gt + 8 * g);
+                bf16x4 vv[4];
+                f32x4 eg[4], dg[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) xs[a][r] = (float)vv[a][r] - eg[a][r] * ks[a][r];
-            bf16x8 xh[2], xl[2];
-            split8(xs[0], xs[1], xh[0], xl[0]);
-            split8(xs[2], xs[3], xh[1], xl[1]);
-            // U = M X (M lower triangular: token tiles 0, 1 need kb = 0 only)
-            f32x4 u[4], u2[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) { u[a] = zero4(); u2[a] = zero4(); }
-#pragma unroll
-            for (int p = 0; p < 6; ++p) {
-                u[ta[p]] = mma(mc.mh[p], xh[tb[p]], u[ta[p]]);
-                u2[ta[p]] = mma(mc.mh[p], xl[tb[p]], u2[ta[p]]);
-                u2[ta[p]] = mma(mc.ml[p], xh[tb[p]], u2[ta[p]]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            fetch(mc, min(i + 1, nchunks - 1));
-            // second half of the K^T fragments
-#pragma unroll
-            for (int t = 4; t < 8; ++t)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) kt[t][kb] = kt_frag(kt0, kt1, t, kb);
-            f32x4 ds[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                u[a] += u2[a];
-                ds[a] = u[a] * dg[a];
-            }
-            bf16x8 dh[2], dl[2];
-            split8(ds[0], ds[1], dh[0], dl[0]);
-            split8(ds[2], ds[3], dh[1], dl[1]);
-            // S <- e^(G_C) S + K^T D
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                f32x4 acc = S[t] * ec;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    acc = mma(kt[t][kb], dh[kb], acc);
-                    acc = mma(kt[t][kb], dl[kb], acc);
+                for (int a = 0; a < 4; ++a) {
+                    vv[a] = read_tr(vl, 2 * 16 * a * kWS);
+                    eg[a] = ld<f32x4>(gl, 4 * (kC + 16 * a));                   // 2^G2 at 16 a + 4 g + r
+                    dg[a] = ld<f32x4>(gd, 4 * (2 * kC + 32 * (a >> 1) + 4 * (a & 1)));  // at rho(a, 4 g + r)
                 }
-                S[t] = acc;
-            }
-            // U (hi + lo) for the output waves
-            bf16x8 uh[2], ul[2];
-            split8(u[0], u[1], uh[0], ul[0]);
-            split8(u[2], u[3], uh[1], ul[1]);
-            lds_u8* utb = lds_at(sm.Ut[wave][i & 1][0] + l_ut);
+                const float ec = gt[2 * kC - 1];
+                lds_u8* kt0 = lds_at(kr + l_kt0);
+                lds_u8* kt1 = lds_at(kr + l_kt1);
+                bf16x8 kt[4][2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                st(utb, 2 * 32 * kb, uh[kb]);
-                st(utb, 2 * (kWS * kUP + 32 * kb), ul[kb]);
-            }
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) kt[t][kb] = kt_frag(kt0, kt1, 4 * hh + t, kb);
+                __builtin_amdgcn_sched_barrier(0);
+                // this half of S as hi + lo B fragments (keys 32 jj + 8 g + e), and its copy for
+                // the output waves
+                bf16x8 sh[2], sl[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) split8(S[2 * u], S[2 * u + 1], sh[u], sl[u]);
+                lds_u8* stb = lds_at(sm.St[i & 1][0] + l_st);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    st(stb, 2 * 32 * (2 * hh + u), sh[u]);
+                    st(stb, 2 * (kWS * kSP + 32 * (2 * hh + u)), sl[u]);
+                }
+                // partial K S over this half's keys: token tile a, rows 16 a + m
+                f32x4 ks[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        ks[a] = mma(kf[u][a], sh[u], ks[a]);
+                        ks[a] = mma(kf[u][a], sl[u], ks[a]);
+                    }
+                lds_u8* exo = lds_at(&sm.Ex[hh][0][lane]);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) st(exo, 16 * 64 * a, ks[a]);
+                lds_barrier();                                           // B1
+                // the full K S: both halves add the two partials in the same order (bitwise equal)
+                lds_u8* ex0 = lds_at(&sm.Ex[0][0][lane]);
+                f32x4 ksf[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x4 p0 = ld<f32x4>(ex0, 16 * 64 * a);
+                    const f32x4 p1 = ld<f32x4>(ex0, 16 * 64 * (4 + a));
+                    ksf[a] = p0 + p1;
+                }
+                // X = V - e^G KS as hi + lo B fragments (tokens 32 kb + 4 g + e for e < 4 and
+                // 32 kb + 16 + 4 g + e - 4 for e >= 4: the stored column order of M)
+                f32x4 xs[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) xs[a][r] = (float)vv[a][r] - eg[a][r] * ksf[a][r];
+                bf16x8 xh[2], xl[2];
+                split8(xs[0], xs[1], xh[0], xl[0]);
+                split8(xs[2], xs[3], xh[1], xl[1]);
+                // U = M X (M lower triangular: token tiles 0, 1 need kb = 0 only)
+                f32x4 u[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) u[a] = zero4();
+#pragma unroll
+                for (int p = 0; p < 6; ++p) {
+                    u[ta[p]] = mma(mc.mh[p], xh[tb[p]], u[ta[p]]);
+                    u[ta[p]] = mma(mc.mh[p], xl[tb[p]], u[ta[p]]);
+                    u[ta[p]] = mma(mc.ml[p], xh[tb[p]], u[ta[p]]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(mc, min(i + 1, nchunks - 1));
+                f32x4 ds[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) ds[a] = u[a] * dg[a];
+                bf16x8 dh[2], dl[2];
+                split8(ds[0], ds[1], dh[0], dl[0]);
+                split8(ds[2], ds[3], dh[1], dl[1]);
+                // S <- e^(G_C) S + K^T D for this half's keys
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    f32x4 acc = S[t] * ec;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        acc = mma(kt[t][kb], dh[kb], acc);
+                        acc = mma(kt[t][kb], dl[kb], acc);
+                    }
+                    S[t] = acc;
+                }
+                // U (hi + lo) for the output waves: this half writes tokens 32 hh .. 32 hh + 31
+                bf16x8 uh, ul;
+                split8(u[2 * hh], u[2 * hh + 1], uh, ul);
+                lds_u8* utb = lds_at(sm.Ut[i & 1][0] + l_ut);
+                st(utb, 2 * 32 * hh, uh);
+                st(utb, 2 * (kWS * kUP + 32 * hh), ul);
+                lds_barrier();                                           // B2
+            };
+            fetch(mc, 0);
+            lds_barrier();  // chunks 0 and 1 staged
+            for (int i = 0; i < nchunks; ++i) step(i);
+            lds_barrier();  // the output waves' last step
             lds_barrier();
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) final_state[state_idx(t, r)] = S[t][r];
         };
-        fetch(mc, 0);
-        lds_barrier();  // chunk 0 staged
-        for (int i = 0; i < nchunks; ++i) step(i);
-        lds_barrier();  // the output waves' last step
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) final_state[state_idx(kt, r)] = S[kt][r];
-    } else {
+        if (wave == 0) chain(std::integral_constant<int, 0>{});
+        else chain(std::integral_constant<int, 1>{});
+    } else if (wave < 4) {
         // ------------------------------------------------ output waves ------------------------
         if (nchunks == 0) return;
-        auto run = [&](auto w2c) {
-            constexpr int w2 = decltype(w2c)::value;     // 0: tiles {0, 3}; 1: tiles {1, 2}
-            constexpr int tiles[2] = {w2, 3 - w2};
+        auto run = [&](auto oc) {
+            constexpr int ow = decltype(oc)::value;      // 0: tiles {0, 3}; 1: tiles {1, 2}
+            constexpr int tiles[2] = {ow, 3 - ow};
             const int l_kf = c * kKR + 8 * (g ^ kswz(c));                 // K row c, logical chunk g
             const int l_st = c * kSP + 8 * g, l_ut = c * kUP + 4 * g;
-            const int l_sk = (lane >> 4) * kKR + 8 * (lane & 15);          // staged K piece (physical)
-            const int l_sv = (lane >> 2) * kVP + 8 * (lane & 3);           // staged V piece
-            // staging: K rows (8 pieces per lane), this workgroup's 32 V columns (2 pieces), the
-            // gate block (48 pieces of 4 floats: lanes 0..23 of each output wave).  Rows past a
-            // partial chunk's end repeat its last row (so every load is in bounds and unmasked):
-            // they meet zero rows and columns of M (beta = 0 there), so they contribute nothing,
-            // and outputs of those rows are never stored.
-            auto fetch_stage = [&](StageIn& f, int ci) {
-                const size_t tok0 = tok0_of(ci);
-                const int L = len_of(ci);
-#pragma unroll
-                for (int it = 0; it < 8; ++it) {
-                    // row 4 (2 it + w') + lane / 16, physical chunk lane % 16: logical chunk
-                    // (lane % 16) ^ kswz(row)
-                    const int e = lane + 64 * (2 * it + w2), t = e >> 4;
-                    const int p = (e & 15) ^ kswz(t);
-                    f.k[it] = *reinterpret_cast<const u32x4*>(k + ((tok0 + min(t, L - 1)) * Hk + kh) * kDK + 8 * p);
-                }
-#pragma unroll
-                for (int it = 0; it < 2; ++it) {
-                    const int e = lane + 64 * (2 * it + w2), t = min(e >> 2, L - 1), p = e & 3;
-                    f.v[it] = *reinterpret_cast<const u32x4*>(
-                        v + ((tok0 + t) * Hv + h) * DV + pair * kSlices * kWS + 8 * p);
-                }
-                const float* gb = ws_G + ((size_t)(slot0 + ci) * Hv + h) * 3 * kC;
-                f.gt = *reinterpret_cast<const f32x4*>(gb + 4 * min(lane + 24 * w2, 47));
-            };
-            auto store_stage = [&](const StageIn& f, int ci) {
-                lds_u8* kl = lds_at(sm.Kr[ci % 3] + l_sk);
-#pragma unroll
-                for (int it = 0; it < 8; ++it)                           // rows 4 (2 it + w') + lane / 16
-                    st(kl, 2 * 4 * (2 * it + w2) * kKR, f.k[it]);
-                lds_u8* vl = lds_at(sm.Vr[ci % 3] + l_sv);
-#pragma unroll
-                for (int it = 0; it < 2; ++it)                           // rows 16 (2 it + w') + lane / 4
-                    st(vl, 2 * 16 * (2 * it + w2) * kVP, f.v[it]);
-                if (lane < 24) *reinterpret_cast<f32x4*>(sm.Gt[ci % 3] + 4 * (lane + 24 * w2)) = f.gt;
-            };
             auto fetch_out = [&](OutIn& f, int ci) {
                 const size_t tok0 = tok0_of(ci);
                 const int L = len_of(ci);
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
+                    // rows past a partial chunk's end repeat its last row: their outputs are never
+                    // stored, and they enter no other row's output
                     const int t = min(16 * tiles[x] + c, L - 1);
                     const __bf16* qr = q + ((tok0 + t) * Hk + kh) * kDK + 8 * g;
 #pragma unroll
                     for (int kb = 0; kb < 4; ++kb) f.q[x][kb] = *reinterpret_cast<const bf16x8*>(qr + 32 * kb);
                 }
             };
-            // one set of staging registers and one of Q registers, each refilled right after its
-            // last use in a step, a whole step ahead of the next use
-            StageIn st;
-            OutIn cur;
-            auto step = [&](int s) {
-                // stage chunk s + 1 (fetched one step ago), then fetch chunk s + 2 into the same
-                // registers (repeats of the last chunk near the end: never read)
-                store_stage(st, s + 1);
-                fetch_stage(st, min(s + 2, nchunks - 1));
-                const int ci = s - 1;                    // the chunk finished in this step
-                const __bf16* kr = sm.Kr[ci % 3];
-                const float* gt = sm.Gt[ci % 3];
+            auto step = [&](int s, const OutIn& cur, OutIn& nxt) {
+                fetch_out(nxt, min(s, nchunks - 1));             // chunk s's Q rows, for the next step
+                const int ci = s - 1;                            // the chunk finished in this step
+                const int slot = ci % kRing;
+                const __bf16* kr = sm.Kr[slot];
+                const float* gt = sm.Gt[slot];
                 const int buf = ci & 1;
-                // LDS operands, all issued up front: K rows of the P^T tiles (b <= 3 - w'), the
-                // gate values, S^T (hi, lo) and U^T (hi, lo) of both slices
-                constexpr int NB = 4 - w2;
-                bf16x8 kf[NB][4];
+                // S^T (hi, lo), U^T (hi, lo) and the gate values of this wave's rows
                 lds_u8* kfl = lds_at(kr + l_kf);
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) kf[b][kb] = ld<bf16x8>(kfl, 2 * (16 * b * kKR + 32 * kb));
-                f32x4 gp[NB];
                 lds_u8* gl = lds_at(gt + 4 * g);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) gp[b] = ld<f32x4>(gl, 4 * 16 * b);
                 float gq[2], eq[2];
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     gq[x] = gt[16 * tiles[x] + c];
                     eq[x] = gt[kC + 16 * tiles[x] + c];
                 }
-                bf16x8 sf[kSlices][2][4], uf[kSlices][2][2];
+                bf16x8 sf[2][4], uf[2][2];
 #pragma unroll
-                for (int j = 0; j < kSlices; ++j)
+                for (int hl = 0; hl < 2; ++hl) {
+                    lds_u8* sp = lds_at(sm.St[buf][hl] + l_st);
 #pragma unroll
-                    for (int hl = 0; hl < 2; ++hl) {
-                        lds_u8* sp = lds_at(sm.St[j][buf][hl] + l_st);
+                    for (int kb = 0; kb < 4; ++kb) sf[hl][kb] = ld<bf16x8>(sp, 2 * 32 * kb);
+                    lds_u8* up = lds_at(sm.Ut[buf][hl] + l_ut);
 #pragma unroll
-                        for (int kb = 0; kb < 4; ++kb) sf[j][hl][kb] = ld<bf16x8>(sp, 2 * 32 * kb);
-                        lds_u8* up = lds_at(sm.Ut[j][buf][hl] + l_ut);
-#pragma unroll
-                        for (int kb = 0; kb < 2; ++kb)
-                            uf[j][hl][kb] = cat44(ld<bf16x4>(up, 2 * 32 * kb), ld<bf16x4>(up, 2 * (32 * kb + 16)));
-                    }
-                __builtin_amdgcn_sched_barrier(0);
-                f32x4 ot[2][kSlices];
+                    for (int kb = 0; kb < 2; ++kb)
+                        uf[hl][kb] = cat44(ld<bf16x4>(up, 2 * 32 * kb), ld<bf16x4>(up, 2 * (32 * kb + 16)));
+                }
+                lds_barrier();                                           // B1
+                f32x4 ot[2];
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int a = tiles[x];
                     const int t = 16 * a + c;
                     // P^T tiles (b, a) = K Q^T for b <= a: rows t' = 16 b + m, masked to t' <= t
+                    bf16x8 kf[4][4];
+#pragma unroll
+                    for (int b = 0; b <= a; ++b)
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) kf[b][kb] = ld<bf16x8>(kfl, 2 * (16 * b * kKR + 32 * kb));
                     f32x4 pt[4];
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
@@ -755,65 +728,97 @@ void chunk_scan_kernel(
                         if (b > a) continue;
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb) pt[b] = mma(kf[b][kb], cur.q[x][kb], pt[b]);
+                        const f32x4 gp = ld<f32x4>(gl, 4 * 16 * b);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int tp = 16 * b + 4 * g + r;
-                            pt[b][r] = tp <= t ? pt[b][r] * exp2_fast(gq[x] - gp[b][r]) : 0.f;
+                            pt[b][r] = tp <= t ? pt[b][r] * exp2_fast(gq[x] - gp[r]) : 0.f;
                         }
                     }
                     // B fragments for P U: reduction rows 32 kb + 4 g + e (e < 4), + 16 (e >= 4)
                     bf16x8 ph[2], pl[2];
                     split8(pt[0], pt[1], ph[0], pl[0]);
                     split8(pt[2], pt[3], ph[1], pl[1]);
+                    f32x4 qs = zero4(), qs2 = zero4();
 #pragma unroll
-                    for (int j = 0; j < kSlices; ++j) {
-                        f32x4 qs = zero4(), qs2 = zero4();
-#pragma unroll
-                        for (int kb = 0; kb < 4; ++kb) {
-                            qs = mma(sf[j][0][kb], cur.q[x][kb], qs);
-                            qs2 = mma(sf[j][1][kb], cur.q[x][kb], qs2);
-                        }
-                        f32x4 acc = (qs + qs2) * eq[x];
-#pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) {
-                            if (2 * kb > a) continue;
-                            acc = mma(uf[j][0][kb], ph[kb], acc);
-                            acc = mma(uf[j][0][kb], pl[kb], acc);
-                            acc = mma(uf[j][1][kb], ph[kb], acc);
-                        }
-                        ot[x][j] = acc;
+                    for (int kb = 0; kb < 4; ++kb) {
+                        qs = mma(sf[0][kb], cur.q[x][kb], qs);
+                        qs2 = mma(sf[1][kb], cur.q[x][kb], qs2);
                     }
+                    f32x4 acc = (qs + qs2) * eq[x];
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        if (2 * kb > a) continue;
+                        acc = mma(uf[0][kb], ph[kb], acc);
+                        acc = mma(uf[0][kb], pl[kb], acc);
+                        acc = mma(uf[1][kb], ph[kb], acc);
+                    }
+                    ot[x] = acc;
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                fetch_out(cur, min(s, nchunks - 1));             // chunk s's Q rows, for the next step
                 const size_t tok0 = tok0_of(ci);
                 const int L = len_of(ci);
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int t = 16 * tiles[x] + c;
-                    if (t < L) {
-#pragma unroll
-                        for (int j = 0; j < kSlices; ++j) {
-                            const int c0 = (pair * kSlices + j) * kWS;
-                            *reinterpret_cast<f32x4*>(o + ((tok0 + t) * Hv + h) * DV + c0 + 4 * g) = ot[x][j];
-                        }
-                    }
+                    if (t < L) *reinterpret_cast<f32x4*>(o + ((tok0 + t) * Hv + h) * DV + c0 + 4 * g) = ot[x];
                 }
-                lds_barrier();
+                lds_barrier();                                           // B2
             };
-            fetch_stage(st, 0);
-            store_stage(st, 0);
-            fetch_stage(st, min(1, nchunks - 1));
-            lds_barrier();  // chunk 0 staged
-            // step 0: stage chunk 1, fetch chunk 2 and chunk 0's Q rows
-            store_stage(st, 1);
-            fetch_stage(st, min(2, nchunks - 1));
-            fetch_out(cur, 0);
+            OutIn fa, fb;
+            lds_barrier();  // chunks 0 and 1 staged
+            // step 0: chunk 0's Q rows
+            fetch_out(fa, 0);
             lds_barrier();
-            for (int s = 1; s <= nchunks; ++s) step(s);
+            lds_barrier();
+            int s = 1;
+            for (; s + 1 <= nchunks; s += 2) {
+                step(s, fa, fb);
+                step(s + 1, fb, fa);
+            }
+            if (s <= nchunks) step(s, fa, fb);
         };
-        if (wave == kSlices) run(std::integral_constant<int, 0>{});
+        if (wave == 2) run(std::integral_constant<int, 0>{});
         else run(std::integral_constant<int, 1>{});
+    } else {
+        // ------------------------------------------------ staging wave ------------------------
+        if (nchunks == 0) return;
+        // K piece of copy instruction ii: byte 1024 ii + 16 lane of the slot, i.e. row t, physical
+        // chunk pc (pc >= 16 is row padding: any in-bounds source will do)
+        int krow[kKDma], kcol[kKDma];
+#pragma unroll
+        for (int ii = 0; ii < kKDma; ++ii) {
+            const int ob = 1024 * ii + 16 * lane;
+            const int t = ob / (2 * kKR), pc = (ob % (2 * kKR)) / 16;
+            krow[ii] = t;
+            kcol[ii] = 8 * (pc < 16 ? (pc ^ kswz(t)) : 0);
+        }
+        auto dma = [&](int ci) {
+            const int slot = ci % kRing;
+            const size_t tok0 = tok0_of(ci);
+            const int L = len_of(ci);
+            const __bf16* kb = k + (tok0 * Hk + kh) * kDK;
+#pragma unroll
+            for (int ii = 0; ii < kKDma; ++ii)
+                copy_to_lds(kb + (size_t)min(krow[ii], L - 1) * Hk * kDK + kcol[ii], sm.Kr[slot] + 512 * ii);
+            const __bf16* vb = v + (tok0 * Hv + h) * DV + c0;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)          // rows 32 jj + lane / 2, columns 8 (lane % 2)
+                copy_to_lds(vb + (size_t)min(32 * jj + (lane >> 1), L - 1) * Hv * DV + 8 * (lane & 1),
+                            sm.Vr[slot] + 512 * jj);
+            const float* gb = ws_G + ((size_t)(slot0 + ci) * Hv + h) * 3 * kC;
+            copy_to_lds(gb + 4 * min(lane, 47), sm.Gt[slot]);
+        };
+        dma(0);
+        dma(min(1, nchunks - 1));
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // chunks 0 and 1 staged
+        for (int s = 0; s <= nchunks; ++s) {
+            __builtin_amdgcn_s_barrier();   // B1
+            dma(min(s + 2, nchunks - 1));   // (repeats of the last chunk near the end: never read)
+            wait_vmcnt<kDmaOps>();          // chunk s + 1's copy (issued one step ago) has landed
+            __builtin_amdgcn_s_barrier();   // B2
+        }
+        wait_vmcnt<0>();
     }
 }
 
@@ -872,7 +877,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)) != hipSuccess)
         return e;
     const int groups = a.N * a.Hk;                        // (sequence, q/k head)
-    const int members = (a.Hv / a.Hk) * (DV / (kWS * kSlices));
+    const int members = (a.Hv / a.Hk) * (DV / kWS);
     const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * members);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kScanThreads), bytes,
                        a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
