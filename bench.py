@@ -43,7 +43,7 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
 # reads on a plain copy of known size (profiles/); None whenever the kernel changed since.
 TRAFFIC_SCAN = None
-TRAFFIC_DECODE = 1084.9e6
+TRAFFIC_DECODE = None
 
 
 def prefill_algorithmic(wl, T: int, B: int, N: int, init_state: bool):

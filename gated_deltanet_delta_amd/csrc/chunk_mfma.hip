@@ -165,8 +165,6 @@ __device__ __forceinline__ bool locate_chunk(int slot, const int32_t* cu_seqlens
 
 // ------------------------------------------------------------------------------------------------
 // Shared helpers.
-constexpr int kKP = kDK + 8;   // row pitch (elements) of 128-wide bf16 rows in LDS
-constexpr int kFP = kC + 4;    // row pitch of 64 x 64 fp32 tiles
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -195,41 +193,77 @@ __device__ __forceinline__ bf16x4 read_tr(lds_u8* b, int off) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// chunk_solve_kernel: one workgroup per (chunk slot, v-head).
+// chunk_solve_kernel: one workgroup per (chunk slot, q/k head), for each of the head's v-heads.
 //
-// Writes the chunk's gate block [3][64] floats: G2 = running sum of g log2(e), 2^G2 and
-// 2^(G2_C - G2) (G2_C = G2 at the chunk's last row; padding rows past the chunk's length have
-// g = 0), and M = T diag(beta) as hi and lo bf16 tiles [64][64] (row-major with the column order
-// described at the store, zero above the diagonal and in rows/columns past the chunk's length).
+// Writes, per (chunk, v-head), the chunk's gate block [3][64] floats: G2 = running sum of
+// g log2(e), 2^G2 and 2^(G2_C - G2) (G2_C = G2 at the chunk's last row; padding rows past the
+// chunk's length have g = 0), and M = T diag(beta) as hi and lo bf16 tiles [64][64] (row-major
+// with the column order described at the store, zero above the diagonal and in rows/columns past
+// the chunk's length).
+//
+// K enters the matrix cores straight from memory (its rows are both operands of K K^T), and
+// K K^T is formed once for all v-heads of the q/k head.  A and T live in shared memory as their
+// lower 16 x 16 blocks only (22 KB in all).
+constexpr int kBP = 17;          // row pitch (floats) of the 16 x 16 blocks of A and T
+__device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }   // a >= b
+
 template <typename TG>
 __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
     const __bf16* __restrict__ k, const TG* __restrict__ g, const TG* __restrict__ beta,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start, int N, int T,
     int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M) {
-    __shared__ __attribute__((aligned(16))) __bf16 sK[kC * kKP];
-    __shared__ __attribute__((aligned(16))) float sA[kC * kFP];
-    __shared__ __attribute__((aligned(16))) float sT[kC * kFP];
-    __shared__ float sG[kC], sB[kC];
+    __shared__ float sA[10][16 * kBP];     // blocks (a, b), a > b, of A
+    __shared__ float sT[10][16 * kBP];     // blocks (a, b), a >= b, of T = (I + A)^-1
+    __shared__ float sB[kC];
 
-    const int slot = blockIdx.x, h = blockIdx.y;
+    const int slot = blockIdx.x, kh = blockIdx.y;
     ChunkLoc loc;
     if (!locate_chunk(slot, cu_seqlens, chunk_start, N, T, nct, loc)) return;
-    const int kh = h / (Hv / Hk);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Gq = Hv / Hk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, gq = lane >> 4;
     const size_t tok0 = (size_t)loc.row * T + loc.t0;
     const int L = loc.len;
 
+    // K K^T as 16x16 tiles; wave w owns diagonal tile (w, w) and some below it: wave 0 (0,0) (1,0);
+    // wave 1 (1,1) (2,1) (2,0); wave 2 (2,2) (3,2); wave 3 (3,3) (3,0) (3,1).  The K rows of the (at
+    // most three) token tiles a wave needs are all loaded before the first product.  K rows past
+    // the chunk's end repeat its last row: they only meet rows with beta = 0.
+    auto kfrag = [&](int t, int kb) {
+        const int r = min(16 * t + c, L - 1);
+        return *reinterpret_cast<const bf16x8*>(k + ((tok0 + r) * Hk + kh) * kDK + 32 * kb + 8 * gq);
+    };
+    // token tiles of the K rows: wave 0 {0, 1}, wave 1 {1, 2, 0}, wave 2 {2, 3}, wave 3 {3, 0, 1}
+    const int tt0 = wave, tt1 = (wave + 1) & 3, tt2 = wave == 1 ? 0 : 1;
+    bf16x8 k0[4], k1[4], k2[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int e = tid + kThreads * it;  // 1024 pieces: row e/16, columns 8 (e%16) .. +7
-        const int t = e >> 4, p = e & 15;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (t < L) x = *reinterpret_cast<const uint4*>(k + ((tok0 + t) * Hk + kh) * kDK + 8 * p);
-        *reinterpret_cast<uint4*>(sK + t * kKP + 8 * p) = x;
+    for (int kb = 0; kb < 4; ++kb) {
+        k0[kb] = kfrag(tt0, kb);
+        k1[kb] = kfrag(tt1, kb);
     }
-    const size_t ws_row = ((size_t)slot * Hv + h) * 3 * kC;
-    if (wave == 0) {
+    if (wave & 1) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) k2[kb] = kfrag(tt2, kb);
+    }
+    auto kkt = [&](const bf16x8* ka, const bf16x8* kb_) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc = mma(ka[kb], kb_[kb], acc);
+        return acc;
+    };
+    // lane (g, c) element r of tile (ta, tb) holds (K K^T)[16 ta + 4 g + r][16 tb + c]
+    const f32x4 kd = kkt(k0, k0);                                  // (w, w)
+    const f32x4 kx = wave == 3 ? kkt(k0, k1) : kkt(k1, k0);        // (1,0) (2,1) (3,2) / (3,0)
+    f32x4 ky = zero4();                                            // (2,0) / (3,1)
+    if (wave == 1) ky = kkt(k1, k2);
+    if (wave == 3) ky = kkt(k0, k2);
+    const int xa = wave == 3 ? 3 : wave + 1, xb = wave == 3 ? 0 : wave;
+    const int ya = wave == 1 ? 2 : 3, yb = wave == 1 ? 0 : 1;
+
+    for (int qh = 0; qh < Gq; ++qh) {
+        const int h = kh * Gq + qh;
+        // the chunk's gates and the running log2-decay G2 (a wave prefix sum, in every wave)
         const float gt = lane < L ? to_f32(g[(tok0 + lane) * Hv + h]) * kLog2e : 0.f;
         const float bt = lane < L ? to_f32(beta[(tok0 + lane) * Hv + h]) : 0.f;
         float G2 = gt;
@@ -238,105 +272,100 @@ __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
             const float y = __shfl_up(G2, off);
             if (lane >= off) G2 += y;
         }
-        sG[lane] = G2;
-        sB[lane] = bt;
-        const float G2c = __shfl(G2, 63);
-        ws_G[ws_row + lane] = G2;
-        ws_G[ws_row + kC + lane] = exp2_fast(G2);
-        ws_G[ws_row + 2 * kC + lane] = exp2_fast(G2c - G2);
-    }
-    for (int e = tid; e < kC * kFP; e += kThreads) sT[e] = 0.f;
-    lds_barrier();
-
-    // A = diag(beta) (K K^T o Gam), strictly lower: 10 lower 16x16 tiles over 4 waves
-    // wave 0: (0,0) (3,3) (3,0); wave 1: (1,1) (3,1) (1,0); wave 2: (2,2) (3,2); wave 3: (2,0) (2,1)
-    auto tile_a = [](int w, int s) {
-        return s == 0 ? (w == 3 ? 2 : w) : s == 1 ? (w == 3 ? 2 : 3) : (w < 2 ? (w == 0 ? 3 : 1) : -1);
-    };
-    auto tile_b = [](int w, int s) {
-        return s == 0 ? (w == 3 ? 0 : w) : s == 1 ? (w == 3 ? 1 : w == 0 ? 3 : w) : 0;
-    };
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        const int ta = tile_a(wave, s), tb = tile_b(wave, s);
-        if (ta < 0) continue;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            acc = mma(lds8(sK + (16 * ta + c) * kKP + 32 * kb + 8 * gq),
-                      lds8(sK + (16 * tb + c) * kKP + 32 * kb + 8 * gq), acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * ta + 4 * gq + r, j = 16 * tb + c;
-            sA[t * kFP + j] = j < t ? sB[t] * acc[r] * exp2_fast(sG[t] - sG[j]) : 0.f;
+        if (wave == 0) {
+            const size_t ws_row = ((size_t)slot * Hv + h) * 3 * kC;
+            const float G2c = __shfl(G2, 63);
+            ws_G[ws_row + lane] = G2;
+            ws_G[ws_row + kC + lane] = exp2_fast(G2);
+            ws_G[ws_row + 2 * kC + lane] = exp2_fast(G2c - G2);
+            sB[lane] = bt;
         }
-    }
-    lds_barrier();
-
-    // T = (I + A)^-1: diagonal blocks, wave w inverts block w (lane c < 16 computes column c)
-    if (c == lane) {
-        const int base = 16 * wave;
-        float x[16];
+        // A = diag(beta) (K K^T o Gam), strictly lower, tile by tile
+        auto atile = [&](int ta, int tb, f32x4 acc) {
+            const float Gj = __shfl(G2, 16 * tb + c);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            float acc = (t == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int j = 0; j < t; ++j) acc -= sA[(base + t) * kFP + base + j] * x[j];
-            x[t] = acc;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) sT[(base + t) * kFP + base + c] = x[t];
-    }
-    lds_barrier();
-    // off-diagonal blocks, by distance d = a - b:  T_ab = -T_aa * sum_{m=b}^{a-1} A_am T_mb
-#pragma unroll
-    for (int d = 1; d < 4; ++d) {
-        if (wave < 4 - d) {
-            const int b = wave, a = wave + d;
-            f32x4 X = zero4();
-            for (int mm = b; mm < a; ++mm) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float av = sA[(16 * a + c) * kFP + 16 * mm + 4 * s + gq];
-                    const float bv = sT[(16 * mm + 4 * s + gq) * kFP + 16 * b + c];
-                    X = mma_f32(av, bv, X);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * ta + 4 * gq + r, j = 16 * tb + c;
+                const float Gt = __shfl(G2, t), Bt = __shfl(bt, t);
+                acc[r] = j < t ? Bt * acc[r] * exp2_fast(Gt - Gj) : 0.f;
             }
-            // -T_aa X with X fed back from the accumulator: step s takes reduction rows 4g + s
-            f32x4 Y = zero4();
+            return acc;
+        };
+        auto store_a = [&](int ta, int tb, const f32x4& x) {
+            float* dst = sA[blk(ta, tb)];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float av = sT[(16 * a + c) * kFP + 16 * a + 4 * gq + s];
-                Y = mma_f32(av, X[s], Y);
+            for (int r = 0; r < 4; ++r) dst[(4 * gq + r) * kBP + c] = x[r];
+        };
+        store_a(xa, xb, atile(xa, xb, kx));
+        if (wave & 1) store_a(ya, yb, atile(ya, yb, ky));
+        // T_ww = (I + A_ww)^-1 by forward substitution, lane c computing column c; the entries of
+        // A_ww come out of the accumulator tile one by one, broadcast with readlane
+        {
+            const f32x4 ad = atile(wave, wave, kd);
+            float x[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float acc = (t == c) ? 1.f : 0.f;
+#pragma unroll
+                for (int j = 0; j < t; ++j)
+                    acc -= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ad[t & 3]), 16 * (t >> 2) + j)) * x[j];
+                x[t] = acc;
             }
+            if (lane < 16) {
+                float* Td = sT[blk(wave, wave)];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(16 * a + 4 * gq + r) * kFP + 16 * b + c] = -Y[r];
+                for (int t = 0; t < 16; ++t) Td[t * kBP + c] = x[t];
+            }
         }
         lds_barrier();
-    }
-
-    // M = T diag(beta) as hi and lo rows: 64 rows x 8 pieces of 8 columns.  Within each block of 32
-    // columns the stored order is the scan kernel's B-fragment order: stored columns 8 g + e are
-    // columns 4 g + e (e < 4) and 16 + 4 g + e - 4 (e >= 4).
-    __bf16* Mh = ws_M + ((size_t)slot * Hv + h) * 2 * kC * kC;
-    __bf16* Ml = Mh + kC * kC;
+        // off-diagonal blocks, by distance d = a - b:  T_ab = -T_aa * sum_{m=b}^{a-1} A_am T_mb
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int e = tid + kThreads * it;
-        const int t = e >> 3, p = e & 7;
-        const int j0 = 32 * (p >> 2) + 4 * (p & 3);
-        const float4 a0 = *reinterpret_cast<const float4*>(sT + t * kFP + j0);
-        const float4 a1 = *reinterpret_cast<const float4*>(sT + t * kFP + j0 + 16);
-        const float tv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        bf16x8 hv, lv;
+        for (int d = 1; d < 4; ++d) {
+            if (wave < 4 - d) {
+                const int b = wave, a = wave + d;
+                f32x4 X = zero4();
+                for (int mm = b; mm < a; ++mm) {
+                    const float* Am = sA[blk(a, mm)];
+                    const float* Tm = sT[blk(mm, b)];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float x = tv[j] * sB[j0 + (j & 3) + 16 * (j >> 2)];
-            hv[j] = hi_of(x);
-            lv[j] = lo_of(x, hv[j]);
+                    for (int s = 0; s < 4; ++s) X = mma_f32(Am[c * kBP + 4 * s + gq], Tm[(4 * s + gq) * kBP + c], X);
+                }
+                // -T_aa X with X fed back from the accumulator: step s takes reduction rows 4g + s
+                const float* Ta = sT[blk(a, a)];
+                f32x4 Y = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Y = mma_f32(Ta[c * kBP + 4 * gq + s], X[s], Y);
+                float* Tab = sT[blk(a, b)];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tab[(4 * gq + r) * kBP + c] = -Y[r];
+            }
+            lds_barrier();
         }
-        *reinterpret_cast<bf16x8*>(Mh + t * kC + 8 * p) = hv;
-        *reinterpret_cast<bf16x8*>(Ml + t * kC + 8 * p) = lv;
+
+        // M = T diag(beta) as hi and lo rows: 64 rows x 8 pieces of 8 columns.  Within each block of
+        // 32 columns the stored order is the scan kernel's B-fragment order: stored columns 8 g + e
+        // are columns 4 g + e (e < 4) and 16 + 4 g + e - 4 (e >= 4).
+        __bf16* Mh = ws_M + ((size_t)slot * Hv + h) * 2 * kC * kC;
+        __bf16* Ml = Mh + kC * kC;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int e = tid + kThreads * it;
+            const int t = e >> 3, p = e & 7;
+            const int j0 = 32 * (p >> 2) + 4 * (p & 3);
+            bf16x8 hv, lv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = j0 + (j & 3) + 16 * (j >> 2);
+                const int ba = t >> 4, bb = col >> 4;
+                const float tv = bb <= ba ? sT[blk(ba, bb)][(t & 15) * kBP + (col & 15)] : 0.f;
+                const float x = tv * sB[col];
+                hv[j] = hi_of(x);
+                lv[j] = lo_of(x, hv[j]);
+            }
+            *reinterpret_cast<bf16x8*>(Mh + t * kC + 8 * p) = hv;
+            *reinterpret_cast<bf16x8*>(Ml + t * kC + 8 * p) = lv;
+        }
+        lds_barrier();                 // sT and sB are rewritten for the next v-head
     }
 }
 
@@ -864,7 +893,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((stages & kStagePrepare) && slots > 0) {
-        hipLaunchKernelGGL((chunk_solve_kernel<TG>), dim3((unsigned)slots, (unsigned)a.Hv),
+        hipLaunchKernelGGL((chunk_solve_kernel<TG>), dim3((unsigned)slots, (unsigned)a.Hk),
                            dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.k),
                            static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta),
                            a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M);

@@ -1,6 +1,6 @@
 // recurrent.hip -- token-serial gated delta rule with the state held in registers.
 //
-// Serves gdn_recurrent_step (decode: T == 1 per call, or a few tokens).  One workgroup of 256
+// Serves gdn_recurrent_step (decode: T == 1 per call, or a few tokens).  One workgroup of 512
 // threads owns one (sequence, v-head) state of DK x DV fp32 values; each thread holds a 4-column
 // float4 strip of RPT rows in registers, so the state is read from HBM once and written once per
 // call.  Per token:
@@ -12,7 +12,9 @@
 //
 // Memory pattern: rows of S are DV floats; a wave covers whole rows with 16-byte loads, so every
 // load/store instruction of a wave touches 64 x 16 B of contiguous memory.  The work is ~1 flop
-// per byte moved: the kernel is bound by HBM bandwidth.
+// per byte moved: the kernel is bound by HBM bandwidth.  The state is read and written with
+// non-temporal accesses: each (sequence, head) state is touched once per call, and streaming it
+// past the caches measured faster for this read-then-write-back pattern.
 
 #include "common.h"
 #include "launch.h"
@@ -20,7 +22,9 @@
 namespace gdn {
 namespace {
 
-constexpr int kRecThreads = 256;
+constexpr int kRecThreads = 512;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <int DK, int DV, typename TIn, typename TG>
 __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
@@ -44,10 +48,10 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     __shared__ float sq[DK], sk[DK], sv[DV];
     __shared__ float red[NW][2 * DV + 1];
 
-    float4* S4 = reinterpret_cast<float4*>(state + (size_t)bh * DK * DV);
-    float4 s[RPT];
+    f32x4v* S4 = reinterpret_cast<f32x4v*>(state + (size_t)bh * DK * DV);
+    f32x4v s[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) s[m] = S4[(size_t)(rg + RG * m) * CG + cg];
+    for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(S4 + (size_t)(rg + RG * m) * CG + cg);
 
     for (int t = 0; t < T; ++t) {
         const size_t tok = (size_t)b * T + t;
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     }
 
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) S4[(size_t)(rg + RG * m) * CG + cg] = s[m];
+    for (int m = 0; m < RPT; ++m) __builtin_nontemporal_store(s[m], S4 + (size_t)(rg + RG * m) * CG + cg);
 }
 
 template <int DK, int DV, typename TIn, typename TG>
