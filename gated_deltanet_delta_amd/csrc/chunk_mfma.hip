@@ -68,8 +68,6 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ __bf16 hi_of(float x) { return (__bf16)x; }
 __device__ __forceinline__ __bf16 lo_of(float x, __bf16 hi) { return (__bf16)(x - (float)hi); }
 
-__device__ __forceinline__ bf16x8 lds8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ bf16x4 lds4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
@@ -261,11 +259,32 @@ __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
     const int xa = wave == 3 ? 3 : wave + 1, xb = wave == 3 ? 0 : wave;
     const int ya = wave == 1 ? 2 : 3, yb = wave == 1 ? 0 : 1;
 
+    // the gates of the first kPre v-heads are loaded together with K (one memory round trip)
+    constexpr int kPre = 4;
+    float gpre[kPre], bpre[kPre];
+    const size_t grow = (tok0 + min(lane, L - 1)) * Hv + (size_t)kh * Gq;
+#pragma unroll
+    for (int qh = 0; qh < kPre; ++qh) {
+        const int qq = min(qh, Gq - 1);
+        gpre[qh] = to_f32(g[grow + qq]);
+        bpre[qh] = to_f32(beta[grow + qq]);
+    }
+
     for (int qh = 0; qh < Gq; ++qh) {
         const int h = kh * Gq + qh;
         // the chunk's gates and the running log2-decay G2 (a wave prefix sum, in every wave)
-        const float gt = lane < L ? to_f32(g[(tok0 + lane) * Hv + h]) * kLog2e : 0.f;
-        const float bt = lane < L ? to_f32(beta[(tok0 + lane) * Hv + h]) : 0.f;
+        float graw, braw;
+        if (qh < kPre) {
+            graw = gpre[0]; braw = bpre[0];
+#pragma unroll
+            for (int j = 1; j < kPre; ++j)
+                if (qh == j) { graw = gpre[j]; braw = bpre[j]; }
+        } else {
+            graw = to_f32(g[grow + qh]);
+            braw = to_f32(beta[grow + qh]);
+        }
+        const float gt = lane < L ? graw * kLog2e : 0.f;
+        const float bt = lane < L ? braw : 0.f;
         float G2 = gt;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -298,19 +317,19 @@ __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
         };
         store_a(xa, xb, atile(xa, xb, kx));
         if (wave & 1) store_a(ya, yb, atile(ya, yb, ky));
-        // T_ww = (I + A_ww)^-1 by forward substitution, lane c computing column c; the entries of
-        // A_ww come out of the accumulator tile one by one, broadcast with readlane
+        // T_ww = (I + A_ww)^-1 by forward substitution, lane c computing column c, column-sweep
+        // order (x_j final, then subtracted from every later row: 15 dependent steps); the entries
+        // of A_ww come out of the accumulator tile one by one, broadcast with readlane
         {
             const f32x4 ad = atile(wave, wave, kd);
             float x[16];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float acc = (t == c) ? 1.f : 0.f;
+            for (int t = 0; t < 16; ++t) x[t] = (t == c) ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < t; ++j)
-                    acc -= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ad[t & 3]), 16 * (t >> 2) + j)) * x[j];
-                x[t] = acc;
-            }
+            for (int j = 0; j < 15; ++j)
+#pragma unroll
+                for (int t = j + 1; t < 16; ++t)
+                    x[t] -= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ad[t & 3]), 16 * (t >> 2) + j)) * x[j];
             if (lane < 16) {
                 float* Td = sT[blk(wave, wave)];
 #pragma unroll
