@@ -14,13 +14,13 @@
 // o_t = S_t^T q_t unrolled over the chunk.  Every decay factor is exp of a non-positive number.
 //
 // Two kernels:
-//   chunk_solve_kernel  one workgroup per (chunk, v-head), all chunks in parallel: the part with a
-//                       serial dependence inside a chunk.  Cumsum, A on the matrix cores, T by a
+//   chunk_solve_kernel  one workgroup per (chunk, q/k head), all chunks in parallel: the part with
+//                       a serial dependence inside a chunk.  Cumsum, A on the matrix cores, T by a
 //                       blocked forward substitution (16 x 16 diagonal blocks by substitution,
 //                       off-diagonal blocks by fp32 matrix-core products), M = T diag(beta) as
 //                       hi + lo bf16 into the workspace (16 KiB per chunk and v-head), and the
 //                       chunk's decay factors.
-//   chunk_scan_kernel   one workgroup per (sequence, v-head, 32 columns of S), walking the chunks
+//   chunk_scan_kernel   one workgroup per (sequence, v-head, 16 columns of S), walking the chunks
 //                       in order with chain and output waves (see there).  With M, the chunk's
 //                       deltas are U = Ut - W S = M (V - diag(e^G) K S), so W and Ut are never
 //                       formed; everything else comes from q, k, v on the fly.
