@@ -18,17 +18,17 @@
 //                       a serial dependence inside a chunk.  Cumsum, A on the matrix cores, T by a
 //                       blocked forward substitution (16 x 16 diagonal blocks by substitution,
 //                       off-diagonal blocks by fp32 matrix-core products), M = T diag(beta) as
-//                       hi + lo bf16 into the workspace (16 KiB per chunk and v-head), and the
-//                       chunk's decay factors.
+//                       hi + lo bf16 into the workspace (12 KiB per chunk and v-head), the chunk's
+//                       decay factors, and N = K K_prev^T (16 KiB per chunk and q/k head).
 //   chunk_scan_kernel   one workgroup per (sequence, v-head, 16 columns of S), walking the chunks
-//                       in order with chain and output waves (see there).  With M, the chunk's
-//                       deltas are U = Ut - W S = M (V - diag(e^G) K S), so W and Ut are never
-//                       formed; everything else comes from q, k, v on the fly.
+//                       in order with chain, state and output waves (see there).  With M, the
+//                       chunk's deltas are U = Ut - W S = M (V - diag(e^G) K S), so W and Ut are
+//                       never formed; everything else comes from q, k, v on the fly.
 //
 // Precision: q, k, v enter the matrix cores as exact bf16 values.  Quantities that feed the output
-// with full weight (S, U, P, M) enter as two bf16 terms hi + lo (hi = bf16(x), lo = bf16(x - hi)),
-// so their products carry ~16 significant bits.  Accumulation is fp32 everywhere; decay factors
-// are applied on the fp32 side.
+// with full weight (S, X, U, D, P, M, N) enter as two bf16 terms hi + lo (hi = bf16(x),
+// lo = bf16(x - hi)), so their products carry ~16 significant bits.  Accumulation is fp32
+// everywhere; decay factors are applied on the fp32 side.
 //
 // Lane layouts used (wave64, checked on the device):
 //   v_mfma_f32_16x16x32_bf16: lane l = 16 g + c holds A[c][8g..8g+7] and B[8g..8g+7][c]; the 16x16
@@ -191,13 +191,61 @@ __device__ __forceinline__ bf16x4 read_tr(lds_u8* b, int off) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Fragment layouts shared by the solve kernel (writer) and the scan kernel (reader).
+//
+// A "fragment" is the A operand of one v_mfma_f32_16x16x32_bf16 as the 64 lanes hold it: lane
+// (g, c) has eight bf16 values, 16 bytes; a fragment is stored as 64 x 16 = 1 KiB with lane l at
+// byte 16 l, so that one wave loads it with one fully coalesced instruction.
+//
+// The B operands these fragments meet in the scan kernel are accumulator tiles fed straight back:
+// tiles 2j and 2j + 1 with natural token rows hand lane (g, c) the tokens 32 j + 4 g + e (e < 4)
+// and 32 j + 16 + 4 g + e - 4 (e >= 4).  Element e of an A fragment's lane (g, c) therefore holds
+// column 32 j + colperm(g, e) of its row, colperm(g, e) = 4 g + (e & 3) + 16 (e >> 2).
+//
+//   M (per chunk and v-head): the nonzero pairs (row tile a, k-step j) of the lower-triangular
+//     M = T diag(beta), in the order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), each as hi then lo:
+//     12 fragments.  Lane (g, c) of pair (a, j) holds row 16 a + c.
+//   N (per chunk and q/k head, chunks with a predecessor in the same sequence only): N = K K_p^T,
+//     rows the chunk's tokens, columns the previous chunk's, all pairs (a, j) in the order
+//     (0,0) (0,1) (1,0) ... (3,1), each as hi then lo: 16 fragments.
+constexpr int kFragElems = 512;  // bf16 per fragment
+constexpr int kMFrags = 12;
+constexpr int kNFrags = 16;
+__host__ __device__ constexpr int m_pair_row(int p) { return p < 2 ? p : (p < 4 ? 2 : 3); }
+__host__ __device__ constexpr int m_pair_step(int p) { return (p == 3 || p == 5) ? 1 : 0; }
+__device__ __forceinline__ int colperm(int g, int e) { return 4 * g + (e & 3) + 16 * (e >> 2); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two RNE bf16 values packed in one register (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ unsigned pack_bf16x2(float x0, float x1) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+}
+
+// x = hi + lo for the eight values {a, b}: hi = bf16(x), lo = bf16(x - hi), as fragments
+__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h, bf16x8& l) {
+    u32x4 hp, lp;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float x0 = p < 2 ? a[2 * p] : b[2 * p - 4];
+        const float x1 = p < 2 ? a[2 * p + 1] : b[2 * p - 3];
+        const unsigned hh = pack_bf16x2(x0, x1);
+        hp[p] = hh;
+        lp[p] = pack_bf16x2(x0 - __uint_as_float(hh << 16), x1 - __uint_as_float(hh & 0xffff0000u));
+    }
+    h = __builtin_bit_cast(bf16x8, hp);
+    l = __builtin_bit_cast(bf16x8, lp);
+}
+
+// ------------------------------------------------------------------------------------------------
 // chunk_solve_kernel: one workgroup per (chunk slot, q/k head), for each of the head's v-heads.
 //
 // Writes, per (chunk, v-head), the chunk's gate block [3][64] floats: G2 = running sum of
 // g log2(e), 2^G2 and 2^(G2_C - G2) (G2_C = G2 at the chunk's last row; padding rows past the
-// chunk's length have g = 0), and M = T diag(beta) as hi and lo bf16 tiles [64][64] (row-major
-// with the column order described at the store, zero above the diagonal and in rows/columns past
-// the chunk's length).
+// chunk's length have g = 0), and M = T diag(beta) as the 12 fragments described above (zero above
+// the diagonal and in rows/columns past the chunk's length).  Per (chunk, q/k head) it writes
+// N = K K_p^T for the scan kernel's K S recurrence.
 //
 // K enters the matrix cores straight from memory (its rows are both operands of K K^T), and
 // K K^T is formed once for all v-heads of the q/k head.  A and T live in shared memory as their
@@ -209,7 +257,8 @@ template <typename TG>
 __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
     const __bf16* __restrict__ k, const TG* __restrict__ g, const TG* __restrict__ beta,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start, int N, int T,
-    int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M) {
+    int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M,
+    __bf16* __restrict__ ws_N) {
     __shared__ float sA[10][16 * kBP];     // blocks (a, b), a > b, of A
     __shared__ float sT[10][16 * kBP];     // blocks (a, b), a >= b, of T = (I + A)^-1
     __shared__ float sB[kC];
@@ -223,6 +272,7 @@ __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
     const int c = lane & 15, gq = lane >> 4;
     const size_t tok0 = (size_t)loc.row * T + loc.t0;
     const int L = loc.len;
+    const bool has_prev = loc.ci > 0;   // the previous chunk (always a full one) is in this sequence
 
     // K K^T as 16x16 tiles; wave w owns diagonal tile (w, w) and some below it: wave 0 (0,0) (1,0);
     // wave 1 (1,1) (2,1) (2,0); wave 2 (2,2) (3,2); wave 3 (3,3) (3,0) (3,1).  The K rows of the (at
@@ -244,6 +294,16 @@ __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) k2[kb] = kfrag(tt2, kb);
     }
+    // the previous chunk's K rows 16 b + c, b = 0..3, for N
+    bf16x8 kp[4][4];
+    if (has_prev) {
+        const __bf16* pb = k + ((tok0 - kC + c) * Hk + kh) * kDK + 8 * gq;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                kp[b][kb] = *reinterpret_cast<const bf16x8*>(pb + (size_t)16 * b * Hk * kDK + 32 * kb);
+    }
     auto kkt = [&](const bf16x8* ka, const bf16x8* kb_) {
         f32x4 acc = zero4();
 #pragma unroll
@@ -258,6 +318,22 @@ __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
     if (wave == 3) ky = kkt(k0, k2);
     const int xa = wave == 3 ? 3 : wave + 1, xb = wave == 3 ? 0 : wave;
     const int ya = wave == 1 ? 2 : 3, yb = wave == 1 ? 0 : 1;
+
+    // N: wave w forms the tiles (b, w) of N^T = K_p K^T, whose lane (g, c) element r is
+    // N[16 w + c][16 b + 4 g + r]; tiles 2j and 2j + 1 together are exactly fragment (w, j)
+    if (has_prev) {
+        f32x4 nt[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) nt[b] = kkt(kp[b], k0);
+        __bf16* nb = ws_N + ((size_t)slot * Hk + kh) * kNFrags * kFragElems + 8 * lane;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            bf16x8 hv, lv;
+            split8(nt[2 * j], nt[2 * j + 1], hv, lv);
+            *reinterpret_cast<bf16x8*>(nb + (2 * (2 * wave + j)) * kFragElems) = hv;
+            *reinterpret_cast<bf16x8*>(nb + (2 * (2 * wave + j) + 1) * kFragElems) = lv;
+        }
+    }
 
     // the gates of the first kPre v-heads are loaded together with K (one memory round trip)
     constexpr int kPre = 4;
@@ -361,68 +437,79 @@ __global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
             lds_barrier();
         }
 
-        // M = T diag(beta) as hi and lo rows: 64 rows x 8 pieces of 8 columns.  Within each block of
-        // 32 columns the stored order is the scan kernel's B-fragment order: stored columns 8 g + e
-        // are columns 4 g + e (e < 4) and 16 + 4 g + e - 4 (e >= 4).
-        __bf16* Mh = ws_M + ((size_t)slot * Hv + h) * 2 * kC * kC;
-        __bf16* Ml = Mh + kC * kC;
+        // M = T diag(beta) as its 12 fragments: item e = (pair p, lane ln) writes the hi and lo
+        // fragment rows of that lane, one 1 KiB fragment per wave and pass
+        __bf16* Mb = ws_M + ((size_t)slot * Hv + h) * kMFrags * kFragElems;
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int e = tid + kThreads * it;
-            const int t = e >> 3, p = e & 7;
-            const int j0 = 32 * (p >> 2) + 4 * (p & 3);
+            if (e >= 6 * 64) break;
+            const int p = e >> 6, ln = e & 63, lg = ln >> 4;
+            const int t = 16 * m_pair_row(p) + (ln & 15), j0 = 32 * m_pair_step(p);
             bf16x8 hv, lv;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int col = j0 + (j & 3) + 16 * (j >> 2);
+                const int col = j0 + colperm(lg, j);
                 const int ba = t >> 4, bb = col >> 4;
                 const float tv = bb <= ba ? sT[blk(ba, bb)][(t & 15) * kBP + (col & 15)] : 0.f;
                 const float x = tv * sB[col];
                 hv[j] = hi_of(x);
                 lv[j] = lo_of(x, hv[j]);
             }
-            *reinterpret_cast<bf16x8*>(Mh + t * kC + 8 * p) = hv;
-            *reinterpret_cast<bf16x8*>(Ml + t * kC + 8 * p) = lv;
+            *reinterpret_cast<bf16x8*>(Mb + (2 * p) * kFragElems + 8 * ln) = hv;
+            *reinterpret_cast<bf16x8*>(Mb + (2 * p + 1) * kFragElems + 8 * ln) = lv;
         }
         lds_barrier();                 // sT and sB are rewritten for the next v-head
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// chunk_scan_kernel: one workgroup of five waves per (sequence, v-head, 16-column slice of S).
+// chunk_scan_kernel: one workgroup of six waves per (sequence, v-head, 16-column slice of S).
 //
-// The slice (128 keys x 16 columns) is carried by two chain waves, one per half of the keys (four
-// 16 x 16 fp32 accumulator tiles each).  Per chunk:
-//     KS = K S                     each half forms its partial over its 64 keys; the partials meet
-//                                  in LDS (barrier B1) and both halves add them in the same order
-//     X = V - diag(e^G) KS,  U = M X,  D = diag(e^(G_C - G)) U      (both halves, identically)
-//     S <- e^(G_C) S + K^T D       each half updates its own keys
-// Every product's result stays in registers and feeds the next product as its B operand.  For that
-// accumulator rows stand for a fixed permutation of keys or tokens: row m (m = 4g + r) of tile a
-// stands for index
-//     rho(a, m) = 32 (a / 2) + 8 (m / 4) + 4 (a % 2) + m % 4,
-// so that tiles 2j and 2j + 1 together hand lane (g, c) the eight consecutive indices
-// 32 j + 8 g .. + 7, exactly the B-operand fragment of a 32-deep product.  (K S tiles use natural
-// token rows instead; the solve kernel stores M's columns in the matching order.)  A operands are
-// plain 16-byte rows (K from LDS, M from memory); K^T for the state update comes from the same K
-// rows through ds_read_b64_tr_b16.
+// Per chunk s of the sequence (start state S_{s-1}, U_s = M_s X_s its deltas):
+//     X_s = V_s - diag(e^G) K_s S_{s-1}
+//     U_s = M_s X_s,   D_s = diag(e^(G_C - G)) U_s
+//     S_s = e^(G_C) S_{s-1} + K_s^T D_s
+//     O_s = diag(e^G) Q_s S_{s-1} + P_s U_s
+// Only X -> U -> D -> X is a true chain from chunk to chunk once the state is eliminated from it:
+//     K_s S_{s-1} = e^(G_C,s-1) K_s S_{s-2} + N_s D_{s-1},     N_s = K_s K_{s-1}^T
+// where K_s S_{s-2} is known a whole chunk earlier.  The roles:
 //
-// Two output waves run one chunk behind: output wave w' owns token tiles {w', 3 - w'} of
-// O^T = S^T Q^T diag(e^G) + U^T P^T, with P^T tiles = K Q^T (masked, decayed) in registers and S^T,
-// U^T from the copies the chain waves leave in LDS.  A staging wave copies each chunk's K rows, V
-// columns and gate block straight from memory into a four-chunk LDS ring (global_load_lds), two
-// chunks ahead of their use.
+//   chain wave (0)   per chunk: N_s D_{s-1}, X_s = Y_s - diag(e^G) N_s D_{s-1}, U_s = M_s X_s and
+//                    D_s, with Y_s = V_s - diag(e^G) e^(G_C,s-1) K_s S_{s-2} from the state waves.
+//                    64 x 16 quantities, four 16 x 16 fp32 accumulator tiles each; N and M from
+//                    the solve kernel, loaded into registers a chunk ahead.
+//   state waves (1, 4)  one per half of the keys (64 keys x 16 columns, four tiles): one chunk
+//                    behind the chain, S <- e^(G_C) S + K^T D from the chain's U; then the half's
+//                    part of Y for the next chunk (half 0 adds V), and S^T (hi + lo) in LDS for
+//                    the output waves.
+//   output waves (2, 3)  one chunk behind the chain: wave w' owns token tiles {w', 3 - w'} of
+//                    O^T = S^T Q^T diag(e^G) + U^T P^T, P^T tiles = K Q^T masked and decayed in
+//                    registers, Q from memory a chunk ahead.
+//   staging wave (5) copies each chunk's K rows, V columns and gate block straight from memory into
+//                    a five-chunk LDS ring (global_load_lds), three chunks ahead of the chain.
 //
-// Waves 0 and 1 (chain) and 2 and 3 (output) have a SIMD each; the staging wave shares SIMD 0 at
-// the lowest priority (the chain waves raise theirs).  Two LDS barriers per chunk step: B1 for the
-// K S partials and B2 at the end.  At step s chain waves do chunk s (ring slot s % 4, copy buffer
-// s % 2); output waves finish chunk s - 1 (slot (s - 1) % 4, buffer (s - 1) % 2); the staging wave
-// starts chunk s + 2's copy into slot (s + 2) % 4 after B1 and waits for chunk s + 1's before B2.
-constexpr int kScanThreads = 320;
+// Waves w and w + 4 share a SIMD: the chain with state half 1, state half 0 with the staging
+// wave; the output waves have one each.  The state waves run at a higher priority than the chain:
+// on the shared SIMD the chain has the slack (measured), and the state half is the one the next
+// chunk waits for.
+//
+// Every product's result stays in registers and feeds the next product as its B operand.  The
+// chain's tiles (and the K S tiles of the state waves) use natural token rows: tiles 2j and 2j + 1
+// then hand lane (g, c) tokens 32 j + 4 g + e (e < 4) and 32 j + 16 + 4 g + e - 4 (e >= 4), the
+// column order of the N and M fragments.  The state tiles stand for keys in the order
+//     rho(a, m) = 32 (a / 2) + 8 (m / 4) + 4 (a % 2) + m % 4      (row m = 4g + r of tile a),
+// so that tiles 2j and 2j + 1 hand lane (g, c) the consecutive keys 32 j + 8 g .. + 7, matching
+// K rows read as plain A fragments; K^T for the state update is read from the same K rows with
+// ds_read_b64_tr_b16.
+//
+// One LDS barrier per chunk step.  Step s: the chain does chunk s, the state waves apply D_{s-1}
+// and form chunk s + 1's Y, the output waves finish chunk s - 1, the staging wave starts chunk
+// s + 3's copy and waits for chunk s + 2's.
+constexpr int kScanThreads = 384;
 constexpr int kWS = 16;          // state columns per workgroup
 constexpr int kSP = kDK + 8;     // row pitch of the S^T copies [column][key]
-constexpr int kUP = kC + 8;      // row pitch of the U^T copies [column][token]
-constexpr int kRing = 4;         // chunks in the staging ring
+constexpr int kRing = 5;         // chunks in the staging ring
 // K ring rows: pitch kKR elements (320 bytes, 20 sixteen-byte chunks, the last 4 unused), and the
 // 16-byte chunk q of row t stored at chunk q ^ ((t >> 2) & 3).  With 64 four-byte banks, both ways
 // the rows are read then touch 16 different chunk positions per 16 lanes: a row fragment (16
@@ -437,8 +524,8 @@ struct ScanLds {
     __bf16 Vr[kRing][kC * kWS];                // V [token][this slice's 16 columns]
     float Gt[kRing][256];                      // gate block: G2, 2^G2, 2^(G2_C - G2) (+ unused)
     __bf16 St[2][2][kWS * kSP];                // S^T at chunk start [buffer][hi, lo]
-    __bf16 Ut[2][2][kWS * kUP];                // U^T [buffer][hi, lo]
-    f32x4 Ex[2][4][64];                        // partial K S [key half][token tile][lane]
+    f32x4 Ut[2][4][64];                        // U [buffer][token tile][lane], the chain's tiles
+    f32x4 Yt[2][2][4][64];                     // Y in two parts [buffer][key half][tile][lane]
 };
 
 // index (token or key) that accumulator row m of tile a stands for
@@ -446,40 +533,18 @@ __device__ __forceinline__ int rho(int a, int m) {
     return 32 * (a >> 1) + 8 * (m >> 2) + 4 * (a & 1) + (m & 3);
 }
 
-// K^T fragment for the state update: lane (g, c) receives K[32 kb + 8 g + e][rho(kt, c)], e = 0..7
-// (keys in the state tiles' row order, tokens consecutive as in the D fragments).  Each half is a
-// transposed read of rows 32 kb + 8 g + 4 h + c / 4 at logical chunk 4 (kt / 2) + c % 4, half
-// kt % 2 of the chunk; `k0`, `k1` hold the ring slot plus the lane's part of the two halves'
-// addresses (the chunk swizzle of those rows depends on g and h only).
-__device__ __forceinline__ bf16x8 kt_frag(lds_u8* k0, lds_u8* k1, int kt, int kb) {
+// K^T fragment for the state update: lane (g, c) receives K[32 kb + 4 g + e][rho(kt, c)] (e < 4)
+// and K[32 kb + 16 + 4 g + e - 4][rho(kt, c)] (e >= 4): keys in the state tiles' row order, tokens
+// as in the chain's D fragments.  Each half is a transposed read of row 32 kb + 4 g (+ 16) + c / 4
+// at logical chunk 4 (kt / 2) + c % 4, half kt % 2 of the chunk; `k0` holds the ring slot plus the
+// lane's part of the address (the chunk swizzle of those rows is g).
+__device__ __forceinline__ bf16x8 kt_frag(lds_u8* k0, int kt, int kb) {
     const int off = 2 * (32 * kb * kKR + 32 * (kt >> 1) + 4 * (kt & 1));
-    return cat44(read_tr(k0, off), read_tr(k1, off));
+    return cat44(read_tr(k0, off), read_tr(k0, off + 2 * 16 * kKR));
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) void glb_void;
 typedef __attribute__((address_space(3))) void lds_void;
-
-// two floats -> two RNE bf16 values packed in one register (one v_cvt_pk_bf16_f32)
-__device__ __forceinline__ unsigned pack_bf16x2(float x0, float x1) {
-    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
-}
-
-// x = hi + lo for the eight values {a, b}: hi = bf16(x), lo = bf16(x - hi), as B fragments
-__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h, bf16x8& l) {
-    u32x4 hp, lp;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float x0 = p < 2 ? a[2 * p] : b[2 * p - 4];
-        const float x1 = p < 2 ? a[2 * p + 1] : b[2 * p - 3];
-        const unsigned hh = pack_bf16x2(x0, x1);
-        hp[p] = hh;
-        lp[p] = pack_bf16x2(x0 - __uint_as_float(hh << 16), x1 - __uint_as_float(hh & 0xffff0000u));
-    }
-    h = __builtin_bit_cast(bf16x8, hp);
-    l = __builtin_bit_cast(bf16x8, lp);
-}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
 template <int n>
@@ -493,11 +558,6 @@ __device__ __forceinline__ void copy_to_lds(const void* src, void* dst) {
     __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)dst, 16, 0, 0);
 }
 
-struct ChainIn {                   // one chunk's M fragments for a chain wave
-    bf16x8 mh[6], ml[6];           // M rows rho(a', c), stored columns 32 kb + 8 g ..: (a', kb) =
-                                   // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-};
-
 struct OutIn {                     // one chunk's Q fragments for an output wave (registers)
     bf16x8 q[2][4];                // Q rows 16 a + c of its two tiles, columns 32 kb + 8 g ..
 };
@@ -508,7 +568,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ order, int N, int T,
     int Hk, int Hv, int nct, int max_slots, const float* __restrict__ ws_G,
-    const __bf16* __restrict__ ws_M, float* __restrict__ o, float* final_state) {
+    const __bf16* __restrict__ ws_M, const __bf16* __restrict__ ws_N, float* __restrict__ o,
+    float* final_state) {
     constexpr int NS = DV / kWS;  // slices per v-head
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     ScanLds& sm = *reinterpret_cast<ScanLds*>(smem_raw);
@@ -540,9 +601,94 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     auto tok0_of = [&](int ci) { return (size_t)row * T + t0 + (size_t)ci * kC; };
     auto len_of = [&](int ci) { return min(kC, t1 - t0 - ci * kC); };
 
-    if (wave < 2) {
-        // ------------------------------------------------ chain waves -------------------------
-        auto chain = [&](auto hc) {
+    if (wave == 0) {
+        // ------------------------------------------------ chain wave --------------------------
+        if (nchunks == 0) return;
+        __builtin_amdgcn_s_setprio(1);
+        bf16x8 mf[kMFrags];              // M_s fragments, refilled with M_{s+1}'s once used
+        bf16x8 nf[kNFrags];              // N_s fragments, likewise
+        auto fetch_m = [&](int ci) {
+            const __bf16* b = ws_M + ((size_t)(slot0 + ci) * Hv + h) * kMFrags * kFragElems + 8 * lane;
+#pragma unroll
+            for (int f = 0; f < kMFrags; ++f) mf[f] = *reinterpret_cast<const bf16x8*>(b + f * kFragElems);
+        };
+        auto fetch_n = [&](int ci) {
+            const __bf16* b = ws_N + ((size_t)(slot0 + ci) * Hk + kh) * kNFrags * kFragElems + 8 * lane;
+#pragma unroll
+            for (int f = 0; f < kNFrags; ++f) nf[f] = *reinterpret_cast<const bf16x8*>(b + f * kFragElems);
+        };
+        f32x4 u[4];                      // U of the previous chunk
+        fetch_m(0);
+        if (nchunks > 1) fetch_n(1);
+        lds_barrier();  // P: chunks 0 and 1 staged
+        lds_barrier();  // B0: Y_0 ready
+        auto step = [&](int s, auto first) {
+            constexpr bool kFirst = decltype(first)::value;
+            const float* gt = sm.Gt[s % kRing];
+            lds_u8* yl = lds_at(&sm.Yt[s & 1][0][0][lane]);
+            lds_u8* gl = lds_at(gt + kC + 4 * g);                    // 2^G2 at rows 16 a + 4 g + r
+            f32x4 y[4], eg[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                y[a] = ld<f32x4>(yl, 16 * 64 * a) + ld<f32x4>(yl, 16 * 64 * (4 + a));
+                eg[a] = ld<f32x4>(gl, 4 * 16 * a);
+            }
+            f32x4 x[4];
+            if constexpr (kFirst) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) x[a] = y[a];
+            } else {
+                // D_{s-1} = diag(e^(G_C - G)) U_{s-1} as hi + lo B fragments
+                lds_u8* dl_ = lds_at(sm.Gt[(s - 1) % kRing] + 2 * kC + 4 * g);
+                f32x4 ds[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) ds[a] = u[a] * ld<f32x4>(dl_, 4 * 16 * a);
+                bf16x8 dh[2], dlo[2];
+                split8(ds[0], ds[1], dh[0], dlo[0]);
+                split8(ds[2], ds[3], dh[1], dlo[1]);
+                // N_s D_{s-1}
+                f32x4 nd[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    nd[a] = zero4();
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        nd[a] = mma(nf[2 * (2 * a + j)], dh[j], nd[a]);
+                        nd[a] = mma(nf[2 * (2 * a + j)], dlo[j], nd[a]);
+                        nd[a] = mma(nf[2 * (2 * a + j) + 1], dh[j], nd[a]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (s + 1 < nchunks) fetch_n(s + 1);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) x[a] = y[a] - eg[a] * nd[a];
+            }
+            bf16x8 xh[2], xl[2];
+            split8(x[0], x[1], xh[0], xl[0]);
+            split8(x[2], x[3], xh[1], xl[1]);
+            // U = M X (M lower triangular: pairs (a, j) with 2 j <= a)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) u[a] = zero4();
+#pragma unroll
+            for (int p = 0; p < 6; ++p) {
+                const int a = m_pair_row(p), j = m_pair_step(p);
+                u[a] = mma(mf[2 * p], xh[j], u[a]);
+                u[a] = mma(mf[2 * p], xl[j], u[a]);
+                u[a] = mma(mf[2 * p + 1], xh[j], u[a]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < nchunks) fetch_m(s + 1);
+            lds_u8* ul = lds_at(&sm.Ut[s & 1][0][lane]);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) st(ul, 16 * 64 * a, u[a]);
+            lds_barrier();
+        };
+        step(0, std::true_type{});
+        for (int s = 1; s < nchunks; ++s) step(s, std::false_type{});
+        lds_barrier();  // the other roles' last step
+    } else if (wave == 1 || wave == 4) {
+        // ------------------------------------------------ state waves -------------------------
+        auto state_role = [&](auto hc) {
             constexpr int hh = decltype(hc)::value;   // key half: state tiles 4 hh .. 4 hh + 3
             auto state_idx = [&](int t, int r) {
                 return sbase + (size_t)rho(4 * hh + t, 4 * g + r) * DV + c0 + c;
@@ -556,17 +702,6 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 return;
             }
             __builtin_amdgcn_s_setprio(2);
-            constexpr int ta[6] = {0, 1, 2, 2, 3, 3}, tb[6] = {0, 0, 0, 1, 0, 1};
-            auto fetch = [&](ChainIn& f, int ci) {
-                const __bf16* mb = ws_M + ((size_t)(slot0 + ci) * Hv + h) * 2 * kC * kC;
-#pragma unroll
-                for (int p = 0; p < 6; ++p) {
-                    const __bf16* mp = mb + rho(ta[p], c) * kC + 32 * tb[p] + 8 * g;
-                    f.mh[p] = *reinterpret_cast<const bf16x8*>(mp);
-                    f.ml[p] = *reinterpret_cast<const bf16x8*>(mp + kC * kC);
-                }
-            };
-
             f32x4 S[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -574,141 +709,104 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 for (int r = 0; r < 4; ++r) S[t][r] = initial_state ? initial_state[state_idx(t, r)] : 0.f;
             // lane parts of the LDS addresses (the rest are compile-time offsets)
             const int l_kf = c * kKR + 8 * (g ^ kswz(c));                 // K row c, logical chunk g
-            const int l_kt0 = (8 * g + (c >> 2)) * kKR + 8 * ((c & 3) ^ kswz(8 * g));
-            const int l_kt1 = (8 * g + 4 + (c >> 2)) * kKR + 8 * ((c & 3) ^ kswz(8 * g + 4));
+            const int l_kt = (4 * g + (c >> 2)) * kKR + 8 * ((c & 3) ^ g);
             const int l_v = (4 * g + (c >> 2)) * kWS + 4 * (c & 3);
-            const int l_st = c * kSP + 8 * g, l_ut = c * kUP + 8 * g;
-
-            // one set of M registers: chunk i's fragments are consumed by U = M X, then the same
-            // registers are refilled with chunk i + 1's, a whole step ahead of their use
-            ChainIn mc;
-            auto step = [&](int i) {
-                const int slot = i % kRing;
-                const __bf16* kr = sm.Kr[slot];
-                const float* gt = sm.Gt[slot];
-                // LDS operands that do not depend on B1, all issued up front: K rows 16 a + c at this
-                // half's keys (logical chunks 4 jj + g, jj = 2 hh + u); V[16 a + 4 g + r][c0 + c]
-                // (one transposed read of four consecutive rows); the decay factors; the K^T
-                // fragments of this half's keys
-                bf16x8 kf[2][4];
-                lds_u8* kfl = lds_at(kr + l_kf);
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int a = 0; a < 4; ++a)
-                        kf[u][a] = ld<bf16x8>(kfl, 2 * (16 * a * kKR + 32 * (2 * hh + u)));
-                lds_u8* vl = lds_at(sm.Vr[slot] + l_v);
-                lds_u8* gl = lds_at(gt + 4 * g);
-                lds_u8* gd = lds_at(gt + 8 * g);
-                bf16x4 vv[4];
-                f32x4 eg[4], dg[4];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    vv[a] = read_tr(vl, 2 * 16 * a * kWS);
-                    eg[a] = ld<f32x4>(gl, 4 * (kC + 16 * a));                   // 2^G2 at 16 a + 4 g + r
-                    dg[a] = ld<f32x4>(gd, 4 * (2 * kC + 32 * (a >> 1) + 4 * (a & 1)));  // at rho(a, 4 g + r)
-                }
-                const float ec = gt[2 * kC - 1];
-                lds_u8* kt0 = lds_at(kr + l_kt0);
-                lds_u8* kt1 = lds_at(kr + l_kt1);
-                bf16x8 kt[4][2];
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) kt[t][kb] = kt_frag(kt0, kt1, 4 * hh + t, kb);
-                __builtin_amdgcn_sched_barrier(0);
-                // this half of S as hi + lo B fragments (keys 32 jj + 8 g + e), and its copy for
-                // the output waves
-                bf16x8 sh[2], sl[2];
+            const int l_st = c * kSP + 8 * g;
+            bf16x8 sh[2], sl[2];             // this half of S as hi + lo B fragments
+                                             // (keys 32 (2 hh + u) + 8 g + e)
+            auto split_s = [&]() {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) split8(S[2 * u], S[2 * u + 1], sh[u], sl[u]);
-                lds_u8* stb = lds_at(sm.St[i & 1][0] + l_st);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    st(stb, 2 * 32 * (2 * hh + u), sh[u]);
-                    st(stb, 2 * (kWS * kSP + 32 * (2 * hh + u)), sl[u]);
-                }
-                // partial K S over this half's keys: token tile a, rows 16 a + m
-                f32x4 ks[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        ks[a] = mma(kf[u][a], sh[u], ks[a]);
-                        ks[a] = mma(kf[u][a], sl[u], ks[a]);
-                    }
-                lds_u8* exo = lds_at(&sm.Ex[hh][0][lane]);
-#pragma unroll
-                for (int a = 0; a < 4; ++a) st(exo, 16 * 64 * a, ks[a]);
-                lds_barrier();                                           // B1
-                // the full K S: both halves add the two partials in the same order (bitwise equal)
-                lds_u8* ex0 = lds_at(&sm.Ex[0][0][lane]);
-                f32x4 ksf[4];
+            };
+            // this half's part of Y for chunk ci: -diag(e^G) e^(G_C, ci - 1) K S over its keys,
+            // plus V in half 0 (ec = that decay factor)
+            auto make_y = [&](int ci, float ec) {
+                const int slot = ci % kRing;
+                lds_u8* kfl = lds_at(sm.Kr[slot] + l_kf);
+                lds_u8* gl = lds_at(sm.Gt[slot] + kC + 4 * g);
+                f32x4 ks[4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const f32x4 p0 = ld<f32x4>(ex0, 16 * 64 * a);
-                    const f32x4 p1 = ld<f32x4>(ex0, 16 * 64 * (4 + a));
-                    ksf[a] = p0 + p1;
-                }
-                // X = V - e^G KS as hi + lo B fragments (tokens 32 kb + 4 g + e for e < 4 and
-                // 32 kb + 16 + 4 g + e - 4 for e >= 4: the stored column order of M)
-                f32x4 xs[4];
+                    bf16x8 kf[2];
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
+                    for (int u = 0; u < 2; ++u) kf[u] = ld<bf16x8>(kfl, 2 * (16 * a * kKR + 32 * (2 * hh + u)));
+                    ks[a] = zero4();
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) xs[a][r] = (float)vv[a][r] - eg[a][r] * ksf[a][r];
-                bf16x8 xh[2], xl[2];
-                split8(xs[0], xs[1], xh[0], xl[0]);
-                split8(xs[2], xs[3], xh[1], xl[1]);
-                // U = M X (M lower triangular: token tiles 0, 1 need kb = 0 only)
-                f32x4 u[4];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) u[a] = zero4();
-#pragma unroll
-                for (int p = 0; p < 6; ++p) {
-                    u[ta[p]] = mma(mc.mh[p], xh[tb[p]], u[ta[p]]);
-                    u[ta[p]] = mma(mc.mh[p], xl[tb[p]], u[ta[p]]);
-                    u[ta[p]] = mma(mc.ml[p], xh[tb[p]], u[ta[p]]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                fetch(mc, min(i + 1, nchunks - 1));
-                f32x4 ds[4];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) ds[a] = u[a] * dg[a];
-                bf16x8 dh[2], dl[2];
-                split8(ds[0], ds[1], dh[0], dl[0]);
-                split8(ds[2], ds[3], dh[1], dl[1]);
-                // S <- e^(G_C) S + K^T D for this half's keys
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    f32x4 acc = S[t] * ec;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        acc = mma(kt[t][kb], dh[kb], acc);
-                        acc = mma(kt[t][kb], dl[kb], acc);
+                    for (int u = 0; u < 2; ++u) {
+                        ks[a] = mma(kf[u], sh[u], ks[a]);
+                        ks[a] = mma(kf[u], sl[u], ks[a]);
                     }
-                    S[t] = acc;
                 }
-                // U (hi + lo) for the output waves: this half writes tokens 32 hh .. 32 hh + 31
-                bf16x8 uh, ul;
-                split8(u[2 * hh], u[2 * hh + 1], uh, ul);
-                lds_u8* utb = lds_at(sm.Ut[i & 1][0] + l_ut);
-                st(utb, 2 * 32 * hh, uh);
-                st(utb, 2 * (kWS * kUP + 32 * hh), ul);
-                lds_barrier();                                           // B2
+                lds_u8* yl = lds_at(&sm.Yt[ci & 1][hh][0][lane]);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x4 eg = ld<f32x4>(gl, 4 * 16 * a) * ec;
+                    f32x4 y;
+                    if constexpr (hh == 0) {
+                        lds_u8* vl = lds_at(sm.Vr[slot] + l_v);
+                        const bf16x4 vv = read_tr(vl, 2 * 16 * a * kWS);        // V[16 a + 4 g + r][c]
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) y[r] = (float)vv[r] - eg[r] * ks[a][r];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) y[r] = -eg[r] * ks[a][r];
+                    }
+                    st(yl, 16 * 64 * a, y);
+                }
             };
-            fetch(mc, 0);
-            lds_barrier();  // chunks 0 and 1 staged
-            for (int i = 0; i < nchunks; ++i) step(i);
-            lds_barrier();  // the output waves' last step
-            lds_barrier();
+            lds_barrier();  // P: chunks 0 and 1 staged
+            split_s();
+            make_y(0, 1.f);
+            lds_barrier();  // B0
+            for (int s = 0; s <= nchunks; ++s) {
+                if (s >= 1) {
+                    // S <- e^(G_C) S + K^T D with chunk s - 1's D, from the chain's U
+                    const int ps = (s - 1) % kRing;
+                    const float* gp = sm.Gt[ps];
+                    const float ec = gp[2 * kC - 1];
+                    lds_u8* ul = lds_at(&sm.Ut[(s - 1) & 1][0][lane]);
+                    lds_u8* dl_ = lds_at(gp + 2 * kC + 4 * g);
+                    f32x4 ds[4];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) ds[a] = ld<f32x4>(ul, 16 * 64 * a) * ld<f32x4>(dl_, 4 * 16 * a);
+                    bf16x8 dh[2], dlo[2];
+                    split8(ds[0], ds[1], dh[0], dlo[0]);
+                    split8(ds[2], ds[3], dh[1], dlo[1]);
+                    lds_u8* ktl = lds_at(sm.Kr[ps] + l_kt);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        bf16x8 kt[2];
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) kt[kb] = kt_frag(ktl, 4 * hh + t, kb);
+                        f32x4 acc = S[t] * ec;
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            acc = mma(kt[kb], dh[kb], acc);
+                            acc = mma(kt[kb], dlo[kb], acc);
+                        }
+                        S[t] = acc;
+                    }
+                }
+                if (s < nchunks) {
+                    // S_{s-1} (chunk s's start state) for the output waves, and chunk s + 1's Y
+                    split_s();
+                    lds_u8* stb = lds_at(sm.St[s & 1][0] + l_st);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        st(stb, 2 * 32 * (2 * hh + u), sh[u]);
+                        st(stb, 2 * (kWS * kSP + 32 * (2 * hh + u)), sl[u]);
+                    }
+                    if (s + 1 < nchunks) make_y(s + 1, sm.Gt[s % kRing][2 * kC - 1]);
+                }
+                lds_barrier();
+            }
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) final_state[state_idx(t, r)] = S[t][r];
         };
-        if (wave == 0) chain(std::integral_constant<int, 0>{});
-        else chain(std::integral_constant<int, 1>{});
+        if (wave == 1) state_role(std::integral_constant<int, 0>{});
+        else state_role(std::integral_constant<int, 1>{});
     } else if (wave < 4) {
         // ------------------------------------------------ output waves ------------------------
         if (nchunks == 0) return;
@@ -716,7 +814,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             constexpr int ow = decltype(oc)::value;      // 0: tiles {0, 3}; 1: tiles {1, 2}
             constexpr int tiles[2] = {ow, 3 - ow};
             const int l_kf = c * kKR + 8 * (g ^ kswz(c));                 // K row c, logical chunk g
-            const int l_st = c * kSP + 8 * g, l_ut = c * kUP + 4 * g;
+            const int l_st = c * kSP + 8 * g;
             auto fetch_out = [&](OutIn& f, int ci) {
                 const size_t tok0 = tok0_of(ci);
                 const int L = len_of(ci);
@@ -752,12 +850,14 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     lds_u8* sp = lds_at(sm.St[buf][hl] + l_st);
 #pragma unroll
                     for (int kb = 0; kb < 4; ++kb) sf[hl][kb] = ld<bf16x8>(sp, 2 * 32 * kb);
-                    lds_u8* up = lds_at(sm.Ut[buf][hl] + l_ut);
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-                        uf[hl][kb] = cat44(ld<bf16x4>(up, 2 * 32 * kb), ld<bf16x4>(up, 2 * (32 * kb + 16)));
                 }
-                lds_barrier();                                           // B1
+                // U^T fragments: lane (g, c) of the chain's tiles 2 kb, 2 kb + 1 holds U at
+                // tokens 32 kb + 4 g + r and 32 kb + 16 + 4 g + r, column c: the P^T row order
+                lds_u8* ul = lds_at(&sm.Ut[buf][0][lane]);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    split8(ld<f32x4>(ul, 16 * 64 * (2 * kb)), ld<f32x4>(ul, 16 * 64 * (2 * kb + 1)), uf[0][kb],
+                           uf[1][kb]);
                 f32x4 ot[2];
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
@@ -810,14 +910,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     const int t = 16 * tiles[x] + c;
                     if (t < L) *reinterpret_cast<f32x4*>(o + ((tok0 + t) * Hv + h) * DV + c0 + 4 * g) = ot[x];
                 }
-                lds_barrier();                                           // B2
+                lds_barrier();
             };
             OutIn fa, fb;
-            lds_barrier();  // chunks 0 and 1 staged
-            // step 0: chunk 0's Q rows
             fetch_out(fa, 0);
-            lds_barrier();
-            lds_barrier();
+            lds_barrier();  // P
+            lds_barrier();  // B0
+            lds_barrier();  // step 0: nothing finishes yet
             int s = 1;
             for (; s + 1 <= nchunks; s += 2) {
                 step(s, fa, fb);
@@ -857,45 +956,52 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             copy_to_lds(gb + 4 * min(lane, 47), sm.Gt[slot]);
         };
         dma(0);
-        dma(min(1, nchunks - 1));
+        if (nchunks > 1) dma(1);
         wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();  // chunks 0 and 1 staged
+        __builtin_amdgcn_s_barrier();       // P: chunks 0 and 1 staged
+        if (nchunks > 2) dma(2);
+        __builtin_amdgcn_s_barrier();       // B0
         for (int s = 0; s <= nchunks; ++s) {
-            __builtin_amdgcn_s_barrier();   // B1
-            dma(min(s + 2, nchunks - 1));   // (repeats of the last chunk near the end: never read)
-            wait_vmcnt<kDmaOps>();          // chunk s + 1's copy (issued one step ago) has landed
-            __builtin_amdgcn_s_barrier();   // B2
+            // chunk s + 3 goes into the slot chunk s - 2 left; chunk s + 2 must have landed before
+            // the step ends
+            if (s + 3 < nchunks) {
+                dma(s + 3);
+                wait_vmcnt<kDmaOps>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            __builtin_amdgcn_s_barrier();
         }
-        wait_vmcnt<0>();
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // workspace layout (each region 256-byte aligned):
 //   chunk_start [N+1] int32 | order [N] int32 | gates [slots][Hv][G2, 2^G2, 2^(G2_C - G2)][64] f32
-//   | M [slots][Hv][hi, lo][64][64] bf16
+//   | M [slots][Hv][12 fragments] bf16 | N [slots][Hk][16 fragments] bf16
 struct Layout {
-    size_t chunk_start, order, G, M, total;
+    size_t chunk_start, order, G, M, Nm, total;
     int slots;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout layout(int B, int T, int Hv, int N) {
+Layout layout(int B, int T, int Hk, int Hv, int N) {
     Layout l;
     l.slots = (int)(((long long)B * T) / kC) + N;  // bounds B*ceil(T/64) and T/64 + N (packed)
     size_t off = 0;
     l.chunk_start = off; off = align256(off + sizeof(int32_t) * (size_t)(N + 1));
     l.order = off;       off = align256(off + sizeof(int32_t) * (size_t)N);
     l.G = off;           off = align256(off + sizeof(float) * (size_t)l.slots * Hv * 3 * kC);
-    l.M = off;           off = align256(off + 2 * (size_t)l.slots * Hv * 2 * kC * kC);
+    l.M = off;           off = align256(off + 2 * (size_t)l.slots * Hv * kMFrags * kFragElems);
+    l.Nm = off;          off = align256(off + 2 * (size_t)l.slots * Hk * kNFrags * kFragElems);
     l.total = off;
     return l;
 }
 
 template <int DV, typename TG>
 hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
-    const Layout lay = layout(a.B, a.T, a.Hv, a.N);
+    const Layout lay = layout(a.B, a.T, a.Hk, a.Hv, a.N);
     char* ws = static_cast<char*>(a.workspace);
     const bool packed = a.cu_seqlens != nullptr;
     const int nct = (a.T + kC - 1) / kC;
@@ -904,6 +1010,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
     const int32_t* order = packed ? reinterpret_cast<const int32_t*>(ws + lay.order) : nullptr;
     float* ws_G = reinterpret_cast<float*>(ws + lay.G);
     __bf16* ws_M = reinterpret_cast<__bf16*>(ws + lay.M);
+    __bf16* ws_N = reinterpret_cast<__bf16*>(ws + lay.Nm);
     hipError_t e;
     if ((stages & kStagePrepare) && packed) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, a.stream, a.cu_seqlens, a.N,
@@ -915,7 +1022,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
         hipLaunchKernelGGL((chunk_solve_kernel<TG>), dim3((unsigned)slots, (unsigned)a.Hk),
                            dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.k),
                            static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta),
-                           a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M);
+                           a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M, ws_N);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (!(stages & kStageScan)) return hipSuccess;
@@ -931,7 +1038,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
                        a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), a.initial_state, a.cu_seqlens, chunk_start,
                        order, a.N, a.T, a.Hk, a.Hv, nct, packed ? lay.slots : a.B * nct, ws_G, ws_M,
-                       a.o, a.final_state);
+                       ws_N, a.o, a.final_state);
     return hipGetLastError();
 }
 
@@ -942,10 +1049,9 @@ bool chunk_mfma_supported(int dk, int dv, gdn_dtype qkv_dtype) {
 }
 
 size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N) {
-    (void)Hk;
     (void)dk;
     (void)dv;
-    return layout(B, T, Hv, N).total;
+    return layout(B, T, Hk, Hv, N).total;
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, unsigned stages) {
