@@ -42,8 +42,8 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
 # reads on a plain copy of known size (profiles/); None whenever the kernel changed since.
-TRAFFIC_SCAN = None
-TRAFFIC_DECODE = 1085269402    # recurrent_kernel<128,128,bf16,f32>, one decode step, B=256
+TRAFFIC_SCAN = 180211507       # chunk_scan_kernel<128>, prefill T=4096
+TRAFFIC_DECODE = 1085246157    # recurrent_kernel<128,128,bf16,f32>, one decode step, B=256
 
 
 def prefill_algorithmic(wl, T: int, B: int, N: int, init_state: bool):
@@ -68,8 +68,8 @@ def decode_algorithmic(wl):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

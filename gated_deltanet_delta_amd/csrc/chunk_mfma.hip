@@ -253,8 +253,10 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
 constexpr int kBP = 17;          // row pitch (floats) of the 16 x 16 blocks of A and T
 __device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }   // a >= b
 
+// (at most 128 registers per lane: four waves per SIMD, so a whole 4096-token prefill's chunk
+// workgroups are resident at once)
 template <typename TG>
-__global__ __launch_bounds__(kThreads) void chunk_solve_kernel(
+__global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     const __bf16* __restrict__ k, const TG* __restrict__ g, const TG* __restrict__ beta,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start, int N, int T,
     int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M,
