@@ -42,7 +42,7 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
 # reads on a plain copy of known size (profiles/); None whenever the kernel changed since.
-TRAFFIC_SCAN = 180211507       # chunk_scan_kernel<128>, prefill T=4096
+TRAFFIC_SCAN = None
 TRAFFIC_DECODE = 1085246157    # recurrent_kernel<128,128,bf16,f32>, one decode step, B=256
 
 

@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (s + 1 < nchunks) fetch_n(s + 1);
+                fetch_n(min(s + 1, nchunks - 1));   // unconditional: see fetch_m
 #pragma unroll
                 for (int a = 0; a < 4; ++a) x[a] = y[a] - eg[a] * nd[a];
             }
@@ -679,7 +679,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 u[a] = mma(mf[2 * p + 1], xh[j], u[a]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (s + 1 < nchunks) fetch_m(s + 1);
+            // unconditional (the last chunk refetches itself): a conditional fetch makes the
+            // compiler's wait before the next use also wait for every load issued after it
+            fetch_m(min(s + 1, nchunks - 1));
             lds_u8* ul = lds_at(&sm.Ut[s & 1][0][lane]);
 #pragma unroll
             for (int a = 0; a < 4; ++a) st(ul, 16 * 64 * a, u[a]);
