@@ -69,7 +69,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -83,7 +83,8 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from gated_deltanet_delta_amd import gdn_chunk_fwd, gdn_recurrent_step, synth, workspace_size
+    from gated_deltanet_delta_amd import (gdn_chunk_fwd, gdn_chunk_fwd_gating, gdn_recurrent_step,
+                                          gdn_recurrent_step_gating, synth, workspace_size)
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -150,6 +151,28 @@ def main() -> int:
 
     ms_prepare = time_stage("prepare")
     ms_scan = time_stage("scan")
+
+    # the same prefill with the gates formed in the kernels from the raw projections a, b
+    raw = x["raw"]
+    ga = torch.from_numpy(raw["a"]).to(wl.gate_dtype).to(dev)
+    gb = torch.from_numpy(raw["b"]).to(wl.gate_dtype).to(dev)
+    gA = torch.from_numpy(raw["A_log"]).to(dev)
+    gdt = torch.from_numpy(raw["dt_bias"]).to(dev)
+
+    def prefill_gating():
+        gdn_chunk_fwd_gating(d["q"], d["k"], d["v"], ga, gb, gA, gdt, d["initial_state"], None,
+                             o=o, final_state=fs, workspace=ws)
+
+    for _ in range(args.warmup):
+        prefill_gating()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        prefill_gating()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_gating = e0.elapsed_time(e1) / args.steps
     achieved_gbs = scan_bytes / (ms_scan / 1e3) / 1e9
     useful_tflops = flops / (ms_events / 1e3) / 1e12
 
@@ -174,6 +197,23 @@ def main() -> int:
     ev1.record()
     torch.cuda.synchronize()
     ms_decode = ev0.elapsed_time(ev1) / nd
+
+    # the decode steps with the gates formed in the kernel
+    graw = [{key: torch.from_numpy(s["raw"][key]).to(dev) for key in ("a", "b")} for s in steps]
+    dA = torch.from_numpy(x0["raw"]["A_log"]).to(dev)
+    ddt = torch.from_numpy(x0["raw"]["dt_bias"]).to(dev)
+
+    def decode_gating_pass():
+        for s, r in zip(dsteps, graw):
+            gdn_recurrent_step_gating(s["q"], s["k"], s["v"], r["a"], r["b"], dA, ddt, state, o=od)
+
+    decode_gating_pass()
+    torch.cuda.synchronize()
+    ev0.record()
+    decode_gating_pass()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_decode_gating = ev0.elapsed_time(ev1) / nd
     state_bytes, total_bytes = decode_algorithmic(wd)
     state_gbs = state_bytes / (ms_decode / 1e3) / 1e9
     total_gbs = total_bytes / (ms_decode / 1e3) / 1e9
@@ -221,6 +261,9 @@ def main() -> int:
                      "call_achieved_gbs": round(nbytes / (ms_events / 1e3) / 1e9, 1),
                      "useful_tflops": round(useful_tflops, 2),
                      "mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4)},
+        "prefill_gating": {"call": "gdn_chunk_fwd_gating (gates formed in the kernels from a, b)",
+                           "ms_per_call_events": round(ms_gating, 5),
+                           "tokens_per_s": round(tokens / (ms_gating / 1e3), 1)},
         "cpu_baseline": cpu,
         "decode": {"metric": "decode state GB/s", "value": round(state_gbs, 1), "unit": "GB/s",
                    "workload": f"decode B={wd.B} Hk={wd.Hk} Hv={wd.Hv} dk=dv={wd.dk}, {nd} one-token "
@@ -229,7 +272,10 @@ def main() -> int:
                    "roofline": {"bound": "hbm", "achieved": round(total_gbs, 1), "peak": MI355X_HBM_GBS,
                                 "unit": "GB/s", "frac": round(total_gbs / MI355X_HBM_GBS, 4),
                                 "traffic": TRAFFIC_DECODE, "kernel": "recurrent_kernel<128,128,bf16,f32>",
-                                "algorithmic_bytes_per_launch": int(total_bytes)}},
+                                "algorithmic_bytes_per_launch": int(total_bytes)},
+                   "gating": {"call": "gdn_recurrent_step_gating (gates formed in the kernel from a, b)",
+                              "ms_per_step": round(ms_decode_gating, 5),
+                              "state_gbs": round(state_bytes / (ms_decode_gating / 1e3) / 1e9, 1)}},
     }
     print(json.dumps(line), flush=True)
     return 0

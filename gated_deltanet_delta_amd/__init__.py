@@ -6,6 +6,7 @@ Python binding.
 The binding only marshals torch tensors into the C ABI declared in include/gdn.h; the library must
 be built (``python -m gated_deltanet_delta_amd.build``) and there is no CPU fallback.
 """
-from .api import (chunk_gated_delta_rule, gdn_chunk_fwd, gdn_recurrent_step,  # noqa: F401
-                  recurrent_gated_delta_rule, workspace_size)
+from .api import (chunk_gated_delta_rule, gdn_chunk_fwd, gdn_chunk_fwd_gating,  # noqa: F401
+                  gdn_recurrent_step, gdn_recurrent_step_gating, recurrent_gated_delta_rule,
+                  workspace_size)
 from ._lib import GdnError  # noqa: F401

@@ -51,6 +51,54 @@ def workspace_size(B: int, T: int, Hk: int, Hv: int, dk: int, dv: int, N: int,
     return int(_lib.load().gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, _DTYPES[qkv_dtype]))
 
 
+def _chunk_call(fn, q, k, v, x, y, A_log, dt_bias, initial_state, cu_seqlens, o, final_state,
+                workspace, gating: bool):
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"{fn.__name__} runs on a GPU; tensors must be on a cuda device")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    xn, yn = ("a", "b") if gating else ("g", "beta")
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(x, (B, T, Hv), xn, dev)
+    _check(y, (B, T, Hv), yn, dev, x.dtype)
+    if gating:
+        _check(A_log, (Hv,), "A_log", dev, torch.float32)
+        _check(dt_bias, (Hv,), "dt_bias", dev, torch.float32)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
+    if initial_state is not None:
+        _check(initial_state, (N, Hv, dk, dv), "initial_state", dev, torch.float32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
+    if final_state is None:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    _check(final_state, (N, Hv, dk, dv), "final_state", dev, torch.float32)
+    qkv, gate = _code(q, "q"), _code(x, xn)
+    ws_bytes = int(lib.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    gates = (_ptr(A_log), _ptr(dt_bias)) if gating else ()
+    st = fn(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(y), *gates, _ptr(initial_state), _ptr(cu_seqlens),
+        B, T, Hk, Hv, dk, dv, N, qkv, gate, _ptr(o), _ptr(final_state), _ptr(workspace),
+        ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
+        _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, fn.__name__)
+    return o, final_state
+
+
 def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                   beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, *, o: Optional[torch.Tensor] = None,
@@ -70,44 +118,51 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
               "scan": lib.gdn_chunk_fwd_scan}[stage]
     except KeyError:
         raise ValueError(f"stage must be 'all', 'prepare' or 'scan', not {stage!r}") from None
+    return _chunk_call(fn, q, k, v, g, beta, None, None, initial_state, cu_seqlens, o, final_state,
+                       workspace, gating=False)
+
+
+def gdn_chunk_fwd_gating(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor,
+                         b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
+                         initial_state: Optional[torch.Tensor] = None,
+                         cu_seqlens: Optional[torch.Tensor] = None, *,
+                         o: Optional[torch.Tensor] = None,
+                         final_state: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gdn_chunk_fwd with the gates formed in the kernels: a, b [B,T,Hv] the raw projections;
+    A_log, dt_bias [Hv] fp32.  beta = sigmoid(b), g = -exp(A_log) softplus(a + dt_bias)."""
+    lib = _lib.load()
+    return _chunk_call(lib.gdn_chunk_fwd_gating, q, k, v, a, b, A_log, dt_bias, initial_state,
+                       cu_seqlens, o, final_state, workspace, gating=True)
+
+
+def _recurrent_call(fn, q, k, v, x, y, A_log, dt_bias, state, o, gating: bool):
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, T, H, d]")
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("gdn_chunk_fwd runs on a GPU; tensors must be on a cuda device")
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+        raise ValueError(f"{fn.__name__} runs on a GPU; tensors must be on a cuda device")
+    xn, yn = ("a", "b") if gating else ("g", "beta")
     _check(q, (B, T, Hk, dk), "q", dev)
     _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
     _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
-    _check(g, (B, T, Hv), "g", dev)
-    _check(beta, (B, T, Hv), "beta", dev, g.dtype)
-    if cu_seqlens is not None:
-        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
-    if initial_state is not None:
-        _check(initial_state, (N, Hv, dk, dv), "initial_state", dev, torch.float32)
+    _check(x, (B, T, Hv), xn, dev)
+    _check(y, (B, T, Hv), yn, dev, x.dtype)
+    if gating:
+        _check(A_log, (Hv,), "A_log", dev, torch.float32)
+        _check(dt_bias, (Hv,), "dt_bias", dev, torch.float32)
+    _check(state, (B, Hv, dk, dv), "state", dev, torch.float32)
     if o is None:
         o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
     _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
-    if final_state is None:
-        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
-    _check(final_state, (N, Hv, dk, dv), "final_state", dev, torch.float32)
-    qkv, gate = _code(q, "q"), _code(g, "g")
-    ws_bytes = int(lib.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv))
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    if workspace is not None:
-        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
-            raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
-    st = fn(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
-        B, T, Hk, Hv, dk, dv, N, qkv, gate, _ptr(o), _ptr(final_state), _ptr(workspace),
-        ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
-        _stream(dev))
+    gates = (_ptr(A_log), _ptr(dt_bias)) if gating else ()
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(y), *gates, _ptr(state), B, T, Hk, Hv, dk, dv,
+            _code(q, "q"), _code(x, xn), _ptr(o), _stream(dev))
     if st != _lib.GDN_SUCCESS:
         raise _lib.GdnError(st, fn.__name__)
-    return o, final_state
+    return o, state
 
 
 def gdn_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -116,28 +171,19 @@ def gdn_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: tor
     """Decode step(s) against a cached state, updated in place.  q,k [B,T,Hk,dk]; v [B,T,Hv,dv];
     g,beta [B,T,Hv]; state [B,Hv,dk,dv] fp32.  Returns (o [B,T,Hv,dv] fp32, state)."""
     lib = _lib.load()
-    if q.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
-    B, T, Hk, dk = q.shape
-    Hv, dv = v.shape[2], v.shape[3]
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("gdn_recurrent_step runs on a GPU; tensors must be on a cuda device")
-    _check(q, (B, T, Hk, dk), "q", dev)
-    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
-    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
-    _check(g, (B, T, Hv), "g", dev)
-    _check(beta, (B, T, Hv), "beta", dev, g.dtype)
-    _check(state, (B, Hv, dk, dv), "state", dev, torch.float32)
-    if o is None:
-        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
-    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
-    st = lib.gdn_recurrent_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, T, Hk, Hv, dk, dv,
-        _code(q, "q"), _code(g, "g"), _ptr(o), _stream(dev))
-    if st != _lib.GDN_SUCCESS:
-        raise _lib.GdnError(st, "gdn_recurrent_step")
-    return o, state
+    return _recurrent_call(lib.gdn_recurrent_step, q, k, v, g, beta, None, None, state, o,
+                           gating=False)
+
+
+def gdn_recurrent_step_gating(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor,
+                              b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
+                              state: torch.Tensor, *,
+                              o: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gdn_recurrent_step with the gates formed in the kernel from a, b [B,T,Hv] and A_log,
+    dt_bias [Hv] fp32."""
+    lib = _lib.load()
+    return _recurrent_call(lib.gdn_recurrent_step_gating, q, k, v, a, b, A_log, dt_bias, state, o,
+                           gating=True)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None):

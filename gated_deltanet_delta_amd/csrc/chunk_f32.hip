@@ -35,7 +35,8 @@ constexpr size_t lds_floats() {
 template <int DK, typename TIn, typename TG>
 __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const TG* __restrict__ g, const TG* __restrict__ beta, const float* initial_state,
+    const TG* __restrict__ g, const TG* __restrict__ beta, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, const float* initial_state,
     const int32_t* __restrict__ cu_seqlens, int T, int Hk, int Hv, int dv,
     float* __restrict__ o, float* final_state) {
     constexpr int LDK = DK + 1, LC = kC + 1, LW = kWS + 1;
@@ -89,8 +90,12 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
             sU[t * LW + c] = t < L ? to_f32(v[((tok0 + t) * Hv + h) * dv + c0 + c]) : 0.f;
         }
         if (tid < kC) {
-            sG[tid] = tid < L ? to_f32(g[(tok0 + tid) * Hv + h]) : 0.f;
-            sB[tid] = tid < L ? to_f32(beta[(tok0 + tid) * Hv + h]) : 0.f;
+            float gt = 0.f, bt = 0.f;
+            if (tid < L)
+                gate_values(to_f32(g[(tok0 + tid) * Hv + h]), to_f32(beta[(tok0 + tid) * Hv + h]), A_log,
+                            dt_bias, h, gt, bt);
+            sG[tid] = gt;
+            sB[tid] = bt;
         }
         __syncthreads();
         if (tid == 0) {
@@ -211,8 +216,9 @@ hipError_t launch_typed(const ChunkArgs& a) {
     const dim3 grid((unsigned)(a.N * a.Hv * (a.dv / kWS))), block(kThreads);
     hipLaunchKernelGGL(kern, grid, block, bytes, a.stream, static_cast<const TIn*>(a.q),
                        static_cast<const TIn*>(a.k), static_cast<const TIn*>(a.v),
-                       static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta),
-                       a.initial_state, a.cu_seqlens, a.T, a.Hk, a.Hv, a.dv, a.o, a.final_state);
+                       static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta), a.A_log,
+                       a.dt_bias, a.initial_state, a.cu_seqlens, a.T, a.Hk, a.Hv, a.dv, a.o,
+                       a.final_state);
     return hipGetLastError();
 }
 

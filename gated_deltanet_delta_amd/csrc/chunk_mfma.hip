@@ -258,6 +258,7 @@ __device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }
 template <typename TG>
 __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     const __bf16* __restrict__ k, const TG* __restrict__ g, const TG* __restrict__ beta,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start, int N, int T,
     int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M,
     __bf16* __restrict__ ws_N) {
@@ -361,8 +362,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
             graw = to_f32(g[grow + qh]);
             braw = to_f32(beta[grow + qh]);
         }
-        const float gt = lane < L ? graw * kLog2e : 0.f;
-        const float bt = lane < L ? braw : 0.f;
+        float gv, bv;
+        gate_values(graw, braw, A_log, dt_bias, h, gv, bv);
+        const float gt = lane < L ? gv * kLog2e : 0.f;
+        const float bt = lane < L ? bv : 0.f;
         float G2 = gt;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -1025,8 +1028,9 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
     if ((stages & kStagePrepare) && slots > 0) {
         hipLaunchKernelGGL((chunk_solve_kernel<TG>), dim3((unsigned)slots, (unsigned)a.Hk),
                            dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.k),
-                           static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta),
-                           a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M, ws_N);
+                           static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta), a.A_log,
+                           a.dt_bias, a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M,
+                           ws_N);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (!(stages & kStageScan)) return hipSuccess;

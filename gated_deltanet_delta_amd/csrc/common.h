@@ -32,6 +32,23 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Gates of one (token, v-head): with `A_log` null, `x` and `y` are g and beta themselves; otherwise
+// they are the raw projections a and b, and beta = sigmoid(b), g = -exp(A_log[h]) softplus(a +
+// dt_bias[h]) (softplus in the form max(z, 0) + log(1 + exp(-|z|)), which neither overflows nor
+// loses the small tail).  g <= 0 then holds by construction.
+__device__ __forceinline__ void gate_values(float x, float y, const float* A_log, const float* dt_bias,
+                                            int h, float& g, float& beta) {
+    if (A_log) {
+        const float z = x + dt_bias[h];
+        const float sp = fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+        g = -expf(A_log[h]) * sp;
+        beta = 1.f / (1.f + expf(-y));
+    } else {
+        g = x;
+        beta = y;
+    }
+}
+
 // Sequence n's token range [t0, t1) inside batch row `row`, clamped to [0, T] so that a malformed
 // cu_seqlens array can only produce wrong numbers, never an access outside the buffers.
 __device__ __forceinline__ void sequence_range(const int32_t* cu_seqlens, int n, int T, int& row,

@@ -58,7 +58,9 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
 namespace {
 
 // Shared body of gdn_chunk_fwd and its two halves: checks, then the selected stages.
+// With A_log set, g and beta carry the raw projections a and b and the kernels form the gates.
 gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                      const float* A_log, const float* dt_bias,
                       const float* initial_state, const int32_t* cu_seqlens, int B, int T, int Hk,
                       int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
                       float* o, float* final_state, void* workspace, size_t workspace_bytes,
@@ -76,11 +78,12 @@ gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g
     for (const void* p : {g, beta})
         if (p && !aligned(p, dtype_bytes(gate_dtype))) return GDN_ERROR_INVALID_VALUE;
     if (cu_seqlens && !aligned(cu_seqlens, 4)) return GDN_ERROR_INVALID_VALUE;
+    if (A_log && (!dt_bias || !aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_ERROR_INVALID_VALUE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
 
-    const gdn::ChunkArgs a{q, k, v, g, beta, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
-                           qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes,
-                           stream};
+    const gdn::ChunkArgs a{q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, B, T, Hk,
+                           Hv, dk, dv, N, qkv_dtype, gate_dtype, o, final_state, workspace,
+                           workspace_bytes, stream};
     hipError_t e;
     if (use_mfma(dk, dv, qkv_dtype)) {
         const size_t need = gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype);
@@ -102,7 +105,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void
                          int B, int T, int Hk, int Hv, int dk, int dv, int N,
                          gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o, float* final_state,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return chunk_call(q, k, v, g, beta, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+    return chunk_call(q, k, v, g, beta, nullptr, nullptr, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
                       qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
                       gdn::kStagePrepare | gdn::kStageScan);
 }
@@ -113,7 +116,7 @@ gdn_status gdn_chunk_fwd_prepare(const void* q, const void* k, const void* v, co
                                  int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
                                  float* final_state, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
-    return chunk_call(q, k, v, g, beta, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+    return chunk_call(q, k, v, g, beta, nullptr, nullptr, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
                       qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
                       gdn::kStagePrepare);
 }
@@ -124,15 +127,19 @@ gdn_status gdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const
                               int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
                               float* final_state, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-    return chunk_call(q, k, v, g, beta, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+    return chunk_call(q, k, v, g, beta, nullptr, nullptr, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
                       qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
                       gdn::kStageScan);
 }
 
-gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const void* g,
-                              const void* beta, float* state, int B, int T, int Hk, int Hv,
-                              int dk, int dv, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
-                              hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status recurrent_call(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const float* A_log, const float* dt_bias, float* state,
+                          int B, int T, int Hk, int Hv, int dk, int dv, gdn_dtype qkv_dtype,
+                          gdn_dtype gate_dtype, float* o, hipStream_t stream) {
     if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERROR_INVALID_VALUE;
     if (B < 1 || T < 1 || Hk < 1 || Hv < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
     if (!dtype_ok(qkv_dtype) || !dtype_ok(gate_dtype)) return GDN_ERROR_INVALID_VALUE;
@@ -145,11 +152,46 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
         if (!aligned(p, dtype_bytes(qkv_dtype))) return GDN_ERROR_INVALID_VALUE;
     for (const void* p : {g, beta})
         if (!aligned(p, dtype_bytes(gate_dtype))) return GDN_ERROR_INVALID_VALUE;
+    if (A_log && (!dt_bias || !aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_ERROR_INVALID_VALUE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
 
-    const gdn::RecurrentArgs a{q, k, v, g, beta, state, B, T, Hk, Hv, dk, dv,
+    const gdn::RecurrentArgs a{q, k, v, g, beta, A_log, dt_bias, state, B, T, Hk, Hv, dk, dv,
                                qkv_dtype, gate_dtype, o, stream};
     return gdn::launch_recurrent(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, float* state, int B, int T, int Hk, int Hv,
+                              int dk, int dv, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
+                              hipStream_t stream) {
+    return recurrent_call(q, k, v, g, beta, nullptr, nullptr, state, B, T, Hk, Hv, dk, dv,
+                          qkv_dtype, gate_dtype, o, stream);
+}
+
+gdn_status gdn_recurrent_step_gating(const void* q, const void* k, const void* v, const void* a,
+                                     const void* b, const float* A_log, const float* dt_bias,
+                                     float* state, int B, int T, int Hk, int Hv, int dk, int dv,
+                                     gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
+                                     hipStream_t stream) {
+    if (!A_log) return GDN_ERROR_INVALID_VALUE;
+    return recurrent_call(q, k, v, a, b, A_log, dt_bias, state, B, T, Hk, Hv, dk, dv, qkv_dtype,
+                          gate_dtype, o, stream);
+}
+
+gdn_status gdn_chunk_fwd_gating(const void* q, const void* k, const void* v, const void* a,
+                                const void* b, const float* A_log, const float* dt_bias,
+                                const float* initial_state, const int32_t* cu_seqlens, int B, int T,
+                                int Hk, int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype,
+                                gdn_dtype gate_dtype, float* o, float* final_state,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!A_log) return GDN_ERROR_INVALID_VALUE;
+    return chunk_call(q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, B, T, Hk, Hv, dk,
+                      dv, N, qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes,
+                      stream, gdn::kStagePrepare | gdn::kStageScan);
 }
 
 }  // extern "C"

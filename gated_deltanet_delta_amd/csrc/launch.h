@@ -11,8 +11,10 @@ struct ChunkArgs {
     const void* q;
     const void* k;
     const void* v;
-    const void* g;
-    const void* beta;
+    const void* g;                 // g, or the raw projection a when A_log is set
+    const void* beta;              // beta, or the raw projection b when A_log is set
+    const float* A_log;            // [Hv] or null: gates formed in the kernels from a, b
+    const float* dt_bias;          // [Hv], with A_log
     const float* initial_state;
     const int32_t* cu_seqlens;
     int B, T, Hk, Hv, dk, dv, N;
@@ -28,8 +30,10 @@ struct RecurrentArgs {
     const void* q;
     const void* k;
     const void* v;
-    const void* g;
+    const void* g;                 // as in ChunkArgs
     const void* beta;
+    const float* A_log;
+    const float* dt_bias;
     float* state;
     int B, T, Hk, Hv, dk, dv;
     gdn_dtype qkv_dtype, gate_dtype;

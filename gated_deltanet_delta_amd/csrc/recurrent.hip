@@ -29,8 +29,9 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 template <int DK, int DV, typename TIn, typename TG>
 __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const TG* __restrict__ g, const TG* __restrict__ beta, float* __restrict__ state,
-    float* __restrict__ o, int T, int Hk, int Hv) {
+    const TG* __restrict__ g, const TG* __restrict__ beta, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, float* __restrict__ state, float* __restrict__ o, int T,
+    int Hk, int Hv) {
     constexpr int CG = DV / 4;               // float4 column groups per row
     constexpr int RG = kRecThreads / CG;     // row groups
     constexpr int RPT = DK / RG;             // rows held per thread
@@ -60,8 +61,8 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
             sk[tid] = to_f32(k[(tok * Hk + kh) * DK + tid]);
         }
         if (tid < DV) sv[tid] = to_f32(v[(tok * Hv + h) * DV + tid]);
-        const float gt = to_f32(g[tok * Hv + h]);
-        const float bt = to_f32(beta[tok * Hv + h]);
+        float gt, bt;
+        gate_values(to_f32(g[tok * Hv + h]), to_f32(beta[tok * Hv + h]), A_log, dt_bias, h, gt, bt);
         __syncthreads();
 
         // Partial column sums over this thread's rows.
@@ -135,7 +136,8 @@ hipError_t launch_typed(const RecurrentArgs& a) {
     hipLaunchKernelGGL((recurrent_kernel<DK, DV, TIn, TG>), grid, block, 0, a.stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), static_cast<const TG*>(a.g),
-                       static_cast<const TG*>(a.beta), a.state, a.o, a.T, a.Hk, a.Hv);
+                       static_cast<const TG*>(a.beta), a.A_log, a.dt_bias, a.state, a.o, a.T, a.Hk,
+                       a.Hv);
     return hipGetLastError();
 }
 

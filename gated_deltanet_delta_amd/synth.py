@@ -146,6 +146,7 @@ def decode_step(wl: Workload, step: int, A_log: np.ndarray) -> Dict[str, torch.T
         v=torch.from_numpy(raw["v"]).to(wl.dtype),
         g=torch.from_numpy(raw["g"]).to(wl.gate_dtype),
         beta=torch.from_numpy(raw["beta"]).to(wl.gate_dtype),
+        raw=raw,
     )
 
 

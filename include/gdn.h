@@ -169,6 +169,40 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
                               gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
                               float* o, hipStream_t stream);
 
+/*
+ * gdn_chunk_fwd_gating, gdn_recurrent_step_gating -- the same two calls with the gates formed inside
+ * the kernels from the layer's raw per-token projections.
+ *
+ * The gate formulas are those of the Qwen3.5 flowchart (wanger-sjtu.github.io, "Core mechanism:
+ * Gated DeltaNet") and of the Qwen3-Next write-up (intelliparadigm.com, section 2.2):
+ *     beta = sigmoid(b),    g = -exp(A_log[h]) * softplus(a + dt_bias[h]),
+ * evaluated in fp32 per (token, v-head) by the kernel that reads the gates, so the caller skips a
+ * pass over [B, T, Hv] and never materialises g and beta.
+ *
+ * Arguments are those of gdn_chunk_fwd / gdn_recurrent_step with g, beta replaced by:
+ *   a, b           [B, T, Hv]  dtype gate_dtype (device), the raw projections
+ *   A_log, dt_bias [Hv]        fp32 (device), per v-head
+ * Checks and status codes are those of the plain calls, plus GDN_ERROR_INVALID_VALUE for a null or
+ * misaligned A_log / dt_bias.  Results equal the plain call's on g, beta computed by these formulas
+ * in fp32.
+ */
+gdn_status gdn_chunk_fwd_gating(const void* q, const void* k, const void* v,
+                                const void* a, const void* b,
+                                const float* A_log, const float* dt_bias,
+                                const float* initial_state, const int32_t* cu_seqlens,
+                                int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                                float* o, float* final_state,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+gdn_status gdn_recurrent_step_gating(const void* q, const void* k, const void* v,
+                                     const void* a, const void* b,
+                                     const float* A_log, const float* dt_bias,
+                                     float* state,
+                                     int B, int T, int Hk, int Hv, int dk, int dv,
+                                     gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                                     float* o, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -88,6 +88,36 @@ def test_recurrent_rejects(lib, kw, status):
     assert rec(lib, **kw) == status
 
 
+def chunk_gating(lib, A_log=P, dt_bias=P, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, s0=None, cu=None, B=1, T=64, Hk=1, Hv=1, dk=64, dv=64, N=1,
+             qkv=F32, gate=F32, o=P, fs=P, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.gdn_chunk_fwd_gating(a["q"], a["k"], a["v"], a["g"], a["beta"], A_log, dt_bias, a["s0"],
+                                    a["cu"], a["B"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["N"],
+                                    a["qkv"], a["gate"], a["o"], a["fs"], a["ws"],
+                                    ctypes.c_size_t(a["ws_bytes"]), None)
+
+
+def rec_gating(lib, A_log=P, dt_bias=P, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, state=P, B=1, T=1, Hk=1, Hv=1, dk=64, dv=64, qkv=F32,
+             gate=F32, o=P)
+    a.update(kw)
+    return lib.gdn_recurrent_step_gating(a["q"], a["k"], a["v"], a["g"], a["beta"], A_log, dt_bias,
+                                         a["state"], a["B"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                                         a["qkv"], a["gate"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A_log=None), INVALID), (dict(dt_bias=None), INVALID),
+    (dict(A_log=P + 2), INVALID), (dict(dt_bias=P + 1), INVALID),
+    (dict(g=None), INVALID), (dict(Hv=3, Hk=2), INVALID), (dict(dk=96), UNSUPPORTED),
+])
+def test_gating_calls_reject(lib, kw, status):
+    # the gating calls check their two extra pointers and everything the plain calls check
+    assert chunk_gating(lib, **kw) == status
+    assert rec_gating(lib, **kw) == status
+
+
 def test_workspace_query_is_host_only(lib):
     # fp32 inputs take the fp32 chunk kernel, which needs no workspace
     assert lib.gdn_chunk_fwd_workspace_size(1, 256, 2, 2, 64, 64, 1, F32) == 0
