@@ -186,6 +186,90 @@ def gdn_recurrent_step_gating(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                            gating=True)
 
 
+def gdn_chunk_fwd_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, state_pool: torch.Tensor, state_indices: torch.Tensor,
+                          cu_seqlens: Optional[torch.Tensor] = None, *,
+                          o: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prefill against a pool of states: sequence n starts from state_pool[state_indices[n]] and its
+    final state is written back there.  state_pool [num_slots,Hv,dk,dv] fp32; state_indices int32
+    [N] (an index outside [0, num_slots) is a padding row: zero start state, no write).  Returns o."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_chunk_fwd_indexed runs on a GPU; tensors must be on a cuda device")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(g, (B, T, Hv), "g", dev)
+    _check(beta, (B, T, Hv), "beta", dev, g.dtype)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [num_slots, Hv, dk, dv]")
+    num_slots = state_pool.shape[0]
+    _check(state_pool, (num_slots, Hv, dk, dv), "state_pool", dev, torch.float32)
+    _check(state_indices, (N,), "state_indices", dev, torch.int32)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
+    qkv, gate = _code(q, "q"), _code(g, "g")
+    ws_bytes = int(lib.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    st = lib.gdn_chunk_fwd_indexed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(state_indices),
+        num_slots, _ptr(cu_seqlens), B, T, Hk, Hv, dk, dv, N, qkv, gate, _ptr(o), _ptr(workspace),
+        ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
+        _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_chunk_fwd_indexed")
+    return o
+
+
+def gdn_recurrent_step_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                               beta: torch.Tensor, state_pool: torch.Tensor,
+                               state_indices: torch.Tensor, *,
+                               o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode step(s) against a pool of states, updated in place: row b uses slot state_indices[b]
+    (outside [0, num_slots): a padding row, left alone, zero outputs).  Returns o."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_recurrent_step_indexed runs on a GPU; tensors must be on a cuda device")
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(g, (B, T, Hv), "g", dev)
+    _check(beta, (B, T, Hv), "beta", dev, g.dtype)
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [num_slots, Hv, dk, dv]")
+    num_slots = state_pool.shape[0]
+    _check(state_pool, (num_slots, Hv, dk, dv), "state_pool", dev, torch.float32)
+    _check(state_indices, (B,), "state_indices", dev, torch.int32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
+    st = lib.gdn_recurrent_step_indexed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(state_indices),
+        num_slots, B, T, Hk, Hv, dk, dv, _code(q, "q"), _code(g, "g"), _ptr(o), _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_recurrent_step_indexed")
+    return o
+
+
 def chunk_gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None):
     """The prefill entry point under its model-side name; see gdn_chunk_fwd."""
     return gdn_chunk_fwd(q, k, v, g, beta, initial_state, cu_seqlens)

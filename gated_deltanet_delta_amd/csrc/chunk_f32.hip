@@ -37,7 +37,8 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TG* __restrict__ g, const TG* __restrict__ beta, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, const float* initial_state,
-    const int32_t* __restrict__ cu_seqlens, int T, int Hk, int Hv, int dv,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ state_indices,
+    int num_slots, int T, int Hk, int Hv, int dv,
     float* __restrict__ o, float* final_state) {
     constexpr int LDK = DK + 1, LC = kC + 1, LW = kWS + 1;
     extern __shared__ float smem[];
@@ -63,10 +64,15 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     const int c0 = sl * kWS;
     const int tid = threadIdx.x;
 
-    const size_t sbase = ((size_t)n * Hv + h) * DK * dv;
+    // the sequence's state: its own, or a pool slot (a padding row starts from zero, writes none)
+    int sslot;
+    const bool has_slot = state_slot(state_indices, num_slots, n, sslot);
+    const float* s_in = has_slot ? initial_state : nullptr;
+    float* s_out = has_slot ? final_state : nullptr;
+    const size_t sbase = ((size_t)sslot * Hv + h) * DK * dv;
     for (int e = tid; e < DK * kWS; e += kThreads) {
         const int i = e / kWS, c = e % kWS;
-        sS[e] = initial_state ? initial_state[sbase + (size_t)i * dv + c0 + c] : 0.f;
+        sS[e] = s_in ? s_in[sbase + (size_t)i * dv + c0 + c] : 0.f;
     }
     __syncthreads();
 
@@ -200,9 +206,11 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
         __syncthreads();
     }
 
-    for (int e = tid; e < DK * kWS; e += kThreads) {
-        const int i = e / kWS, c = e % kWS;
-        final_state[sbase + (size_t)i * dv + c0 + c] = sS[e];
+    if (s_out) {
+        for (int e = tid; e < DK * kWS; e += kThreads) {
+            const int i = e / kWS, c = e % kWS;
+            s_out[sbase + (size_t)i * dv + c0 + c] = sS[e];
+        }
     }
 }
 
@@ -217,7 +225,8 @@ hipError_t launch_typed(const ChunkArgs& a) {
     hipLaunchKernelGGL(kern, grid, block, bytes, a.stream, static_cast<const TIn*>(a.q),
                        static_cast<const TIn*>(a.k), static_cast<const TIn*>(a.v),
                        static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta), a.A_log,
-                       a.dt_bias, a.initial_state, a.cu_seqlens, a.T, a.Hk, a.Hv, a.dv, a.o,
+                       a.dt_bias, a.initial_state, a.cu_seqlens, a.state_indices, a.num_slots, a.T,
+                       a.Hk, a.Hv, a.dv, a.o,
                        a.final_state);
     return hipGetLastError();
 }

@@ -571,6 +571,7 @@ template <int DV>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ state_indices, int num_slots,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ order, int N, int T,
     int Hk, int Hv, int nct, int max_slots, const float* __restrict__ ws_G,
     const __bf16* __restrict__ ws_M, const __bf16* __restrict__ ws_N, float* __restrict__ o,
@@ -597,7 +598,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const int slot0 = cu_seqlens ? chunk_start[n] : n * nct;
     // (a malformed cu_seqlens can claim more chunks than the workspace holds: stop at its end)
     const int nchunks = min((t1 - t0 + kC - 1) / kC, max(0, max_slots - slot0));
-    const size_t sbase = ((size_t)n * Hv + h) * kDK * DV;
+    // the sequence's state: its own, or a pool slot (a padding row starts from zero, writes none)
+    int sslot;
+    const bool has_slot = state_slot(state_indices, num_slots, n, sslot);
+    const float* s_in = has_slot ? initial_state : nullptr;
+    float* s_out = has_slot ? final_state : nullptr;
+    const size_t sbase = ((size_t)sslot * Hv + h) * kDK * DV;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -701,11 +707,13 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 return sbase + (size_t)rho(4 * hh + t, 4 * g + r) * DV + c0 + c;
             };
             if (nchunks == 0) {  // zero-length sequence: the state passes through
+                if (s_out) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                    for (int t = 0; t < 4; ++t)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        final_state[state_idx(t, r)] = initial_state ? initial_state[state_idx(t, r)] : 0.f;
+                        for (int r = 0; r < 4; ++r)
+                            s_out[state_idx(t, r)] = s_in ? s_in[state_idx(t, r)] : 0.f;
+                }
                 return;
             }
             __builtin_amdgcn_s_setprio(2);
@@ -713,7 +721,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[t][r] = initial_state ? initial_state[state_idx(t, r)] : 0.f;
+                for (int r = 0; r < 4; ++r) S[t][r] = s_in ? s_in[state_idx(t, r)] : 0.f;
             // lane parts of the LDS addresses (the rest are compile-time offsets)
             const int l_kf = c * kKR + 8 * (g ^ kswz(c));                 // K row c, logical chunk g
             const int l_kt = (4 * g + (c >> 2)) * kKR + 8 * ((c & 3) ^ g);
@@ -807,10 +815,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 }
                 lds_barrier();
             }
+            if (s_out) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) final_state[state_idx(t, r)] = S[t][r];
+                    for (int r = 0; r < 4; ++r) s_out[state_idx(t, r)] = S[t][r];
+            }
         };
         if (wave == 1) state_role(std::integral_constant<int, 0>{});
         else state_role(std::integral_constant<int, 1>{});
@@ -1044,7 +1054,8 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
     const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * members);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kScanThreads), bytes,
                        a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), a.initial_state, a.cu_seqlens, chunk_start,
+                       static_cast<const __bf16*>(a.v), a.initial_state, a.cu_seqlens,
+                       a.state_indices, a.num_slots, chunk_start,
                        order, a.N, a.T, a.Hk, a.Hv, nct, packed ? lay.slots : a.B * nct, ws_G, ws_M,
                        ws_N, a.o, a.final_state);
     return hipGetLastError();

@@ -49,6 +49,20 @@ __device__ __forceinline__ void gate_values(float x, float y, const float* A_log
     }
 }
 
+// State slot of sequence (or batch row) n: n itself, or state_indices[n] in a pool of num_slots
+// states.  An index outside [0, num_slots) marks a padding row, which has no state: false is
+// returned and slot is set to 0 (any in-bounds value; nothing is read or written through it).
+__device__ __forceinline__ bool state_slot(const int32_t* state_indices, int num_slots, int n, int& slot) {
+    if (!state_indices) {
+        slot = n;
+        return true;
+    }
+    const int s = state_indices[n];
+    const bool ok = s >= 0 && s < num_slots;
+    slot = ok ? s : 0;
+    return ok;
+}
+
 // Sequence n's token range [t0, t1) inside batch row `row`, clamped to [0, T] so that a malformed
 // cu_seqlens array can only produce wrong numbers, never an access outside the buffers.
 __device__ __forceinline__ void sequence_range(const int32_t* cu_seqlens, int n, int T, int& row,

@@ -59,9 +59,10 @@ namespace {
 
 // Shared body of gdn_chunk_fwd and its two halves: checks, then the selected stages.
 // With A_log set, g and beta carry the raw projections a and b and the kernels form the gates.
+// With state_indices set, initial_state and final_state are the same pool of num_slots states.
 gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                      const float* A_log, const float* dt_bias,
-                      const float* initial_state, const int32_t* cu_seqlens, int B, int T, int Hk,
+                      const float* A_log, const float* dt_bias, const int32_t* state_indices,
+                      int num_slots, const float* initial_state, const int32_t* cu_seqlens, int B, int T, int Hk,
                       int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
                       float* o, float* final_state, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, unsigned stages) {
@@ -79,11 +80,14 @@ gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g
         if (p && !aligned(p, dtype_bytes(gate_dtype))) return GDN_ERROR_INVALID_VALUE;
     if (cu_seqlens && !aligned(cu_seqlens, 4)) return GDN_ERROR_INVALID_VALUE;
     if (A_log && (!dt_bias || !aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_ERROR_INVALID_VALUE;
+    if (state_indices && (num_slots < 1 || !aligned(state_indices, 4) ||
+                          !sizes_fit(num_slots, 1, Hv, (long long)dk * dv)))
+        return GDN_ERROR_INVALID_VALUE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
 
-    const gdn::ChunkArgs a{q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, B, T, Hk,
-                           Hv, dk, dv, N, qkv_dtype, gate_dtype, o, final_state, workspace,
-                           workspace_bytes, stream};
+    const gdn::ChunkArgs a{q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens,
+                           state_indices, num_slots, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, o,
+                           final_state, workspace, workspace_bytes, stream};
     hipError_t e;
     if (use_mfma(dk, dv, qkv_dtype)) {
         const size_t need = gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype);
@@ -105,7 +109,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void
                          int B, int T, int Hk, int Hv, int dk, int dv, int N,
                          gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o, float* final_state,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return chunk_call(q, k, v, g, beta, nullptr, nullptr, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+    return chunk_call(q, k, v, g, beta, nullptr, nullptr, nullptr, 0, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
                       qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
                       gdn::kStagePrepare | gdn::kStageScan);
 }
@@ -116,7 +120,7 @@ gdn_status gdn_chunk_fwd_prepare(const void* q, const void* k, const void* v, co
                                  int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
                                  float* final_state, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
-    return chunk_call(q, k, v, g, beta, nullptr, nullptr, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+    return chunk_call(q, k, v, g, beta, nullptr, nullptr, nullptr, 0, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
                       qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
                       gdn::kStagePrepare);
 }
@@ -127,7 +131,7 @@ gdn_status gdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const
                               int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
                               float* final_state, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-    return chunk_call(q, k, v, g, beta, nullptr, nullptr, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
+    return chunk_call(q, k, v, g, beta, nullptr, nullptr, nullptr, 0, initial_state, cu_seqlens, B, T, Hk, Hv, dk, dv, N,
                       qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes, stream,
                       gdn::kStageScan);
 }
@@ -136,15 +140,20 @@ gdn_status gdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const
 
 namespace {
 
+// With state_indices set, state is a pool of num_slots states and row b uses slot state_indices[b].
 gdn_status recurrent_call(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, const float* A_log, const float* dt_bias, float* state,
-                          int B, int T, int Hk, int Hv, int dk, int dv, gdn_dtype qkv_dtype,
-                          gdn_dtype gate_dtype, float* o, hipStream_t stream) {
+                          const int32_t* state_indices, int num_slots, int B, int T, int Hk, int Hv,
+                          int dk, int dv, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
+                          hipStream_t stream) {
     if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERROR_INVALID_VALUE;
     if (B < 1 || T < 1 || Hk < 1 || Hv < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
     if (!dtype_ok(qkv_dtype) || !dtype_ok(gate_dtype)) return GDN_ERROR_INVALID_VALUE;
     if (dk < 1 || dv < 1) return GDN_ERROR_INVALID_VALUE;
     if (!sizes_fit(B, T, Hv, dv > dk ? dv : dk) || !sizes_fit(B, 1, Hv, (long long)dk * dv))
+        return GDN_ERROR_INVALID_VALUE;
+    if (state_indices && (num_slots < 1 || !aligned(state_indices, 4) ||
+                          !sizes_fit(num_slots, 1, Hv, (long long)dk * dv)))
         return GDN_ERROR_INVALID_VALUE;
     for (const void* p : {(const void*)state, (const void*)o})
         if (!aligned16(p)) return GDN_ERROR_INVALID_VALUE;
@@ -155,8 +164,8 @@ gdn_status recurrent_call(const void* q, const void* k, const void* v, const voi
     if (A_log && (!dt_bias || !aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_ERROR_INVALID_VALUE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
 
-    const gdn::RecurrentArgs a{q, k, v, g, beta, A_log, dt_bias, state, B, T, Hk, Hv, dk, dv,
-                               qkv_dtype, gate_dtype, o, stream};
+    const gdn::RecurrentArgs a{q, k, v, g, beta, A_log, dt_bias, state, state_indices, num_slots,
+                               B, T, Hk, Hv, dk, dv, qkv_dtype, gate_dtype, o, stream};
     return gdn::launch_recurrent(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
 }
 
@@ -168,8 +177,30 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
                               const void* beta, float* state, int B, int T, int Hk, int Hv,
                               int dk, int dv, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
                               hipStream_t stream) {
-    return recurrent_call(q, k, v, g, beta, nullptr, nullptr, state, B, T, Hk, Hv, dk, dv,
-                          qkv_dtype, gate_dtype, o, stream);
+    return recurrent_call(q, k, v, g, beta, nullptr, nullptr, state, nullptr, 0, B, T, Hk, Hv, dk,
+                          dv, qkv_dtype, gate_dtype, o, stream);
+}
+
+gdn_status gdn_recurrent_step_indexed(const void* q, const void* k, const void* v, const void* g,
+                                      const void* beta, float* state_pool,
+                                      const int32_t* state_indices, int num_slots, int B, int T,
+                                      int Hk, int Hv, int dk, int dv, gdn_dtype qkv_dtype,
+                                      gdn_dtype gate_dtype, float* o, hipStream_t stream) {
+    if (!state_indices) return GDN_ERROR_INVALID_VALUE;
+    return recurrent_call(q, k, v, g, beta, nullptr, nullptr, state_pool, state_indices, num_slots,
+                          B, T, Hk, Hv, dk, dv, qkv_dtype, gate_dtype, o, stream);
+}
+
+gdn_status gdn_chunk_fwd_indexed(const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, float* state_pool, const int32_t* state_indices,
+                                 int num_slots, const int32_t* cu_seqlens, int B, int T, int Hk,
+                                 int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype,
+                                 gdn_dtype gate_dtype, float* o, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    if (!state_indices) return GDN_ERROR_INVALID_VALUE;
+    return chunk_call(q, k, v, g, beta, nullptr, nullptr, state_indices, num_slots, state_pool,
+                      cu_seqlens, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, o, state_pool,
+                      workspace, workspace_bytes, stream, gdn::kStagePrepare | gdn::kStageScan);
 }
 
 gdn_status gdn_recurrent_step_gating(const void* q, const void* k, const void* v, const void* a,
@@ -178,8 +209,8 @@ gdn_status gdn_recurrent_step_gating(const void* q, const void* k, const void* v
                                      gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
                                      hipStream_t stream) {
     if (!A_log) return GDN_ERROR_INVALID_VALUE;
-    return recurrent_call(q, k, v, a, b, A_log, dt_bias, state, B, T, Hk, Hv, dk, dv, qkv_dtype,
-                          gate_dtype, o, stream);
+    return recurrent_call(q, k, v, a, b, A_log, dt_bias, state, nullptr, 0, B, T, Hk, Hv, dk, dv,
+                          qkv_dtype, gate_dtype, o, stream);
 }
 
 gdn_status gdn_chunk_fwd_gating(const void* q, const void* k, const void* v, const void* a,
@@ -189,7 +220,7 @@ gdn_status gdn_chunk_fwd_gating(const void* q, const void* k, const void* v, con
                                 gdn_dtype gate_dtype, float* o, float* final_state,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!A_log) return GDN_ERROR_INVALID_VALUE;
-    return chunk_call(q, k, v, a, b, A_log, dt_bias, initial_state, cu_seqlens, B, T, Hk, Hv, dk,
+    return chunk_call(q, k, v, a, b, A_log, dt_bias, nullptr, 0, initial_state, cu_seqlens, B, T, Hk, Hv, dk,
                       dv, N, qkv_dtype, gate_dtype, o, final_state, workspace, workspace_bytes,
                       stream, gdn::kStagePrepare | gdn::kStageScan);
 }

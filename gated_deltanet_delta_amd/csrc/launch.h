@@ -17,6 +17,8 @@ struct ChunkArgs {
     const float* dt_bias;          // [Hv], with A_log
     const float* initial_state;
     const int32_t* cu_seqlens;
+    const int32_t* state_indices;  // [N] or null: states live in a pool, sequence n in slot [n]
+    int num_slots;                 // pool size with state_indices
     int B, T, Hk, Hv, dk, dv, N;
     gdn_dtype qkv_dtype, gate_dtype;
     float* o;
@@ -35,6 +37,8 @@ struct RecurrentArgs {
     const float* A_log;
     const float* dt_bias;
     float* state;
+    const int32_t* state_indices;  // [B] or null: as in ChunkArgs
+    int num_slots;
     int B, T, Hk, Hv, dk, dv;
     gdn_dtype qkv_dtype, gate_dtype;
     float* o;

@@ -30,8 +30,9 @@ template <int DK, int DV, typename TIn, typename TG>
 __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TG* __restrict__ g, const TG* __restrict__ beta, const float* __restrict__ A_log,
-    const float* __restrict__ dt_bias, float* __restrict__ state, float* __restrict__ o, int T,
-    int Hk, int Hv) {
+    const float* __restrict__ dt_bias, float* __restrict__ state,
+    const int32_t* __restrict__ state_indices, int num_slots, float* __restrict__ o, int T, int Hk,
+    int Hv) {
     constexpr int CG = DV / 4;               // float4 column groups per row
     constexpr int RG = kRecThreads / CG;     // row groups
     constexpr int RPT = DK / RG;             // rows held per thread
@@ -45,11 +46,18 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     const int bh = blockIdx.x;  // b * Hv + h
     const int b = bh / Hv, h = bh % Hv;
     const int kh = h / (Hv / Hk);
+    int slot;  // the row's state: its own, or a pool slot
+    if (!state_slot(state_indices, num_slots, b, slot)) {
+        // a padding row: no state to advance; its outputs are zero
+        for (int t = 0; t < T; ++t)
+            for (int e = tid; e < DV; e += kRecThreads) o[(((size_t)b * T + t) * Hv + h) * DV + e] = 0.f;
+        return;
+    }
 
     __shared__ float sq[DK], sk[DK], sv[DV];
     __shared__ float red[NW][2 * DV + 1];
 
-    f32x4v* S4 = reinterpret_cast<f32x4v*>(state + (size_t)bh * DK * DV);
+    f32x4v* S4 = reinterpret_cast<f32x4v*>(state + ((size_t)slot * Hv + h) * DK * DV);
     f32x4v s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(S4 + (size_t)(rg + RG * m) * CG + cg);
@@ -136,8 +144,8 @@ hipError_t launch_typed(const RecurrentArgs& a) {
     hipLaunchKernelGGL((recurrent_kernel<DK, DV, TIn, TG>), grid, block, 0, a.stream,
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), static_cast<const TG*>(a.g),
-                       static_cast<const TG*>(a.beta), a.A_log, a.dt_bias, a.state, a.o, a.T, a.Hk,
-                       a.Hv);
+                       static_cast<const TG*>(a.beta), a.A_log, a.dt_bias, a.state, a.state_indices,
+                       a.num_slots, a.o, a.T, a.Hk, a.Hv);
     return hipGetLastError();
 }
 

@@ -203,6 +203,43 @@ gdn_status gdn_recurrent_step_gating(const void* q, const void* k, const void* v
                                      gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
                                      float* o, hipStream_t stream);
 
+/*
+ * gdn_chunk_fwd_indexed, gdn_recurrent_step_indexed -- the two calls against a pool of cached
+ * states, for continuous batching.
+ *
+ * The pages' decode loop (jsqmd.com, section 2.2) carries each request's state from one call to the
+ * next, and the Qwen3.5 write-up ("Cache and state switching") keeps those states in a cache that the
+ * serving side switches between requests.  Here the cache is one pool and each sequence (prefill)
+ * or batch row (decode) names its slot:
+ *   state_pool     [num_slots, Hv, dk, dv] fp32 (device), read and written in place
+ *   state_indices  [N] int32 (device; N = number of sequences, B for decode): slot of each one
+ * Sequence n starts from state_pool[state_indices[n]] and its final state is written back to the
+ * same slot.  An index outside [0, num_slots) marks a padding row: prefill runs it from a zero state
+ * and writes no state; decode leaves every state alone and writes zeros to the row's outputs.  The
+ * valid indices of one call must be distinct (two rows on one slot race).  Slots not named are not
+ * touched.  A prefill of a new request expects a zeroed slot.
+ *
+ * Other arguments, checks and status codes are those of gdn_chunk_fwd / gdn_recurrent_step
+ * (gdn_chunk_fwd_indexed has no initial_state / final_state: the pool is both); in addition
+ * num_slots >= 1 and a null or misaligned state_indices give GDN_ERROR_INVALID_VALUE.  The indices
+ * themselves are read on the device only.
+ */
+gdn_status gdn_chunk_fwd_indexed(const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 float* state_pool, const int32_t* state_indices, int num_slots,
+                                 const int32_t* cu_seqlens,
+                                 int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                 gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                                 float* o,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+gdn_status gdn_recurrent_step_indexed(const void* q, const void* k, const void* v,
+                                      const void* g, const void* beta,
+                                      float* state_pool, const int32_t* state_indices, int num_slots,
+                                      int B, int T, int Hk, int Hv, int dk, int dv,
+                                      gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                                      float* o, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -150,3 +150,32 @@ def test_binding_refuses_cpu_tensors():
         gdn_chunk_fwd(x, x, x, gg, gg)
     with pytest.raises(ValueError):
         gdn_recurrent_step(x, x, x, gg, gg, torch.zeros(1, 1, 64, 64))
+
+
+def chunk_indexed(lib, pool=P, idx=P, num_slots=4, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=None, B=1, T=64, Hk=1, Hv=1, dk=64, dv=64, N=1, qkv=F32,
+             gate=F32, o=P, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.gdn_chunk_fwd_indexed(a["q"], a["k"], a["v"], a["g"], a["beta"], pool, idx, num_slots,
+                                     a["cu"], a["B"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["N"],
+                                     a["qkv"], a["gate"], a["o"], a["ws"], ctypes.c_size_t(a["ws_bytes"]),
+                                     None)
+
+
+def rec_indexed(lib, pool=P, idx=P, num_slots=4, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, B=1, T=1, Hk=1, Hv=1, dk=64, dv=64, qkv=F32, gate=F32, o=P)
+    a.update(kw)
+    return lib.gdn_recurrent_step_indexed(a["q"], a["k"], a["v"], a["g"], a["beta"], pool, idx, num_slots,
+                                          a["B"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["qkv"],
+                                          a["gate"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(idx=None), INVALID), (dict(pool=None), INVALID), (dict(num_slots=0), INVALID),
+    (dict(idx=P + 2), INVALID), (dict(pool=P + 4), INVALID), (dict(q=None), INVALID),
+    (dict(Hv=3, Hk=2), INVALID), (dict(dv=32), UNSUPPORTED),
+])
+def test_indexed_calls_reject(lib, kw, status):
+    # the pool calls check the pool, the indices and everything the plain calls check
+    assert chunk_indexed(lib, **kw) == status
+    assert rec_indexed(lib, **kw) == status
