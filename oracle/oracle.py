@@ -14,6 +14,9 @@ Contents
              "Softplus + dt_bias", "Exp and Neg", "Mul -> g") and of the Qwen3-Next architecture
              write-up (intelliparadigm.com, section 2.2 "linear attention module", step 2 "gate
              generation"), in fp64.
+``gated_rmsnorm``  the output norm of the layer (the Qwen3.5 page's "Output and gated RMSNorm"
+             section): each head vector of the core output is RMS-normalised, scaled by a learned
+             per-channel weight and gated by the z branch through SiLU, in fp64 numpy.
 ``chunked``  the chunk-parallel (WY/UT) form of the same rule in fp64 numpy.  It is not the
              definition: it exists to show, against ``forward``, that the block algebra a chunked
              kernel uses reaches the token-by-token result exactly (up to rounding order).
@@ -146,6 +149,25 @@ def gates(a: np.ndarray, b: np.ndarray, A_log: np.ndarray, dt_bias: np.ndarray) 
     g = -np.exp(np.asarray(A_log, dtype=np.float64)) * softplus
     beta = 1.0 / (1.0 + np.exp(-b))
     return g, beta
+
+
+def gated_rmsnorm(x: np.ndarray, z: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """y = x / sqrt(mean(x^2) + eps) * weight * silu(z) over the last axis (one head vector), fp64.
+
+    Qwen3.5 Gated DeltaNet page (wanger-sjtu.github.io), section "Output and gated RMSNorm" and the
+    flowchart nodes "AttnOut -> Norm (Qwen3_5MoeRMSNormGated or FusedRMSNormGated)", "Z -> Norm":
+    the core output is normalised and then gated by z in the manner of SwiGLU, i.e. multiplied by
+    silu(z) = z * sigmoid(z).  The normalisation is RMSNorm over the head dimension with a learned
+    per-channel weight; the Qwen3-Next article's section 3.2 shows the same rsqrt(mean(x^2) + eps)
+    normalisation for the model's other norms.  (Reading taken: the weight multiplies directly; the
+    "1 + weight" zero-centred form of that section belongs to the non-gated norms.)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    inv_rms = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    silu = z / (1.0 + np.exp(-z))
+    return x * inv_rms * w * silu
 
 
 def chunked(

@@ -292,6 +292,42 @@ def test_synth_gates_follow_oracle_gates():
 
 
 # ----------------------------------------------------------------------------------------------
+# gated RMSNorm
+
+def test_gated_rmsnorm_hand_worked():
+    """d = 2 by hand: x = (3, 4) has mean square 12.5, so x / rms = (3, 4) / sqrt(12.5) =
+    (0.848528..., 1.131370...); weight (2, 0.5); z = (0, 2): silu(0) = 0, silu(2) = 2 / (1 + e^-2)
+    = 1.761594...; so y = (0, 1.131371 * 0.5 * 1.761594) = (0, 0.996508...)."""
+    y = O.gated_rmsnorm(np.array([3.0, 4.0]), np.array([0.0, 2.0]), np.array([2.0, 0.5]), 0.0)
+    assert y[0] == 0.0
+    assert np.isclose(y[1], 4.0 / np.sqrt(12.5) * 0.5 * 2.0 / (1.0 + np.exp(-2.0)), rtol=1e-15)
+    assert np.isclose(y[1], 0.9965081, rtol=1e-6)
+
+
+def test_gated_rmsnorm_closed_forms():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 7, 64))
+    w = rng.uniform(0.5, 1.5, 64)
+    big = np.full_like(x, 40.0)                 # silu(z) = z (to 1e-17) for z = 40
+    y = O.gated_rmsnorm(x, big, np.ones(64), 0.0)
+    # with weight 1 and a constant gate, the rows have rms exactly 40
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 40.0, rtol=1e-12)
+    # scale invariance (eps = 0), sign equivariance
+    assert np.allclose(O.gated_rmsnorm(3.7 * x, big, w, 0.0), O.gated_rmsnorm(x, big, w, 0.0), rtol=1e-12)
+    assert np.allclose(O.gated_rmsnorm(-x, big, w, 0.0), -O.gated_rmsnorm(x, big, w, 0.0), rtol=1e-12)
+    # a zero gate closes the output, a very negative gate nearly does
+    assert np.all(O.gated_rmsnorm(x, np.zeros_like(x), w, 1e-6) == 0.0)
+    assert np.max(np.abs(O.gated_rmsnorm(x, np.full_like(x, -40.0), w, 1e-6))) < 1e-14
+    # the gate and the weight act per channel and commute
+    z = rng.standard_normal(x.shape)
+    assert np.allclose(O.gated_rmsnorm(x, z, w, 1e-6), O.gated_rmsnorm(x, z, np.ones(64), 1e-6) * w)
+    # eps only matters against the mean square: a zero row stays zero, a tiny row is damped
+    assert np.all(O.gated_rmsnorm(np.zeros(8), np.ones(8), np.ones(8), 1e-6) == 0.0)
+    small = O.gated_rmsnorm(np.full(8, 1e-6), np.full(8, 40.0), np.ones(8), 1e-6)
+    assert np.allclose(small, 40.0 * 1e-6 / np.sqrt(1e-12 + 1e-6), rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
 # sampling and threading do not change results
 
 def test_unit_mask_and_threads(orc):
