@@ -83,8 +83,9 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from gated_deltanet_delta_amd import (gdn_chunk_fwd, gdn_chunk_fwd_gating, gdn_recurrent_step,
-                                          gdn_recurrent_step_gating, synth, workspace_size)
+    from gated_deltanet_delta_amd import (gdn_chunk_fwd, gdn_chunk_fwd_gating, gdn_gated_rmsnorm,
+                                          gdn_recurrent_step, gdn_recurrent_step_gating, synth,
+                                          workspace_size)
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -176,6 +177,23 @@ def main() -> int:
     achieved_gbs = scan_bytes / (ms_scan / 1e3) / 1e9
     useful_tflops = flops / (ms_events / 1e3) / 1e12
 
+    # ---------------- the gated output norm on the prefill's o ---------------------------------
+    # (z drawn here with its own seed: the workloads do not define the z branch)
+    zr = torch.from_numpy(np.random.default_rng(99).standard_normal(tuple(o.shape), dtype=np.float32))
+    zn = zr.to(torch.bfloat16).to(dev)
+    wn = torch.ones(wl.dv, dtype=torch.float32, device=dev)
+    yn = torch.empty(tuple(o.shape), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        gdn_gated_rmsnorm(o, zn, wn, 1e-6, out=yn)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        gdn_gated_rmsnorm(o, zn, wn, 1e-6, out=yn)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_norm = e0.elapsed_time(e1) / args.steps
+    norm_bytes = o.numel() * (4 + 2 + 2) + wl.dv * 4
+
     # ---------------- decode ------------------------------------------------------------------
     wd = synth.WORKLOADS["decode"]
     x0 = synth.make(wd)
@@ -264,6 +282,13 @@ def main() -> int:
         "prefill_gating": {"call": "gdn_chunk_fwd_gating (gates formed in the kernels from a, b)",
                            "ms_per_call_events": round(ms_gating, 5),
                            "tokens_per_s": round(tokens / (ms_gating / 1e3), 1)},
+        "gated_rmsnorm": {"call": "gdn_gated_rmsnorm on the prefill's o (fp32 in, bf16 z and out)",
+                          "rows": o.numel() // wl.dv, "d": wl.dv,
+                          "ms_per_call_events": round(ms_norm, 5),
+                          "roofline": {"bound": "hbm", "achieved": round(norm_bytes / (ms_norm / 1e3) / 1e9, 1),
+                                       "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                                       "frac": round(norm_bytes / (ms_norm / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
+                                       "algorithmic_bytes_per_launch": int(norm_bytes)}},
         "cpu_baseline": cpu,
         "decode": {"metric": "decode state GB/s", "value": round(state_gbs, 1), "unit": "GB/s",
                    "workload": f"decode B={wd.B} Hk={wd.Hk} Hv={wd.Hv} dk=dv={wd.dk}, {nd} one-token "

@@ -270,6 +270,33 @@ def gdn_recurrent_step_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     return o
 
 
+def gdn_gated_rmsnorm(x: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
+                      out_dtype: torch.dtype = torch.bfloat16,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer's gated output norm over the last axis: x fp32 [..., d] (e.g. o of
+    gdn_chunk_fwd), z [..., d] bf16 or fp32, weight [d] fp32.
+    Returns x / sqrt(mean(x^2) + eps) * weight * silu(z) in ``out_dtype``."""
+    lib = _lib.load()
+    if x.dim() < 1:
+        raise ValueError("x must have a channel axis")
+    d = x.shape[-1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_gated_rmsnorm runs on a GPU; tensors must be on a cuda device")
+    _check(x, tuple(x.shape), "x", dev, torch.float32)
+    _check(z, tuple(x.shape), "z", dev)
+    _check(weight, (d,), "weight", dev, torch.float32)
+    if out is None:
+        out = torch.empty(tuple(x.shape), dtype=out_dtype, device=dev)
+    _check(out, tuple(x.shape), "out", dev)
+    rows = x.numel() // d if d else 0
+    st = lib.gdn_gated_rmsnorm(_ptr(x), _ptr(z), _ptr(weight), float(eps), rows, d, _code(z, "z"),
+                               _code(out, "out"), _ptr(out), _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_gated_rmsnorm")
+    return out
+
+
 def chunk_gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None):
     """The prefill entry point under its model-side name; see gdn_chunk_fwd."""
     return gdn_chunk_fwd(q, k, v, g, beta, initial_state, cu_seqlens)

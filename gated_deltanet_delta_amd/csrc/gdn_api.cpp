@@ -225,4 +225,19 @@ gdn_status gdn_chunk_fwd_gating(const void* q, const void* k, const void* v, con
                       stream, gdn::kStagePrepare | gdn::kStageScan);
 }
 
+gdn_status gdn_gated_rmsnorm(const float* x, const void* z, const float* weight, float eps,
+                             int64_t rows, int d, gdn_dtype z_dtype, gdn_dtype out_dtype, void* out,
+                             hipStream_t stream) {
+    if (rows < 0 || !dtype_ok(z_dtype) || !dtype_ok(out_dtype)) return GDN_ERROR_INVALID_VALUE;
+    if (!(eps >= 0.f) || eps > 3.0e38f) return GDN_ERROR_INVALID_VALUE;   // also rejects NaN
+    if (rows > 0 && (!x || !z || !weight || !out)) return GDN_ERROR_INVALID_VALUE;
+    if (d < 1 || !sizes_fit(rows, 1, 1, d)) return GDN_ERROR_INVALID_VALUE;
+    if (!aligned16(x) || !aligned16(weight) || !aligned(z, 4 * dtype_bytes(z_dtype)) ||
+        !aligned(out, 4 * dtype_bytes(out_dtype)))
+        return GDN_ERROR_INVALID_VALUE;
+    if (!head_dim_ok(d)) return GDN_ERROR_NOT_SUPPORTED;
+    const gdn::NormArgs a{x, z, weight, eps, (long long)rows, d, z_dtype, out_dtype, out, stream};
+    return gdn::launch_gated_rmsnorm(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+}
+
 }  // extern "C"

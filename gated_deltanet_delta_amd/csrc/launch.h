@@ -45,6 +45,21 @@ struct RecurrentArgs {
     hipStream_t stream;
 };
 
+struct NormArgs {
+    const float* x;                // [rows, d] fp32
+    const void* z;                 // [rows, d] z_dtype
+    const float* weight;           // [d] fp32
+    float eps;
+    long long rows;
+    int d;
+    gdn_dtype z_dtype, out_dtype;
+    void* out;                     // [rows, d] out_dtype
+    hipStream_t stream;
+};
+
+// The gated output norm (one row per head vector).
+hipError_t launch_gated_rmsnorm(const NormArgs& a);
+
 // Token-serial kernel: the state stays in registers for all T tokens of a call.
 hipError_t launch_recurrent(const RecurrentArgs& a);
 

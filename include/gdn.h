@@ -240,6 +240,28 @@ gdn_status gdn_recurrent_step_indexed(const void* q, const void* k, const void* 
                                       gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
                                       float* o, hipStream_t stream);
 
+/*
+ * gdn_gated_rmsnorm -- the layer's gated output norm, applied to the gated delta rule's output.
+ *
+ * The Qwen3.5 Gated DeltaNet page (wanger-sjtu.github.io, section "Output and gated RMSNorm", and
+ * its flowchart nodes "AttnOut -> Norm", "Z -> Norm") sends the core output and the z branch into
+ * one norm that normalises and then gates in the manner of SwiGLU.  Per row (one head vector of
+ * d channels):
+ *     y = x / sqrt(mean(x^2) + eps) * weight * silu(z),     silu(z) = z / (1 + exp(-z)),
+ * in fp32 (the RMS normalisation as the Qwen3-Next article's section 3.2 writes it).
+ *
+ *   x       [rows, d] fp32 (device): e.g. o of gdn_chunk_fwd viewed as [B*T*Hv, dv]
+ *   z       [rows, d] z_dtype (device)
+ *   weight  [d] fp32 (device), per channel
+ *   out     [rows, d] out_dtype (device); must not overlap x or z
+ * Sizes: rows >= 0 (0: nothing is enqueued), d 64 or 128 (others: GDN_ERROR_NOT_SUPPORTED),
+ * eps >= 0 and finite.  x and weight 16-byte aligned, z and out aligned to 4 elements.
+ * Errors: GDN_ERROR_INVALID_VALUE for null pointers (rows > 0), bad sizes, dtypes or alignment.
+ */
+gdn_status gdn_gated_rmsnorm(const float* x, const void* z, const float* weight, float eps,
+                             int64_t rows, int d, gdn_dtype z_dtype, gdn_dtype out_dtype,
+                             void* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

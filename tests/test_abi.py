@@ -179,3 +179,23 @@ def test_indexed_calls_reject(lib, kw, status):
     # the pool calls check the pool, the indices and everything the plain calls check
     assert chunk_indexed(lib, **kw) == status
     assert rec_indexed(lib, **kw) == status
+
+
+def norm(lib, x=P, z=P, w=P, eps=1e-6, rows=8, d=128, zt=BF16, ot=BF16, out=P):
+    return lib.gdn_gated_rmsnorm(x, z, w, eps, rows, d, zt, ot, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(z=None), INVALID), (dict(w=None), INVALID), (dict(out=None), INVALID),
+    (dict(rows=-1), INVALID), (dict(d=0), INVALID), (dict(zt=5), INVALID), (dict(ot=-1), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(x=P + 8), INVALID), (dict(w=P + 4), INVALID), (dict(z=P + 4), INVALID),
+    (dict(out=P + 2, ot=F32), INVALID), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+])
+def test_gated_rmsnorm_rejects(lib, kw, status):
+    assert norm(lib, **kw) == status
+
+
+def test_gated_rmsnorm_zero_rows_is_a_no_op(lib):
+    # nothing to do: accepted without touching (or even needing) any buffer
+    assert norm(lib, x=None, z=None, w=None, out=None, rows=0) == _lib.GDN_SUCCESS
