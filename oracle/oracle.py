@@ -17,6 +17,9 @@ Contents
 ``gated_rmsnorm``  the output norm of the layer (the Qwen3.5 page's "Output and gated RMSNorm"
              section): each head vector of the core output is RMS-normalised, scaled by a learned
              per-channel weight and gated by the z branch through SiLU, in fp64 numpy.
+``causal_conv1d``  the depthwise causal convolution the QKV mixture passes through before the rule
+             (the Qwen3.5 page's flowchart node "conv1d, Depthwise Causal Conv" and its
+             conv_states cache), per sequence, carrying the last inputs in fp64 numpy.
 ``chunked``  the chunk-parallel (WY/UT) form of the same rule in fp64 numpy.  It is not the
              definition: it exists to show, against ``forward``, that the block algebra a chunked
              kernel uses reaches the token-by-token result exactly (up to rounding order).
@@ -168,6 +171,40 @@ def gated_rmsnorm(x: np.ndarray, z: np.ndarray, weight: np.ndarray, eps: float) 
     inv_rms = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
     silu = z / (1.0 + np.exp(-z))
     return x * inv_rms * w * silu
+
+
+def causal_conv1d(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray] = None,
+                  state: Optional[np.ndarray] = None, silu: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """One sequence: x [L, C], weight [C, W], bias [C] or None, state [W-1, C] (the W-1 inputs before
+    this sequence, oldest first) or None for zeros.  Returns (y [L, C], new state [W-1, C]), fp64.
+
+    Qwen3.5 Gated DeltaNet page (wanger-sjtu.github.io): the flowchart sends the QKV mixture through
+    "conv1d, Depthwise Causal Conv" before it splits into q, k, v, reads "conv_states" on the decode
+    path and ends in "Update Conv Cache"; its section on the convolution layer describes a causal
+    convolution that gathers local context.  Depthwise: each channel has its own W taps.  Causal:
+    output t sees inputs t-W+1 .. t only, the inputs before the sequence coming from the cache (zeros
+    without one):
+        y[t, c] = sum_j weight[c, j] * xp[t + j, c] + bias[c],   xp = [state; x]
+    and the new cache holds the last W-1 rows of xp.  The kernel width varies across the pages (4, 8,
+    12-16 by context length; 5 elsewhere), so W is a parameter.  The pages name no activation after
+    the convolution: none is the default reading; ``silu`` applies x * sigmoid(x) to y for callers
+    whose model has one.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    L, C = x.shape
+    W = w.shape[1]
+    st = np.zeros((W - 1, C)) if state is None else np.asarray(state, dtype=np.float64)
+    xp = np.concatenate([st, x], axis=0)
+    y = np.zeros((L, C))
+    for t in range(L):
+        for j in range(W):
+            y[t] += w[:, j] * xp[t + j]
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float64)
+    if silu:
+        y = y / (1.0 + np.exp(-y))
+    return y, xp[xp.shape[0] - (W - 1):].copy()
 
 
 def chunked(

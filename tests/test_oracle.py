@@ -328,6 +328,59 @@ def test_gated_rmsnorm_closed_forms():
 
 
 # ----------------------------------------------------------------------------------------------
+# causal conv1d
+
+def test_conv1d_impulse_response():
+    """A unit impulse at t0 in channel c returns that channel's taps reversed: y[t0 + i] = w[c, W-1-i]."""
+    rng = np.random.default_rng(4)
+    C, W, L, t0 = 3, 5, 12, 4
+    w = rng.standard_normal((C, W))
+    x = np.zeros((L, C))
+    x[t0, 1] = 1.0
+    y, st = O.causal_conv1d(x, w)
+    for i in range(W):
+        assert y[t0 + i, 1] == w[1, W - 1 - i]
+    assert np.all(y[:t0] == 0) and np.all(y[t0 + W:] == 0) and np.all(y[:, [0, 2]] == 0)
+    assert st.shape == (W - 1, C) and np.all(st == x[L - W + 1:])
+
+
+def test_conv1d_equals_numpy_convolve():
+    """Per channel the causal conv is the full convolution with the taps reversed, cut to the first L."""
+    rng = np.random.default_rng(5)
+    C, W, L = 4, 4, 30
+    w, x, b = rng.standard_normal((C, W)), rng.standard_normal((L, C)), rng.standard_normal(C)
+    y, _ = O.causal_conv1d(x, w, b)
+    for c in range(C):
+        ref = np.convolve(x[:, c], w[c, ::-1])[:L] + b[c]
+        assert np.allclose(y[:, c], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_conv1d_split_and_carry():
+    """Two calls carrying the cache equal one call over the concatenation, for every cut, including
+    pieces shorter than the W-1 rows of the cache (and empty ones)."""
+    rng = np.random.default_rng(6)
+    C, W, L = 3, 6, 17
+    w, x, s0 = rng.standard_normal((C, W)), rng.standard_normal((L, C)), rng.standard_normal((W - 1, C))
+    y, s = O.causal_conv1d(x, w, None, s0, silu=True)
+    for cut in range(L + 1):
+        y1, s1 = O.causal_conv1d(x[:cut], w, None, s0, silu=True)
+        y2, s2 = O.causal_conv1d(x[cut:], w, None, s1, silu=True)
+        assert np.allclose(np.concatenate([y1, y2]), y, rtol=1e-13, atol=1e-13)
+        assert np.array_equal(s2, s)
+    # an empty piece leaves the cache as it was
+    _, same = O.causal_conv1d(x[:0], w, None, s0)
+    assert np.array_equal(same, s0)
+
+
+def test_conv1d_silu_and_width_one():
+    rng = np.random.default_rng(7)
+    x, w = rng.standard_normal((9, 2)), rng.standard_normal((2, 1))
+    y, st = O.causal_conv1d(x, w, silu=True)             # W = 1: a per-channel scale, no cache
+    lin = x * w[:, 0]
+    assert np.allclose(y, lin / (1.0 + np.exp(-lin)), rtol=1e-14) and st.shape == (0, 2)
+
+
+# ----------------------------------------------------------------------------------------------
 # sampling and threading do not change results
 
 def test_unit_mask_and_threads(orc):
