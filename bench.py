@@ -83,7 +83,8 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from gated_deltanet_delta_amd import (gdn_chunk_fwd, gdn_chunk_fwd_gating, gdn_gated_rmsnorm,
+    from gated_deltanet_delta_amd import (gdn_causal_conv1d, gdn_chunk_fwd, gdn_chunk_fwd_gating,
+                                          gdn_gated_rmsnorm,
                                           gdn_recurrent_step, gdn_recurrent_step_gating, synth,
                                           workspace_size)
 
@@ -194,6 +195,25 @@ def main() -> int:
     ms_norm = e0.elapsed_time(e1) / args.steps
     norm_bytes = o.numel() * (4 + 2 + 2) + wl.dv * 4
 
+    # ---------------- the causal conv1d of the QKV mixture (2 Hk dk + Hv dv channels) -----------
+    # (inputs drawn here with their own seed: the workloads define q, k, v after the conv)
+    Cc, Wc = 2 * wl.Hk * wl.dk + wl.Hv * wl.dv, 4
+    crng = np.random.default_rng(98)
+    xc = torch.from_numpy(crng.standard_normal((1, T, Cc), dtype=np.float32)).to(wl.dtype).to(dev)
+    wc = torch.from_numpy((0.5 * crng.standard_normal((Cc, Wc))).astype(np.float32)).to(dev)
+    sc = torch.zeros((1, Wc - 1, Cc), dtype=wl.dtype, device=dev)
+    yc = torch.empty_like(xc)
+    for _ in range(args.warmup):
+        gdn_causal_conv1d(xc, wc, None, sc, silu=True, y=yc)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        gdn_causal_conv1d(xc, wc, None, sc, silu=True, y=yc)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_conv = e0.elapsed_time(e1) / args.steps
+    conv_bytes = 2 * xc.numel() * xc.element_size() + Cc * Wc * 4 + 2 * sc.numel() * sc.element_size()
+
     # ---------------- decode ------------------------------------------------------------------
     wd = synth.WORKLOADS["decode"]
     x0 = synth.make(wd)
@@ -282,6 +302,13 @@ def main() -> int:
         "prefill_gating": {"call": "gdn_chunk_fwd_gating (gates formed in the kernels from a, b)",
                            "ms_per_call_events": round(ms_gating, 5),
                            "tokens_per_s": round(tokens / (ms_gating / 1e3), 1)},
+        "causal_conv1d": {"call": "gdn_causal_conv1d, QKV mixture of the prefill (bf16, W = 4, SiLU, cache)",
+                          "tokens": T, "channels": Cc, "width": Wc,
+                          "ms_per_call_events": round(ms_conv, 5),
+                          "roofline": {"bound": "hbm", "achieved": round(conv_bytes / (ms_conv / 1e3) / 1e9, 1),
+                                       "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                                       "frac": round(conv_bytes / (ms_conv / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
+                                       "algorithmic_bytes_per_launch": int(conv_bytes)}},
         "gated_rmsnorm": {"call": "gdn_gated_rmsnorm on the prefill's o (fp32 in, bf16 z and out)",
                           "rows": o.numel() // wl.dv, "d": wl.dv,
                           "ms_per_call_events": round(ms_norm, 5),

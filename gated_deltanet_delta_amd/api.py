@@ -297,6 +297,50 @@ def gdn_gated_rmsnorm(x: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, ep
     return out
 
 
+def gdn_causal_conv1d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                      conv_state: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None,
+                      state_indices: Optional[torch.Tensor] = None, *, silu: bool = False,
+                      y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Depthwise causal convolution over time: x [B, T, C] (bf16 or fp32; packed sequences with
+    cu_seqlens use B == 1), weight [C, W] fp32, bias [C] fp32 or None, conv_state [N, W-1, C] in x's
+    dtype (or a pool [num_slots, W-1, C] with state_indices [N] int32), updated in place; None: zero
+    history, nothing kept.  Returns y [B, T, C] in x's dtype."""
+    lib = _lib.load()
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be [B, T, C] and weight [C, W]")
+    B, T, C = x.shape
+    W = weight.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_causal_conv1d runs on a GPU; tensors must be on a cuda device")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(x, (B, T, C), "x", dev)
+    _check(weight, (C, W), "weight", dev, torch.float32)
+    if bias is not None:
+        _check(bias, (C,), "bias", dev, torch.float32)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
+    num_slots = 0
+    if state_indices is not None:
+        if conv_state is None:
+            raise ValueError("state_indices needs a conv_state pool")
+        _check(state_indices, (N,), "state_indices", dev, torch.int32)
+        num_slots = conv_state.shape[0]
+    if conv_state is not None:
+        _check(conv_state, (num_slots if state_indices is not None else N, W - 1, C), "conv_state", dev,
+               x.dtype)
+    if y is None:
+        y = torch.empty((B, T, C), dtype=x.dtype, device=dev)
+    _check(y, (B, T, C), "y", dev, x.dtype)
+    st = lib.gdn_causal_conv1d(_ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), _ptr(state_indices),
+                               num_slots, _ptr(cu_seqlens), B, T, C, W, N, _code(x, "x"), int(bool(silu)),
+                               _ptr(y), _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_causal_conv1d")
+    return y
+
+
 def chunk_gated_delta_rule(q, k, v, g, beta, initial_state=None, cu_seqlens=None):
     """The prefill entry point under its model-side name; see gdn_chunk_fwd."""
     return gdn_chunk_fwd(q, k, v, g, beta, initial_state, cu_seqlens)

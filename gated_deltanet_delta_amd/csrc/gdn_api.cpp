@@ -240,4 +240,30 @@ gdn_status gdn_gated_rmsnorm(const float* x, const void* z, const float* weight,
     return gdn::launch_gated_rmsnorm(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
 }
 
+gdn_status gdn_causal_conv1d(const void* x, const float* weight, const float* bias,
+                             void* conv_state, const int32_t* state_indices, int num_slots,
+                             const int32_t* cu_seqlens, int B, int T, int C, int W, int N,
+                             gdn_dtype x_dtype, int silu, void* y, hipStream_t stream) {
+    if (B < 1 || T < 0 || C < 1 || N < 1 || !dtype_ok(x_dtype)) return GDN_ERROR_INVALID_VALUE;
+    if (cu_seqlens ? B != 1 : N != B) return GDN_ERROR_INVALID_VALUE;
+    if (C % 4 != 0 || !sizes_fit(B, T, 1, C)) return GDN_ERROR_INVALID_VALUE;
+    if (W < 1 || W > 16) return GDN_ERROR_NOT_SUPPORTED;
+    if (T > 0 && (!x || !weight || !y)) return GDN_ERROR_INVALID_VALUE;
+    if (W == 1) {                   // no input history exists: the cache arguments are ignored
+        conv_state = nullptr;
+        state_indices = nullptr;
+    }
+    if (state_indices && (!conv_state || num_slots < 1 || !aligned(state_indices, 4) ||
+                          !sizes_fit(num_slots, W, 1, C)))
+        return GDN_ERROR_INVALID_VALUE;
+    if (conv_state && !state_indices && !sizes_fit(N, W, 1, C)) return GDN_ERROR_INVALID_VALUE;
+    const uintptr_t v4 = 4 * dtype_bytes(x_dtype);
+    if (!aligned(x, v4) || !aligned(y, v4) || !aligned(conv_state, v4) || !aligned(weight, 4) ||
+        !aligned16(bias) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return GDN_ERROR_INVALID_VALUE;
+    const gdn::ConvArgs a{x, weight, bias, conv_state, state_indices, num_slots, cu_seqlens, B, T, C, W,
+                          N, x_dtype, silu ? 1 : 0, y, stream};
+    return gdn::launch_causal_conv1d(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+}
+
 }  // extern "C"

@@ -57,6 +57,24 @@ struct NormArgs {
     hipStream_t stream;
 };
 
+struct ConvArgs {
+    const void* x;                 // [B, T, C] x_dtype (packed: B == 1, sequences by cu_seqlens)
+    const float* weight;           // [C, W]
+    const float* bias;             // [C] or null
+    void* conv_state;              // [N or num_slots, W - 1, C] x_dtype, or null
+    const int32_t* state_indices;  // [N] or null
+    int num_slots;
+    const int32_t* cu_seqlens;     // [N + 1] or null
+    int B, T, C, W, N;
+    gdn_dtype x_dtype;
+    int silu;
+    void* y;                       // [B, T, C] x_dtype
+    hipStream_t stream;
+};
+
+// Depthwise causal convolution with its carried input cache.
+hipError_t launch_causal_conv1d(const ConvArgs& a);
+
 // The gated output norm (one row per head vector).
 hipError_t launch_gated_rmsnorm(const NormArgs& a);
 

@@ -262,6 +262,37 @@ gdn_status gdn_gated_rmsnorm(const float* x, const void* z, const float* weight,
                              int64_t rows, int d, gdn_dtype z_dtype, gdn_dtype out_dtype,
                              void* out, hipStream_t stream);
 
+/*
+ * gdn_causal_conv1d -- the depthwise causal convolution of the QKV mixture, with its cache.
+ *
+ * The Qwen3.5 Gated DeltaNet page (wanger-sjtu.github.io) sends the QKV mixture (2K + V channels)
+ * through "conv1d, Depthwise Causal Conv" before splitting it into q, k, v; the decode path reads the
+ * conv_states cache and the layer then updates it ("Update Conv Cache").  Per sequence n and channel
+ * c, with xp = [cache_n; x_n] (the W - 1 inputs before the sequence, oldest first, then its own):
+ *     y[t, c] = act(sum_j weight[c, j] * xp[t + j, c] + bias[c])
+ * and the cache of n becomes the last W - 1 rows of xp.  A prefill is one call over whole sequences,
+ * a decode step the same call with T == 1.  The kernel width differs across the pages (4, 8, 12-16
+ * by context length on one, 5 on another), so W (1 .. 16) is an argument.  The pages name no
+ * activation: silu = 0 gives none; silu != 0 applies act(u) = u / (1 + exp(-u)).  fp32 arithmetic.
+ *
+ *   x           [B, T, C] x_dtype (device); packed sequences with cu_seqlens use B == 1
+ *   weight      [C, W] fp32 (device); weight[c, W - 1] multiplies the current input
+ *   bias        [C] fp32 (device) or NULL
+ *   conv_state  [N, W - 1, C] x_dtype (device) or NULL (zeros in, nothing written); with
+ *               state_indices, a pool [num_slots, W - 1, C] whose slot state_indices[n] serves
+ *               sequence n (an index outside [0, num_slots): zeros in, nothing written).  Updated in
+ *               place for every sequence with at least one token; the valid indices must be distinct.
+ *               With W == 1 there is no history: conv_state and state_indices are ignored.
+ *   cu_seqlens  [N + 1] int32 (device) or NULL (then N == B, sequence b = batch row b)
+ *   y           [B, T, C] x_dtype (device); must not overlap x or the cache
+ * Sizes: C a multiple of 4, W 1 .. 16 (others: GDN_ERROR_NOT_SUPPORTED), T >= 0.  x, y and
+ * conv_state aligned to 4 elements, bias to 16 bytes.
+ */
+gdn_status gdn_causal_conv1d(const void* x, const float* weight, const float* bias,
+                             void* conv_state, const int32_t* state_indices, int num_slots,
+                             const int32_t* cu_seqlens, int B, int T, int C, int W, int N,
+                             gdn_dtype x_dtype, int silu, void* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -199,3 +199,21 @@ def test_gated_rmsnorm_rejects(lib, kw, status):
 def test_gated_rmsnorm_zero_rows_is_a_no_op(lib):
     # nothing to do: accepted without touching (or even needing) any buffer
     assert norm(lib, x=None, z=None, w=None, out=None, rows=0) == _lib.GDN_SUCCESS
+
+
+def conv(lib, x=P, w=P, b=None, st=None, idx=None, ns=0, cu=None, B=1, T=8, C=64, W=4, N=1, xt=BF16, silu=0,
+         y=P):
+    return lib.gdn_causal_conv1d(x, w, b, st, idx, ns, cu, B, T, C, W, N, xt, silu, y, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
+    (dict(B=0), INVALID), (dict(T=-1), INVALID), (dict(C=0), INVALID), (dict(C=6), INVALID), (dict(N=0), INVALID),
+    (dict(N=2), INVALID), (dict(cu=P, B=2, N=2), INVALID), (dict(xt=9), INVALID),
+    (dict(idx=P), INVALID), (dict(idx=P, st=P, ns=0), INVALID), (dict(idx=P + 2, st=P, ns=3), INVALID),
+    (dict(x=P + 2), INVALID), (dict(y=P + 4), INVALID), (dict(st=P + 2), INVALID), (dict(b=P + 4), INVALID),
+    (dict(w=P + 2), INVALID), (dict(cu=P + 2), INVALID),
+    (dict(W=0), UNSUPPORTED), (dict(W=17), UNSUPPORTED),
+])
+def test_causal_conv1d_rejects(lib, kw, status):
+    assert conv(lib, **kw) == status
