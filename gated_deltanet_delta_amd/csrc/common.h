@@ -49,6 +49,11 @@ __device__ __forceinline__ void gate_values(float x, float y, const float* A_log
     }
 }
 
+// SiLU, u * sigmoid(u), from the hardware exp2 and reciprocal (each within about an ulp).  The
+// correctly rounded library exp and an IEEE division cost some 25 instructions per element, which a
+// streaming kernel cannot hide behind its memory traffic.
+__device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.f + __expf(-u)); }
+
 // State slot of sequence (or batch row) n: n itself, or state_indices[n] in a pool of num_slots
 // states.  An index outside [0, num_slots) marks a padding row, which has no state: false is
 // returned and slot is set to 0 (any in-bounds value; nothing is read or written through it).

@@ -56,8 +56,7 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     f32x4n y;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float silu = zv[i] / (1.f + expf(-zv[i]));
-        y[i] = xv[i] * inv_rms * wv[i] * silu;
+        y[i] = xv[i] * inv_rms * wv[i] * silu(zv[i]);
     }
     store4(out + base, y);
 }

@@ -50,9 +50,13 @@ def draw(rng, L, C, W, N, dtype):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("silu", [False, True])
-def test_conv1d_batched(dtype, silu):
-    rng = np.random.default_rng(31)
-    B, T, C, W = 3, 150, 1040, 4            # T spans three 64-token blocks; C spans two workgroups
+@pytest.mark.parametrize("B,T", [(3, 150), (4, 16)])
+def test_conv1d_batched(dtype, silu, B, T):
+    """Equal-length batch rows.  T = 150: sequence starts fall inside tiles, and the first tokens of
+    the later rows straddle two tiles (their caches rewritten by the second launch).  T = 16: every row
+    starts on a tile boundary, so every cache is rewritten in the first launch and the second skipped."""
+    rng = np.random.default_rng(31 + T)
+    C, W = 1040, 4                          # C spans two workgroups
     x, w, b, st = draw(rng, B * T, C, W, B, dtype)
     dev = "cuda"
     st_d = st.to(dev)
@@ -98,6 +102,28 @@ def test_conv1d_packed_pool(W):
             assert np.array_equal(got[i], new[named[i]]), f"slot {i}"
         else:
             assert np.array_equal(got[i], f(pool[i])), f"slot {i} should be untouched"
+
+
+@pytest.mark.parametrize("W", [2, 4, 7])
+def test_conv1d_short_sequences(W):
+    """Packed sequences of a few tokens each (a decode batch mixed with short requests): the kernel
+    takes them one token per thread; one-token sequences rewrite their cache in the same launch, the
+    25-token one in the second."""
+    rng = np.random.default_rng(50 + W)
+    lens = [1, 1, 0, 2, 1, 5, 1, 1, 25, 1, 3, 1]
+    N, C, L = len(lens), 264, sum(lens)
+    x, w, b, st = draw(rng, L, C, W, N, torch.bfloat16)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    dev = "cuda"
+    st_d = st.to(dev)
+    y = gdn_causal_conv1d(x.view(1, L, C).to(dev), w.to(dev), b.to(dev), st_d, cu.to(dev), silu=True)
+    torch.cuda.synchronize()
+    f = lambda t: t.double().cpu().numpy()
+    ref, scale, new = reference(f(x), f(w), f(b), f(st), lens, True)
+    close(f(y).reshape(L, C), ref, scale, torch.bfloat16, f"short sequences W={W} y")
+    for n in range(N):
+        want = new[n] if lens[n] > 0 else f(st)[n]
+        assert np.array_equal(f(st_d)[n], want), f"cache of sequence {n}"
 
 
 def test_conv1d_decode_steps_equal_prefill_bitwise():
