@@ -20,6 +20,8 @@ Contents
 ``causal_conv1d``  the depthwise causal convolution the QKV mixture passes through before the rule
              (the Qwen3.5 page's flowchart node "conv1d, Depthwise Causal Conv" and its
              conv_states cache), per sequence, carrying the last inputs in fp64 numpy.
+``l2norm``   the optional normalisation of each q and k head vector to unit length before the rule
+             (a reading: the pages do not state how q and k are scaled), in fp64 numpy.
 ``chunked``  the chunk-parallel (WY/UT) form of the same rule in fp64 numpy.  It is not the
              definition: it exists to show, against ``forward``, that the block algebra a chunked
              kernel uses reaches the token-by-token result exactly (up to rounding order).
@@ -171,6 +173,21 @@ def gated_rmsnorm(x: np.ndarray, z: np.ndarray, weight: np.ndarray, eps: float) 
     inv_rms = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
     silu = z / (1.0 + np.exp(-z))
     return x * inv_rms * w * silu
+
+
+def l2norm(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """x / sqrt(sum(x^2) + eps) over the last axis (one q or k head vector), fp64.
+
+    Not on the pages, which feed q and k to the rule without stating their scale.  The rule corrects
+    the state along the current key (Qwen3.5 page, "core mechanism": the old value stored along k is
+    replaced by the new one in proportion beta); that correction is an exact partial overwrite only
+    for a unit key, for which I - beta k k^T scales the state's component along k by 1 - beta.  This
+    step makes q and k unit vectors before the rule.  Reading taken for its form: a plain L2
+    normalisation with eps inside the square root, eps = 1e-6 (the eps the Qwen3-Next article's
+    section 3.2 uses for the model's RMS norms).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
 
 
 def causal_conv1d(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray] = None,

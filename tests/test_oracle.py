@@ -381,6 +381,50 @@ def test_conv1d_silu_and_width_one():
 
 
 # ----------------------------------------------------------------------------------------------
+# q/k L2 normalisation
+
+def test_l2norm_hand_worked_and_library():
+    """(3, 4) has length 5; at eps = 0 the step is x / numpy.linalg.norm(x); a zero vector stays zero."""
+    y = O.l2norm(np.array([3.0, 4.0]), eps=0.0)
+    assert np.array_equal(y, np.array([0.6, 0.8]))
+    y = O.l2norm(np.array([3.0, 4.0]))                    # eps = 1e-6 inside the root: 5.0000001
+    assert np.allclose(y, np.array([3.0, 4.0]) / np.sqrt(25.000001), rtol=1e-15)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 3, 16))
+    ref = x / np.linalg.norm(x, axis=-1, keepdims=True)
+    assert np.allclose(O.l2norm(x, eps=0.0), ref, rtol=1e-14, atol=0)
+    assert np.array_equal(O.l2norm(np.zeros((2, 4))), np.zeros((2, 4)))
+
+
+def test_l2norm_scale_invariance_and_unit_inputs():
+    """Rescaling a vector leaves its normalised form unchanged up to eps; unit vectors only lose the
+    factor 1 / sqrt(1 + eps)."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((4, 32))
+    for c in (1e-2, 7.0, 1e3):
+        assert np.allclose(O.l2norm(c * x, eps=0.0), O.l2norm(x, eps=0.0), rtol=1e-14, atol=0)
+    u = x / np.linalg.norm(x, axis=-1, keepdims=True)
+    assert np.allclose(O.l2norm(u), u / np.sqrt(1.0 + 1e-6), rtol=1e-14, atol=0)
+
+
+def test_l2norm_makes_the_correction_an_overwrite(orc):
+    """With a key of length 3 along e0 and beta = 1, g = 0, normalising the key turns the correction
+    into an exact overwrite: from S0 = e0 w^T the state becomes e0 v^T and a query along e0 reads v.
+    Unnormalised, (I - 9 e0 e0^T) would flip and amplify the stored row instead."""
+    dk = dv = 4
+    q = np.zeros((1, 1, 1, dk)); q[..., 0] = 2.0
+    k = np.zeros((1, 1, 1, dk)); k[..., 0] = 3.0
+    v = np.arange(1.0, dv + 1).reshape(1, 1, 1, dv)
+    g, beta = np.zeros((1, 1, 1)), np.ones((1, 1, 1))
+    s0 = np.zeros((1, 1, dk, dv)); s0[0, 0, 0] = [5.0, -1.0, 2.0, 0.5]
+    o, fs = orc.forward(O.l2norm(q, eps=0.0), O.l2norm(k, eps=0.0), v, g, beta, s0)
+    want = np.zeros((dk, dv)); want[0] = v[0, 0, 0]
+    assert np.array_equal(fs[0, 0], want) and np.array_equal(o[0, 0, 0], v[0, 0, 0])
+    _, raw = orc.forward(q, k, v, g, beta, s0)
+    assert raw[0, 0, 0, 0] == (1 - 9) * 5.0 + 3.0 * 1.0
+
+
+# ----------------------------------------------------------------------------------------------
 # sampling and threading do not change results
 
 def test_unit_mask_and_threads(orc):
