@@ -19,7 +19,10 @@ GDN_BF16 = 1
 EXPORTED = ("gdn_status_string", "gdn_version", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
             "gdn_chunk_fwd_prepare", "gdn_chunk_fwd_scan", "gdn_recurrent_step",
             "gdn_chunk_fwd_gating", "gdn_recurrent_step_gating", "gdn_chunk_fwd_indexed",
-            "gdn_recurrent_step_indexed", "gdn_gated_rmsnorm", "gdn_causal_conv1d")
+            "gdn_recurrent_step_indexed", "gdn_gated_rmsnorm", "gdn_causal_conv1d",
+            "gdn_chunk_fwd_ex", "gdn_recurrent_step_ex")
+
+GDN_FLAG_QK_L2NORM = 1
 
 _lib = None
 
@@ -64,6 +67,11 @@ def load() -> ctypes.CDLL:
     lib.gdn_gated_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_int64, i32, i32, i32, vp, vp]
     lib.gdn_causal_conv1d.restype = i32
     lib.gdn_causal_conv1d.argtypes = [vp] * 5 + [i32] + [vp] + [i32] * 5 + [i32, i32] + [vp, vp]
+    u32 = ctypes.c_uint
+    lib.gdn_chunk_fwd_ex.restype = i32
+    lib.gdn_chunk_fwd_ex.argtypes = [vp] * 10 + [i32] + [vp] + [i32] * 7 + [i32, i32] + [u32] + [vp, vp, sz, vp]
+    lib.gdn_recurrent_step_ex.restype = i32
+    lib.gdn_recurrent_step_ex.argtypes = [vp] * 9 + [i32] + [i32] * 6 + [i32, i32] + [u32] + [vp, vp]
     _lib = lib
     return lib
 

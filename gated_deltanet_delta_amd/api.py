@@ -270,6 +270,129 @@ def gdn_recurrent_step_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     return o
 
 
+def gdn_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, *, A_log: Optional[torch.Tensor] = None,
+                     dt_bias: Optional[torch.Tensor] = None,
+                     initial_state: Optional[torch.Tensor] = None,
+                     final_state: Optional[torch.Tensor] = None,
+                     state_indices: Optional[torch.Tensor] = None,
+                     cu_seqlens: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                     o: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The chunked call with every option: A_log, dt_bias [Hv] fp32 make g, beta the raw projections
+    a, b; state_indices int32 [N] makes initial_state a pool [num_slots,Hv,dk,dv] read and written in
+    place (it is then also the returned final state); qk_l2norm normalises q and k to unit length
+    inside the kernels.  Returns (o, final_state)."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_chunk_fwd_ex runs on a GPU; tensors must be on a cuda device")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    gating = A_log is not None
+    xn, yn = ("a", "b") if gating else ("g", "beta")
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(g, (B, T, Hv), xn, dev)
+    _check(beta, (B, T, Hv), yn, dev, g.dtype)
+    if gating:
+        _check(A_log, (Hv,), "A_log", dev, torch.float32)
+        _check(dt_bias, (Hv,), "dt_bias", dev, torch.float32)
+    elif dt_bias is not None:
+        raise ValueError("dt_bias needs A_log")
+    if cu_seqlens is not None:
+        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
+    num_slots = 0
+    if state_indices is not None:
+        if initial_state is None or initial_state.dim() != 4 or final_state is not None:
+            raise ValueError("with state_indices, initial_state is the pool [num_slots, Hv, dk, dv] "
+                             "and final_state is not given")
+        num_slots = initial_state.shape[0]
+        _check(initial_state, (num_slots, Hv, dk, dv), "state pool", dev, torch.float32)
+        _check(state_indices, (N,), "state_indices", dev, torch.int32)
+        final_state = initial_state
+    else:
+        if initial_state is not None:
+            _check(initial_state, (N, Hv, dk, dv), "initial_state", dev, torch.float32)
+        if final_state is None:
+            final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+        _check(final_state, (N, Hv, dk, dv), "final_state", dev, torch.float32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
+    qkv, gate = _code(q, "q"), _code(g, xn)
+    ws_bytes = int(lib.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    flags = _lib.GDN_FLAG_QK_L2NORM if qk_l2norm else 0
+    st = lib.gdn_chunk_fwd_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias), _ptr(initial_state),
+        _ptr(final_state), _ptr(state_indices), num_slots, _ptr(cu_seqlens), B, T, Hk, Hv, dk, dv, N,
+        qkv, gate, flags, _ptr(o), _ptr(workspace),
+        ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
+        _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_chunk_fwd_ex")
+    return o, final_state
+
+
+def gdn_recurrent_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, state: torch.Tensor, *,
+                          A_log: Optional[torch.Tensor] = None,
+                          dt_bias: Optional[torch.Tensor] = None,
+                          state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                          o: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The decode call with every option: raw gates (A_log, dt_bias), a state pool (state_indices
+    int32 [B]; state is then [num_slots,Hv,dk,dv]) and qk_l2norm.  Returns (o, state)."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_recurrent_step_ex runs on a GPU; tensors must be on a cuda device")
+    gating = A_log is not None
+    xn, yn = ("a", "b") if gating else ("g", "beta")
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(g, (B, T, Hv), xn, dev)
+    _check(beta, (B, T, Hv), yn, dev, g.dtype)
+    if gating:
+        _check(A_log, (Hv,), "A_log", dev, torch.float32)
+        _check(dt_bias, (Hv,), "dt_bias", dev, torch.float32)
+    elif dt_bias is not None:
+        raise ValueError("dt_bias needs A_log")
+    num_slots = 0
+    if state_indices is not None:
+        if state.dim() != 4:
+            raise ValueError("state must be the pool [num_slots, Hv, dk, dv]")
+        num_slots = state.shape[0]
+        _check(state, (num_slots, Hv, dk, dv), "state pool", dev, torch.float32)
+        _check(state_indices, (B,), "state_indices", dev, torch.int32)
+    else:
+        _check(state, (B, Hv, dk, dv), "state", dev, torch.float32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
+    flags = _lib.GDN_FLAG_QK_L2NORM if qk_l2norm else 0
+    st = lib.gdn_recurrent_step_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias), _ptr(state),
+        _ptr(state_indices), num_slots, B, T, Hk, Hv, dk, dv, _code(q, "q"), _code(g, xn), flags,
+        _ptr(o), _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_recurrent_step_ex")
+    return o, state
+
+
 def gdn_gated_rmsnorm(x: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
                       out_dtype: torch.dtype = torch.bfloat16,
                       out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -13,6 +13,8 @@
 // Unrolling the per-token rule over the chunk gives exactly these identities.  A short last chunk
 // is zero-padded: padded tokens have beta = 0 and g = 0, which leave the state untouched.
 //
+// With qk_l2norm, each staged row of K and Q is scaled to unit length in LDS (fp32) first.
+//
 // All operands live in LDS (~125 KB at dk = 128).  This path favours plain, exact fp32 arithmetic
 // over speed; bf16 inputs take the matrix-core kernels instead.
 
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
     const TG* __restrict__ g, const TG* __restrict__ beta, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, const float* initial_state,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ state_indices,
-    int num_slots, int T, int Hk, int Hv, int dv,
+    int num_slots, int T, int Hk, int Hv, int dv, int qk_l2norm,
     float* __restrict__ o, float* final_state) {
     constexpr int LDK = DK + 1, LC = kC + 1, LW = kWS + 1;
     extern __shared__ float smem[];
@@ -104,6 +106,17 @@ __global__ __launch_bounds__(kThreads) void chunk_f32_kernel(
             sB[tid] = bt;
         }
         __syncthreads();
+        if (qk_l2norm) {
+            // 2 kC rows (K then Q), two threads per row, each over half of it
+            const int r = tid >> 1, half = tid & 1;
+            float* xr = (r < kC ? sK + r * LDK : sQ + (r - kC) * LDK) + half * (DK / 2);
+            float ss = 0.f;
+            for (int i = 0; i < DK / 2; ++i) ss += xr[i] * xr[i];
+            ss += __shfl_xor(ss, 1);
+            const float rn = 1.f / sqrtf(ss + kL2Eps);
+            for (int i = 0; i < DK / 2; ++i) xr[i] *= rn;
+            __syncthreads();
+        }
         if (tid == 0) {
             float acc = 0.f;
             for (int t = 0; t < kC; ++t) {
@@ -226,8 +239,7 @@ hipError_t launch_typed(const ChunkArgs& a) {
                        static_cast<const TIn*>(a.k), static_cast<const TIn*>(a.v),
                        static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta), a.A_log,
                        a.dt_bias, a.initial_state, a.cu_seqlens, a.state_indices, a.num_slots, a.T,
-                       a.Hk, a.Hv, a.dv, a.o,
-                       a.final_state);
+                       a.Hk, a.Hv, a.dv, a.qk_l2norm, a.o, a.final_state);
     return hipGetLastError();
 }
 

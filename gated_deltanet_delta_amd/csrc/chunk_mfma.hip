@@ -54,6 +54,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;      // chunk length
+constexpr int kGRows = 4;   // rows of a chunk's gate block (of kC floats each)
 constexpr int kDK = 128;    // key dimension handled by this file
 constexpr int kThreads = 256;
 
@@ -241,11 +242,17 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
 // ------------------------------------------------------------------------------------------------
 // chunk_solve_kernel: one workgroup per (chunk slot, q/k head), for each of the head's v-heads.
 //
-// Writes, per (chunk, v-head), the chunk's gate block [3][64] floats: G2 = running sum of
-// g log2(e), 2^G2 and 2^(G2_C - G2) (G2_C = G2 at the chunk's last row; padding rows past the
-// chunk's length have g = 0), and M = T diag(beta) as the 12 fragments described above (zero above
-// the diagonal and in rows/columns past the chunk's length).  Per (chunk, q/k head) it writes
+// Writes, per (chunk, v-head), the chunk's gate block [4][64] floats: G2 = running sum of
+// g log2(e), 2^G2, 2^(G2_C - G2) (G2_C = G2 at the chunk's last row; padding rows past the
+// chunk's length have g = 0) and, with L2, the key scales r_t = 1 / |k_t| (row 3; row 2 then holds
+// r 2^(G2_C - G2)); and M = T diag(beta) as the 12 fragments described above (zero above the
+// diagonal and in rows/columns past the chunk's length).  Per (chunk, q/k head) it writes
 // N = K K_p^T for the scan kernel's K S recurrence.
+//
+// L2 (q and k normalised to unit length): the normalised keys are diag(r) K, so the chunk's
+// K K^T becomes diag(r) K K^T diag(r) (applied to the product tiles in fp32), and every later use of
+// a normalised key is a per-token factor on the scan kernel's fp32 side; K itself stays the exact
+// bf16 input.
 //
 // K enters the matrix cores straight from memory (its rows are both operands of K K^T), and
 // K K^T is formed once for all v-heads of the q/k head.  A and T live in shared memory as their
@@ -255,7 +262,7 @@ __device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }
 
 // (at most 128 registers per lane: four waves per SIMD, so a whole 4096-token prefill's chunk
 // workgroups are resident at once)
-template <typename TG>
+template <typename TG, bool L2>
 __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     const __bf16* __restrict__ k, const TG* __restrict__ g, const TG* __restrict__ beta,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
@@ -265,6 +272,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     __shared__ float sA[10][16 * kBP];     // blocks (a, b), a > b, of A
     __shared__ float sT[10][16 * kBP];     // blocks (a, b), a >= b, of T = (I + A)^-1
     __shared__ float sB[kC];
+    __shared__ float sRk[kC];              // (L2) 1 / |k_t|
 
     const int slot = blockIdx.x, kh = blockIdx.y;
     ChunkLoc loc;
@@ -314,8 +322,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         return acc;
     };
     // lane (g, c) element r of tile (ta, tb) holds (K K^T)[16 ta + 4 g + r][16 tb + c]
-    const f32x4 kd = kkt(k0, k0);                                  // (w, w)
-    const f32x4 kx = wave == 3 ? kkt(k0, k1) : kkt(k1, k0);        // (1,0) (2,1) (3,2) / (3,0)
+    f32x4 kd = kkt(k0, k0);                                        // (w, w)
+    f32x4 kx = wave == 3 ? kkt(k0, k1) : kkt(k1, k0);              // (1,0) (2,1) (3,2) / (3,0)
     f32x4 ky = zero4();                                            // (2,0) / (3,1)
     if (wave == 1) ky = kkt(k1, k2);
     if (wave == 3) ky = kkt(k0, k2);
@@ -336,6 +344,26 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
             *reinterpret_cast<bf16x8*>(nb + (2 * (2 * wave + j)) * kFragElems) = hv;
             *reinterpret_cast<bf16x8*>(nb + (2 * (2 * wave + j) + 1) * kFragElems) = lv;
         }
+    }
+
+    if constexpr (L2) {
+        // r_t = 1 / sqrt(|k_t|^2 + eps) for token tile `wave`: |k_t|^2 is the diagonal of its tile
+        // (w, w) of K K^T, held by lane (g, c) with c / 4 == g as element c % 4.  Then
+        // K K^T -> diag(r) K K^T diag(r).
+        if ((c >> 2) == gq) {
+            const int r = c & 3;
+            const float d = r == 0 ? kd[0] : (r == 1 ? kd[1] : (r == 2 ? kd[2] : kd[3]));
+            sRk[16 * wave + c] = 1.f / sqrtf(d + kL2Eps);
+        }
+        lds_barrier();
+        auto scale_tile = [&](f32x4& acc, int ta, int tb) {
+            const float rj = sRk[16 * tb + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= sRk[16 * ta + 4 * gq + r] * rj;
+        };
+        scale_tile(kd, wave, wave);
+        scale_tile(kx, xa, xb);
+        if (wave & 1) scale_tile(ky, ya, yb);
     }
 
     // the gates of the first kPre v-heads are loaded together with K (one memory round trip)
@@ -373,11 +401,17 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
             if (lane >= off) G2 += y;
         }
         if (wave == 0) {
-            const size_t ws_row = ((size_t)slot * Hv + h) * 3 * kC;
+            const size_t ws_row = ((size_t)slot * Hv + h) * kGRows * kC;
             const float G2c = __shfl(G2, 63);
             ws_G[ws_row + lane] = G2;
             ws_G[ws_row + kC + lane] = exp2_fast(G2);
-            ws_G[ws_row + 2 * kC + lane] = exp2_fast(G2c - G2);
+            const float dec = exp2_fast(G2c - G2);
+            if constexpr (L2) {
+                ws_G[ws_row + 2 * kC + lane] = sRk[lane] * dec;
+                ws_G[ws_row + 3 * kC + lane] = sRk[lane];
+            } else {
+                ws_G[ws_row + 2 * kC + lane] = dec;
+            }
             sB[lane] = bt;
         }
         // A = diag(beta) (K K^T o Gam), strictly lower, tile by tile
@@ -494,6 +528,12 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
 //   staging wave (5) copies each chunk's K rows, V columns and gate block straight from memory into
 //                    a five-chunk LDS ring (global_load_lds), three chunks ahead of the chain.
 //
+// L2 (q and k normalised to unit length, r = 1 / |k|, rq = 1 / |q| per token): the kernel keeps the
+// exact bf16 K and Q and applies the scales on the fp32 side.  D carries r already (the solve's
+// gate block row 2), so S <- e^(G_C) S + K^T D and N_s D_{s-1} need nothing more; the e^G factors
+// of Y and X take r_s; P's entries take r of their key token; the output takes rq, formed by the
+// output waves from the Q rows they load.
+//
 // Waves w and w + 4 share a SIMD: the chain with state half 1, state half 0 with the staging
 // wave; the output waves have one each.  The state waves run at a higher priority than the chain:
 // on the shared SIMD the chain has the slack (measured), and the state half is the one the next
@@ -527,7 +567,7 @@ __host__ __device__ constexpr int kswz(int t) { return (t >> 2) & 3; }
 struct ScanLds {
     __bf16 Kr[kRing][kC * kKR];                // K rows [token][key]
     __bf16 Vr[kRing][kC * kWS];                // V [token][this slice's 16 columns]
-    float Gt[kRing][256];                      // gate block: G2, 2^G2, 2^(G2_C - G2) (+ unused)
+    float Gt[kRing][kGRows * kC];              // gate block: G2, 2^G2, (r) 2^(G2_C - G2), (r)
     __bf16 St[2][2][kWS * kSP];                // S^T at chunk start [buffer][hi, lo]
     f32x4 Ut[2][4][64];                        // U [buffer][token tile][lane], the chain's tiles
     f32x4 Yt[2][2][4][64];                     // Y in two parts [buffer][key half][tile][lane]
@@ -567,7 +607,7 @@ struct OutIn {                     // one chunk's Q fragments for an output wave
     bf16x8 q[2][4];                // Q rows 16 a + c of its two tiles, columns 32 kb + 8 g ..
 };
 
-template <int DV>
+template <int DV, bool L2>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
@@ -643,6 +683,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             for (int a = 0; a < 4; ++a) {
                 y[a] = ld<f32x4>(yl, 16 * 64 * a) + ld<f32x4>(yl, 16 * 64 * (4 + a));
                 eg[a] = ld<f32x4>(gl, 4 * 16 * a);
+                if constexpr (L2) eg[a] *= ld<f32x4>(gl, 4 * 16 * a + 4 * 2 * kC);      // r_s
             }
             f32x4 x[4];
             if constexpr (kFirst) {
@@ -755,7 +796,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 lds_u8* yl = lds_at(&sm.Yt[ci & 1][hh][0][lane]);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const f32x4 eg = ld<f32x4>(gl, 4 * 16 * a) * ec;
+                    f32x4 eg = ld<f32x4>(gl, 4 * 16 * a) * ec;
+                    if constexpr (L2) eg *= ld<f32x4>(gl, 4 * 16 * a + 4 * 2 * kC);      // r_s
                     f32x4 y;
                     if constexpr (hh == 0) {
                         lds_u8* vl = lds_at(sm.Vr[slot] + l_v);
@@ -894,10 +936,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb) pt[b] = mma(kf[b][kb], cur.q[x][kb], pt[b]);
                         const f32x4 gp = ld<f32x4>(gl, 4 * 16 * b);
+                        f32x4 rk = {1.f, 1.f, 1.f, 1.f};
+                        if constexpr (L2) rk = ld<f32x4>(gl, 4 * 16 * b + 4 * 3 * kC);   // r of key tp
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int tp = 16 * b + 4 * g + r;
-                            pt[b][r] = tp <= t ? pt[b][r] * exp2_fast(gq[x] - gp[r]) : 0.f;
+                            pt[b][r] = tp <= t ? pt[b][r] * exp2_fast(gq[x] - gp[r]) * rk[r] : 0.f;
                         }
                     }
                     // B fragments for P U: reduction rows 32 kb + 4 g + e (e < 4), + 16 (e >= 4)
@@ -917,6 +961,20 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                         acc = mma(uf[0][kb], ph[kb], acc);
                         acc = mma(uf[0][kb], pl[kb], acc);
                         acc = mma(uf[1][kb], ph[kb], acc);
+                    }
+                    if constexpr (L2) {
+                        // rq = 1 / sqrt(|q_t|^2 + eps): lane (g, c) holds 32 of row t's keys
+                        float ss = 0.f;
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const float qv = (float)cur.q[x][kb][e];
+                                ss += qv * qv;
+                            }
+                        ss += __shfl_xor(ss, 16);
+                        ss += __shfl_xor(ss, 32);
+                        acc *= 1.f / sqrtf(ss + kL2Eps);
                     }
                     ot[x] = acc;
                 }
@@ -969,8 +1027,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             for (int jj = 0; jj < 2; ++jj)          // rows 32 jj + lane / 2, columns 8 (lane % 2)
                 copy_to_lds(vb + (size_t)min(32 * jj + (lane >> 1), L - 1) * Hv * DV + 8 * (lane & 1),
                             sm.Vr[slot] + 512 * jj);
-            const float* gb = ws_G + ((size_t)(slot0 + ci) * Hv + h) * 3 * kC;
-            copy_to_lds(gb + 4 * min(lane, 47), sm.Gt[slot]);
+            const float* gb = ws_G + ((size_t)(slot0 + ci) * Hv + h) * kGRows * kC;
+            copy_to_lds(gb + 4 * min(lane, L2 ? 63 : 47), sm.Gt[slot]);     // (row 3 only with L2)
         };
         dma(0);
         if (nchunks > 1) dma(1);
@@ -994,7 +1052,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 
 // ------------------------------------------------------------------------------------------------
 // workspace layout (each region 256-byte aligned):
-//   chunk_start [N+1] int32 | order [N] int32 | gates [slots][Hv][G2, 2^G2, 2^(G2_C - G2)][64] f32
+//   chunk_start [N+1] int32 | order [N] int32 | gates [slots][Hv][G2, 2^G2, 2^(G2_C - G2), r][64] f32
 //   | M [slots][Hv][12 fragments] bf16 | N [slots][Hk][16 fragments] bf16
 struct Layout {
     size_t chunk_start, order, G, M, Nm, total;
@@ -1009,14 +1067,14 @@ Layout layout(int B, int T, int Hk, int Hv, int N) {
     size_t off = 0;
     l.chunk_start = off; off = align256(off + sizeof(int32_t) * (size_t)(N + 1));
     l.order = off;       off = align256(off + sizeof(int32_t) * (size_t)N);
-    l.G = off;           off = align256(off + sizeof(float) * (size_t)l.slots * Hv * 3 * kC);
+    l.G = off;           off = align256(off + sizeof(float) * (size_t)l.slots * Hv * kGRows * kC);
     l.M = off;           off = align256(off + 2 * (size_t)l.slots * Hv * kMFrags * kFragElems);
     l.Nm = off;          off = align256(off + 2 * (size_t)l.slots * Hk * kNFrags * kFragElems);
     l.total = off;
     return l;
 }
 
-template <int DV, typename TG>
+template <int DV, typename TG, bool L2>
 hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
     const Layout lay = layout(a.B, a.T, a.Hk, a.Hv, a.N);
     char* ws = static_cast<char*>(a.workspace);
@@ -1036,7 +1094,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((stages & kStagePrepare) && slots > 0) {
-        hipLaunchKernelGGL((chunk_solve_kernel<TG>), dim3((unsigned)slots, (unsigned)a.Hk),
+        hipLaunchKernelGGL((chunk_solve_kernel<TG, L2>), dim3((unsigned)slots, (unsigned)a.Hk),
                            dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.k),
                            static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta), a.A_log,
                            a.dt_bias, a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M,
@@ -1044,7 +1102,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (!(stages & kStageScan)) return hipSuccess;
-    const auto kern = chunk_scan_kernel<DV>;
+    const auto kern = chunk_scan_kernel<DV, L2>;
     const size_t bytes = sizeof(ScanLds);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)) != hipSuccess)
@@ -1073,10 +1131,15 @@ size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, i
     return layout(B, T, Hk, Hv, N).total;
 }
 
-hipError_t launch_chunk_mfma(const ChunkArgs& a, unsigned stages) {
+template <bool L2>
+hipError_t launch_l2(const ChunkArgs& a, unsigned stages) {
     const bool g_bf16 = a.gate_dtype == GDN_BF16;
-    if (a.dv == 128) return g_bf16 ? launch_dv<128, bf16_t>(a, stages) : launch_dv<128, float>(a, stages);
-    return g_bf16 ? launch_dv<64, bf16_t>(a, stages) : launch_dv<64, float>(a, stages);
+    if (a.dv == 128) return g_bf16 ? launch_dv<128, bf16_t, L2>(a, stages) : launch_dv<128, float, L2>(a, stages);
+    return g_bf16 ? launch_dv<64, bf16_t, L2>(a, stages) : launch_dv<64, float, L2>(a, stages);
+}
+
+hipError_t launch_chunk_mfma(const ChunkArgs& a, unsigned stages) {
+    return a.qk_l2norm ? launch_l2<true>(a, stages) : launch_l2<false>(a, stages);
 }
 
 }  // namespace gdn

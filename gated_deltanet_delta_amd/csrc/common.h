@@ -49,6 +49,9 @@ __device__ __forceinline__ void gate_values(float x, float y, const float* A_log
     }
 }
 
+// eps of the optional q/k L2 normalisation x / sqrt(|x|^2 + eps) (the eps of the model's RMS norms)
+constexpr float kL2Eps = 1e-6f;
+
 // SiLU, u * sigmoid(u), from the hardware exp2 and reciprocal (each within about an ulp).  The
 // correctly rounded library exp and an IEEE division cost some 25 instructions per element, which a
 // streaming kernel cannot hide behind its memory traffic.

@@ -65,7 +65,7 @@ gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g
                       int num_slots, const float* initial_state, const int32_t* cu_seqlens, int B, int T, int Hk,
                       int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
                       float* o, float* final_state, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream, unsigned stages) {
+                      hipStream_t stream, unsigned stages, int qk_l2norm = 0) {
     if (!final_state) return GDN_ERROR_INVALID_VALUE;
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERROR_INVALID_VALUE;
     if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
@@ -87,7 +87,7 @@ gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g
 
     const gdn::ChunkArgs a{q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens,
                            state_indices, num_slots, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, o,
-                           final_state, workspace, workspace_bytes, stream};
+                           final_state, workspace, workspace_bytes, stream, qk_l2norm};
     hipError_t e;
     if (use_mfma(dk, dv, qkv_dtype)) {
         const size_t need = gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype);
@@ -145,7 +145,7 @@ gdn_status recurrent_call(const void* q, const void* k, const void* v, const voi
                           const void* beta, const float* A_log, const float* dt_bias, float* state,
                           const int32_t* state_indices, int num_slots, int B, int T, int Hk, int Hv,
                           int dk, int dv, gdn_dtype qkv_dtype, gdn_dtype gate_dtype, float* o,
-                          hipStream_t stream) {
+                          hipStream_t stream, int qk_l2norm = 0) {
     if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERROR_INVALID_VALUE;
     if (B < 1 || T < 1 || Hk < 1 || Hv < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
     if (!dtype_ok(qkv_dtype) || !dtype_ok(gate_dtype)) return GDN_ERROR_INVALID_VALUE;
@@ -165,7 +165,7 @@ gdn_status recurrent_call(const void* q, const void* k, const void* v, const voi
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
 
     const gdn::RecurrentArgs a{q, k, v, g, beta, A_log, dt_bias, state, state_indices, num_slots,
-                               B, T, Hk, Hv, dk, dv, qkv_dtype, gate_dtype, o, stream};
+                               B, T, Hk, Hv, dk, dv, qkv_dtype, gate_dtype, o, stream, qk_l2norm};
     return gdn::launch_recurrent(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
 }
 
@@ -264,6 +264,32 @@ gdn_status gdn_causal_conv1d(const void* x, const float* weight, const float* bi
     const gdn::ConvArgs a{x, weight, bias, conv_state, state_indices, num_slots, cu_seqlens, B, T, C, W,
                           N, x_dtype, silu ? 1 : 0, y, stream};
     return gdn::launch_causal_conv1d(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+}
+
+gdn_status gdn_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* A_log, const float* dt_bias,
+                            const float* initial_state, float* final_state,
+                            const int32_t* state_indices, int num_slots, const int32_t* cu_seqlens,
+                            int B, int T, int Hk, int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype,
+                            gdn_dtype gate_dtype, unsigned flags, float* o, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if ((flags & ~GDN_FLAG_QK_L2NORM) || (dt_bias && !A_log)) return GDN_ERROR_INVALID_VALUE;
+    if (state_indices && initial_state != final_state) return GDN_ERROR_INVALID_VALUE;
+    return chunk_call(q, k, v, g, beta, A_log, dt_bias, state_indices, num_slots, initial_state,
+                      cu_seqlens, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, o, final_state,
+                      workspace, workspace_bytes, stream, gdn::kStagePrepare | gdn::kStageScan,
+                      (flags & GDN_FLAG_QK_L2NORM) ? 1 : 0);
+}
+
+gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, const float* A_log, const float* dt_bias,
+                                 float* state, const int32_t* state_indices, int num_slots, int B,
+                                 int T, int Hk, int Hv, int dk, int dv, gdn_dtype qkv_dtype,
+                                 gdn_dtype gate_dtype, unsigned flags, float* o, hipStream_t stream) {
+    if ((flags & ~GDN_FLAG_QK_L2NORM) || (dt_bias && !A_log)) return GDN_ERROR_INVALID_VALUE;
+    return recurrent_call(q, k, v, g, beta, A_log, dt_bias, state, state_indices, num_slots, B, T,
+                          Hk, Hv, dk, dv, qkv_dtype, gate_dtype, o, stream,
+                          (flags & GDN_FLAG_QK_L2NORM) ? 1 : 0);
 }
 
 }  // extern "C"

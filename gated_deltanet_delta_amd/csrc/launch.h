@@ -26,6 +26,7 @@ struct ChunkArgs {
     void* workspace;
     size_t workspace_bytes;
     hipStream_t stream;
+    int qk_l2norm;                 // q, k normalised to unit length inside the kernels
 };
 
 struct RecurrentArgs {
@@ -43,6 +44,7 @@ struct RecurrentArgs {
     gdn_dtype qkv_dtype, gate_dtype;
     float* o;
     hipStream_t stream;
+    int qk_l2norm;                 // as in ChunkArgs
 };
 
 struct NormArgs {

@@ -8,7 +8,8 @@
 //     a = exp(g);  p = S^T k;  u = beta (v - a p);  o = a S^T q + u (k . q);  S = a S + k u^T
 //
 // which is the decay -> predict -> correct -> read order of the rule with the two column
-// reductions (S^T k and S^T q) taken from the same register pass over the old state.
+// reductions (S^T k and S^T q) taken from the same register pass over the old state.  With
+// qk_l2norm, the staged q and k are first scaled to unit length in LDS (fp32).
 //
 // Memory pattern: rows of S are DV floats; a wave covers whole rows with 16-byte loads, so every
 // load/store instruction of a wave touches 64 x 16 B of contiguous memory.  The work is ~1 flop
@@ -32,7 +33,7 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
     const TG* __restrict__ g, const TG* __restrict__ beta, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, float* __restrict__ state,
     const int32_t* __restrict__ state_indices, int num_slots, float* __restrict__ o, int T, int Hk,
-    int Hv) {
+    int Hv, int qk_l2norm) {
     constexpr int CG = DV / 4;               // float4 column groups per row
     constexpr int RG = kRecThreads / CG;     // row groups
     constexpr int RPT = DK / RG;             // rows held per thread
@@ -72,6 +73,18 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(
         float gt, bt;
         gate_values(to_f32(g[tok * Hv + h]), to_f32(beta[tok * Hv + h]), A_log, dt_bias, h, gt, bt);
         __syncthreads();
+        if (qk_l2norm) {
+            if (wave < 2) {                              // wave 0 scales k, wave 1 q
+                float* x = wave == 0 ? sk : sq;
+                float ss = 0.f;
+                for (int i = lane; i < DK; i += kWave) ss += x[i] * x[i];
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) ss += __shfl_xor(ss, off);
+                const float rn = 1.f / sqrtf(ss + kL2Eps);
+                for (int i = lane; i < DK; i += kWave) x[i] *= rn;
+            }
+            __syncthreads();
+        }
 
         // Partial column sums over this thread's rows.
         float pk0 = 0.f, pk1 = 0.f, pk2 = 0.f, pk3 = 0.f;
@@ -145,7 +158,7 @@ hipError_t launch_typed(const RecurrentArgs& a) {
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), static_cast<const TG*>(a.g),
                        static_cast<const TG*>(a.beta), a.A_log, a.dt_bias, a.state, a.state_indices,
-                       a.num_slots, a.o, a.T, a.Hk, a.Hv);
+                       a.num_slots, a.o, a.T, a.Hk, a.Hv, a.qk_l2norm);
     return hipGetLastError();
 }
 

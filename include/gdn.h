@@ -241,6 +241,44 @@ gdn_status gdn_recurrent_step_indexed(const void* q, const void* k, const void* 
                                       float* o, hipStream_t stream);
 
 /*
+ * gdn_chunk_fwd_ex, gdn_recurrent_step_ex -- the two calls with every option at once: raw gates,
+ * a state pool, and flags.
+ *
+ *   A_log, dt_bias   NULL: g and beta are the gates (gdn_chunk_fwd); both set: g and beta are the raw
+ *                    projections a and b and the gates are formed as in gdn_chunk_fwd_gating
+ *   state_indices    NULL: initial_state / final_state (chunk) or state (decode) are per sequence as
+ *                    in the plain calls; set: they are one pool [num_slots, Hv, dk, dv] addressed as in
+ *                    gdn_chunk_fwd_indexed (for the chunk call initial_state must equal final_state)
+ *   flags            0 or GDN_FLAG_QK_L2NORM: q and k are normalised to unit length per (token,
+ *                    q/k head) inside the kernels before the rule, q / sqrt(|q|^2 + 1e-6) and likewise
+ *                    for k, in fp32 (the pages feed q and k to the rule without stating their scale;
+ *                    the state correction along k is an exact partial overwrite only for unit keys)
+ * Everything else, and every check and status code, is that of the plain calls; an unknown flag bit,
+ * dt_bias without A_log, or a pool chunk call whose initial_state differs from final_state gives
+ * GDN_ERROR_INVALID_VALUE.  With flags == 0 the results equal those of the matching plain, gating or
+ * indexed call.
+ */
+#define GDN_FLAG_QK_L2NORM 1u
+gdn_status gdn_chunk_fwd_ex(const void* q, const void* k, const void* v,
+                            const void* g, const void* beta,
+                            const float* A_log, const float* dt_bias,
+                            const float* initial_state, float* final_state,
+                            const int32_t* state_indices, int num_slots,
+                            const int32_t* cu_seqlens,
+                            int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                            gdn_dtype qkv_dtype, gdn_dtype gate_dtype, unsigned flags,
+                            float* o,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 const float* A_log, const float* dt_bias,
+                                 float* state, const int32_t* state_indices, int num_slots,
+                                 int B, int T, int Hk, int Hv, int dk, int dv,
+                                 gdn_dtype qkv_dtype, gdn_dtype gate_dtype, unsigned flags,
+                                 float* o, hipStream_t stream);
+
+/*
  * gdn_gated_rmsnorm -- the layer's gated output norm, applied to the gated delta rule's output.
  *
  * The Qwen3.5 Gated DeltaNet page (wanger-sjtu.github.io, section "Output and gated RMSNorm", and

@@ -181,6 +181,46 @@ def test_indexed_calls_reject(lib, kw, status):
     assert rec_indexed(lib, **kw) == status
 
 
+def chunk_ex(lib, A_log=None, dt_bias=None, s0=None, fs=P, idx=None, num_slots=0, flags=0, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=None, B=1, T=64, Hk=1, Hv=1, dk=64, dv=64, N=1, qkv=F32,
+             gate=F32, o=P, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.gdn_chunk_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], A_log, dt_bias, s0, fs, idx,
+                                num_slots, a["cu"], a["B"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                                a["N"], a["qkv"], a["gate"], flags, a["o"], a["ws"],
+                                ctypes.c_size_t(a["ws_bytes"]), None)
+
+
+def rec_ex(lib, A_log=None, dt_bias=None, state=P, idx=None, num_slots=0, flags=0, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, B=1, T=1, Hk=1, Hv=1, dk=64, dv=64, qkv=F32, gate=F32, o=P)
+    a.update(kw)
+    return lib.gdn_recurrent_step_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], A_log, dt_bias, state,
+                                     idx, num_slots, a["B"], a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                                     a["qkv"], a["gate"], flags, a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=2), INVALID), (dict(flags=0x80000001), INVALID),     # unknown flag bits
+    (dict(dt_bias=P), INVALID),                                       # dt_bias without A_log
+    (dict(A_log=P), INVALID),                                         # A_log without dt_bias
+    (dict(A_log=P + 2, dt_bias=P), INVALID),
+    (dict(idx=P, num_slots=0, s0=P), INVALID), (dict(idx=P + 2, num_slots=4, s0=P), INVALID),
+    (dict(q=None, flags=1), INVALID), (dict(Hv=3, Hk=2, flags=1), INVALID),
+    (dict(dk=96, flags=1), UNSUPPORTED),
+])
+def test_ex_calls_reject(lib, kw, status):
+    # the option-taking calls check their options and everything the plain calls check
+    assert chunk_ex(lib, **kw) == status
+    rkw = {key: val for key, val in kw.items() if key != "s0"}
+    assert rec_ex(lib, **rkw) == status
+
+
+def test_ex_chunk_pool_must_be_both_states(lib):
+    # with state_indices the chunk call's initial and final state are one pool
+    assert chunk_ex(lib, idx=P, num_slots=4, s0=P, fs=P + 256) == INVALID
+    assert chunk_ex(lib, idx=P, num_slots=4, s0=None, fs=P) == INVALID
+
+
 def norm(lib, x=P, z=P, w=P, eps=1e-6, rows=8, d=128, zt=BF16, ot=BF16, out=P):
     return lib.gdn_gated_rmsnorm(x, z, w, eps, rows, d, zt, ot, out, None)
 
