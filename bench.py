@@ -83,7 +83,8 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from gated_deltanet_delta_amd import (gdn_causal_conv1d, gdn_chunk_fwd, gdn_chunk_fwd_gating,
+    from gated_deltanet_delta_amd import (gdn_causal_conv1d, gdn_chunk_fwd, gdn_chunk_fwd_ex,
+                                          gdn_chunk_fwd_gating,
                                           gdn_gated_rmsnorm,
                                           gdn_recurrent_step, gdn_recurrent_step_gating, synth,
                                           workspace_size)
@@ -175,6 +176,22 @@ def main() -> int:
     e1.record()
     torch.cuda.synchronize()
     ms_gating = e0.elapsed_time(e1) / args.steps
+
+    # and with q, k normalised to unit length in the kernels as well (every fused input step)
+    def prefill_gating_l2():
+        gdn_chunk_fwd_ex(d["q"], d["k"], d["v"], ga, gb, A_log=gA, dt_bias=gdt,
+                         initial_state=d["initial_state"], qk_l2norm=True, o=o, final_state=fs,
+                         workspace=ws)
+
+    for _ in range(args.warmup):
+        prefill_gating_l2()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        prefill_gating_l2()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_gating_l2 = e0.elapsed_time(e1) / args.steps
     achieved_gbs = scan_bytes / (ms_scan / 1e3) / 1e9
     useful_tflops = flops / (ms_events / 1e3) / 1e12
 
@@ -302,6 +319,10 @@ def main() -> int:
         "prefill_gating": {"call": "gdn_chunk_fwd_gating (gates formed in the kernels from a, b)",
                            "ms_per_call_events": round(ms_gating, 5),
                            "tokens_per_s": round(tokens / (ms_gating / 1e3), 1)},
+        "prefill_gating_l2norm": {"call": "gdn_chunk_fwd_ex (gates from a, b and q, k L2-normalised, "
+                                          "both in the kernels)",
+                                  "ms_per_call_events": round(ms_gating_l2, 5),
+                                  "tokens_per_s": round(tokens / (ms_gating_l2 / 1e3), 1)},
         "causal_conv1d": {"call": "gdn_causal_conv1d, QKV mixture of the prefill (bf16, W = 4, SiLU, cache)",
                           "tokens": T, "channels": Cc, "width": Wc,
                           "ms_per_call_events": round(ms_conv, 5),

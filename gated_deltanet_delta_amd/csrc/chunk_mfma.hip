@@ -54,7 +54,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;      // chunk length
-constexpr int kGRows = 4;   // rows of a chunk's gate block (of kC floats each)
+constexpr int kGRows = 5;   // rows of a chunk's gate block (of kC floats each)
 constexpr int kDK = 128;    // key dimension handled by this file
 constexpr int kThreads = 256;
 
@@ -242,17 +242,17 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
 // ------------------------------------------------------------------------------------------------
 // chunk_solve_kernel: one workgroup per (chunk slot, q/k head), for each of the head's v-heads.
 //
-// Writes, per (chunk, v-head), the chunk's gate block [4][64] floats: G2 = running sum of
+// Writes, per (chunk, v-head), the chunk's gate block [5][64] floats: G2 = running sum of
 // g log2(e), 2^G2, 2^(G2_C - G2) (G2_C = G2 at the chunk's last row; padding rows past the
-// chunk's length have g = 0) and, with L2, the key scales r_t = 1 / |k_t| (row 3; row 2 then holds
-// r 2^(G2_C - G2)); and M = T diag(beta) as the 12 fragments described above (zero above the
-// diagonal and in rows/columns past the chunk's length).  Per (chunk, q/k head) it writes
+// chunk's length have g = 0) and, with L2, the key and query scales r_t = 1 / |k_t| and
+// rq_t = 1 / |q_t| (rows 3 and 4); and M = T diag(beta) as the 12 fragments described above (zero
+// above the diagonal and in rows/columns past the chunk's length).  Per (chunk, q/k head) it writes
 // N = K K_p^T for the scan kernel's K S recurrence.
 //
 // L2 (q and k normalised to unit length): the normalised keys are diag(r) K, so the chunk's
 // K K^T becomes diag(r) K K^T diag(r) (applied to the product tiles in fp32), and every later use of
-// a normalised key is a per-token factor on the scan kernel's fp32 side; K itself stays the exact
-// bf16 input.
+// a normalised key or query is a per-token factor on the scan kernel's fp32 side; K and Q
+// themselves stay the exact bf16 inputs.
 //
 // K enters the matrix cores straight from memory (its rows are both operands of K K^T), and
 // K K^T is formed once for all v-heads of the q/k head.  A and T live in shared memory as their
@@ -264,15 +264,14 @@ __device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }
 // workgroups are resident at once)
 template <typename TG, bool L2>
 __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
-    const __bf16* __restrict__ k, const TG* __restrict__ g, const TG* __restrict__ beta,
-    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const TG* __restrict__ g,
+    const TG* __restrict__ beta, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start, int N, int T,
     int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M,
     __bf16* __restrict__ ws_N) {
     __shared__ float sA[10][16 * kBP];     // blocks (a, b), a > b, of A
     __shared__ float sT[10][16 * kBP];     // blocks (a, b), a >= b, of T = (I + A)^-1
     __shared__ float sB[kC];
-    __shared__ float sRk[kC];              // (L2) 1 / |k_t|
 
     const int slot = blockIdx.x, kh = blockIdx.y;
     ChunkLoc loc;
@@ -346,26 +345,40 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         }
     }
 
-    if constexpr (L2) {
-        // r_t = 1 / sqrt(|k_t|^2 + eps) for token tile `wave`: |k_t|^2 is the diagonal of its tile
-        // (w, w) of K K^T, held by lane (g, c) with c / 4 == g as element c % 4.  Then
-        // K K^T -> diag(r) K K^T diag(r).
-        if ((c >> 2) == gq) {
-            const int r = c & 3;
-            const float d = r == 0 ? kd[0] : (r == 1 ? kd[1] : (r == 2 ? kd[2] : kd[3]));
-            sRk[16 * wave + c] = 1.f / sqrtf(d + kL2Eps);
-        }
-        lds_barrier();
-        auto scale_tile = [&](f32x4& acc, int ta, int tb) {
-            const float rj = sRk[16 * tb + c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= sRk[16 * ta + 4 * gq + r] * rj;
-        };
-        scale_tile(kd, wave, wave);
-        scale_tile(kx, xa, xb);
-        if (wave & 1) scale_tile(ky, ya, yb);
-    }
 
+    if constexpr (L2) {
+        // r_t = 1 / sqrt(|k_t|^2 + eps) for the rows of the wave's K tiles (lane (g, c) holds 32 of
+        // row 16 tt + c's keys; the sum over g leaves every lane with its column's r), then
+        // K K^T -> diag(r) K K^T diag(r) tile by tile: a tile's column factor is the lane's own, its
+        // row factors come from lanes 4 g + r.  Each wave writes r of its own tile `wave` to the gate
+        // blocks of every v-head.
+        auto rnorm = [&](const bf16x8* kf) {
+            float ss = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = (float)kf[kb][e];
+                    ss += x * x;
+                }
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            return 1.f / sqrtf(ss + kL2Eps);
+        };
+        const float r0 = rnorm(k0), r1 = rnorm(k1), r2 = (wave & 1) ? rnorm(k2) : 1.f;
+        auto scale_tile = [&](f32x4& acc, float rrow, float rcol) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= __shfl(rrow, 4 * gq + r) * rcol;
+        };
+        scale_tile(kd, r0, r0);
+        if (wave == 3) scale_tile(kx, r0, r1);       // (3, 0): rows k0, columns k1
+        else scale_tile(kx, r1, r0);                 // (w + 1, w)
+        if (wave == 1) scale_tile(ky, r1, r2);       // (2, 0)
+        if (wave == 3) scale_tile(ky, r0, r2);       // (3, 1)
+        if (gq == 0)
+            for (int qh = 0; qh < Gq; ++qh)
+                ws_G[((size_t)slot * Hv + kh * Gq + qh) * kGRows * kC + 3 * kC + 16 * wave + c] = r0;
+    }
     // the gates of the first kPre v-heads are loaded together with K (one memory round trip)
     constexpr int kPre = 4;
     float gpre[kPre], bpre[kPre];
@@ -405,13 +418,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
             const float G2c = __shfl(G2, 63);
             ws_G[ws_row + lane] = G2;
             ws_G[ws_row + kC + lane] = exp2_fast(G2);
-            const float dec = exp2_fast(G2c - G2);
-            if constexpr (L2) {
-                ws_G[ws_row + 2 * kC + lane] = sRk[lane] * dec;
-                ws_G[ws_row + 3 * kC + lane] = sRk[lane];
-            } else {
-                ws_G[ws_row + 2 * kC + lane] = dec;
-            }
+            ws_G[ws_row + 2 * kC + lane] = exp2_fast(G2c - G2);
             sB[lane] = bt;
         }
         // A = diag(beta) (K K^T o Gam), strictly lower, tile by tile
@@ -500,6 +507,30 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         }
         lds_barrier();                 // sT and sB are rewritten for the next v-head
     }
+    if constexpr (L2) {
+        // rq_t = 1 / sqrt(|q_t|^2 + eps) for token tile `wave` (lane (g, c): 32 of row 16 wave + c's
+        // keys), into every v-head's gate block; read last, when the solve's registers are free
+        const int qrow = min(16 * wave + c, L - 1);
+        const __bf16* qr = q + ((tok0 + qrow) * Hk + kh) * kDK + 8 * gq;
+        bf16x8 qf[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qf[kb] = *reinterpret_cast<const bf16x8*>(qr + 32 * kb);
+        float ss = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = (float)qf[kb][e];
+                ss += x * x;
+            }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        if (gq == 0) {
+            const float rq = 1.f / sqrtf(ss + kL2Eps);
+            for (int qh = 0; qh < Gq; ++qh)
+                ws_G[((size_t)slot * Hv + kh * Gq + qh) * kGRows * kC + 4 * kC + 16 * wave + c] = rq;
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -528,11 +559,10 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
 //   staging wave (5) copies each chunk's K rows, V columns and gate block straight from memory into
 //                    a five-chunk LDS ring (global_load_lds), three chunks ahead of the chain.
 //
-// L2 (q and k normalised to unit length, r = 1 / |k|, rq = 1 / |q| per token): the kernel keeps the
-// exact bf16 K and Q and applies the scales on the fp32 side.  D carries r already (the solve's
-// gate block row 2), so S <- e^(G_C) S + K^T D and N_s D_{s-1} need nothing more; the e^G factors
-// of Y and X take r_s; P's entries take r of their key token; the output takes rq, formed by the
-// output waves from the Q rows they load.
+// L2 (q and k normalised to unit length, r = 1 / |k|, rq = 1 / |q| per token, from the solve's gate
+// block): the kernel keeps the exact bf16 K and Q and applies the scales on the fp32 side.  The
+// chain hands out diag(r) U in place of U, which is what the normalised keys' K^T D, N_s D_{s-1} and
+// P U need; the e^G factors of Y and X take r_s; the output rows take rq.
 //
 // Waves w and w + 4 share a SIMD: the chain with state half 1, state half 0 with the staging
 // wave; the output waves have one each.  The state waves run at a higher priority than the chain:
@@ -561,13 +591,14 @@ constexpr int kRing = 5;         // chunks in the staging ring
 // rows, one chunk each) and a transposed fragment (4 consecutive rows x 4 consecutive chunks).
 constexpr int kKR = 160;
 constexpr int kKDma = kC * kKR * 2 / 1024;   // 1 KiB copy instructions per K slot (20)
-constexpr int kDmaOps = kKDma + 2 + 1;      // per chunk: K, V (2 KiB), gate block (768 bytes)
+// copy instructions per chunk: K, V (2 KiB), gate block (768 bytes; with L2 1 KiB + 256 bytes)
+constexpr int kDmaOps = kKDma + 2 + 1;
 __host__ __device__ constexpr int kswz(int t) { return (t >> 2) & 3; }
 
 struct ScanLds {
     __bf16 Kr[kRing][kC * kKR];                // K rows [token][key]
     __bf16 Vr[kRing][kC * kWS];                // V [token][this slice's 16 columns]
-    float Gt[kRing][kGRows * kC];              // gate block: G2, 2^G2, (r) 2^(G2_C - G2), (r)
+    float Gt[kRing][kGRows * kC];              // gate block: G2, 2^G2, 2^(G2_C - G2), (r, rq)
     __bf16 St[2][2][kWS * kSP];                // S^T at chunk start [buffer][hi, lo]
     f32x4 Ut[2][4][64];                        // U [buffer][token tile][lane], the chain's tiles
     f32x4 Yt[2][2][4][64];                     // Y in two parts [buffer][key half][tile][lane]
@@ -678,12 +709,15 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             const float* gt = sm.Gt[s % kRing];
             lds_u8* yl = lds_at(&sm.Yt[s & 1][0][0][lane]);
             lds_u8* gl = lds_at(gt + kC + 4 * g);                    // 2^G2 at rows 16 a + 4 g + r
-            f32x4 y[4], eg[4];
+            f32x4 y[4], eg[4], rk[4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 y[a] = ld<f32x4>(yl, 16 * 64 * a) + ld<f32x4>(yl, 16 * 64 * (4 + a));
                 eg[a] = ld<f32x4>(gl, 4 * 16 * a);
-                if constexpr (L2) eg[a] *= ld<f32x4>(gl, 4 * 16 * a + 4 * 2 * kC);      // r_s
+                if constexpr (L2) {
+                    rk[a] = ld<f32x4>(gl, 4 * 16 * a + 4 * 2 * kC);                     // r_s
+                    eg[a] *= rk[a];
+                }
             }
             f32x4 x[4];
             if constexpr (kFirst) {
@@ -727,6 +761,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 u[a] = mma(mf[2 * p], xh[j], u[a]);
                 u[a] = mma(mf[2 * p], xl[j], u[a]);
                 u[a] = mma(mf[2 * p + 1], xh[j], u[a]);
+            }
+            if constexpr (L2) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) u[a] *= rk[a];         // diag(r) U
             }
             __builtin_amdgcn_sched_barrier(0);
             // unconditional (the last chunk refetches itself): a conditional fetch makes the
@@ -897,11 +935,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 // S^T (hi, lo), U^T (hi, lo) and the gate values of this wave's rows
                 lds_u8* kfl = lds_at(kr + l_kf);
                 lds_u8* gl = lds_at(gt + 4 * g);
-                float gq[2], eq[2];
+                float gq[2], eq[2], rq[2];
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     gq[x] = gt[16 * tiles[x] + c];
                     eq[x] = gt[kC + 16 * tiles[x] + c];
+                    if constexpr (L2) rq[x] = gt[4 * kC + 16 * tiles[x] + c];
                 }
                 bf16x8 sf[2][4], uf[2][2];
 #pragma unroll
@@ -936,12 +975,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
                         for (int kb = 0; kb < 4; ++kb) pt[b] = mma(kf[b][kb], cur.q[x][kb], pt[b]);
                         const f32x4 gp = ld<f32x4>(gl, 4 * 16 * b);
-                        f32x4 rk = {1.f, 1.f, 1.f, 1.f};
-                        if constexpr (L2) rk = ld<f32x4>(gl, 4 * 16 * b + 4 * 3 * kC);   // r of key tp
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int tp = 16 * b + 4 * g + r;
-                            pt[b][r] = tp <= t ? pt[b][r] * exp2_fast(gq[x] - gp[r]) * rk[r] : 0.f;
+                            pt[b][r] = tp <= t ? pt[b][r] * exp2_fast(gq[x] - gp[r]) : 0.f;
                         }
                     }
                     // B fragments for P U: reduction rows 32 kb + 4 g + e (e < 4), + 16 (e >= 4)
@@ -962,20 +999,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                         acc = mma(uf[0][kb], pl[kb], acc);
                         acc = mma(uf[1][kb], ph[kb], acc);
                     }
-                    if constexpr (L2) {
-                        // rq = 1 / sqrt(|q_t|^2 + eps): lane (g, c) holds 32 of row t's keys
-                        float ss = 0.f;
-#pragma unroll
-                        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const float qv = (float)cur.q[x][kb][e];
-                                ss += qv * qv;
-                            }
-                        ss += __shfl_xor(ss, 16);
-                        ss += __shfl_xor(ss, 32);
-                        acc *= 1.f / sqrtf(ss + kL2Eps);
-                    }
+                    if constexpr (L2) acc *= rq[x];
                     ot[x] = acc;
                 }
                 const size_t tok0 = tok0_of(ci);
@@ -1028,7 +1052,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 copy_to_lds(vb + (size_t)min(32 * jj + (lane >> 1), L - 1) * Hv * DV + 8 * (lane & 1),
                             sm.Vr[slot] + 512 * jj);
             const float* gb = ws_G + ((size_t)(slot0 + ci) * Hv + h) * kGRows * kC;
-            copy_to_lds(gb + 4 * min(lane, L2 ? 63 : 47), sm.Gt[slot]);     // (row 3 only with L2)
+            if constexpr (L2) {
+                copy_to_lds(gb + 4 * lane, sm.Gt[slot]);                  // rows 0-3
+                if (lane < 16) copy_to_lds(gb + 4 * kC + 4 * lane, sm.Gt[slot] + 4 * kC);   // row 4
+            } else {
+                copy_to_lds(gb + 4 * min(lane, 47), sm.Gt[slot]);         // rows 0-2
+            }
         };
         dma(0);
         if (nchunks > 1) dma(1);
@@ -1041,7 +1070,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             // the step ends
             if (s + 3 < nchunks) {
                 dma(s + 3);
-                wait_vmcnt<kDmaOps>();
+                wait_vmcnt<kDmaOps + (L2 ? 1 : 0)>();
             } else {
                 wait_vmcnt<0>();
             }
@@ -1095,7 +1124,8 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
     }
     if ((stages & kStagePrepare) && slots > 0) {
         hipLaunchKernelGGL((chunk_solve_kernel<TG, L2>), dim3((unsigned)slots, (unsigned)a.Hk),
-                           dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.k),
+                           dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.q),
+                           static_cast<const __bf16*>(a.k),
                            static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta), a.A_log,
                            a.dt_bias, a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M,
                            ws_N);
