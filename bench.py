@@ -81,8 +81,11 @@ def main() -> int:
         return 2
 
     import numpy as np
+    import ctypes
+
     import torch
 
+    from gated_deltanet_delta_amd import _lib
     from gated_deltanet_delta_amd import (gdn_causal_conv1d, gdn_chunk_fwd, gdn_chunk_fwd_ex,
                                           gdn_chunk_fwd_gating,
                                           gdn_gated_rmsnorm,
@@ -195,21 +198,38 @@ def main() -> int:
     achieved_gbs = scan_bytes / (ms_scan / 1e3) / 1e9
     useful_tflops = flops / (ms_events / 1e3) / 1e12
 
+    clib = _lib.load()
+
+    def time_c(fn, arg_sets):
+        """ms per call of a C entry point over args.steps back-to-back calls (after the warm-up),
+        cycling through the argument sets: three sets of buffers are larger than the GPU's 256 MB
+        last-level cache, so every call reads and writes HBM rather than the previous call's lines."""
+        for i in range(args.warmup):
+            if fn(*arg_sets[i % len(arg_sets)]) != 0:
+                raise RuntimeError(f"{fn.__name__} failed")
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            fn(*arg_sets[i % len(arg_sets)])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
     # ---------------- the gated output norm on the prefill's o ---------------------------------
     # (z drawn here with its own seed: the workloads do not define the z branch)
     zr = torch.from_numpy(np.random.default_rng(99).standard_normal(tuple(o.shape), dtype=np.float32))
     zn = zr.to(torch.bfloat16).to(dev)
     wn = torch.ones(wl.dv, dtype=torch.float32, device=dev)
     yn = torch.empty(tuple(o.shape), dtype=torch.bfloat16, device=dev)
-    for _ in range(args.warmup):
-        gdn_gated_rmsnorm(o, zn, wn, 1e-6, out=yn)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        gdn_gated_rmsnorm(o, zn, wn, 1e-6, out=yn)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_norm = e0.elapsed_time(e1) / args.steps
+    norm_sets = [(o, zn, yn)] + [(o.clone(), zn.clone(), torch.empty_like(yn)) for _ in range(2)]
+    # One call through the binding checks the arguments; the timed calls go to the C entry point with
+    # the arguments marshalled once, so that a kernel of a few tens of microseconds is not paced by
+    # the binding's host-side work.
+    gdn_gated_rmsnorm(o, zn, wn, 1e-6, out=yn)
+    cstream = torch.cuda.current_stream().cuda_stream
+    norm_args = [(ox.data_ptr(), zx.data_ptr(), wn.data_ptr(), ctypes.c_float(1e-6), o.numel() // wl.dv,
+                  wl.dv, _lib.GDN_BF16, _lib.GDN_BF16, yx.data_ptr(), cstream) for ox, zx, yx in norm_sets]
+    ms_norm = time_c(clib.gdn_gated_rmsnorm, norm_args)
     norm_bytes = o.numel() * (4 + 2 + 2) + wl.dv * 4
 
     # ---------------- the causal conv1d of the QKV mixture (2 Hk dk + Hv dv channels) -----------
@@ -220,15 +240,11 @@ def main() -> int:
     wc = torch.from_numpy((0.5 * crng.standard_normal((Cc, Wc))).astype(np.float32)).to(dev)
     sc = torch.zeros((1, Wc - 1, Cc), dtype=wl.dtype, device=dev)
     yc = torch.empty_like(xc)
-    for _ in range(args.warmup):
-        gdn_causal_conv1d(xc, wc, None, sc, silu=True, y=yc)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        gdn_causal_conv1d(xc, wc, None, sc, silu=True, y=yc)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_conv = e0.elapsed_time(e1) / args.steps
+    gdn_causal_conv1d(xc, wc, None, sc, silu=True, y=yc)
+    conv_sets = [(xc, yc)] + [(xc.clone(), torch.empty_like(yc)) for _ in range(2)]
+    conv_args = [(xx.data_ptr(), wc.data_ptr(), None, sc.data_ptr(), None, 0, None, 1, T, Cc, Wc, 1,
+                  _lib.GDN_BF16, 1, yx.data_ptr(), cstream) for xx, yx in conv_sets]
+    ms_conv = time_c(clib.gdn_causal_conv1d, conv_args)
     conv_bytes = 2 * xc.numel() * xc.element_size() + Cc * Wc * 4 + 2 * sc.numel() * sc.element_size()
 
     # ---------------- decode ------------------------------------------------------------------
