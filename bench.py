@@ -42,8 +42,10 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
 # reads on a plain copy of known size (profiles/); None whenever the kernel changed since.
-TRAFFIC_SCAN = None
-TRAFFIC_DECODE = 1085246157    # recurrent_kernel<128,128,bf16,f32>, one decode step, B=256
+TRAFFIC_SCAN = 180236148      # chunk_scan_kernel<128>, prefill B=1 T=4096
+TRAFFIC_DECODE = 1085280816    # recurrent_kernel<128,128,bf16,f32>, one decode step, B=256
+TRAFFIC_CONV = 134710246       # causal_conv1d_kernel<4,8,bf16>, T=4096, C=8192
+TRAFFIC_NORM = 134250675       # gated_rmsnorm_kernel<128,bf16,bf16>, 4096 x 32 rows
 
 
 def prefill_algorithmic(wl, T: int, B: int, N: int, init_state: bool):
@@ -345,6 +347,7 @@ def main() -> int:
                           "roofline": {"bound": "hbm", "achieved": round(conv_bytes / (ms_conv / 1e3) / 1e9, 1),
                                        "peak": MI355X_HBM_GBS, "unit": "GB/s",
                                        "frac": round(conv_bytes / (ms_conv / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
+                                       "traffic": TRAFFIC_CONV,
                                        "algorithmic_bytes_per_launch": int(conv_bytes)}},
         "gated_rmsnorm": {"call": "gdn_gated_rmsnorm on the prefill's o (fp32 in, bf16 z and out)",
                           "rows": o.numel() // wl.dv, "d": wl.dv,
@@ -352,6 +355,7 @@ def main() -> int:
                           "roofline": {"bound": "hbm", "achieved": round(norm_bytes / (ms_norm / 1e3) / 1e9, 1),
                                        "peak": MI355X_HBM_GBS, "unit": "GB/s",
                                        "frac": round(norm_bytes / (ms_norm / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
+                                       "traffic": TRAFFIC_NORM,
                                        "algorithmic_bytes_per_launch": int(norm_bytes)}},
         "cpu_baseline": cpu,
         "decode": {"metric": "decode state GB/s", "value": round(state_gbs, 1), "unit": "GB/s",
