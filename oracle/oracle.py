@@ -20,6 +20,8 @@ Contents
 ``causal_conv1d``  the depthwise causal convolution the QKV mixture passes through before the rule
              (the Qwen3.5 page's flowchart node "conv1d, Depthwise Causal Conv" and its
              conv_states cache), per sequence, carrying the last inputs in fp64 numpy.
+``backward`` the gradients of ``forward`` (reverse-mode over its token steps, fp64, in
+             ``gdn_oracle.c``), for the training direction of the chunked call.
 ``l2norm``   the optional normalisation of each q and k head vector to unit length before the rule
              (a reading: the pages do not state how q and k are scaled), in fp64 numpy.
 ``chunked``  the chunk-parallel (WY/UT) form of the same rule in fp64 numpy.  It is not the
@@ -68,6 +70,12 @@ class Oracle:
             ctypes.c_int, ctypes.POINTER(ctypes.c_ubyte), ctypes.c_int, dp, dp,
         ]
         lib.gdn_oracle_default_threads.restype = ctypes.c_int
+        lib.gdn_oracle_backward.restype = ctypes.c_int
+        lib.gdn_oracle_backward.argtypes = [
+            dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, dp, dp, ctypes.c_int, dp, dp, dp, dp, dp, dp,
+        ]
         self._lib = lib
 
     def default_threads(self) -> int:
@@ -119,6 +127,53 @@ class Oracle:
         return o, fs
 
 
+    def backward(
+        self,
+        q: np.ndarray,
+        k: np.ndarray,
+        v: np.ndarray,
+        g: np.ndarray,
+        beta: np.ndarray,
+        d_o: np.ndarray,
+        initial_state: Optional[np.ndarray] = None,
+        d_final: Optional[np.ndarray] = None,
+        cu_seqlens: Optional[np.ndarray] = None,
+        threads: int = 0,
+    ) -> Tuple[np.ndarray, ...]:
+        """Gradients (dq, dk, dv, dg, dbeta, d_initial_state) in fp64 of a scalar loss whose
+        gradients with respect to the outputs are ``d_o`` [B,T,Hv,dv] and ``d_final``
+        [N,Hv,dk,dv] (None: zero): reverse-mode differentiation of ``forward``'s token steps
+        (``gdn_oracle_backward`` in ``gdn_oracle.c``)."""
+        B, T, Hk, dk = q.shape
+        Hv, dv = v.shape[2], v.shape[3]
+        if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) or beta.shape != g.shape:
+            raise ValueError("inconsistent shapes")
+        if d_o.shape != v.shape:
+            raise ValueError("d_o shape")
+        N = B if cu_seqlens is None else len(cu_seqlens) - 1
+        arrs = [np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, g, beta)]
+        s0 = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float64)
+        df = None if d_final is None else np.ascontiguousarray(d_final, dtype=np.float64)
+        for x, what in ((s0, "initial_state"), (df, "d_final")):
+            if x is not None and x.shape != (N, Hv, dk, dv):
+                raise ValueError(what + " shape")
+        do = np.ascontiguousarray(d_o, dtype=np.float64)
+        cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        outs = [np.full(a.shape, np.nan) for a in arrs] + [np.full((N, Hv, dk, dv), np.nan)]
+        dp = ctypes.POINTER(ctypes.c_double)
+        ptr = lambda a: a.ctypes.data_as(dp)  # noqa: E731
+        rc = self._lib.gdn_oracle_backward(
+            *(ptr(a) for a in arrs),
+            None if s0 is None else ptr(s0),
+            None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            B, T, Hk, Hv, dk, dv, N, ptr(do), None if df is None else ptr(df), int(threads),
+            *(ptr(a) for a in outs),
+        )
+        if rc != 0:
+            raise ValueError(f"gdn_oracle_backward returned {rc}")
+        return tuple(outs)
+
+
 _default: Optional[Oracle] = None
 
 
@@ -132,6 +187,11 @@ def _oracle() -> Oracle:
 def forward(*args, **kwargs) -> Tuple[np.ndarray, np.ndarray]:
     """Token-by-token fp64 gated delta rule; see ``Oracle.forward``."""
     return _oracle().forward(*args, **kwargs)
+
+
+def backward(*args, **kwargs) -> Tuple[np.ndarray, ...]:
+    """Gradients of the token-by-token rule; see ``Oracle.backward``."""
+    return _oracle().backward(*args, **kwargs)
 
 
 def default_threads() -> int:

@@ -425,6 +425,76 @@ def test_l2norm_makes_the_correction_an_overwrite(orc):
 
 
 # ----------------------------------------------------------------------------------------------
+# backward pass
+
+def _fd_case(rng, lens, Hk, Hv, dk, dv, with_state):
+    T = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = len(lens)
+    k = rng.standard_normal((1, T, Hk, dk))
+    k = 0.9 * k / np.linalg.norm(k, axis=-1, keepdims=True)
+    x = dict(q=rng.standard_normal((1, T, Hk, dk)), k=k, v=rng.standard_normal((1, T, Hv, dv)),
+             g=-rng.uniform(0.01, 0.5, (1, T, Hv)), beta=rng.uniform(0.1, 0.9, (1, T, Hv)),
+             s0=rng.standard_normal((N, Hv, dk, dv)) if with_state else None)
+    return x, cu
+
+
+def pin_backward_fd(orc, lens=(5, 0, 70), with_state=True, with_dfinal=True):
+    """Every gradient element equals the central difference of L = <w_o, o> + <w_S, S_T> computed with
+    the forward oracle (h = 1e-5, error O(h^2)): packed sequences (an empty one, one longer than the
+    backward's 64-token recompute pieces), two v-heads sharing a q/k head (dq, dk sum over both)."""
+    rng = np.random.default_rng(20 + len(lens))
+    Hk, Hv, dk, dv = 1, 2, 3, 2
+    x, cu = _fd_case(rng, lens, Hk, Hv, dk, dv, with_state)
+    wo = rng.standard_normal((1, int(sum(lens)), Hv, dv))
+    ws = rng.standard_normal((len(lens), Hv, dk, dv)) if with_dfinal else None
+
+    def loss(xx):
+        o, fs = orc.forward(xx["q"], xx["k"], xx["v"], xx["g"], xx["beta"], xx["s0"], cu)
+        return float(np.sum(wo * o) + (np.sum(ws * fs) if ws is not None else 0.0))
+
+    grads = dict(zip(("q", "k", "v", "g", "beta", "s0"),
+                     orc.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], wo, x["s0"], ws, cu)))
+    h = 1e-5
+    for name in ("q", "k", "v", "g", "beta", "s0"):
+        if x[name] is None:
+            continue
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {key: (val.copy() if val is not None else None) for key, val in x.items()}
+            xm = {key: (val.copy() if val is not None else None) for key, val in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        assert np.allclose(grads[name], fd, rtol=1e-6, atol=1e-8), (name, np.max(np.abs(grads[name] - fd)))
+
+
+@pytest.mark.parametrize("lens,with_state,with_dfinal", [((5, 0, 70), True, True), ((12,), False, False)])
+def test_backward_matches_finite_differences(orc, lens, with_state, with_dfinal):
+    pin_backward_fd(orc, lens, with_state, with_dfinal)
+
+
+def test_backward_without_writes_is_a_pure_decay(orc):
+    """beta = 0: nothing is written, so k and v get no gradient at all and S_t = e^{G_t} S0, whence
+    dq_t = e^{G_t} S0 do_t and dS0 = sum_t e^{G_t} q_t do_t^T (one sequence, one head)."""
+    rng = np.random.default_rng(27)
+    T, dk, dv = 9, 3, 4
+    q, k = rng.standard_normal((1, T, 1, dk)), rng.standard_normal((1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, dv))
+    g = -rng.uniform(0.0, 0.7, (1, T, 1))
+    beta = np.zeros((1, T, 1))
+    s0 = rng.standard_normal((1, 1, dk, dv))
+    do = rng.standard_normal((1, T, 1, dv))
+    dq, dkk, dvv, dg, db, ds0 = orc.backward(q, k, v, g, beta, do, s0)
+    assert np.all(dkk == 0.0) and np.all(dvv == 0.0)
+    G = np.cumsum(g[0, :, 0])
+    for t in range(T):
+        assert np.allclose(dq[0, t, 0], np.exp(G[t]) * s0[0, 0] @ do[0, t, 0], rtol=1e-13)
+    want = sum(np.exp(G[t]) * np.outer(q[0, t, 0], do[0, t, 0]) for t in range(T))
+    assert np.allclose(ds0[0, 0], want, rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------------------------
 # sampling and threading do not change results
 
 def test_unit_mask_and_threads(orc):
@@ -468,6 +538,34 @@ MUTANTS = {
     "drop_last_token": ("const int t1 = cu_seqlens ? cu_seqlens[n + 1] : T;",
                         "const int t1 = cu_seqlens ? cu_seqlens[n + 1] : T - 1;"),
 }
+
+
+BACKWARD_MUTANTS = {
+    "bw_drop_predict_term": ("dkt[i] += st * dp[j];", ";"),
+    "bw_dg_sign": ("dgt += st * dS[e];", "dgt -= st * dS[e];"),
+    "bw_undecayed_D": ("for (size_t e = 0; e < SS; ++e) D[e] = a * dS[e];",
+                       "for (size_t e = 0; e < SS; ++e) D[e] = dS[e];"),
+    "bw_dbeta_from_v": ("db += du[j] * pv[j];", "db += du[j] * vt[j];"),
+    "bw_dq_from_previous_state": ("dqt[i] += St[(size_t)i * dv + j] * dot[j];",
+                                  "dqt[i] += Sp[(size_t)i * dv + j] * dot[j];"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_pin_catches_planted_mistakes(tmp_path, name):
+    """The finite-difference pin fails for each typical slip planted in the backward pass (the
+    mutant's forward is untouched, so its differences are still the true gradients)."""
+    src = open(O.SOURCE).read()
+    find, repl = BACKWARD_MUTANTS[name]
+    assert src.count(find) == 1, f"mutation site for {name} no longer in the oracle source"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(find, repl))
+    lib = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-std=c99", str(path), "-o", lib, "-lm"],
+                   check=True)
+    with pytest.raises(AssertionError):
+        pin_backward_fd(O.Oracle(lib))
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
