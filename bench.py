@@ -89,7 +89,7 @@ def main() -> int:
 
     from gated_deltanet_delta_amd import _lib
     from gated_deltanet_delta_amd import (gdn_causal_conv1d, gdn_chunk_fwd, gdn_chunk_fwd_ex,
-                                          gdn_chunk_fwd_gating,
+                                          gdn_chunk_bwd, gdn_chunk_fwd_gating,
                                           gdn_gated_rmsnorm,
                                           gdn_recurrent_step, gdn_recurrent_step_gating, synth,
                                           workspace_size)
@@ -249,6 +249,25 @@ def main() -> int:
     ms_conv = time_c(clib.gdn_causal_conv1d, conv_args)
     conv_bytes = 2 * xc.numel() * xc.element_size() + Cc * Wc * 4 + 2 * sc.numel() * sc.element_size()
 
+    # ---------------- the backward pass of the prefill (training) -------------------------------
+    # (the loss gradients d_o, d_final drawn here with their own seed)
+    brng = np.random.default_rng(97)
+    d_o = torch.from_numpy(brng.standard_normal(tuple(o.shape), dtype=np.float32)).to(dev)
+    d_fin = torch.from_numpy(brng.standard_normal(tuple(fs.shape), dtype=np.float32)).to(dev)
+    bws = torch.empty(int(clib.gdn_chunk_bwd_workspace_size(1, T, wl.Hk, wl.Hv, wl.dk, wl.dv, 1)),
+                      dtype=torch.uint8, device=dev)
+    bwd_calls = max(3, args.steps // 20)
+    for _ in range(2):
+        gdn_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, d["initial_state"], d_fin, workspace=bws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(bwd_calls):
+        gdn_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, d["initial_state"], d_fin, workspace=bws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_bwd = e0.elapsed_time(e1) / bwd_calls
+    del bws
+
     # ---------------- decode ------------------------------------------------------------------
     wd = synth.WORKLOADS["decode"]
     x0 = synth.make(wd)
@@ -357,6 +376,10 @@ def main() -> int:
                                        "frac": round(norm_bytes / (ms_norm / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
                                        "traffic": TRAFFIC_NORM,
                                        "algorithmic_bytes_per_launch": int(norm_bytes)}},
+        "backward": {"call": "gdn_chunk_bwd (dq, dk, dv, dg, dbeta, d_initial of the prefill; fp32 "
+                             "vector arithmetic, first implementation)",
+                     "calls": bwd_calls, "ms_per_call_events": round(ms_bwd, 4),
+                     "tokens_per_s": round(tokens / (ms_bwd / 1e3), 1)},
         "cpu_baseline": cpu,
         "decode": {"metric": "decode state GB/s", "value": round(state_gbs, 1), "unit": "GB/s",
                    "workload": f"decode B={wd.B} Hk={wd.Hk} Hv={wd.Hv} dk=dv={wd.dk}, {nd} one-token "

@@ -393,6 +393,57 @@ def gdn_recurrent_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: 
     return o, state
 
 
+def gdn_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, d_o: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                  d_final: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+                  need_d_initial: bool = True,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, ...]:
+    """Backward pass of gdn_chunk_fwd: (dq, dk, dv, dg, dbeta, d_initial_state) in fp32 from the
+    gradients d_o [B,T,Hv,dv] and d_final [N,Hv,dk,dv] (None: zero) of the outputs.  d_initial_state
+    is None when need_d_initial is False."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_chunk_bwd runs on a GPU; tensors must be on a cuda device")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(g, (B, T, Hv), "g", dev)
+    _check(beta, (B, T, Hv), "beta", dev, g.dtype)
+    _check(d_o, (B, T, Hv, dv), "d_o", dev, torch.float32)
+    if initial_state is not None:
+        _check(initial_state, (N, Hv, dk, dv), "initial_state", dev, torch.float32)
+    if d_final is not None:
+        _check(d_final, (N, Hv, dk, dv), "d_final", dev, torch.float32)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, Hk, dk), **f32)
+    dk_ = torch.empty((B, T, Hk, dk), **f32)
+    dv_ = torch.zeros((B, T, Hv, dv), **f32)
+    dg = torch.empty((B, T, Hv), **f32)
+    db = torch.empty((B, T, Hv), **f32)
+    ds0 = torch.empty((N, Hv, dk, dv), **f32) if need_d_initial else None
+    ws_bytes = int(lib.gdn_chunk_bwd_workspace_size(B, T, Hk, Hv, dk, dv, N))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    st = lib.gdn_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_o),
+        _ptr(d_final), B, T, Hk, Hv, dk, dv, N, _code(q, "q"), _code(g, "g"), _ptr(dq), _ptr(dk_), _ptr(dv_),
+        _ptr(dg), _ptr(db), _ptr(ds0), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_chunk_bwd")
+    return dq, dk_, dv_, dg, db, ds0
+
+
 def gdn_gated_rmsnorm(x: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
                       out_dtype: torch.dtype = torch.bfloat16,
                       out: Optional[torch.Tensor] = None) -> torch.Tensor:

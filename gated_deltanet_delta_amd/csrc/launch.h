@@ -74,6 +74,33 @@ struct ConvArgs {
     hipStream_t stream;
 };
 
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* initial_state;    // [N, Hv, dk, dv] or null
+    const int32_t* cu_seqlens;
+    const float* d_o;              // [B, T, Hv, dv]
+    const float* d_final;          // [N, Hv, dk, dv] or null
+    int B, T, Hk, Hv, dk, dv, N;
+    gdn_dtype qkv_dtype, gate_dtype;
+    float* dq;                     // [B, T, Hk, dk]
+    float* dk_out;                 // [B, T, Hk, dk]
+    float* dv_out;                 // [B, T, Hv, dv]
+    float* dg;                     // [B, T, Hv]
+    float* dbeta;                  // [B, T, Hv]
+    float* d_initial;              // [N, Hv, dk, dv] or null
+    void* workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+};
+
+// Backward pass of the chunked rule (fp32 arithmetic).
+size_t chunk_bwd_workspace_size(int B, int T, int Hv, int dk, int dv, int N);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
+
 // Depthwise causal convolution with its carried input cache.
 hipError_t launch_causal_conv1d(const ConvArgs& a);
 

@@ -279,6 +279,40 @@ gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v,
                                  float* o, hipStream_t stream);
 
 /*
+ * gdn_chunk_bwd -- the backward pass of gdn_chunk_fwd, for training: the gradients of a scalar loss
+ * with respect to q, k, v, g, beta and the initial state, given its gradients d_o with respect to
+ * o and d_final with respect to the final state.
+ *
+ * The Qwen3-Next article (jsqmd.com, section 2.2) names the chunked call as the training form of the
+ * rule; this is its reverse: the chunk's products taken in reverse order (the UT/WY form of the
+ * forward, differentiated), with the states at the chunk starts recomputed by a forward sweep.
+ * fp32 arithmetic throughout.
+ *
+ * Inputs (device): q, k, v, g, beta, initial_state, cu_seqlens as in gdn_chunk_fwd (the gates as g
+ * and beta; no pool); d_o [B, T, Hv, dv] fp32; d_final [N, Hv, dk, dv] fp32 or NULL (zero).
+ * Outputs (device, fp32, every element written): d_q, d_k [B, T, Hk, dk] (summed over the v-heads
+ * that share a q/k head); d_v [B, T, Hv, dv]; d_g, d_beta [B, T, Hv]; d_initial_state
+ * [N, Hv, dk, dv] or NULL (not computed).  Tokens outside every packed sequence get zero d_q, d_k,
+ * d_g, d_beta and an untouched d_v.
+ * Workspace: gdn_chunk_bwd_workspace_size bytes, 256-byte aligned (the chunk-start states and the
+ * partial sums of each 16-column slice of the state).
+ * Sizes and dtypes as in gdn_chunk_fwd; dk and dv 64 or 128 (others: GDN_ERROR_NOT_SUPPORTED).
+ * Errors: GDN_ERROR_INVALID_VALUE for null or misaligned pointers (element alignment), bad sizes or
+ * dtypes; GDN_ERROR_WORKSPACE for a missing, short or misaligned workspace.
+ */
+size_t gdn_chunk_bwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N);
+gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v,
+                         const void* g, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         const float* d_o, const float* d_final,
+                         int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                         gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                         float* d_q, float* d_k, float* d_v, float* d_g, float* d_beta,
+                         float* d_initial_state,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * gdn_gated_rmsnorm -- the layer's gated output norm, applied to the gated delta rule's output.
  *
  * The Qwen3.5 Gated DeltaNet page (wanger-sjtu.github.io, section "Output and gated RMSNorm", and

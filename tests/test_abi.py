@@ -221,6 +221,30 @@ def test_ex_chunk_pool_must_be_both_states(lib):
     assert chunk_ex(lib, idx=P, num_slots=4, s0=None, fs=P) == INVALID
 
 
+def bwd(lib, q=P, k=P, v=P, g=P, beta=P, s0=None, cu=None, do=P, dfin=None, B=1, T=64, Hk=1, Hv=1,
+        dk=64, dv=64, N=1, qkv=F32, gate=F32, dq=P, dkk=P, dvv=P, dg=P, db=P, ds0=None, ws=P,
+        ws_bytes=1 << 40):
+    return lib.gdn_chunk_bwd(q, k, v, g, beta, s0, cu, do, dfin, B, T, Hk, Hv, dk, dv, N, qkv, gate, dq, dkk,
+                             dvv, dg, db, ds0, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(db=None), INVALID),
+    (dict(B=0), INVALID), (dict(Hv=3, Hk=2), INVALID), (dict(N=2), INVALID), (dict(cu=P, B=2, N=2), INVALID),
+    (dict(qkv=5), INVALID), (dict(do=P + 2), INVALID), (dict(q=P + 1, qkv=BF16), INVALID),
+    (dict(dk=96), UNSUPPORTED), (dict(dv=32), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=P + 16), WORKSPACE),
+])
+def test_backward_rejects(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_backward_workspace_query_is_host_only(lib):
+    assert lib.gdn_chunk_bwd_workspace_size(1, 4096, 16, 32, 128, 128, 1) > 0
+    assert lib.gdn_chunk_bwd_workspace_size(1, 4096, 16, 33, 128, 128, 1) == 0   # Hv % Hk
+    assert lib.gdn_chunk_bwd_workspace_size(1, 4096, 16, 32, 96, 128, 1) == 0    # head size
+
+
 def norm(lib, x=P, z=P, w=P, eps=1e-6, rows=8, d=128, zt=BF16, ot=BF16, out=P):
     return lib.gdn_gated_rmsnorm(x, z, w, eps, rows, d, zt, ot, out, None)
 
