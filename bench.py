@@ -36,6 +36,15 @@ if ROOT not in sys.path:
 
 MI355X_HBM_GBS = 8000.0        # HBM3E peak, GB/s
 MI355X_BF16_TFLOPS = 2500.0    # dense bf16 matrix peak, TFLOP/s
+MI355X_F32_TFLOPS = 157.3      # fp32 vector peak, TFLOP/s
+
+# The chunked backward's products per 64-token chunk and v-head at dk = dv = 128, each counted once
+# (not per state slice): K K^T, Q K^T (lower halves); the forward sweep's K S, T (beta X), K^T (f U);
+# the reverse sweep's K S, T (beta X), K D, Q S, P^T dO, T^T dU, dY U^T, dO U^T (lower halves where
+# triangular), the dq / dk terms dO S^T, U D^T, dY S^T, the state gradient's Q^T dO, K^T dY, and the
+# three C x C x dk products of dq and dk: 12.19 M multiply-adds, 2 flops each, per 64 tokens.
+BWD_FLOPS_PER_TOKEN_VHEAD = 2 * (64 * 64 * 128 + 10 * 64 * 128 * 128 + 6 * 64 * 64 * 128 // 2
+                                 + 3 * 64 * 64 * 128 // 2) // 64
 CHUNK = 64
 
 METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next shape, 1 GPU"
@@ -266,6 +275,7 @@ def main() -> int:
     e1.record()
     torch.cuda.synchronize()
     ms_bwd = e0.elapsed_time(e1) / bwd_calls
+    bwd_flops = BWD_FLOPS_PER_TOKEN_VHEAD * tokens * wl.Hv
     del bws
 
     # ---------------- decode ------------------------------------------------------------------
@@ -377,9 +387,14 @@ def main() -> int:
                                        "traffic": TRAFFIC_NORM,
                                        "algorithmic_bytes_per_launch": int(norm_bytes)}},
         "backward": {"call": "gdn_chunk_bwd (dq, dk, dv, dg, dbeta, d_initial of the prefill; fp32 "
-                             "vector arithmetic, first implementation)",
+                             "vector arithmetic)",
                      "calls": bwd_calls, "ms_per_call_events": round(ms_bwd, 4),
-                     "tokens_per_s": round(tokens / (ms_bwd / 1e3), 1)},
+                     "tokens_per_s": round(tokens / (ms_bwd / 1e3), 1),
+                     "roofline": {"bound": "alu", "achieved": round(bwd_flops / (ms_bwd / 1e3) / 1e12, 3),
+                                  "peak": MI355X_F32_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(bwd_flops / (ms_bwd / 1e3) / 1e12 / MI355X_F32_TFLOPS, 4),
+                                  "flops_per_token_vhead": BWD_FLOPS_PER_TOKEN_VHEAD,
+                                  "algorithmic_flops_per_call": int(bwd_flops)}},
         "cpu_baseline": cpu,
         "decode": {"metric": "decode state GB/s", "value": round(state_gbs, 1), "unit": "GB/s",
                    "workload": f"decode B={wd.B} Hk={wd.Hk} Hv={wd.Hv} dk=dv={wd.dk}, {nd} one-token "
