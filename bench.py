@@ -42,7 +42,7 @@ MI355X_F32_TFLOPS = 157.3      # fp32 vector peak, TFLOP/s
 # (not per state slice): K K^T, Q K^T (lower halves); the forward sweep's K S, T (beta X), K^T (f U);
 # the reverse sweep's K S, T (beta X), K D, Q S, P^T dO, T^T dU, dY U^T, dO U^T (lower halves where
 # triangular), the dq / dk terms dO S^T, U D^T, dY S^T, the state gradient's Q^T dO, K^T dY, and the
-# three C x C x dk products of dq and dk: 12.19 M multiply-adds, 2 flops each, per 64 tokens.
+# three C x C x dk products of dq and dk: 13.37 M multiply-adds, 2 flops each, per 64 tokens.
 BWD_FLOPS_PER_TOKEN_VHEAD = 2 * (64 * 64 * 128 + 10 * 64 * 128 * 128 + 6 * 64 * 64 * 128 // 2
                                  + 3 * 64 * 64 * 128 // 2) // 64
 CHUNK = 64
