@@ -30,7 +30,10 @@
 //   bwd_combine_kernel  one workgroup per (chunk, q/k head): sums the slices' partials (and the
 //                     v-heads sharing the q/k head) in a fixed order, forms the three C x C x dk
 //                     products once, and writes dq, dk, dg and dbeta.
-// All products run on the vector ALU out of LDS, with small register tiles.
+// The slice kernel's products run on the fp32 matrix cores; the prepare and combine kernels' on the
+// vector ALU with small register tiles.
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -53,6 +56,48 @@ __device__ __forceinline__ float sum64(float x) {
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
     return x;
+}
+
+// 8 consecutive input elements as fp32 (one 16-byte load for bf16, two for fp32)
+struct F8 {
+    float x[8];
+};
+__device__ __forceinline__ F8 load8(const bf16_t* p) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+    F8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.x[2 * i] = __uint_as_float(w[i] << 16);
+        r.x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    return r;
+}
+__device__ __forceinline__ F8 load8(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    return F8{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+}
+
+// Rows [0, kC) x DK of a [token][head][DK] input into LDS rows of pitch LK, every load issued before
+// the first LDS write; rows past Lc read row Lc - 1 (in bounds) and store zeros.
+template <int DK, int LK, int NT, typename TIn>
+__device__ __forceinline__ void stage_rows(const TIn* __restrict__ src, size_t tok0, int Hh, int head, int Lc,
+                                           float* dst, int tid) {
+    constexpr int PER = kC * DK / 8 / NT;       // 8-element pieces per thread
+    F8 v[PER];
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int e = tid + NT * it, t = e / (DK / 8), c8 = 8 * (e % (DK / 8));
+        const int tr = t < Lc ? t : Lc - 1;
+        v[it] = load8(src + ((tok0 + tr) * Hh + head) * DK + c8);
+    }
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int e = tid + NT * it, t = e / (DK / 8), c8 = 8 * (e % (DK / 8));
+        const float m = t < Lc ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[t * LK + c8 + j] = m * v[it].x[j];
+    }
 }
 
 // Chunk slots: the chunks of sequence 0, then sequence 1, ...  (nct chunks per batch row without
@@ -128,13 +173,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     if (!bwd_locate(slot, cu_seqlens, N, T, n, row, cs, L)) return;
     const int tid = threadIdx.x;
     const size_t tok0 = (size_t)row * T + cs;
-    for (int e = tid; e < kC * DK; e += kThreads) {
-        const int t = e / DK, i = e % DK;
-        const bool in = t < L;
-        const size_t off = ((tok0 + t) * Hk + kh) * DK + i;
-        sK[t * LK + i] = in ? to_f32(k[off]) : 0.f;
-        sQ[t * LK + i] = in ? to_f32(q[off]) : 0.f;
-    }
+    stage_rows<DK, LK, kThreads>(k, tok0, Hk, kh, L, sK, tid);
+    stage_rows<DK, LK, kThreads>(q, tok0, Hk, kh, L, sQ, tid);
     __syncthreads();
     // K K^T and Q K^T: thread (ty, tx) forms the 4 x 4 tiles rows 4 ty.., columns 4 tx..
     {
@@ -205,28 +245,37 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------
-// The slice kernel runs 512 threads (two waves per SIMD, to hide LDS latency; more leaves too few
-// registers): each row of a C x 16 slice product gets 16 lanes, each row of a C x C product a wave.
+// The slice kernel: 512 threads, eight waves.  Every product is a chain of fp32 matrix-core
+// instructions on 16 x 16 tiles (v_mfma_f32_16x16x4f32: lane (g, c) = (lane / 16, lane % 16) feeds
+// A[c][k + g] and B[k + g][c]; element r of the result is row 4 g + r, column c), each wave owning
+// whole tiles: the C x 16 slice products one row tile per wave, the C x C gradients two tiles per
+// wave, the dq / dk terms four.  Operands come straight from LDS, two reads per 1024 multiply-adds.
 constexpr int kST = 512;
 constexpr int kSW = kST / kWave;                // waves
+
+typedef float f32x4b __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4b mfma4(float a, float b, f32x4b c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 template <int DK>
 struct SliceLds {
     static constexpr int LK = DK + 1, LW = kW + 1;
     float K[kC * LK];
     float Q[kC * LK];
-    float S[DK * kW];        // chunk-start state, this slice
-    float D[DK * kW];        // dL/dS at the chunk end, this slice
+    float S[DK * LW];        // chunk-start state, this slice
+    float D[DK * LW];        // dL/dS at the chunk end, this slice
     float T[kC * kLC];       // T, then E = dP o P + dBm o Bm
-    float B[kC * kLC];       // Bm
+    float B[kC * kLC];       // Bm, then dA o Bm
     float P[kC * kLC];       // P
     float VX[kC * LW];       // V, then X
     float KS[kC * LW];
     float U[kC * LW];
     float dO[kC * LW];
-    float dU[kC * LW];       // dU, then dY
+    float dU[kC * LW];
+    float KD[kC * LW];       // K D, then dY
     float G[kC], gam[kC], f[kC], beta[kC];
-    float r_qsdo[kC], r_ksdx[kC], r_kdu[kC], r_db[kC], r_e[kC], dG[kC];
+    float r_qsdo[kC], r_ksdx[kC], r_kdu[kC], r_db[kC], dG[kC];
     float red[kSW];
     int slot0;
 };
@@ -242,6 +291,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     float* __restrict__ dv_out, float* __restrict__ d_initial, long long rows, int max_slots) {
     using L = SliceLds<DK>;
     constexpr int LK = L::LK, LW = L::LW;
+    constexpr int KT = DK / 16;                  // key tiles
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     L& sm = *reinterpret_cast<L*>(smem_raw);
 
@@ -254,9 +304,13 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     const int c0 = sl * kW;
     int row, t0, t1;
     sequence_range(cu_seqlens, n, T, row, t0, t1);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cc = tid & 15, rg = tid >> 4;                  // (row, column) of slice work
-    constexpr int RPT = kC * kW / kST;                        // rows per thread (1)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int gl = lane >> 4, cl = lane & 15;                      // (g, c) of the tile layout
+    // Every product's LDS addresses derive from (g, c); left alone, the compiler hoists all of them
+    // out of the chunk loops and runs out of registers.  Passing (g, c) through an empty asm at the
+    // top of each chunk makes them loop-variant, so they are formed where they are used.
+    auto refresh_lane = [&]() { asm volatile("" : "+v"(gl), "+v"(cl)); };
     if (tid == 0) sm.slot0 = bwd_slot0(cu_seqlens, n, T);
     __syncthreads();
     const int slot0 = sm.slot0;
@@ -264,34 +318,53 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     const int nchunks = min((t1 - t0 + kC - 1) / kC, max(0, max_slots - slot0));
     const size_t SSL = (size_t)DK * dv;                       // one full state
     auto ck_at = [&](int ci) { return ckpt + ((size_t)(slot0 + ci) * Hv + h) * SSL; };
+    const f32x4b z4 = {0.f, 0.f, 0.f, 0.f};
 
     // the chunk's inputs: K (and Q), this slice of V (and dO), the gates, G, gamma, f; T (and Bm, P)
-    auto load_chunk = [&](int ci, bool rev) {
+    auto load_chunk = [&](int ci, auto rev_c) {
+        constexpr bool rev = decltype(rev_c)::value;
         const int cs = t0 + ci * kC, Lc = min(kC, t1 - cs);
         const size_t tok0 = (size_t)row * T + cs;
-        for (int e = tid; e < kC * DK; e += kST) {
-            const int t = e / DK, i = e % DK;
-            const bool in = t < Lc;
-            const size_t off = ((tok0 + t) * Hk + kh) * DK + i;
-            sm.K[t * LK + i] = in ? to_f32(k[off]) : 0.f;
-            if (rev) sm.Q[t * LK + i] = in ? to_f32(q[off]) : 0.f;
-        }
-        for (int e = tid; e < kC * kW; e += kST) {
-            const int t = e / kW, c = e % kW;
-            const bool in = t < Lc;
-            const size_t off = ((tok0 + t) * Hv + h) * dv + c0 + c;
-            sm.VX[t * LW + c] = in ? to_f32(v[off]) : 0.f;
-            if (rev) sm.dO[t * LW + c] = in ? d_o[off] : 0.f;
-        }
+        // the three C x C matrices: 16-byte pieces, all loads first
+        constexpr int NM = rev ? 3 : 1, PM = kMat / 4 / kST;
         const float* mT = mats + ((size_t)(slot0 + ci) * Hv + h) * 3 * kMat;
-        for (int e = tid; e < kMat; e += kST) {
-            const int t = e / kC, j = e % kC;
-            sm.T[t * kLC + j] = mT[e];
-            if (rev) {
-                sm.B[t * kLC + j] = mT[kMat + e];
-                sm.P[t * kLC + j] = mT[2 * kMat + e];
-            }
+        float4 mv[NM][PM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int it = 0; it < PM; ++it)
+                mv[m][it] = *reinterpret_cast<const float4*>(mT + m * kMat + 4 * (tid + kST * it));
+        // this slice of V (and dO): one element per thread and row pass
+        constexpr int PV = kC * kW / kST;
+        float vv[PV], ov[PV];
+#pragma unroll
+        for (int it = 0; it < PV; ++it) {
+            const int e = tid + kST * it, t = e / kW, c = e % kW;
+            const int tr = t < Lc ? t : Lc - 1;
+            const size_t off = ((tok0 + tr) * Hv + h) * dv + c0 + c;
+            vv[it] = (t < Lc ? 1.f : 0.f) * to_f32(v[off]);
+            if (rev) ov[it] = (t < Lc ? 1.f : 0.f) * d_o[off];
         }
+        stage_rows<DK, LK, kST>(k, tok0, Hk, kh, Lc, sm.K, tid);
+        if (rev) stage_rows<DK, LK, kST>(q, tok0, Hk, kh, Lc, sm.Q, tid);
+#pragma unroll
+        for (int it = 0; it < PV; ++it) {
+            const int e = tid + kST * it, t = e / kW, c = e % kW;
+            sm.VX[t * LW + c] = vv[it];
+            if (rev) sm.dO[t * LW + c] = ov[it];
+        }
+        float* mdst[3] = {sm.T, sm.B, sm.P};
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int it = 0; it < PM; ++it) {
+                const int e = 4 * (tid + kST * it), t = e / kC, j = e % kC;
+                float* d = mdst[m] + t * kLC + j;
+                d[0] = mv[m][it].x;
+                d[1] = mv[m][it].y;
+                d[2] = mv[m][it].z;
+                d[3] = mv[m][it].w;
+            }
         if (tid < kC) {
             const bool in = tid < Lc;
             sm.G[tid] = in ? to_f32(g[(tok0 + tid) * Hv + h]) : 0.f;
@@ -302,47 +375,91 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         __syncthreads();
         return Lc;
     };
-    // KS, X = V - gamma KS (in place over V), U = T diag(beta) X; 16 lanes per row, 4 rows each
-    auto ks_x_u = [&]() {
+    // row tile a of M S (M = K or Q, C x DK, S DK x 16): A = M[16 a + c][k + g], B = S[k + g][c]
+    auto rows_times_state = [&](const float* M, const float* Sx, int a) {
+        f32x4b acc = z4;
+#pragma unroll 2
+        for (int kk = 0; kk < DK; kk += 4) acc = mfma4(M[(16 * a + cl) * LK + kk + gl], Sx[(kk + gl) * LW + cl], acc);
+        return acc;
+    };
+    // K S and X = V - gamma K S (waves 0-3); with `qs`, also the row sums (QS).dO (waves 4-7)
+    auto ks_x = [&](bool qs) {
+        if (wave < 4) {
+            const int a = wave;
+            const f32x4b acc = rows_times_state(sm.K, sm.S, a);
 #pragma unroll
-        for (int it = 0; it < RPT; ++it) {
-            const int t = rg + (kST / kW) * it, c = cc;
-            float ks = 0.f;
-            for (int i = 0; i < DK; ++i) ks += sm.K[t * LK + i] * sm.S[i * kW + c];
-            sm.KS[t * LW + c] = ks;
-            sm.VX[t * LW + c] -= sm.gam[t] * ks;
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * a + 4 * gl + r;
+                sm.KS[t * LW + cl] = acc[r];
+                sm.VX[t * LW + cl] -= sm.gam[t] * acc[r];
+            }
+        } else if (qs) {
+            const int a = wave - 4;
+            const f32x4b acc = rows_times_state(sm.Q, sm.S, a);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * a + 4 * gl + r;
+                const float s = sum16(acc[r] * sm.dO[t * LW + cl]);
+                if (cl == 0) sm.r_qsdo[t] = s;
+            }
         }
         __syncthreads();
+    };
+    // U = T diag(beta) X (waves 0-3, T lower triangular); with `kd`, K D into KD (waves 4-7)
+    auto u_kd = [&](bool kd) {
+        if (wave < 4) {
+            const int a = wave;
+            f32x4b acc = z4;
+            for (int kk = 0; kk < 16 * (a + 1); kk += 4)
+                acc = mfma4(sm.T[(16 * a + cl) * kLC + kk + gl], sm.beta[kk + gl] * sm.VX[(kk + gl) * LW + cl], acc);
 #pragma unroll
-        for (int it = 0; it < RPT; ++it) {
-            const int t = rg + (kST / kW) * it, c = cc;
-            float u = 0.f;
-            for (int j = 0; j <= t; ++j) u += sm.T[t * kLC + j] * sm.beta[j] * sm.VX[j * LW + c];
-            sm.U[t * LW + c] = u;
+            for (int r = 0; r < 4; ++r) sm.U[(16 * a + 4 * gl + r) * LW + cl] = acc[r];
+        } else if (kd) {
+            const int a = wave - 4;
+            const f32x4b acc = rows_times_state(sm.K, sm.D, a);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.KD[(16 * a + 4 * gl + r) * LW + cl] = acc[r];
         }
         __syncthreads();
+    };
+    // key tile b of M^T (w o Y) over the chunk (M = K or Q [C][DK], Y C x 16, w per token)
+    auto keys_times = [&](const float* M, const float* Y, const float* w1, const float* w2, int b) {
+        f32x4b acc = z4;
+#pragma unroll 2
+        for (int kk = 0; kk < kC; kk += 4) {
+            const int t = kk + gl;
+            float wt = w1[t];
+            if (w2) wt *= w2[t];
+            acc = mfma4(M[t * LK + 16 * b + cl], wt * Y[t * LW + cl], acc);
+        }
+        return acc;
     };
 
     // ---------------- forward sweep: the state at every chunk start ----------------------------
     const size_t sbase = ((size_t)n * Hv + h) * SSL;
     for (int e = tid; e < DK * kW; e += kST) {
         const int i = e / kW, c = e % kW;
-        sm.S[e] = initial_state ? initial_state[sbase + (size_t)i * dv + c0 + c] : 0.f;
+        sm.S[i * LW + c] = initial_state ? initial_state[sbase + (size_t)i * dv + c0 + c] : 0.f;
     }
     __syncthreads();
     for (int ci = 0; ci < nchunks; ++ci) {
+        refresh_lane();
         for (int e = tid; e < DK * kW; e += kST) {
             const int i = e / kW, c = e % kW;
-            ck_at(ci)[(size_t)i * dv + c0 + c] = sm.S[e];
+            ck_at(ci)[(size_t)i * dv + c0 + c] = sm.S[i * LW + c];
         }
-        load_chunk(ci, false);
-        ks_x_u();
+        load_chunk(ci, std::false_type{});
+        ks_x(false);
+        u_kd(false);
+        // S <- gamma_C S + K^T diag(f) U, key tile b per wave
         const float gC = sm.gam[kC - 1];
-        for (int e = tid; e < DK * kW; e += kST) {
-            const int i = e / kW, c = e % kW;
-            float acc = 0.f;
-            for (int t = 0; t < kC; ++t) acc += sm.K[t * LK + i] * sm.f[t] * sm.U[t * LW + c];
-            sm.S[e] = gC * sm.S[e] + acc;
+        for (int b = wave; b < KT; b += kSW) {
+            const f32x4b acc = keys_times(sm.K, sm.U, sm.f, nullptr, b);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float* sp = &sm.S[(16 * b + 4 * gl + r) * LW + cl];
+                *sp = gC * *sp + acc[r];
+            }
         }
         __syncthreads();
     }
@@ -350,161 +467,167 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     // ---------------- reverse sweep ------------------------------------------------------------
     for (int e = tid; e < DK * kW; e += kST) {
         const int i = e / kW, c = e % kW;
-        sm.D[e] = d_final ? d_final[sbase + (size_t)i * dv + c0 + c] : 0.f;
+        sm.D[i * LW + c] = d_final ? d_final[sbase + (size_t)i * dv + c0 + c] : 0.f;
     }
     for (int ci = nchunks - 1; ci >= 0; --ci) {
+        refresh_lane();
         const int cs = t0 + ci * kC;
         const size_t tok0 = (size_t)row * T + cs;
         const int slot = slot0 + ci;
         for (int e = tid; e < DK * kW; e += kST) {
             const int i = e / kW, c = e % kW;
-            sm.S[e] = ck_at(ci)[(size_t)i * dv + c0 + c];
+            sm.S[i * LW + c] = ck_at(ci)[(size_t)i * dv + c0 + c];
         }
-        const int Lc = load_chunk(ci, true);
-        ks_x_u();
+        const int Lc = load_chunk(ci, std::true_type{});
+        ks_x(true);
+        u_kd(true);
 
-        // dU = P^T dO + f (K D); row sums (QS).dO and (KD).U
+        // dU = P^T dO + f (K D) (P lower triangular: rows t' >= t), and the row sums (KD).U
+        if (wave < 4) {
+            const int a = wave;
+            f32x4b acc = z4;
+            for (int kk = 16 * a; kk < kC; kk += 4)
+                acc = mfma4(sm.P[(kk + gl) * kLC + 16 * a + cl], sm.dO[(kk + gl) * LW + cl], acc);
 #pragma unroll
-        for (int it = 0; it < RPT; ++it) {
-            const int t = rg + (kST / kW) * it, c = cc;
-            float kd = 0.f, qs = 0.f;
-            for (int i = 0; i < DK; ++i) {
-                kd += sm.K[t * LK + i] * sm.D[i * kW + c];
-                qs += sm.Q[t * LK + i] * sm.S[i * kW + c];
-            }
-            float pdo = 0.f;
-            for (int tp = t; tp < kC; ++tp) pdo += sm.P[tp * kLC + t] * sm.dO[tp * LW + c];
-            sm.dU[t * LW + c] = pdo + sm.f[t] * kd;
-            const float a = sum16(qs * sm.dO[t * LW + c]);
-            const float b = sum16(kd * sm.U[t * LW + c]);
-            if (c == 0) {
-                sm.r_qsdo[t] = a;
-                sm.r_kdu[t] = b;
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * a + 4 * gl + r;
+                const float kd = sm.KD[t * LW + cl];
+                sm.dU[t * LW + cl] = acc[r] + sm.f[t] * kd;
+                const float s = sum16(kd * sm.U[t * LW + cl]);
+                if (cl == 0) sm.r_kdu[t] = s;
             }
         }
         __syncthreads();
-        // dY = T^T dU (in place, through registers), dX = beta dY = dV; row sums X.dY and (KS).dX
-        float dy[RPT];
+        // dY = T^T dU (into KD), dX = beta dY = dV, and the row sums X.dY and (KS).dX
+        if (wave < 4) {
+            const int a = wave;
+            f32x4b acc = z4;
+            for (int kk = 16 * a; kk < kC; kk += 4)
+                acc = mfma4(sm.T[(kk + gl) * kLC + 16 * a + cl], sm.dU[(kk + gl) * LW + cl], acc);
 #pragma unroll
-        for (int it = 0; it < RPT; ++it) {
-            const int t = rg + (kST / kW) * it, c = cc;
-            float acc = 0.f;
-            for (int tp = t; tp < kC; ++tp) acc += sm.T[tp * kLC + t] * sm.dU[tp * LW + c];
-            dy[it] = acc;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < RPT; ++it) {
-            const int t = rg + (kST / kW) * it, c = cc;
-            sm.dU[t * LW + c] = dy[it];
-            const float dx = sm.beta[t] * dy[it];
-            if (t < Lc) dv_out[((tok0 + t) * Hv + h) * dv + c0 + c] = dx;
-            const float a = sum16(sm.VX[t * LW + c] * dy[it]);
-            const float b = sum16(sm.KS[t * LW + c] * dx);
-            if (c == 0) {
-                sm.r_db[t] = a;
-                sm.r_ksdx[t] = b;
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * a + 4 * gl + r;
+                const float dy = acc[r], dx = sm.beta[t] * dy;
+                sm.KD[t * LW + cl] = dy;
+                if (t < Lc) dv_out[((tok0 + t) * Hv + h) * dv + c0 + cl] = dx;
+                const float s1 = sum16(sm.VX[t * LW + cl] * dy);
+                const float s2 = sum16(sm.KS[t * LW + cl] * dx);
+                if (cl == 0) {
+                    sm.r_db[t] = s1;
+                    sm.r_ksdx[t] = s2;
+                }
             }
         }
         __syncthreads();
-        // the C x C gradients, one wave per row t, lane j: this slice's dP o Gam and dBm o Gam go to
-        // the workspace, E = dP o P + dBm o Bm stays for dG
+        // the C x C gradients, tile (a, b) = (p / 4, p % 4) for p = wave, wave + 8: this slice's
+        // dP o Gam and dBm o Gam to the workspace; E = dP o P + dBm o Bm into T and dA o Bm into B
         float* pP = pmat + (((size_t)slot * Hv + h) * slices + sl) * 2 * kMat;
         float* pB = pP + kMat;
-        for (int it = 0; it < kC / kSW; ++it) {
-            const int t = wave + kSW * it, j = lane;
-            float dyu = 0.f, dou = 0.f;
+        for (int p = wave; p < 16; p += kSW) {
+            const int a = p >> 2, b = p & 3;
+            f32x4b dyu = z4, dou = z4;
+            if (b <= a) {
 #pragma unroll
-            for (int c = 0; c < kW; ++c) {
-                const float uj = sm.U[j * LW + c];
-                dyu += sm.dU[t * LW + c] * uj;
-                dou += sm.dO[t * LW + c] * uj;
+                for (int kk = 0; kk < kW; kk += 4) {
+                    const float ub = sm.U[(16 * b + cl) * LW + kk + gl];
+                    dyu = mfma4(sm.KD[(16 * a + cl) * LW + kk + gl], ub, dyu);
+                    dou = mfma4(sm.dO[(16 * a + cl) * LW + kk + gl], ub, dou);
+                }
             }
-            const float dA = j < t ? -dyu : 0.f;
-            const float dP = j <= t ? dou : 0.f;
-            const float bm = sm.B[t * kLC + j], p = sm.P[t * kLC + j];
-            const float dec = j <= t ? expf(sm.G[t] - sm.G[j]) : 0.f;
-            const float dbm = sm.beta[t] * dA;
-            const float e_tj = dP * p + dbm * bm;
-            sm.T[t * kLC + j] = e_tj;
-            pP[t * kC + j] = dP * dec;
-            pB[t * kC + j] = dbm * dec;
-            const float db = sum64(dA * bm);
-            const float er = sum64(e_tj);
-            if (lane == 0) {
-                sm.r_db[t] += db;
-                sm.r_e[t] = er;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * a + 4 * gl + r, j = 16 * b + cl;
+                const float dA = j < t ? -dyu[r] : 0.f;
+                const float dP = j <= t ? dou[r] : 0.f;
+                const float bm = sm.B[t * kLC + j], pv = sm.P[t * kLC + j];
+                const float dec = j <= t ? expf(sm.G[t] - sm.G[j]) : 0.f;
+                const float dbm = sm.beta[t] * dA;
+                sm.T[t * kLC + j] = dP * pv + dbm * bm;
+                sm.B[t * kLC + j] = dA * bm;
+                pP[t * kC + j] = dP * dec;
+                pB[t * kC + j] = dbm * dec;
             }
         }
         // <S, D> over the slice, for dG at the chunk's last row
         float sd = 0.f;
-        for (int e = tid; e < DK * kW; e += kST) sd += sm.S[e] * sm.D[e];
+        for (int e = tid; e < DK * kW; e += kST) {
+            const int i = e / kW, c = e % kW;
+            sd += sm.S[i * LW + c] * sm.D[i * LW + c];
+        }
         sd = sum64(sd);
         if (lane == 0) sm.red[wave] = sd;
         __syncthreads();
 
-        // this slice's dq, dk terms through S, U, D: gamma dO S^T, f U D^T - gamma beta dY S^T
+        // this slice's dq, dk terms through S, U, D: gamma dO S^T and f U D^T - gamma beta dY S^T,
+        // tile (a, b) of C x DK for p = 4 wave .. 4 wave + 3 (when DK = 64, waves 4-7 have none)
         float* pq = part_dq + (size_t)sl * rows * Hv * DK;
         float* pk = part_dk + (size_t)sl * rows * Hv * DK;
-        for (int e = tid; e < kC * DK; e += kST) {
-            const int t = e / DK, i = e % DK;
-            if (t >= Lc) continue;
-            float dos = 0.f, fud = 0.f, dys = 0.f;
+        for (int p = 4 * wave; p < 4 * wave + 4 && p < 4 * KT; ++p) {
+            const int a = p / KT, b = p % KT;
+            f32x4b aq = z4, au = z4, ay = z4;
 #pragma unroll
-            for (int c = 0; c < kW; ++c) {
-                const float sic = sm.S[i * kW + c];
-                dos += sm.dO[t * LW + c] * sic;
-                fud += sm.U[t * LW + c] * sm.D[i * kW + c];
-                dys += sm.dU[t * LW + c] * sic;
+            for (int kk = 0; kk < kW; kk += 4) {
+                const float sb = sm.S[(16 * b + cl) * LW + kk + gl];
+                aq = mfma4(sm.dO[(16 * a + cl) * LW + kk + gl], sb, aq);
+                ay = mfma4(sm.KD[(16 * a + cl) * LW + kk + gl], sb, ay);
+                au = mfma4(sm.U[(16 * a + cl) * LW + kk + gl], sm.D[(16 * b + cl) * LW + kk + gl], au);
             }
-            const size_t o = ((tok0 + t) * Hv + h) * DK + i;
-            pq[o] = sm.gam[t] * dos;
-            pk[o] = sm.f[t] * fud - sm.gam[t] * sm.beta[t] * dys;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * a + 4 * gl + r;
+                if (t < Lc) {
+                    const size_t o = ((tok0 + t) * Hv + h) * DK + 16 * b + cl;
+                    pq[o] = sm.gam[t] * aq[r];
+                    pk[o] = sm.f[t] * au[r] - sm.gam[t] * sm.beta[t] * ay[r];
+                }
+            }
         }
-        // dG (this slice's part) and its reverse running sum, by the first wave (lane = row t)
+        // dG (this slice's part) and its reverse running sum, by the first wave (lane = row t);
+        // rows and columns of E, and the rows of dA o Bm for dbeta
         if (tid < kC) {
             const int t = tid;
-            float ce = 0.f;
-            for (int r = 0; r < kC; ++r) ce += sm.T[r * kLC + t];
+            float re = 0.f, ce = 0.f, rb = 0.f;
+            for (int r = 0; r < kC; ++r) {
+                re += sm.T[t * kLC + r];
+                ce += sm.T[r * kLC + t];
+                rb += sm.B[t * kLC + r];
+            }
             const float fkdu = sum64(sm.f[t] * sm.r_kdu[t]);
             float sdt = 0.f;
             for (int w = 0; w < kSW; ++w) sdt += sm.red[w];
-            float x = sm.gam[t] * sm.r_qsdo[t] - sm.gam[t] * sm.r_ksdx[t] - sm.f[t] * sm.r_kdu[t] + sm.r_e[t] - ce;
+            float x = sm.gam[t] * sm.r_qsdo[t] - sm.gam[t] * sm.r_ksdx[t] - sm.f[t] * sm.r_kdu[t] + re - ce;
             if (t == kC - 1) x += sm.gam[kC - 1] * sdt + fkdu;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
                 const float y = __shfl_down(x, off);
                 if (t + off < kWave) x += y;
             }
-            sm.dG[t] = x;
+            if (t < Lc) {
+                const size_t o = (size_t)sl * rows * Hv + (tok0 + t) * Hv + h;
+                part_dg[o] = x;
+                part_db[o] = sm.r_db[t] + rb;
+            }
         }
         __syncthreads();
-        if (tid < Lc) {
-            const size_t o = (size_t)sl * rows * Hv + (tok0 + tid) * Hv + h;
-            part_dg[o] = sm.dG[tid];
-            part_db[o] = sm.r_db[tid];
-        }
         // dL/dS for the previous chunk: gamma_C D + Q^T diag(gamma) dO - K^T diag(gamma beta) dY
-        const float gC = sm.gam[kC - 1];
-        float nd[DK * kW / kST];
+        {
+            const float gC = sm.gam[kC - 1];
+            for (int b = wave; b < KT; b += kSW) {
+                const f32x4b a1 = keys_times(sm.Q, sm.dO, sm.gam, nullptr, b);
+                const f32x4b a2 = keys_times(sm.K, sm.KD, sm.gam, sm.beta, b);
 #pragma unroll
-        for (int r = 0; r < DK * kW / kST; ++r) {
-            const int e = tid + kST * r, i = e / kW, c = e % kW;
-            float acc = 0.f;
-            for (int t = 0; t < kC; ++t)
-                acc += sm.gam[t] * (sm.Q[t * LK + i] * sm.dO[t * LW + c] -
-                                    sm.K[t * LK + i] * sm.beta[t] * sm.dU[t * LW + c]);
-            nd[r] = gC * sm.D[e] + acc;
+                for (int r = 0; r < 4; ++r) {
+                    float* dp = &sm.D[(16 * b + 4 * gl + r) * LW + cl];
+                    *dp = gC * *dp + a1[r] - a2[r];
+                }
+            }
         }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < DK * kW / kST; ++r) sm.D[tid + kST * r] = nd[r];
         __syncthreads();
     }
     if (d_initial) {
         for (int e = tid; e < DK * kW; e += kST) {
             const int i = e / kW, c = e % kW;
-            d_initial[sbase + (size_t)i * dv + c0 + c] = sm.D[e];
+            d_initial[sbase + (size_t)i * dv + c0 + c] = sm.D[i * LW + c];
         }
     }
 }
@@ -529,25 +652,48 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     const int tid = threadIdx.x;
     const size_t tok0 = (size_t)row * T + cs;
     const int G = Hv / Hk;
-    for (int e = tid; e < kC * DK; e += kThreads) {
-        const int t = e / DK, i = e % DK;
-        const bool in = t < L;
-        const size_t off = ((tok0 + t) * Hk + kh) * DK + i;
-        sK[t * LK + i] = in ? to_f32(k[off]) : 0.f;
-        sQ[t * LK + i] = in ? to_f32(q[off]) : 0.f;
-    }
-    // the two C x C matrices, summed over v-heads and slices; B symmetrised
-    for (int e = tid; e < kMat; e += kThreads) {
-        const int t = e / kC, j = e % kC;
-        float ap = 0.f, ab = 0.f;
+    stage_rows<DK, LK, kThreads>(k, tok0, Hk, kh, L, sK, tid);
+    stage_rows<DK, LK, kThreads>(q, tok0, Hk, kh, L, sQ, tid);
+    // the two C x C matrices, summed over v-heads and slices (each partial's loads issued together),
+    // then B symmetrised in LDS
+    {
+        constexpr int PE = kMat / kThreads;
+        float ap[PE], ab[PE];
+#pragma unroll
+        for (int it = 0; it < PE; ++it) ap[it] = ab[it] = 0.f;
         for (int x = 0; x < G; ++x)
             for (int s = 0; s < slices; ++s) {
                 const float* pm = pmat + (((size_t)slot * Hv + kh * G + x) * slices + s) * 2 * kMat;
-                ap += pm[e];
-                ab += pm[kMat + e] + pm[kMat + j * kC + t];
+                float lp[PE], lb[PE];
+#pragma unroll
+                for (int it = 0; it < PE; ++it) {
+                    lp[it] = pm[tid + kThreads * it];
+                    lb[it] = pm[kMat + tid + kThreads * it];
+                }
+#pragma unroll
+                for (int it = 0; it < PE; ++it) {
+                    ap[it] += lp[it];
+                    ab[it] += lb[it];
+                }
             }
-        sP[t * kLC + j] = ap;
-        sB[t * kLC + j] = ab;
+#pragma unroll
+        for (int it = 0; it < PE; ++it) {
+            const int e = tid + kThreads * it, t = e / kC, j = e % kC;
+            sP[t * kLC + j] = ap[it];
+            sB[t * kLC + j] = ab[it];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < PE; ++it) {
+            const int e = tid + kThreads * it, t = e / kC, j = e % kC;
+            ab[it] = sB[t * kLC + j] + sB[j * kLC + t];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < PE; ++it) {
+            const int e = tid + kThreads * it, t = e / kC, j = e % kC;
+            sB[t * kLC + j] = ab[it];
+        }
     }
     __syncthreads();
     // dq, dk: thread (ty, tx) owns rows 4 ty .. 4 ty + 3 and keys tx, tx + 16, ..
@@ -576,6 +722,28 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
                     ak[r][m] += pt[r] * qj[m] + b[r] * kj[m];
                 }
         }
+        // the slices' terms, summed over v-heads and slices (rows past L read row L - 1, in bounds)
+        for (int x = 0; x < G; ++x)
+            for (int s = 0; s < slices; ++s) {
+                float lq[4][NI], lk[4][NI];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = min(4 * ty + r, L - 1);
+#pragma unroll
+                    for (int m = 0; m < NI; ++m) {
+                        const size_t o = (((size_t)s * rows + tok0 + t) * Hv + kh * G + x) * DK + tx + 16 * m;
+                        lq[r][m] = part_dq[o];
+                        lk[r][m] = part_dk[o];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int m = 0; m < NI; ++m) {
+                        aq[r][m] += lq[r][m];
+                        ak[r][m] += lk[r][m];
+                    }
+            }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * ty + r;
@@ -583,15 +751,8 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
 #pragma unroll
             for (int m = 0; m < NI; ++m) {
                 const int i = tx + 16 * m;
-                float sq = aq[r][m], skk = ak[r][m];
-                for (int x = 0; x < G; ++x)
-                    for (int s = 0; s < slices; ++s) {
-                        const size_t o = (((size_t)s * rows + tok0 + t) * Hv + kh * G + x) * DK + i;
-                        sq += part_dq[o];
-                        skk += part_dk[o];
-                    }
-                dq[((tok0 + t) * Hk + kh) * DK + i] = sq;
-                dk[((tok0 + t) * Hk + kh) * DK + i] = skk;
+                dq[((tok0 + t) * Hk + kh) * DK + i] = aq[r][m];
+                dk[((tok0 + t) * Hk + kh) * DK + i] = ak[r][m];
             }
         }
     }

@@ -314,8 +314,9 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void
     if (dk < 1 || dv < 1) return GDN_ERROR_INVALID_VALUE;
     if (!sizes_fit(B, T, Hv, dv > dk ? dv : dk) || !sizes_fit(N, 1, Hv, (long long)dk * dv))
         return GDN_ERROR_INVALID_VALUE;
-    for (const void* p : {q, k, v})
-        if (p && !aligned(p, dtype_bytes(qkv_dtype))) return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {q, k})
+        if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
+    if (v && !aligned(v, dtype_bytes(qkv_dtype))) return GDN_ERROR_INVALID_VALUE;
     for (const void* p : {g, beta})
         if (p && !aligned(p, dtype_bytes(gate_dtype))) return GDN_ERROR_INVALID_VALUE;
     for (const void* p : {(const void*)initial_state, (const void*)d_o, (const void*)d_final, (const void*)dq,

@@ -297,8 +297,9 @@ gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v,
  * Workspace: gdn_chunk_bwd_workspace_size bytes, 256-byte aligned (the chunk-start states and the
  * partial sums of each 16-column slice of the state).
  * Sizes and dtypes as in gdn_chunk_fwd; dk and dv 64 or 128 (others: GDN_ERROR_NOT_SUPPORTED).
- * Errors: GDN_ERROR_INVALID_VALUE for null or misaligned pointers (element alignment), bad sizes or
- * dtypes; GDN_ERROR_WORKSPACE for a missing, short or misaligned workspace.
+ * Alignment: q and k 16 bytes, every other pointer its element size.
+ * Errors: GDN_ERROR_INVALID_VALUE for null or misaligned pointers, bad sizes or dtypes;
+ * GDN_ERROR_WORKSPACE for a missing, short or misaligned workspace.
  */
 size_t gdn_chunk_bwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N);
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v,

@@ -232,6 +232,7 @@ def bwd(lib, q=P, k=P, v=P, g=P, beta=P, s0=None, cu=None, do=P, dfin=None, B=1,
     (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(db=None), INVALID),
     (dict(B=0), INVALID), (dict(Hv=3, Hk=2), INVALID), (dict(N=2), INVALID), (dict(cu=P, B=2, N=2), INVALID),
     (dict(qkv=5), INVALID), (dict(do=P + 2), INVALID), (dict(q=P + 1, qkv=BF16), INVALID),
+    (dict(k=P + 8, qkv=BF16), INVALID), (dict(v=P + 2), INVALID),   # q, k 16-byte; v its element
     (dict(dk=96), UNSUPPORTED), (dict(dv=32), UNSUPPORTED),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=P + 16), WORKSPACE),
 ])
