@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 
 MI355X_HBM_GBS = 8000.0        # HBM3E peak, GB/s
 MI355X_BF16_TFLOPS = 2500.0    # dense bf16 matrix peak, TFLOP/s
-MI355X_F32_TFLOPS = 157.3      # fp32 vector peak, TFLOP/s
+MI355X_F32_TFLOPS = 157.3      # fp32 peak (vector and dense matrix alike), TFLOP/s
 
 # The chunked backward's products per 64-token chunk and v-head at dk = dv = 128, each counted once
 # (not per state slice): K K^T, Q K^T (lower halves); the forward sweep's K S, T (beta X), K^T (f U);
@@ -387,10 +387,10 @@ def main() -> int:
                                        "traffic": TRAFFIC_NORM,
                                        "algorithmic_bytes_per_launch": int(norm_bytes)}},
         "backward": {"call": "gdn_chunk_bwd (dq, dk, dv, dg, dbeta, d_initial of the prefill; fp32 "
-                             "vector arithmetic)",
+                             "arithmetic, the slice kernel on fp32 matrix cores)",
                      "calls": bwd_calls, "ms_per_call_events": round(ms_bwd, 4),
                      "tokens_per_s": round(tokens / (ms_bwd / 1e3), 1),
-                     "roofline": {"bound": "alu", "achieved": round(bwd_flops / (ms_bwd / 1e3) / 1e12, 3),
+                     "roofline": {"bound": "mfma", "achieved": round(bwd_flops / (ms_bwd / 1e3) / 1e12, 3),
                                   "peak": MI355X_F32_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(bwd_flops / (ms_bwd / 1e3) / 1e12 / MI355X_F32_TFLOPS, 4),
                                   "flops_per_token_vhead": BWD_FLOPS_PER_TOKEN_VHEAD,
