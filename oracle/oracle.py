@@ -22,6 +22,8 @@ Contents
              conv_states cache), per sequence, carrying the last inputs in fp64 numpy.
 ``backward`` the gradients of ``forward`` (reverse-mode over its token steps, fp64, in
              ``gdn_oracle.c``), for the training direction of the chunked call.
+``backward_ex`` the same with the layer's input steps (raw gates, q/k normalisation) differentiated
+             through as well.
 ``l2norm``   the optional normalisation of each q and k head vector to unit length before the rule
              (a reading: the pages do not state how q and k are scaled), in fp64 numpy.
 ``chunked``  the chunk-parallel (WY/UT) form of the same rule in fp64 numpy.  It is not the
@@ -192,6 +194,47 @@ def forward(*args, **kwargs) -> Tuple[np.ndarray, np.ndarray]:
 def backward(*args, **kwargs) -> Tuple[np.ndarray, ...]:
     """Gradients of the token-by-token rule; see ``Oracle.backward``."""
     return _oracle().backward(*args, **kwargs)
+
+
+def backward_ex(q, k, v, a, b, A_log, dt_bias, d_o, initial_state=None, d_final=None, cu_seqlens=None,
+                qk_l2norm=False, eps=1e-6):
+    """Gradients of the layer call with its options, fp64: q, k raw (normalised first when
+    ``qk_l2norm``), gates from the raw projections a, b [B,T,Hv] and A_log, dt_bias [Hv].
+
+    Returns (dq, dk, dv, da, db, dA_log, ddt_bias, d_initial_state).  Composition of ``backward`` with
+    the derivatives of the two input steps, written from their formulas:
+      beta = sigmoid(b):                     db = dbeta * beta (1 - beta)
+      g = -exp(A_log) softplus(a + dt_bias):  da = dg * (-exp(A_log) sigmoid(a + dt_bias)),
+                                              dA_log = sum over tokens of dg * g, ddt_bias = sum of da
+      x^ = x r, r = 1 / sqrt(|x|^2 + eps):    dx = r dx^ - r^3 (x . dx^) x
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    A_log = np.asarray(A_log, dtype=np.float64)
+    dt_bias = np.asarray(dt_bias, dtype=np.float64)
+    g, beta = gates(a, b, A_log, dt_bias)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    qn, kn = (l2norm(q, eps), l2norm(k, eps)) if qk_l2norm else (q, k)
+    dqn, dkn, dv, dg, dbeta, ds0 = backward(qn, kn, v, g, beta, d_o, initial_state, d_final, cu_seqlens)
+
+    def through_norm(x, dxn):
+        r = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+        return r * dxn - r ** 3 * np.sum(x * dxn, axis=-1, keepdims=True) * x
+
+    dq = through_norm(q, dqn) if qk_l2norm else dqn
+    dk = through_norm(k, dkn) if qk_l2norm else dkn
+    db = dbeta * beta * (1.0 - beta)
+    da = dg * (-np.exp(A_log) / (1.0 + np.exp(-(a + dt_bias))))
+    if cu_seqlens is not None:   # tokens outside every sequence carry no gradient
+        inside = np.zeros(a.shape[1], dtype=bool)
+        inside[int(cu_seqlens[0]):int(cu_seqlens[-1])] = True
+        da = np.where(inside[None, :, None], da, 0.0)
+        dg = np.where(inside[None, :, None], dg, 0.0)
+        db = np.where(inside[None, :, None], db, 0.0)
+    dA_log = np.sum(dg * g, axis=(0, 1))
+    ddt = np.sum(da, axis=(0, 1))
+    return dq, dk, dv, da, db, dA_log, ddt, ds0
 
 
 def default_threads() -> int:

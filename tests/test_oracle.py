@@ -474,6 +474,42 @@ def test_backward_matches_finite_differences(orc, lens, with_state, with_dfinal)
     pin_backward_fd(orc, lens, with_state, with_dfinal)
 
 
+@pytest.mark.parametrize("qk_l2norm", [False, True])
+def test_backward_ex_matches_finite_differences(orc, qk_l2norm):
+    """The gradients through the input steps (raw gates a, b, A_log, dt_bias; q, k normalised) equal
+    central differences of the composed forward oracle, for every element of every input."""
+    rng = np.random.default_rng(30 + qk_l2norm)
+    lens, Hk, Hv, dk, dv = (3, 0, 9), 1, 2, 3, 2
+    T, N = sum(lens), len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = dict(q=rng.standard_normal((1, T, Hk, dk)), k=rng.standard_normal((1, T, Hk, dk)),
+             v=rng.standard_normal((1, T, Hv, dv)), a=rng.standard_normal((1, T, Hv)),
+             b=rng.standard_normal((1, T, Hv)), A_log=np.log(rng.uniform(0.2, 2.0, Hv)),
+             dt_bias=0.3 * rng.standard_normal(Hv), s0=rng.standard_normal((N, Hv, dk, dv)))
+    wo = rng.standard_normal((1, T, Hv, dv))
+    ws = rng.standard_normal((N, Hv, dk, dv))
+
+    def loss(xx):
+        g, beta = O.gates(xx["a"], xx["b"], xx["A_log"], xx["dt_bias"])
+        q, k = (O.l2norm(xx["q"]), O.l2norm(xx["k"])) if qk_l2norm else (xx["q"], xx["k"])
+        o, fs = orc.forward(q, k, xx["v"], g, beta, xx["s0"], cu)
+        return float(np.sum(wo * o) + np.sum(ws * fs))
+
+    got = dict(zip(("q", "k", "v", "a", "b", "A_log", "dt_bias", "s0"),
+                   O.backward_ex(x["q"], x["k"], x["v"], x["a"], x["b"], x["A_log"], x["dt_bias"], wo, x["s0"],
+                                 ws, cu, qk_l2norm=qk_l2norm)))
+    h = 1e-5
+    for name, val in x.items():
+        fd = np.zeros_like(val)
+        for idx in np.ndindex(val.shape):
+            xp = {key: vv.copy() for key, vv in x.items()}
+            xm = {key: vv.copy() for key, vv in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * h)
+        assert np.allclose(got[name], fd, rtol=1e-6, atol=1e-8), (name, np.max(np.abs(got[name] - fd)))
+
+
 def test_backward_without_writes_is_a_pure_decay(orc):
     """beta = 0: nothing is written, so k and v get no gradient at all and S_t = e^{G_t} S0, whence
     dq_t = e^{G_t} S0 do_t and dS0 = sum_t e^{G_t} q_t do_t^T (one sequence, one head)."""
