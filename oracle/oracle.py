@@ -199,10 +199,12 @@ def backward(*args, **kwargs) -> Tuple[np.ndarray, ...]:
 def backward_ex(q, k, v, a, b, A_log, dt_bias, d_o, initial_state=None, d_final=None, cu_seqlens=None,
                 qk_l2norm=False, eps=1e-6):
     """Gradients of the layer call with its options, fp64: q, k raw (normalised first when
-    ``qk_l2norm``), gates from the raw projections a, b [B,T,Hv] and A_log, dt_bias [Hv].
+    ``qk_l2norm``), gates from the raw projections a, b [B,T,Hv] and A_log, dt_bias [Hv] (with
+    ``A_log`` None, a and b are g and beta themselves and there is no gate step).
 
-    Returns (dq, dk, dv, da, db, dA_log, ddt_bias, d_initial_state).  Composition of ``backward`` with
-    the derivatives of the two input steps, written from their formulas:
+    Returns (dq, dk, dv, da, db, dA_log, ddt_bias, d_initial_state), dA_log and ddt_bias None without
+    a gate step.  Composition of ``backward`` with the derivatives of the two input steps, written
+    from their formulas:
       beta = sigmoid(b):                     db = dbeta * beta (1 - beta)
       g = -exp(A_log) softplus(a + dt_bias):  da = dg * (-exp(A_log) sigmoid(a + dt_bias)),
                                               dA_log = sum over tokens of dg * g, ddt_bias = sum of da
@@ -210,9 +212,12 @@ def backward_ex(q, k, v, a, b, A_log, dt_bias, d_o, initial_state=None, d_final=
     """
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
-    A_log = np.asarray(A_log, dtype=np.float64)
-    dt_bias = np.asarray(dt_bias, dtype=np.float64)
-    g, beta = gates(a, b, A_log, dt_bias)
+    if A_log is None:
+        g, beta = a, b
+    else:
+        A_log = np.asarray(A_log, dtype=np.float64)
+        dt_bias = np.asarray(dt_bias, dtype=np.float64)
+        g, beta = gates(a, b, A_log, dt_bias)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     qn, kn = (l2norm(q, eps), l2norm(k, eps)) if qk_l2norm else (q, k)
@@ -224,6 +229,8 @@ def backward_ex(q, k, v, a, b, A_log, dt_bias, d_o, initial_state=None, d_final=
 
     dq = through_norm(q, dqn) if qk_l2norm else dqn
     dk = through_norm(k, dkn) if qk_l2norm else dkn
+    if A_log is None:
+        return dq, dk, dv, dg, dbeta, None, None, ds0
     db = dbeta * beta * (1.0 - beta)
     da = dg * (-np.exp(A_log) / (1.0 + np.exp(-(a + dt_bias))))
     if cu_seqlens is not None:   # tokens outside every sequence carry no gradient

@@ -474,11 +474,12 @@ def test_backward_matches_finite_differences(orc, lens, with_state, with_dfinal)
     pin_backward_fd(orc, lens, with_state, with_dfinal)
 
 
-@pytest.mark.parametrize("qk_l2norm", [False, True])
-def test_backward_ex_matches_finite_differences(orc, qk_l2norm):
+@pytest.mark.parametrize("qk_l2norm,raw", [(False, True), (True, True), (True, False)])
+def test_backward_ex_matches_finite_differences(orc, qk_l2norm, raw):
     """The gradients through the input steps (raw gates a, b, A_log, dt_bias; q, k normalised) equal
-    central differences of the composed forward oracle, for every element of every input."""
-    rng = np.random.default_rng(30 + qk_l2norm)
+    central differences of the composed forward oracle, for every element of every input.  Without
+    raw gates (A_log None) the gates enter as g and beta themselves."""
+    rng = np.random.default_rng(30 + qk_l2norm + 2 * raw)
     lens, Hk, Hv, dk, dv = (3, 0, 9), 1, 2, 3, 2
     T, N = sum(lens), len(lens)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -486,18 +487,27 @@ def test_backward_ex_matches_finite_differences(orc, qk_l2norm):
              v=rng.standard_normal((1, T, Hv, dv)), a=rng.standard_normal((1, T, Hv)),
              b=rng.standard_normal((1, T, Hv)), A_log=np.log(rng.uniform(0.2, 2.0, Hv)),
              dt_bias=0.3 * rng.standard_normal(Hv), s0=rng.standard_normal((N, Hv, dk, dv)))
+    if not raw:   # g <= 0 and beta in (0, 1) drawn directly
+        x["a"] = -rng.uniform(0.0, 1.5, (1, T, Hv))
+        x["b"] = rng.uniform(0.05, 0.95, (1, T, Hv))
+        del x["A_log"], x["dt_bias"]
     wo = rng.standard_normal((1, T, Hv, dv))
     ws = rng.standard_normal((N, Hv, dk, dv))
 
     def loss(xx):
-        g, beta = O.gates(xx["a"], xx["b"], xx["A_log"], xx["dt_bias"])
+        if raw:
+            g, beta = O.gates(xx["a"], xx["b"], xx["A_log"], xx["dt_bias"])
+        else:
+            g, beta = xx["a"], xx["b"]
         q, k = (O.l2norm(xx["q"]), O.l2norm(xx["k"])) if qk_l2norm else (xx["q"], xx["k"])
         o, fs = orc.forward(q, k, xx["v"], g, beta, xx["s0"], cu)
         return float(np.sum(wo * o) + np.sum(ws * fs))
 
-    got = dict(zip(("q", "k", "v", "a", "b", "A_log", "dt_bias", "s0"),
-                   O.backward_ex(x["q"], x["k"], x["v"], x["a"], x["b"], x["A_log"], x["dt_bias"], wo, x["s0"],
-                                 ws, cu, qk_l2norm=qk_l2norm)))
+    out = O.backward_ex(x["q"], x["k"], x["v"], x["a"], x["b"], x.get("A_log"), x.get("dt_bias"), wo, x["s0"],
+                        ws, cu, qk_l2norm=qk_l2norm)
+    got = dict(zip(("q", "k", "v", "a", "b", "A_log", "dt_bias", "s0"), out))
+    if not raw:
+        assert got["A_log"] is None and got["dt_bias"] is None
     h = 1e-5
     for name, val in x.items():
         fd = np.zeros_like(val)
