@@ -98,7 +98,7 @@ def main() -> int:
 
     from gated_deltanet_delta_amd import _lib
     from gated_deltanet_delta_amd import (gdn_causal_conv1d, gdn_chunk_fwd, gdn_chunk_fwd_ex,
-                                          gdn_chunk_bwd, gdn_chunk_fwd_gating,
+                                          gdn_chunk_bwd, gdn_chunk_bwd_ex, gdn_chunk_fwd_gating,
                                           gdn_gated_rmsnorm,
                                           gdn_recurrent_step, gdn_recurrent_step_gating, synth,
                                           workspace_size)
@@ -278,6 +278,26 @@ def main() -> int:
     bwd_flops = BWD_FLOPS_PER_TOKEN_VHEAD * tokens * wl.Hv
     del bws
 
+    # the same through every input option (gates from a, b and q, k normalised, both differentiated)
+    bws = torch.empty(int(clib.gdn_chunk_bwd_ex_workspace_size(1, T, wl.Hk, wl.Hv, wl.dk, wl.dv, 1, _lib.GDN_BF16,
+                                                                1, 0, _lib.GDN_FLAG_QK_L2NORM)),
+                      dtype=torch.uint8, device=dev)
+
+    def bwd_every_option():
+        gdn_chunk_bwd_ex(d["q"], d["k"], d["v"], ga, gb, d_o, A_log=gA, dt_bias=gdt,
+                         initial_state=d["initial_state"], d_final=d_fin, qk_l2norm=True, workspace=bws)
+
+    for _ in range(2):
+        bwd_every_option()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(bwd_calls):
+        bwd_every_option()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_bwd_ex = e0.elapsed_time(e1) / bwd_calls
+    del bws
+
     # ---------------- decode ------------------------------------------------------------------
     wd = synth.WORKLOADS["decode"]
     x0 = synth.make(wd)
@@ -394,7 +414,11 @@ def main() -> int:
                                   "peak": MI355X_F32_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(bwd_flops / (ms_bwd / 1e3) / 1e12 / MI355X_F32_TFLOPS, 4),
                                   "flops_per_token_vhead": BWD_FLOPS_PER_TOKEN_VHEAD,
-                                  "algorithmic_flops_per_call": int(bwd_flops)}},
+                                  "algorithmic_flops_per_call": int(bwd_flops)},
+                     "every_option": {"call": "gdn_chunk_bwd_ex (gates from a, b and q, k L2-normalised, "
+                                              "both differentiated: da, db, dA_log, ddt_bias, raw dq, dk)",
+                                      "ms_per_call_events": round(ms_bwd_ex, 4),
+                                      "tokens_per_s": round(tokens / (ms_bwd_ex / 1e3), 1)}},
         "cpu_baseline": cpu,
         "decode": {"metric": "decode state GB/s", "value": round(state_gbs, 1), "unit": "GB/s",
                    "workload": f"decode B={wd.B} Hk={wd.Hk} Hv={wd.Hv} dk=dv={wd.dk}, {nd} one-token "

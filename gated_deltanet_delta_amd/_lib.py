@@ -21,7 +21,7 @@ EXPORTED = ("gdn_status_string", "gdn_version", "gdn_chunk_fwd_workspace_size", 
             "gdn_chunk_fwd_gating", "gdn_recurrent_step_gating", "gdn_chunk_fwd_indexed",
             "gdn_recurrent_step_indexed", "gdn_gated_rmsnorm", "gdn_causal_conv1d",
             "gdn_chunk_fwd_ex", "gdn_recurrent_step_ex", "gdn_chunk_bwd_workspace_size",
-            "gdn_chunk_bwd")
+            "gdn_chunk_bwd", "gdn_chunk_bwd_ex_workspace_size", "gdn_chunk_bwd_ex")
 
 GDN_FLAG_QK_L2NORM = 1
 
@@ -75,6 +75,11 @@ def load() -> ctypes.CDLL:
     lib.gdn_chunk_bwd_workspace_size.argtypes = [i32] * 7
     lib.gdn_chunk_bwd.restype = i32
     lib.gdn_chunk_bwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, i32] + [vp] * 6 + [vp, sz, vp]
+    lib.gdn_chunk_bwd_ex_workspace_size.restype = sz
+    lib.gdn_chunk_bwd_ex_workspace_size.argtypes = [i32] * 7 + [i32, i32, i32, u32]
+    lib.gdn_chunk_bwd_ex.restype = i32
+    lib.gdn_chunk_bwd_ex.argtypes = ([vp] * 9 + [i32] + [vp] * 3 + [i32] * 7 + [i32, i32, u32] + [vp] * 8
+                                     + [vp, sz, vp])
     lib.gdn_recurrent_step_ex.restype = i32
     lib.gdn_recurrent_step_ex.argtypes = [vp] * 9 + [i32] + [i32] * 6 + [i32, i32] + [u32] + [vp, vp]
     _lib = lib

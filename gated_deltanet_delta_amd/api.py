@@ -444,6 +444,81 @@ def gdn_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     return dq, dk_, dv_, dg, db, ds0
 
 
+def gdn_chunk_bwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, d_o: torch.Tensor, *, A_log: Optional[torch.Tensor] = None,
+                     dt_bias: Optional[torch.Tensor] = None,
+                     initial_state: Optional[torch.Tensor] = None,
+                     state_indices: Optional[torch.Tensor] = None,
+                     d_final: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                     qk_l2norm: bool = False, need_d_initial: bool = True,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[Optional[torch.Tensor], ...]:
+    """Backward pass of gdn_chunk_fwd_ex with the same options.  Returns (dq, dk, dv, dg, dbeta,
+    dA_log, ddt_bias, d_initial_state): with A_log set, g and beta are the raw projections a, b and
+    dg, dbeta are da, db, and dA_log, ddt_bias [Hv] are returned (else None); with state_indices,
+    initial_state is the pool [num_slots,Hv,dk,dv] and d_initial_state is per sequence; with
+    qk_l2norm, dq and dk are with respect to the raw q and k."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_chunk_bwd_ex runs on a GPU; tensors must be on a cuda device")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    gating = A_log is not None
+    xn, yn = ("a", "b") if gating else ("g", "beta")
+    _check(q, (B, T, Hk, dk), "q", dev)
+    _check(k, (B, T, Hk, dk), "k", dev, q.dtype)
+    _check(v, (B, T, Hv, dv), "v", dev, q.dtype)
+    _check(g, (B, T, Hv), xn, dev)
+    _check(beta, (B, T, Hv), yn, dev, g.dtype)
+    _check(d_o, (B, T, Hv, dv), "d_o", dev, torch.float32)
+    if gating:
+        _check(A_log, (Hv,), "A_log", dev, torch.float32)
+        _check(dt_bias, (Hv,), "dt_bias", dev, torch.float32)
+    elif dt_bias is not None:
+        raise ValueError("dt_bias needs A_log")
+    num_slots = 0
+    if state_indices is not None:
+        if initial_state is None or initial_state.dim() != 4:
+            raise ValueError("with state_indices, initial_state is the pool [num_slots, Hv, dk, dv]")
+        num_slots = initial_state.shape[0]
+        _check(initial_state, (num_slots, Hv, dk, dv), "state pool", dev, torch.float32)
+        _check(state_indices, (N,), "state_indices", dev, torch.int32)
+    elif initial_state is not None:
+        _check(initial_state, (N, Hv, dk, dv), "initial_state", dev, torch.float32)
+    if d_final is not None:
+        _check(d_final, (N, Hv, dk, dv), "d_final", dev, torch.float32)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, Hk, dk), **f32)
+    dk_ = torch.empty((B, T, Hk, dk), **f32)
+    dv_ = torch.zeros((B, T, Hv, dv), **f32)
+    dg = torch.empty((B, T, Hv), **f32)
+    db = torch.empty((B, T, Hv), **f32)
+    dA = torch.empty((Hv,), **f32) if gating else None
+    ddt = torch.empty((Hv,), **f32) if gating else None
+    ds0 = torch.empty((N, Hv, dk, dv), **f32) if need_d_initial else None
+    flags = _lib.GDN_FLAG_QK_L2NORM if qk_l2norm else 0
+    qkv, gate = _code(q, "q"), _code(g, xn)
+    ws_bytes = int(lib.gdn_chunk_bwd_ex_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv, int(gating),
+                                                       int(state_indices is not None), flags))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    st = lib.gdn_chunk_bwd_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias), _ptr(initial_state),
+        _ptr(state_indices), num_slots, _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final), B, T, Hk, Hv, dk, dv, N,
+        qkv, gate, flags, _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db), _ptr(dA), _ptr(ddt), _ptr(ds0),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_chunk_bwd_ex")
+    return dq, dk_, dv_, dg, db, dA, ddt, ds0
+
+
 def gdn_gated_rmsnorm(x: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
                       out_dtype: torch.dtype = torch.bfloat16,
                       out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -28,7 +28,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 SOURCES = ["gdn_api.cpp", "recurrent.hip", "chunk_f32.hip", "chunk_mfma.hip", "norm.hip", "conv1d.hip",
-           "chunk_bwd.hip"]
+           "chunk_bwd.hip", "chunk_bwd_ex.hip"]
 
 # Per-source code-generation options.  chunk_mfma.hip: matrix-core results go to ordinary VGPRs
 # (not AGPRs), because every product there is post-processed on the vector ALU (splits, decays),

@@ -292,6 +292,68 @@ gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v, co
                           (flags & GDN_FLAG_QK_L2NORM) ? 1 : 0);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared body of gdn_chunk_bwd and gdn_chunk_bwd_ex: every check, then the launches.
+gdn_status bwd_call(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    const float* A_log, const float* dt_bias, const float* initial_state,
+                    const int32_t* state_indices, int num_slots, const int32_t* cu_seqlens, const float* d_o,
+                    const float* d_final, int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                    gdn_dtype qkv_dtype, gdn_dtype gate_dtype, unsigned flags, float* dq, float* dk_out,
+                    float* dv_out, float* dg, float* dbeta, float* d_A_log, float* d_dt_bias,
+                    float* d_initial, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (T > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk_out || !dv_out || !dg || !dbeta))
+        return GDN_ERROR_INVALID_VALUE;
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
+    if (!dtype_ok(qkv_dtype) || !dtype_ok(gate_dtype)) return GDN_ERROR_INVALID_VALUE;
+    if (cu_seqlens ? B != 1 : N != B) return GDN_ERROR_INVALID_VALUE;
+    if (dk < 1 || dv < 1) return GDN_ERROR_INVALID_VALUE;
+    if (!sizes_fit(B, T, Hv, dv > dk ? dv : dk) || !sizes_fit(N, 1, Hv, (long long)dk * dv))
+        return GDN_ERROR_INVALID_VALUE;
+    if ((flags & ~GDN_FLAG_QK_L2NORM) || (dt_bias && !A_log)) return GDN_ERROR_INVALID_VALUE;
+    if (A_log && (!dt_bias || !d_A_log || !d_dt_bias)) return GDN_ERROR_INVALID_VALUE;
+    if (state_indices && (!initial_state || num_slots < 1 || !sizes_fit(num_slots, 1, Hv, (long long)dk * dv)))
+        return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {q, k})
+        if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
+    if (state_indices && !aligned16(initial_state)) return GDN_ERROR_INVALID_VALUE;
+    if (v && !aligned(v, dtype_bytes(qkv_dtype))) return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {g, beta})
+        if (p && !aligned(p, dtype_bytes(gate_dtype))) return GDN_ERROR_INVALID_VALUE;
+    for (const void* p : {(const void*)initial_state, (const void*)d_o, (const void*)d_final, (const void*)dq,
+                          (const void*)dk_out, (const void*)dv_out, (const void*)dg, (const void*)dbeta,
+                          (const void*)d_initial, (const void*)cu_seqlens, (const void*)A_log,
+                          (const void*)dt_bias, (const void*)d_A_log, (const void*)d_dt_bias,
+                          (const void*)state_indices})
+        if (p && !aligned(p, 4)) return GDN_ERROR_INVALID_VALUE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
+    if (A_log && Hv > gdn::kBwdExMaxHv) return GDN_ERROR_NOT_SUPPORTED;
+    const bool ex = A_log || state_indices || flags;
+    const size_t need = ex ? gdn_chunk_bwd_ex_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype, A_log != nullptr,
+                                                             state_indices != nullptr, flags)
+                           : gdn_chunk_bwd_workspace_size(B, T, Hk, Hv, dk, dv, N);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GDN_ERROR_WORKSPACE;
+    const gdn::BwdArgs a{q, k, v, g, beta, initial_state, cu_seqlens, d_o, d_final, B, T, Hk, Hv, dk, dv, N,
+                         qkv_dtype, gate_dtype, dq, dk_out, dv_out, dg, dbeta, d_initial, workspace,
+                         workspace_bytes, stream};
+    hipError_t e;
+    if (ex) {
+        const gdn::BwdExArgs x{a, A_log, dt_bias, state_indices, num_slots,
+                               (flags & GDN_FLAG_QK_L2NORM) ? 1 : 0, d_A_log, d_dt_bias};
+        e = gdn::launch_chunk_bwd_ex(x);
+    } else {
+        e = gdn::launch_chunk_bwd(a);
+    }
+    return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t gdn_chunk_bwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N) {
     if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return 0;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return 0;
@@ -306,31 +368,30 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void
                          float* dq, float* dk_out, float* dv_out, float* dg, float* dbeta,
                          float* d_initial, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-    if (T > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk_out || !dv_out || !dg || !dbeta))
-        return GDN_ERROR_INVALID_VALUE;
-    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
-    if (!dtype_ok(qkv_dtype) || !dtype_ok(gate_dtype)) return GDN_ERROR_INVALID_VALUE;
-    if (cu_seqlens ? B != 1 : N != B) return GDN_ERROR_INVALID_VALUE;
-    if (dk < 1 || dv < 1) return GDN_ERROR_INVALID_VALUE;
-    if (!sizes_fit(B, T, Hv, dv > dk ? dv : dk) || !sizes_fit(N, 1, Hv, (long long)dk * dv))
-        return GDN_ERROR_INVALID_VALUE;
-    for (const void* p : {q, k})
-        if (p && !aligned16(p)) return GDN_ERROR_INVALID_VALUE;
-    if (v && !aligned(v, dtype_bytes(qkv_dtype))) return GDN_ERROR_INVALID_VALUE;
-    for (const void* p : {g, beta})
-        if (p && !aligned(p, dtype_bytes(gate_dtype))) return GDN_ERROR_INVALID_VALUE;
-    for (const void* p : {(const void*)initial_state, (const void*)d_o, (const void*)d_final, (const void*)dq,
-                          (const void*)dk_out, (const void*)dv_out, (const void*)dg, (const void*)dbeta,
-                          (const void*)d_initial, (const void*)cu_seqlens})
-        if (p && !aligned(p, 4)) return GDN_ERROR_INVALID_VALUE;
-    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
-    const size_t need = gdn_chunk_bwd_workspace_size(B, T, Hk, Hv, dk, dv, N);
-    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
-        return GDN_ERROR_WORKSPACE;
-    const gdn::BwdArgs a{q, k, v, g, beta, initial_state, cu_seqlens, d_o, d_final, B, T, Hk, Hv, dk, dv, N,
-                         qkv_dtype, gate_dtype, dq, dk_out, dv_out, dg, dbeta, d_initial, workspace,
-                         workspace_bytes, stream};
-    return gdn::launch_chunk_bwd(a) == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH_FAILURE;
+    return bwd_call(q, k, v, g, beta, nullptr, nullptr, initial_state, nullptr, 0, cu_seqlens, d_o, d_final,
+                    B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, 0u, dq, dk_out, dv_out, dg, dbeta,
+                    nullptr, nullptr, d_initial, workspace, workspace_bytes, stream);
+}
+
+size_t gdn_chunk_bwd_ex_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                       gdn_dtype qkv_dtype, int raw_gates, int pool, unsigned flags) {
+    if (!gdn_chunk_bwd_workspace_size(B, T, Hk, Hv, dk, dv, N) || !dtype_ok(qkv_dtype)) return 0;
+    return gdn::chunk_bwd_ex_workspace_size(B, T, Hk, Hv, dk, dv, N, raw_gates != 0, pool != 0,
+                                            (flags & GDN_FLAG_QK_L2NORM) != 0, qkv_dtype);
+}
+
+gdn_status gdn_chunk_bwd_ex(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* A_log, const float* dt_bias,
+                            const float* initial_state, const int32_t* state_indices, int num_slots,
+                            const int32_t* cu_seqlens, const float* d_o, const float* d_final, int B,
+                            int T, int Hk, int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype,
+                            gdn_dtype gate_dtype, unsigned flags, float* dq, float* dk_out,
+                            float* dv_out, float* dg, float* dbeta, float* d_A_log, float* d_dt_bias,
+                            float* d_initial, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    return bwd_call(q, k, v, g, beta, A_log, dt_bias, initial_state, state_indices, num_slots, cu_seqlens,
+                    d_o, d_final, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, flags, dq, dk_out, dv_out,
+                    dg, dbeta, d_A_log, d_dt_bias, d_initial, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

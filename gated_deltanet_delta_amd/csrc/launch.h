@@ -101,6 +101,22 @@ struct BwdArgs {
 size_t chunk_bwd_workspace_size(int B, int T, int Hv, int dk, int dv, int N);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
 
+// The same with the forward's input options: raw gates, q/k normalisation, a state pool.
+struct BwdExArgs {
+    BwdArgs base;                  // g, beta hold a, b with A_log; initial_state is the pool with state_indices
+    const float* A_log;            // [Hv] or null
+    const float* dt_bias;          // [Hv], with A_log
+    const int32_t* state_indices;  // [N] or null
+    int num_slots;
+    int qk_l2norm;
+    float* dA_log;                 // [Hv], with A_log
+    float* ddt_bias;               // [Hv], with A_log
+};
+constexpr int kBwdExMaxHv = 2048;  // v-heads the raw-gate gradients support (one block's tile)
+size_t chunk_bwd_ex_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N, bool raw_gates,
+                                   bool pool, bool l2, gdn_dtype qkv_dtype);
+hipError_t launch_chunk_bwd_ex(const BwdExArgs& a);
+
 // Depthwise causal convolution with its carried input cache.
 hipError_t launch_causal_conv1d(const ConvArgs& a);
 

@@ -314,6 +314,55 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v,
                          hipStream_t stream);
 
 /*
+ * gdn_chunk_bwd_ex -- the backward pass of gdn_chunk_fwd_ex: the same gradients through the forward's
+ * input options, so a layer that lets the library form its gates and normalise q and k trains
+ * through the same call.
+ *
+ * The gate formulas are those of the Qwen3.5 flowchart (wanger-sjtu.github.io, "Core mechanism:
+ * Gated DeltaNet") and of the Qwen3-Next write-up (intelliparadigm.com, section 2.2), differentiated:
+ *     beta = sigmoid(b)                     ->  d_b = d_beta beta (1 - beta)
+ *     g = -exp(A_log) softplus(a + dt_bias)  ->  d_a = d_g (-exp(A_log) sigmoid(a + dt_bias)),
+ *                                              d_A_log[h] = sum over tokens of d_g g,
+ *                                              d_dt_bias[h] = sum over tokens of d_a
+ * and the q/k normalisation x^ = x / sqrt(|x|^2 + 1e-6) (GDN_FLAG_QK_L2NORM, as in gdn_chunk_fwd_ex):
+ *     d_x = r d_x^ - r^3 (x . d_x^) x,   r = 1 / sqrt(|x|^2 + 1e-6).
+ * The rule's own gradients are those of gdn_chunk_bwd on the formed gates and normalised q, k.
+ *
+ * Arguments are those of gdn_chunk_bwd plus:
+ *   A_log, dt_bias   NULL: g and beta are the gates; both set: g and beta are the raw projections a
+ *                    and b [B, T, Hv] (gate_dtype) and d_g, d_beta receive d_a, d_b
+ *   d_A_log, d_dt_bias  [Hv] fp32 (device), written (not accumulated) when A_log is set, else unused
+ *   state_indices    NULL: initial_state is per sequence as in gdn_chunk_bwd; set: initial_state is
+ *                    the pool [num_slots, Hv, dk, dv] of gdn_chunk_fwd_ex (16-byte aligned) and
+ *                    sequence n started from slot state_indices[n] (a zero state for an index outside
+ *                    [0, num_slots), a padding row).  d_initial_state stays per sequence
+ *                    [N, Hv, dk, dv]: the gradient with respect to the state each sequence started from.
+ *   flags            0 or GDN_FLAG_QK_L2NORM (q, k are the raw vectors; d_q, d_k are with respect to them)
+ * Workspace: gdn_chunk_bwd_ex_workspace_size bytes for the same sizes and options (raw_gates: A_log
+ * set; pool: state_indices set), 256-byte aligned.  It adds to gdn_chunk_bwd's the formed gates, the
+ * normalised q and k (and v widened to fp32 when q, k, v are bf16) and the gathered start states.
+ * With no option set the call is gdn_chunk_bwd.  Determinism: d_A_log and d_dt_bias are summed in a
+ * fixed order (per-block fp64 partial sums), so repeated calls give identical bits.
+ * Errors: those of gdn_chunk_bwd, plus GDN_ERROR_INVALID_VALUE for an unknown flag bit, dt_bias without
+ * A_log, A_log without d_A_log / d_dt_bias, a pool without initial_state or with num_slots < 1;
+ * GDN_ERROR_NOT_SUPPORTED for raw gates with more than 2048 v-heads.
+ */
+size_t gdn_chunk_bwd_ex_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                       gdn_dtype qkv_dtype, int raw_gates, int pool, unsigned flags);
+gdn_status gdn_chunk_bwd_ex(const void* q, const void* k, const void* v,
+                            const void* g, const void* beta,
+                            const float* A_log, const float* dt_bias,
+                            const float* initial_state, const int32_t* state_indices, int num_slots,
+                            const int32_t* cu_seqlens,
+                            const float* d_o, const float* d_final,
+                            int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                            gdn_dtype qkv_dtype, gdn_dtype gate_dtype, unsigned flags,
+                            float* d_q, float* d_k, float* d_v, float* d_g, float* d_beta,
+                            float* d_A_log, float* d_dt_bias, float* d_initial_state,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
  * gdn_gated_rmsnorm -- the layer's gated output norm, applied to the gated delta rule's output.
  *
  * The Qwen3.5 Gated DeltaNet page (wanger-sjtu.github.io, section "Output and gated RMSNorm", and

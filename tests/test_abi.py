@@ -246,6 +246,39 @@ def test_backward_workspace_query_is_host_only(lib):
     assert lib.gdn_chunk_bwd_workspace_size(1, 4096, 16, 32, 96, 128, 1) == 0    # head size
 
 
+def bwd_ex(lib, q=P, k=P, v=P, g=P, beta=P, A_log=None, dt_bias=None, s0=None, idx=None, num_slots=0,
+           cu=None, do=P, dfin=None, B=1, T=64, Hk=1, Hv=1, dk=64, dv=64, N=1, qkv=F32, gate=F32, flags=0,
+           dq=P, dkk=P, dvv=P, dg=P, db=P, dA=None, ddt=None, ds0=None, ws=P, ws_bytes=1 << 40):
+    return lib.gdn_chunk_bwd_ex(q, k, v, g, beta, A_log, dt_bias, s0, idx, num_slots, cu, do, dfin, B, T, Hk,
+                                Hv, dk, dv, N, qkv, gate, flags, dq, dkk, dvv, dg, db, dA, ddt, ds0, ws,
+                                ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=2), INVALID), (dict(dt_bias=P), INVALID),                       # unknown flag; bias alone
+    (dict(A_log=P, dt_bias=P), INVALID), (dict(A_log=P, dt_bias=P, dA=P), INVALID),  # no gate gradients
+    (dict(A_log=P + 2, dt_bias=P, dA=P, ddt=P), INVALID),                        # misaligned A_log
+    (dict(idx=P, num_slots=4), INVALID), (dict(idx=P, num_slots=0, s0=P), INVALID),  # pool without states
+    (dict(idx=P, num_slots=4, s0=P + 4), INVALID),                               # pool not 16-byte aligned
+    (dict(idx=P + 2, num_slots=4, s0=P), INVALID),                               # misaligned indices
+    (dict(A_log=P, dt_bias=P, dA=P, ddt=P, Hk=2050, Hv=4100), UNSUPPORTED),       # raw gates, > 2048 v-heads
+    (dict(q=None, flags=1), INVALID), (dict(dk=96, flags=1), UNSUPPORTED),
+    (dict(ws_bytes=16, flags=1), WORKSPACE), (dict(ws=None, idx=P, num_slots=2, s0=P), WORKSPACE),
+])
+def test_backward_ex_rejects(lib, kw, status):
+    assert bwd_ex(lib, **kw) == status
+
+
+def test_backward_ex_workspace_grows_with_each_option(lib):
+    base = lib.gdn_chunk_bwd_workspace_size(1, 4096, 16, 32, 128, 128, 1)
+    size = lambda *o: lib.gdn_chunk_bwd_ex_workspace_size(1, 4096, 16, 32, 128, 128, 1, BF16, *o)  # noqa: E731
+    assert size(0, 0, 0) >= base
+    assert size(1, 0, 0) >= size(0, 0, 0) + 2 * 4 * 4096 * 32             # formed g and beta, fp32
+    assert size(0, 0, 1) >= size(0, 0, 0) + 4 * 4096 * (2 * 16 + 32) * 128  # q^, k^ and v as fp32
+    assert size(0, 1, 0) >= size(0, 0, 0) + 4 * 32 * 128 * 128               # one gathered state
+    assert lib.gdn_chunk_bwd_ex_workspace_size(1, 4096, 16, 33, 128, 128, 1, BF16, 1, 1, 1) == 0
+
+
 def norm(lib, x=P, z=P, w=P, eps=1e-6, rows=8, d=128, zt=BF16, ot=BF16, out=P):
     return lib.gdn_gated_rmsnorm(x, z, w, eps, rows, d, zt, ot, out, None)
 
