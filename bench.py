@@ -298,6 +298,50 @@ def main() -> int:
     ms_bwd_ex = e0.elapsed_time(e1) / bwd_calls
     del bws
 
+    # ---------------- the long-context and packed variable-length prefills ---------------------
+    # (the same call on the two larger prefill workloads, each with its own initial states; reported
+    # beside the headline prefill, which the value and roofline describe)
+    def time_workload(name, calls):
+        wx = synth.WORKLOADS[name]
+        xx = synth.make(wx)
+        dd = {key: (None if xx[key] is None else xx[key].to(dev).contiguous())
+              for key in ("q", "k", "v", "g", "beta", "initial_state", "cu_seqlens")}
+        del xx
+        Tt = dd["q"].shape[1]
+        Nn = wx.n_seqs if wx.n_seqs else wx.B
+        oo = torch.empty((1, Tt, wx.Hv, wx.dv), dtype=torch.float32, device=dev)
+        ff = torch.empty((Nn, wx.Hv, wx.dk, wx.dv), dtype=torch.float32, device=dev)
+        wss = torch.empty(max(workspace_size(1, Tt, wx.Hk, wx.Hv, wx.dk, wx.dv, Nn, wx.dtype), 1),
+                          dtype=torch.uint8, device=dev)
+
+        def call():
+            gdn_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"], dd["cu_seqlens"],
+                          o=oo, final_state=ff, workspace=wss)
+
+        call()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(calls):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / calls
+        nb, fl, _ = prefill_algorithmic(wx, Tt, 1, Nn, wx.init_state)
+        shape = (f"{Nn} packed sequences of {wx.len_range[0]}..{wx.len_range[1]} tokens" if wx.n_seqs
+                 else f"B=1 T={Tt}")
+        res = {"workload": f"{name}: {shape}, Hk={wx.Hk} Hv={wx.Hv} dk=dv={wx.dk} bf16 in, fp32 initial "
+                           f"state(s) and out", "tokens": Tt, "calls": calls,
+               "ms_per_call_events": round(ms, 4), "tokens_per_s": round(Tt / (ms / 1e3), 1),
+               "achieved_gbs": round(nb / (ms / 1e3) / 1e9, 1),
+               "hbm_frac": round(nb / (ms / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
+               "useful_tflops": round(fl / (ms / 1e3) / 1e12, 2)}
+        del dd, oo, ff, wss
+        torch.cuda.empty_cache()
+        return res
+
+    long_res = time_workload("long", 5)
+    varlen_res = time_workload("varlen", 3)
+
     # ---------------- decode ------------------------------------------------------------------
     wd = synth.WORKLOADS["decode"]
     x0 = synth.make(wd)
@@ -383,6 +427,8 @@ def main() -> int:
                      "call_achieved_gbs": round(nbytes / (ms_events / 1e3) / 1e9, 1),
                      "useful_tflops": round(useful_tflops, 2),
                      "mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4)},
+        "prefill_long": long_res,
+        "prefill_varlen": varlen_res,
         "prefill_gating": {"call": "gdn_chunk_fwd_gating (gates formed in the kernels from a, b)",
                            "ms_per_call_events": round(ms_gating, 5),
                            "tokens_per_s": round(tokens / (ms_gating / 1e3), 1)},
