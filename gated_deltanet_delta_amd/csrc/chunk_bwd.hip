@@ -378,8 +378,11 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     // row tile a of M S (M = K or Q, C x DK, S DK x 16): A = M[16 a + c][k + g], B = S[k + g][c]
     auto rows_times_state = [&](const float* M, const float* Sx, int a) {
         f32x4b acc = z4;
-#pragma unroll 2
-        for (int kk = 0; kk < DK; kk += 4) acc = mfma4(M[(16 * a + cl) * LK + kk + gl], Sx[(kk + gl) * LW + cl], acc);
+        // (16-deep blocks of four products, so that a block's LDS reads are in flight together)
+        for (int k0 = 0; k0 < DK; k0 += 16)
+#pragma unroll
+            for (int kk = k0; kk < k0 + 16; kk += 4)
+                acc = mfma4(M[(16 * a + cl) * LK + kk + gl], Sx[(kk + gl) * LW + cl], acc);
         return acc;
     };
     // K S and X = V - gamma K S (waves 0-3); with `qs`, also the row sums (QS).dO (waves 4-7)
@@ -410,8 +413,10 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         if (wave < 4) {
             const int a = wave;
             f32x4b acc = z4;
-            for (int kk = 0; kk < 16 * (a + 1); kk += 4)
-                acc = mfma4(sm.T[(16 * a + cl) * kLC + kk + gl], sm.beta[kk + gl] * sm.VX[(kk + gl) * LW + cl], acc);
+            for (int k0 = 0; k0 < 16 * (a + 1); k0 += 16)
+#pragma unroll
+                for (int kk = k0; kk < k0 + 16; kk += 4)
+                    acc = mfma4(sm.T[(16 * a + cl) * kLC + kk + gl], sm.beta[kk + gl] * sm.VX[(kk + gl) * LW + cl], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.U[(16 * a + 4 * gl + r) * LW + cl] = acc[r];
         } else if (kd) {
@@ -425,13 +430,14 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     // key tile b of M^T (w o Y) over the chunk (M = K or Q [C][DK], Y C x 16, w per token)
     auto keys_times = [&](const float* M, const float* Y, const float* w1, const float* w2, int b) {
         f32x4b acc = z4;
-#pragma unroll 2
-        for (int kk = 0; kk < kC; kk += 4) {
-            const int t = kk + gl;
-            float wt = w1[t];
-            if (w2) wt *= w2[t];
-            acc = mfma4(M[t * LK + 16 * b + cl], wt * Y[t * LW + cl], acc);
-        }
+        for (int k0 = 0; k0 < kC; k0 += 16)
+#pragma unroll
+            for (int kk = k0; kk < k0 + 16; kk += 4) {
+                const int t = kk + gl;
+                float wt = w1[t];
+                if (w2) wt *= w2[t];
+                acc = mfma4(M[t * LK + 16 * b + cl], wt * Y[t * LW + cl], acc);
+            }
         return acc;
     };
 
@@ -486,8 +492,10 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         if (wave < 4) {
             const int a = wave;
             f32x4b acc = z4;
-            for (int kk = 16 * a; kk < kC; kk += 4)
-                acc = mfma4(sm.P[(kk + gl) * kLC + 16 * a + cl], sm.dO[(kk + gl) * LW + cl], acc);
+            for (int k0 = 16 * a; k0 < kC; k0 += 16)
+#pragma unroll
+                for (int kk = k0; kk < k0 + 16; kk += 4)
+                    acc = mfma4(sm.P[(kk + gl) * kLC + 16 * a + cl], sm.dO[(kk + gl) * LW + cl], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * a + 4 * gl + r;
@@ -502,8 +510,10 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         if (wave < 4) {
             const int a = wave;
             f32x4b acc = z4;
-            for (int kk = 16 * a; kk < kC; kk += 4)
-                acc = mfma4(sm.T[(kk + gl) * kLC + 16 * a + cl], sm.dU[(kk + gl) * LW + cl], acc);
+            for (int k0 = 16 * a; k0 < kC; k0 += 16)
+#pragma unroll
+                for (int kk = k0; kk < k0 + 16; kk += 4)
+                    acc = mfma4(sm.T[(kk + gl) * kLC + 16 * a + cl], sm.dU[(kk + gl) * LW + cl], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * a + 4 * gl + r;
