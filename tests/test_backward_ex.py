@@ -170,3 +170,19 @@ def test_backward_ex_full_prefill_T4096():
     s0 = x["initial_state"]
     got = run(x, a, b, A, dt, d_o, d_final, s0, qk_l2norm=True)
     compare("bwd_ex full prefill", got, reference(x, a, b, A, dt, d_o, d_final, f64(s0), True))
+
+
+def test_backward_ex_no_tokens():
+    """No tokens with every option: the start-state gradient is d_final itself, dA_log and ddt_bias
+    are zero, and a padding row of the pool still gets its (passed-through) gradient."""
+    wl = with_dims(WL["prefill"], B=2, Hk=1, Hv=2, dk=64, dv=64, init_state=True)
+    x = synth.make(wl, T=0, seed=121)
+    a, b, A, dt = raw_gates(x, torch.bfloat16, 122)
+    pool = torch.from_numpy((0.02 * np.random.default_rng(123).standard_normal(
+        (3, wl.Hv, wl.dk, wl.dv))).astype(np.float32))
+    idx = torch.tensor([2, -1], dtype=torch.int32)
+    d_o, d_final = output_grads((2, 0, wl.Hv, wl.dv), (2, wl.Hv, wl.dk, wl.dv), 124)
+    got = run(x, a, b, A, dt, d_o, d_final, pool, idx=idx, qk_l2norm=True)
+    assert all(t.numel() == 0 for t in got[:5])
+    assert torch.equal(got[5].cpu(), torch.zeros(wl.Hv)) and torch.equal(got[6].cpu(), torch.zeros(wl.Hv))
+    assert torch.equal(got[7].cpu(), d_final)
