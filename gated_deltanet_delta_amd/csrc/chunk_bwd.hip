@@ -24,14 +24,16 @@
 //   bwd_slice_kernel  one workgroup per (sequence, v-head, 16-column slice of the state): a forward
 //                     sweep for the chunk-start states, then the chunks in reverse with everything
 //                     that involves the slice's columns: dV, dL/dS, this slice's parts of dbeta and
-//                     dG, of the dq/dk terms that go through S, U or D, and of the two C x C
-//                     matrices dP o Gam and dBm o Gam.  Columns never interact, so these are exact
-//                     partial sums over the slices.
-//   bwd_combine_kernel  one workgroup per (chunk, q/k head): sums the slices' partials (and the
-//                     v-heads sharing the q/k head) in a fixed order, forms the three C x C x dk
-//                     products once, and writes dq, dk, dg and dbeta.
-// The slice kernel's products run on the fp32 matrix cores; the prepare and combine kernels' on the
-// vector ALU with small register tiles.
+//                     dG and of the two C x C matrices dP o Gam and dBm o Gam (columns never
+//                     interact, so these are exact partial sums over the slices), and its columns of
+//                     U, dY and of D at every chunk's end, for the combine kernel.
+//   bwd_combine_kernel  one workgroup per (chunk, q/k head), on the fp32 matrix cores: the dq and dk
+//                     terms through the state (dO S^T, U D^T, dY S^T, contracted over dv for every
+//                     v-head of the q/k head) and the three C x C x dk products with the C x C
+//                     matrices summed over the slices and v-heads in a fixed order; then dq, dk, dg
+//                     and dbeta.
+// The slice kernel's products run on the fp32 matrix cores; the prepare kernel's on the vector ALU
+// with small register tiles.
 
 #include <type_traits>
 
@@ -286,8 +288,8 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     const TG* __restrict__ g, const TG* __restrict__ beta, const float* __restrict__ initial_state,
     const int32_t* __restrict__ cu_seqlens, const float* __restrict__ d_o,
     const float* __restrict__ d_final, int T, int Hk, int Hv, int dv, const float* __restrict__ mats,
-    float* __restrict__ ckpt, float* __restrict__ pmat, float* __restrict__ part_dq,
-    float* __restrict__ part_dk, float* __restrict__ part_dg, float* __restrict__ part_db,
+    float* __restrict__ ckpt, float* __restrict__ pmat, float* __restrict__ ws_d,
+    float* __restrict__ ws_u, float* __restrict__ ws_y, float* __restrict__ part_dg, float* __restrict__ part_db,
     float* __restrict__ dv_out, float* __restrict__ d_initial, long long rows, int max_slots) {
     using L = SliceLds<DK>;
     constexpr int LK = L::LK, LW = L::LW;
@@ -480,9 +482,11 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         const int cs = t0 + ci * kC;
         const size_t tok0 = (size_t)row * T + cs;
         const int slot = slot0 + ci;
+        float* wd = ws_d + ((size_t)slot * Hv + h) * SSL;
         for (int e = tid; e < DK * kW; e += kST) {
             const int i = e / kW, c = e % kW;
             sm.S[i * LW + c] = ck_at(ci)[(size_t)i * dv + c0 + c];
+            wd[(size_t)i * dv + c0 + c] = sm.D[i * LW + c];    // D at this chunk's end, for the combine
         }
         const int Lc = load_chunk(ci, std::true_type{});
         ks_x(true);
@@ -514,11 +518,15 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
 #pragma unroll
                 for (int kk = k0; kk < k0 + 16; kk += 4)
                     acc = mfma4(sm.T[(kk + gl) * kLC + 16 * a + cl], sm.dU[(kk + gl) * LW + cl], acc);
+            float* wu = ws_u + ((size_t)slot * Hv + h) * kC * dv + c0 + cl;
+            float* wy = ws_y + ((size_t)slot * Hv + h) * kC * dv + c0 + cl;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * a + 4 * gl + r;
                 const float dy = acc[r], dx = sm.beta[t] * dy;
                 sm.KD[t * LW + cl] = dy;
+                wu[(size_t)t * dv] = sm.U[t * LW + cl];     // U and dY (zero past the chunk's end),
+                wy[(size_t)t * dv] = dy;                    // for the combine
                 if (t < Lc) dv_out[((tok0 + t) * Hv + h) * dv + c0 + cl] = dx;
                 const float s1 = sum16(sm.VX[t * LW + cl] * dy);
                 const float s2 = sum16(sm.KS[t * LW + cl] * dx);
@@ -568,30 +576,6 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         if (lane == 0) sm.red[wave] = sd;
         __syncthreads();
 
-        // this slice's dq, dk terms through S, U, D: gamma dO S^T and f U D^T - gamma beta dY S^T,
-        // tile (a, b) of C x DK for p = 4 wave .. 4 wave + 3 (when DK = 64, waves 4-7 have none)
-        float* pq = part_dq + (size_t)sl * rows * Hv * DK;
-        float* pk = part_dk + (size_t)sl * rows * Hv * DK;
-        for (int p = 4 * wave; p < 4 * wave + 4 && p < 4 * KT; ++p) {
-            const int a = p / KT, b = p % KT;
-            f32x4b aq = z4, au = z4, ay = z4;
-#pragma unroll
-            for (int kk = 0; kk < kW; kk += 4) {
-                const float sb = sm.S[(16 * b + cl) * LW + kk + gl];
-                aq = mfma4(sm.dO[(16 * a + cl) * LW + kk + gl], sb, aq);
-                ay = mfma4(sm.KD[(16 * a + cl) * LW + kk + gl], sb, ay);
-                au = mfma4(sm.U[(16 * a + cl) * LW + kk + gl], sm.D[(16 * b + cl) * LW + kk + gl], au);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * a + 4 * gl + r;
-                if (t < Lc) {
-                    const size_t o = ((tok0 + t) * Hv + h) * DK + 16 * b + cl;
-                    pq[o] = sm.gam[t] * aq[r];
-                    pk[o] = sm.f[t] * au[r] - sm.gam[t] * sm.beta[t] * ay[r];
-                }
-            }
-        }
         // dG (this slice's part) and its reverse running sum, by the first wave (lane = row t);
         // rows and columns of E, and the rows of dA o Bm for dbeta
         if (tid < kC) {
@@ -643,29 +627,139 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------
-// One workgroup per (chunk, q/k head): dq = the slices' terms + (dP o Gam) K, and
-// dk = their terms + (dP o Gam)^T Q + ((dBm o Gam) + (dBm o Gam)^T) K, with the two C x C matrices
-// summed over the slices and the v-heads of the q/k head; dg and dbeta summed over the slices.
-template <int DK, typename TIn>
+// One workgroup per (chunk, q/k head): dq and dk of the chunk's tokens, summed over the v-heads of the
+// q/k head, and dg and dbeta (summed over the slices' partials):
+//     dq = sum_h diag(gamma) dO S^T + (dP o Gam) K
+//     dk = sum_h [diag(f) U D^T - diag(gamma beta) dY S^T] + (dP o Gam)^T Q + ((dBm o Gam) + (dBm o Gam)^T) K
+// with S the chunk-start state (the forward sweep's checkpoint), D the state gradient at the chunk's
+// end, U and dY from the slice kernel, and the C x C matrices summed over v-heads and slices.  All of
+// it runs on the fp32 matrix cores: wave w owns the 16 x 16 output tiles p = w, w + 4, .. of dq and
+// of dk (row tile p / KT, key tile p % KT) and accumulates every term into them.  The first three
+// products contract over dv, taken in 32-column tiles staged in LDS per v-head; the last three over
+// the chunk's tokens.
+constexpr int kTC = 32;          // dv columns per staged tile of the state products
+constexpr int kLT = kTC + 4;     // pitch of those tiles: rows 16 a + c, columns k + g land in distinct banks
+constexpr int kLCc = kC + 4;     // pitch of the C x C matrices in the combine kernel
+
+template <int DK>
+struct CombineLds {
+    static constexpr int LK = DK + 16;   // K, Q rows: reads at rows k + g, columns 16 b + c are conflict-free
+    struct StateTerms {
+        float S[DK * kLT], D[DK * kLT];              // [key][column]
+        float O[kC * kLT], U[kC * kLT], Y[kC * kLT]; // [token][column], scaled by gamma, f, -gamma beta
+    };
+    struct ChunkTerms {
+        float K[kC * LK], Q[kC * LK];
+        float P[kC * kLCc], B[kC * kLCc];
+    };
+    union {
+        StateTerms st;
+        ChunkTerms ct;
+    };
+    float G[kC], gam[kC], f[kC], beta[kC];
+};
+
+template <int DK, typename TIn, typename TG>
 __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
-    const TIn* __restrict__ q, const TIn* __restrict__ k, const int32_t* __restrict__ cu_seqlens, int N,
-    int T, int Hk, int Hv, int slices, long long rows, const float* __restrict__ pmat,
-    const float* __restrict__ part_dq, const float* __restrict__ part_dk, const float* __restrict__ part_dg,
-    const float* __restrict__ part_db, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dg,
-    float* __restrict__ db) {
-    constexpr int LK = DK + 1;
-    __shared__ float sK[kC * LK], sQ[kC * LK];
-    __shared__ float sP[kC * kLC], sB[kC * kLC];
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TG* __restrict__ g,
+    const TG* __restrict__ beta, const float* __restrict__ d_o, const int32_t* __restrict__ cu_seqlens,
+    int N, int T, int Hk, int Hv, int dv, int slices, long long rows, const float* __restrict__ pmat,
+    const float* __restrict__ ckpt, const float* __restrict__ ws_d, const float* __restrict__ ws_u,
+    const float* __restrict__ ws_y, const float* __restrict__ part_dg, const float* __restrict__ part_db,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dg, float* __restrict__ db) {
+    using Lds = CombineLds<DK>;
+    constexpr int LK = Lds::LK;
+    constexpr int KT = DK / 16;                  // key tiles
+    constexpr int NT = 4 * KT / 4;               // output tiles per wave (of dq, and of dk)
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    Lds& sm = *reinterpret_cast<Lds*>(smem_raw);
     const int slot = blockIdx.x, kh = blockIdx.y;
     int n, row, cs, L;
     if (!bwd_locate(slot, cu_seqlens, N, T, n, row, cs, L)) return;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int gl = lane >> 4, cl = lane & 15;
     const size_t tok0 = (size_t)row * T + cs;
     const int G = Hv / Hk;
-    stage_rows<DK, LK, kThreads>(k, tok0, Hk, kh, L, sK, tid);
-    stage_rows<DK, LK, kThreads>(q, tok0, Hk, kh, L, sQ, tid);
-    // the two C x C matrices, summed over v-heads and slices (each partial's loads issued together),
-    // then B symmetrised in LDS
+    const f32x4b z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4b aq[NT], ak[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) aq[j] = ak[j] = z4;
+
+    // ---- the state terms, per v-head and 32-column tile of dv ----
+    for (int x = 0; x < G; ++x) {
+        const int h = kh * G + x;
+        if (tid < kC) {
+            const bool in = tid < L;
+            sm.G[tid] = in ? to_f32(g[(tok0 + tid) * Hv + h]) : 0.f;
+            sm.beta[tid] = in ? to_f32(beta[(tok0 + tid) * Hv + h]) : 0.f;
+        }
+        __syncthreads();
+        chunk_decays(sm.G, sm.gam, sm.f, tid);
+        __syncthreads();
+        const float* Sg = ckpt + ((size_t)slot * Hv + h) * DK * dv;
+        const float* Dg = ws_d + ((size_t)slot * Hv + h) * DK * dv;
+        const float* Ug = ws_u + ((size_t)slot * Hv + h) * kC * dv;
+        const float* Yg = ws_y + ((size_t)slot * Hv + h) * kC * dv;
+        for (int c0 = 0; c0 < dv; c0 += kTC) {
+            // stage (16-byte pieces, all loads first): S, D [DK][32], gamma dO, f U, -gamma beta dY [C][32]
+            constexpr int PS = DK * kTC / 4 / kThreads, PT = kC * kTC / 4 / kThreads;
+            float4 vs[PS], vd[PS], vo[PT], vu[PT], vy[PT];
+#pragma unroll
+            for (int it = 0; it < PS; ++it) {
+                const int e = 4 * (tid + kThreads * it), i = e / kTC, c = e % kTC;
+                vs[it] = *reinterpret_cast<const float4*>(Sg + (size_t)i * dv + c0 + c);
+                vd[it] = *reinterpret_cast<const float4*>(Dg + (size_t)i * dv + c0 + c);
+            }
+#pragma unroll
+            for (int it = 0; it < PT; ++it) {
+                const int e = 4 * (tid + kThreads * it), t = e / kTC, c = e % kTC;
+                const float* op = d_o + ((tok0 + min(t, L - 1)) * Hv + h) * dv + c0 + c;   // (4-byte aligned)
+                vo[it] = make_float4(op[0], op[1], op[2], op[3]);
+                vu[it] = *reinterpret_cast<const float4*>(Ug + (size_t)t * dv + c0 + c);
+                vy[it] = *reinterpret_cast<const float4*>(Yg + (size_t)t * dv + c0 + c);
+            }
+#pragma unroll
+            for (int it = 0; it < PS; ++it) {
+                const int e = 4 * (tid + kThreads * it), i = e / kTC, c = e % kTC;
+                *reinterpret_cast<float4*>(&sm.st.S[i * kLT + c]) = vs[it];
+                *reinterpret_cast<float4*>(&sm.st.D[i * kLT + c]) = vd[it];
+            }
+#pragma unroll
+            for (int it = 0; it < PT; ++it) {
+                const int e = 4 * (tid + kThreads * it), t = e / kTC, c = e % kTC;
+                const float so = t < L ? sm.gam[t] : 0.f, su = sm.f[t], sy = -sm.gam[t] * sm.beta[t];
+                *reinterpret_cast<float4*>(&sm.st.O[t * kLT + c]) =
+                    make_float4(so * vo[it].x, so * vo[it].y, so * vo[it].z, so * vo[it].w);
+                *reinterpret_cast<float4*>(&sm.st.U[t * kLT + c]) =
+                    make_float4(su * vu[it].x, su * vu[it].y, su * vu[it].z, su * vu[it].w);
+                *reinterpret_cast<float4*>(&sm.st.Y[t * kLT + c]) =
+                    make_float4(sy * vy[it].x, sy * vy[it].y, sy * vy[it].z, sy * vy[it].w);
+            }
+            __syncthreads();
+            // (each tile's 32 columns summed on their own, then added to the running totals: short
+            // fp32 chains instead of one chain over every v-head and column)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int p = wave + 4 * j, a = p / KT, b = p % KT;
+                f32x4b tq = z4, tk = z4;
+#pragma unroll
+                for (int kk = 0; kk < kTC; kk += 4) {
+                    const float sb = sm.st.S[(16 * b + cl) * kLT + kk + gl];
+                    tq = mfma4(sm.st.O[(16 * a + cl) * kLT + kk + gl], sb, tq);
+                    tk = mfma4(sm.st.Y[(16 * a + cl) * kLT + kk + gl], sb, tk);
+                    tk = mfma4(sm.st.U[(16 * a + cl) * kLT + kk + gl], sm.st.D[(16 * b + cl) * kLT + kk + gl], tk);
+                }
+                aq[j] += tq;
+                ak[j] += tk;
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- the chunk terms: K, Q, and the C x C matrices summed over v-heads and slices ----
+    stage_rows<DK, LK, kThreads>(k, tok0, Hk, kh, L, sm.ct.K, tid);
+    stage_rows<DK, LK, kThreads>(q, tok0, Hk, kh, L, sm.ct.Q, tid);
     {
         constexpr int PE = kMat / kThreads;
         float ap[PE], ab[PE];
@@ -689,80 +783,51 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
 #pragma unroll
         for (int it = 0; it < PE; ++it) {
             const int e = tid + kThreads * it, t = e / kC, j = e % kC;
-            sP[t * kLC + j] = ap[it];
-            sB[t * kLC + j] = ab[it];
+            sm.ct.P[t * kLCc + j] = ap[it];
+            sm.ct.B[t * kLCc + j] = ab[it];
         }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < PE; ++it) {
             const int e = tid + kThreads * it, t = e / kC, j = e % kC;
-            ab[it] = sB[t * kLC + j] + sB[j * kLC + t];
+            ab[it] = sm.ct.B[t * kLCc + j] + sm.ct.B[j * kLCc + t];
         }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < PE; ++it) {
             const int e = tid + kThreads * it, t = e / kC, j = e % kC;
-            sB[t * kLC + j] = ab[it];
+            sm.ct.B[t * kLCc + j] = ab[it];
         }
     }
     __syncthreads();
-    // dq, dk: thread (ty, tx) owns rows 4 ty .. 4 ty + 3 and keys tx, tx + 16, ..
-    {
-        constexpr int NI = DK / 16;
-        const int ty = tid >> 4, tx = tid & 15;
-        float aq[4][NI] = {}, ak[4][NI] = {};
-        for (int j = 0; j < kC; ++j) {
-            float p[4], pt[4], b[4], kj[NI], qj[NI];
+    // dq += P' K, dk += P'^T Q + B' K over the chunk's tokens (16-deep blocks of four products)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[r] = sP[(4 * ty + r) * kLC + j];
-                pt[r] = sP[j * kLC + 4 * ty + r];
-                b[r] = sB[(4 * ty + r) * kLC + j];
+    for (int j = 0; j < NT; ++j) {
+        const int p = wave + 4 * j, a = p / KT, b = p % KT;
+        for (int k0 = 0; k0 < kC; k0 += 16) {
+            f32x4b tq = z4, tk = z4;
+#pragma unroll
+            for (int kk = k0; kk < k0 + 16; kk += 4) {
+                const float kb_ = sm.ct.K[(kk + gl) * LK + 16 * b + cl];
+                tq = mfma4(sm.ct.P[(16 * a + cl) * kLCc + kk + gl], kb_, tq);
+                tk = mfma4(sm.ct.P[(kk + gl) * kLCc + 16 * a + cl], sm.ct.Q[(kk + gl) * LK + 16 * b + cl], tk);
+                tk = mfma4(sm.ct.B[(16 * a + cl) * kLCc + kk + gl], kb_, tk);
             }
-#pragma unroll
-            for (int m = 0; m < NI; ++m) {
-                kj[m] = sK[j * LK + tx + 16 * m];
-                qj[m] = sQ[j * LK + tx + 16 * m];
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int m = 0; m < NI; ++m) {
-                    aq[r][m] += p[r] * kj[m];
-                    ak[r][m] += pt[r] * qj[m] + b[r] * kj[m];
-                }
+            aq[j] += tq;
+            ak[j] += tk;
         }
-        // the slices' terms, summed over v-heads and slices (rows past L read row L - 1, in bounds)
-        for (int x = 0; x < G; ++x)
-            for (int s = 0; s < slices; ++s) {
-                float lq[4][NI], lk[4][NI];
+    }
+    // lane (g, c) of tile (a, b), element r: row 16 a + 4 g + r, key 16 b + c
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = min(4 * ty + r, L - 1);
-#pragma unroll
-                    for (int m = 0; m < NI; ++m) {
-                        const size_t o = (((size_t)s * rows + tok0 + t) * Hv + kh * G + x) * DK + tx + 16 * m;
-                        lq[r][m] = part_dq[o];
-                        lk[r][m] = part_dk[o];
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int m = 0; m < NI; ++m) {
-                        aq[r][m] += lq[r][m];
-                        ak[r][m] += lk[r][m];
-                    }
-            }
+    for (int j = 0; j < NT; ++j) {
+        const int p = wave + 4 * j, a = p / KT, b = p % KT;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 4 * ty + r;
-            if (t >= L) continue;
-#pragma unroll
-            for (int m = 0; m < NI; ++m) {
-                const int i = tx + 16 * m;
-                dq[((tok0 + t) * Hk + kh) * DK + i] = aq[r][m];
-                dk[((tok0 + t) * Hk + kh) * DK + i] = ak[r][m];
+            const int t = 16 * a + 4 * gl + r;
+            if (t < L) {
+                const size_t o = ((tok0 + t) * Hk + kh) * DK + 16 * b + cl;
+                dq[o] = aq[j][r];
+                dk[o] = ak[j][r];
             }
         }
     }
@@ -792,7 +857,7 @@ __global__ __launch_bounds__(kThreads) void bwd_zero_kernel(float* __restrict__ 
 }
 
 struct BwdLayout {
-    size_t ckpt, mats, pmat, pq, pk, pg, pb, total;
+    size_t ckpt, mats, pmat, wd, wu, wy, pg, pb, total;
     int slots;
 };
 
@@ -807,8 +872,9 @@ BwdLayout bwd_layout(int B, int T, int Hv, int dk, int dv, int N) {
     l.ckpt = off; off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * dk * dv);
     l.mats = off; off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * 3 * kMat);
     l.pmat = off; off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * slices * 2 * kMat);
-    l.pq = off;   off = align256b(off + sizeof(float) * (size_t)slices * rows * Hv * dk);
-    l.pk = off;   off = align256b(off + sizeof(float) * (size_t)slices * rows * Hv * dk);
+    l.wd = off;   off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * dk * dv);
+    l.wu = off;   off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * kC * dv);
+    l.wy = off;   off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * kC * dv);
     l.pg = off;   off = align256b(off + sizeof(float) * (size_t)slices * rows * Hv);
     l.pb = off;   off = align256b(off + sizeof(float) * (size_t)slices * rows * Hv);
     l.total = off;
@@ -826,8 +892,9 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
     float* ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
     float* mats = reinterpret_cast<float*>(ws + lay.mats);
     float* pmat = reinterpret_cast<float*>(ws + lay.pmat);
-    float* pq = reinterpret_cast<float*>(ws + lay.pq);
-    float* pk = reinterpret_cast<float*>(ws + lay.pk);
+    float* wd = reinterpret_cast<float*>(ws + lay.wd);
+    float* wu = reinterpret_cast<float*>(ws + lay.wu);
+    float* wy = reinterpret_cast<float*>(ws + lay.wy);
     float* pg = reinterpret_cast<float*>(ws + lay.pg);
     float* pb = reinterpret_cast<float*>(ws + lay.pb);
     hipError_t e;
@@ -848,7 +915,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), static_cast<const TG*>(a.g),
                        static_cast<const TG*>(a.beta), a.initial_state, a.cu_seqlens, a.d_o, a.d_final,
-                       a.T, a.Hk, a.Hv, a.dv, mats, ckpt, pmat, pq, pk, pg, pb, a.dv_out, a.d_initial, rows,
+                       a.T, a.Hk, a.Hv, a.dv, mats, ckpt, pmat, wd, wu, wy, pg, pb, a.dv_out, a.d_initial, rows,
                        lay.slots);
     if ((e = hipGetLastError()) != hipSuccess || rows == 0) return e;
     if (packed) {
@@ -858,10 +925,15 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (slots > 0) {
-        hipLaunchKernelGGL((bwd_combine_kernel<DK, TIn>), dim3((unsigned)slots, (unsigned)a.Hk), dim3(kThreads), 0,
-                           a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), a.cu_seqlens,
-                           a.N, a.T, a.Hk, a.Hv, slices, rows, pmat, pq, pk, pg, pb, a.dq, a.dk_out, a.dg,
-                           a.dbeta);
+        const auto ck = bwd_combine_kernel<DK, TIn, TG>;
+        const size_t cbytes = sizeof(CombineLds<DK>);
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(ck),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)cbytes)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(ck, dim3((unsigned)slots, (unsigned)a.Hk), dim3(kThreads), cbytes, a.stream,
+                           static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), static_cast<const TG*>(a.g),
+                           static_cast<const TG*>(a.beta), a.d_o, a.cu_seqlens, a.N, a.T, a.Hk, a.Hv, a.dv, slices,
+                           rows, pmat, ckpt, wd, wu, wy, pg, pb, a.dq, a.dk_out, a.dg, a.dbeta);
     }
     return hipGetLastError();
 }
