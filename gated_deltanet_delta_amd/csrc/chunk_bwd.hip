@@ -23,15 +23,15 @@
 //                     decayed Bm and P and the triangular inverse T, to the workspace.
 //   bwd_slice_kernel  one workgroup per (sequence, v-head, 16-column slice of the state): a forward
 //                     sweep for the chunk-start states, then the chunks in reverse with everything
-//                     that involves the slice's columns: dV, dL/dS, this slice's parts of dbeta and
-//                     dG and of the two C x C matrices dP o Gam and dBm o Gam (columns never
-//                     interact, so these are exact partial sums over the slices), and its columns of
-//                     U, dY and of D at every chunk's end, for the combine kernel.
-//   bwd_combine_kernel  one workgroup per (chunk, q/k head), on the fp32 matrix cores: the dq and dk
-//                     terms through the state (dO S^T, U D^T, dY S^T, contracted over dv for every
-//                     v-head of the q/k head) and the three C x C x dk products with the C x C
-//                     matrices summed over the slices and v-heads in a fixed order; then dq, dk, dg
-//                     and dbeta.
+//                     that involves only the slice's columns: dV, dL/dS, and this slice's parts of
+//                     dbeta and dG through the state (columns never interact, so these are exact
+//                     partial sums over the slices), and its columns of U, dY and of D at every
+//                     chunk's end, for the combine kernel.
+//   bwd_combine_kernel  one workgroup per (chunk, q/k head), on the fp32 matrix cores: per v-head the
+//                     C x C gradients dP, dA (contracted over dv) and their dG and dbeta terms; the
+//                     dq and dk terms through the state (dO S^T, U D^T, dY S^T) and the three
+//                     C x C x dk products with the C x C matrices summed over the v-heads in a fixed
+//                     order; then dq, dk, dg and dbeta.
 // The slice kernel's products run on the fp32 matrix cores; the prepare kernel's on the vector ALU
 // with small register tiles.
 
@@ -267,8 +267,7 @@ struct SliceLds {
     float Q[kC * LK];
     float S[DK * LW];        // chunk-start state, this slice
     float D[DK * LW];        // dL/dS at the chunk end, this slice
-    float T[kC * kLC];       // T, then E = dP o P + dBm o Bm
-    float B[kC * kLC];       // Bm, then dA o Bm
+    float T[kC * kLC];       // T
     float P[kC * kLC];       // P
     float VX[kC * LW];       // V, then X
     float KS[kC * LW];
@@ -288,7 +287,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     const TG* __restrict__ g, const TG* __restrict__ beta, const float* __restrict__ initial_state,
     const int32_t* __restrict__ cu_seqlens, const float* __restrict__ d_o,
     const float* __restrict__ d_final, int T, int Hk, int Hv, int dv, const float* __restrict__ mats,
-    float* __restrict__ ckpt, float* __restrict__ pmat, float* __restrict__ ws_d,
+    float* __restrict__ ckpt, float* __restrict__ ws_d,
     float* __restrict__ ws_u, float* __restrict__ ws_y, float* __restrict__ part_dg, float* __restrict__ part_db,
     float* __restrict__ dv_out, float* __restrict__ d_initial, long long rows, int max_slots) {
     using L = SliceLds<DK>;
@@ -328,14 +327,15 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         const int cs = t0 + ci * kC, Lc = min(kC, t1 - cs);
         const size_t tok0 = (size_t)row * T + cs;
         // the three C x C matrices: 16-byte pieces, all loads first
-        constexpr int NM = rev ? 3 : 1, PM = kMat / 4 / kST;
+        // (T, and in the reverse sweep P: matrices 0 and 2 of the prep kernel's T, Bm, P)
+        constexpr int NM = rev ? 2 : 1, PM = kMat / 4 / kST;
         const float* mT = mats + ((size_t)(slot0 + ci) * Hv + h) * 3 * kMat;
         float4 mv[NM][PM];
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int it = 0; it < PM; ++it)
-                mv[m][it] = *reinterpret_cast<const float4*>(mT + m * kMat + 4 * (tid + kST * it));
+                mv[m][it] = *reinterpret_cast<const float4*>(mT + 2 * m * kMat + 4 * (tid + kST * it));
         // this slice of V (and dO): one element per thread and row pass
         constexpr int PV = kC * kW / kST;
         float vv[PV], ov[PV];
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
             sm.VX[t * LW + c] = vv[it];
             if (rev) sm.dO[t * LW + c] = ov[it];
         }
-        float* mdst[3] = {sm.T, sm.B, sm.P};
+        float* mdst[2] = {sm.T, sm.P};
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -537,35 +537,6 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
             }
         }
         __syncthreads();
-        // the C x C gradients, tile (a, b) = (p / 4, p % 4) for p = wave, wave + 8: this slice's
-        // dP o Gam and dBm o Gam to the workspace; E = dP o P + dBm o Bm into T and dA o Bm into B
-        float* pP = pmat + (((size_t)slot * Hv + h) * slices + sl) * 2 * kMat;
-        float* pB = pP + kMat;
-        for (int p = wave; p < 16; p += kSW) {
-            const int a = p >> 2, b = p & 3;
-            f32x4b dyu = z4, dou = z4;
-            if (b <= a) {
-#pragma unroll
-                for (int kk = 0; kk < kW; kk += 4) {
-                    const float ub = sm.U[(16 * b + cl) * LW + kk + gl];
-                    dyu = mfma4(sm.KD[(16 * a + cl) * LW + kk + gl], ub, dyu);
-                    dou = mfma4(sm.dO[(16 * a + cl) * LW + kk + gl], ub, dou);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * a + 4 * gl + r, j = 16 * b + cl;
-                const float dA = j < t ? -dyu[r] : 0.f;
-                const float dP = j <= t ? dou[r] : 0.f;
-                const float bm = sm.B[t * kLC + j], pv = sm.P[t * kLC + j];
-                const float dec = j <= t ? expf(sm.G[t] - sm.G[j]) : 0.f;
-                const float dbm = sm.beta[t] * dA;
-                sm.T[t * kLC + j] = dP * pv + dbm * bm;
-                sm.B[t * kLC + j] = dA * bm;
-                pP[t * kC + j] = dP * dec;
-                pB[t * kC + j] = dbm * dec;
-            }
-        }
         // <S, D> over the slice, for dG at the chunk's last row
         float sd = 0.f;
         for (int e = tid; e < DK * kW; e += kST) {
@@ -576,20 +547,14 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         if (lane == 0) sm.red[wave] = sd;
         __syncthreads();
 
-        // dG (this slice's part) and its reverse running sum, by the first wave (lane = row t);
-        // rows and columns of E, and the rows of dA o Bm for dbeta
+        // dG (this slice's part: the terms through the state; those of the C x C matrices are the
+        // combine kernel's) and its reverse running sum, by the first wave (lane = row t)
         if (tid < kC) {
             const int t = tid;
-            float re = 0.f, ce = 0.f, rb = 0.f;
-            for (int r = 0; r < kC; ++r) {
-                re += sm.T[t * kLC + r];
-                ce += sm.T[r * kLC + t];
-                rb += sm.B[t * kLC + r];
-            }
             const float fkdu = sum64(sm.f[t] * sm.r_kdu[t]);
             float sdt = 0.f;
             for (int w = 0; w < kSW; ++w) sdt += sm.red[w];
-            float x = sm.gam[t] * sm.r_qsdo[t] - sm.gam[t] * sm.r_ksdx[t] - sm.f[t] * sm.r_kdu[t] + re - ce;
+            float x = sm.gam[t] * sm.r_qsdo[t] - sm.gam[t] * sm.r_ksdx[t] - sm.f[t] * sm.r_kdu[t];
             if (t == kC - 1) x += sm.gam[kC - 1] * sdt + fkdu;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
@@ -599,7 +564,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
             if (t < Lc) {
                 const size_t o = (size_t)sl * rows * Hv + (tok0 + t) * Hv + h;
                 part_dg[o] = x;
-                part_db[o] = sm.r_db[t] + rb;
+                part_db[o] = sm.r_db[t];
             }
         }
         __syncthreads();
@@ -627,16 +592,18 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------
-// One workgroup per (chunk, q/k head): dq and dk of the chunk's tokens, summed over the v-heads of the
-// q/k head, and dg and dbeta (summed over the slices' partials):
+// One workgroup per (chunk, q/k head): everything that needs a v-head's whole dv.  Per v-head h of
+// the q/k head, with S the chunk-start state (the forward sweep's checkpoint), D the state gradient
+// at the chunk's end, and U, dY from the slice kernel:
+//     dP = (dO U^T) (j <= t),   dA = -(dY U^T) (j < t),   dBm = diag(beta) dA
+//     E = dP o P + dBm o Bm:    dG_t += (rows - columns of E)_t,   dbeta_t += (rows of dA o Bm)_t
+// added, as reverse running sums for dg, to the slices' partials; then, summed over the v-heads,
 //     dq = sum_h diag(gamma) dO S^T + (dP o Gam) K
 //     dk = sum_h [diag(f) U D^T - diag(gamma beta) dY S^T] + (dP o Gam)^T Q + ((dBm o Gam) + (dBm o Gam)^T) K
-// with S the chunk-start state (the forward sweep's checkpoint), D the state gradient at the chunk's
-// end, U and dY from the slice kernel, and the C x C matrices summed over v-heads and slices.  All of
-// it runs on the fp32 matrix cores: wave w owns the 16 x 16 output tiles p = w, w + 4, .. of dq and
-// of dk (row tile p / KT, key tile p % KT) and accumulates every term into them.  The first three
-// products contract over dv, taken in 32-column tiles staged in LDS per v-head; the last three over
-// the chunk's tokens.
+// All products run on the fp32 matrix cores.  Wave w owns the 16 x 16 output tiles p = w, w + 4, ..
+// of dq and of dk (row tile p / KT, key tile p % KT) and the tiles (a, w) of the C x C matrices.  The
+// products over dv take it in 32-column tiles staged in LDS; each tile's (and each 16-token block's)
+// sum is formed on its own and then added to the running total, which keeps the fp32 chains short.
 constexpr int kTC = 32;          // dv columns per staged tile of the state products
 constexpr int kLT = kTC + 4;     // pitch of those tiles: rows 16 a + c, columns k + g land in distinct banks
 constexpr int kLCc = kC + 4;     // pitch of the C x C matrices in the combine kernel
@@ -647,6 +614,10 @@ struct CombineLds {
     struct StateTerms {
         float S[DK * kLT], D[DK * kLT];              // [key][column]
         float O[kC * kLT], U[kC * kLT], Y[kC * kLT]; // [token][column], scaled by gamma, f, -gamma beta
+        float Ou[kC * kLT], Uu[kC * kLT], Yu[kC * kLT];  // the same unscaled, for dP and dA
+    };
+    struct CCTerms {                                 // (over S and D once a v-head's dv is done)
+        float E[kC * kLCc], F[kC * kLCc];            // E and dA o Bm
     };
     struct ChunkTerms {
         float K[kC * LK], Q[kC * LK];
@@ -654,6 +625,7 @@ struct CombineLds {
     };
     union {
         StateTerms st;
+        CCTerms cc;
         ChunkTerms ct;
     };
     float G[kC], gam[kC], f[kC], beta[kC];
@@ -663,14 +635,14 @@ template <int DK, typename TIn, typename TG>
 __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TG* __restrict__ g,
     const TG* __restrict__ beta, const float* __restrict__ d_o, const int32_t* __restrict__ cu_seqlens,
-    int N, int T, int Hk, int Hv, int dv, int slices, long long rows, const float* __restrict__ pmat,
+    int N, int T, int Hk, int Hv, int dv, int slices, long long rows, const float* __restrict__ mats,
     const float* __restrict__ ckpt, const float* __restrict__ ws_d, const float* __restrict__ ws_u,
     const float* __restrict__ ws_y, const float* __restrict__ part_dg, const float* __restrict__ part_db,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dg, float* __restrict__ db) {
     using Lds = CombineLds<DK>;
     constexpr int LK = Lds::LK;
     constexpr int KT = DK / 16;                  // key tiles
-    constexpr int NT = 4 * KT / 4;               // output tiles per wave (of dq, and of dk)
+    constexpr int NT = KT;                       // output tiles per wave (of dq, and of dk)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Lds& sm = *reinterpret_cast<Lds*>(smem_raw);
     const int slot = blockIdx.x, kh = blockIdx.y;
@@ -685,8 +657,10 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     f32x4b aq[NT], ak[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) aq[j] = ak[j] = z4;
+    f32x4b sp[4], sb[4];                         // sum over v-heads of dP o Gam, dBm o Gam: tiles (j, wave)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sp[j] = sb[j] = z4;
 
-    // ---- the state terms, per v-head and 32-column tile of dv ----
     for (int x = 0; x < G; ++x) {
         const int h = kh * G + x;
         if (tid < kC) {
@@ -701,8 +675,13 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
         const float* Dg = ws_d + ((size_t)slot * Hv + h) * DK * dv;
         const float* Ug = ws_u + ((size_t)slot * Hv + h) * kC * dv;
         const float* Yg = ws_y + ((size_t)slot * Hv + h) * kC * dv;
+        f32x4b cp[4], ca[4];                     // dO U^T and dY U^T, tiles (j, wave)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cp[j] = ca[j] = z4;
+        // ---- the products over dv, 32 columns at a time ----
         for (int c0 = 0; c0 < dv; c0 += kTC) {
-            // stage (16-byte pieces, all loads first): S, D [DK][32], gamma dO, f U, -gamma beta dY [C][32]
+            // stage (16-byte pieces, all loads first): S, D [DK][32]; dO, U, dY [C][32], unscaled and
+            // scaled by gamma, f and -gamma beta
             constexpr int PS = DK * kTC / 4 / kThreads, PT = kC * kTC / 4 / kThreads;
             float4 vs[PS], vd[PS], vo[PT], vu[PT], vy[PT];
 #pragma unroll
@@ -715,7 +694,8 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
             for (int it = 0; it < PT; ++it) {
                 const int e = 4 * (tid + kThreads * it), t = e / kTC, c = e % kTC;
                 const float* op = d_o + ((tok0 + min(t, L - 1)) * Hv + h) * dv + c0 + c;   // (4-byte aligned)
-                vo[it] = make_float4(op[0], op[1], op[2], op[3]);
+                const float m = t < L ? 1.f : 0.f;
+                vo[it] = make_float4(m * op[0], m * op[1], m * op[2], m * op[3]);
                 vu[it] = *reinterpret_cast<const float4*>(Ug + (size_t)t * dv + c0 + c);
                 vy[it] = *reinterpret_cast<const float4*>(Yg + (size_t)t * dv + c0 + c);
             }
@@ -725,78 +705,126 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
                 *reinterpret_cast<float4*>(&sm.st.S[i * kLT + c]) = vs[it];
                 *reinterpret_cast<float4*>(&sm.st.D[i * kLT + c]) = vd[it];
             }
+            auto scaled = [](float s_, float4 v) { return make_float4(s_ * v.x, s_ * v.y, s_ * v.z, s_ * v.w); };
 #pragma unroll
             for (int it = 0; it < PT; ++it) {
                 const int e = 4 * (tid + kThreads * it), t = e / kTC, c = e % kTC;
-                const float so = t < L ? sm.gam[t] : 0.f, su = sm.f[t], sy = -sm.gam[t] * sm.beta[t];
-                *reinterpret_cast<float4*>(&sm.st.O[t * kLT + c]) =
-                    make_float4(so * vo[it].x, so * vo[it].y, so * vo[it].z, so * vo[it].w);
-                *reinterpret_cast<float4*>(&sm.st.U[t * kLT + c]) =
-                    make_float4(su * vu[it].x, su * vu[it].y, su * vu[it].z, su * vu[it].w);
-                *reinterpret_cast<float4*>(&sm.st.Y[t * kLT + c]) =
-                    make_float4(sy * vy[it].x, sy * vy[it].y, sy * vy[it].z, sy * vy[it].w);
+                *reinterpret_cast<float4*>(&sm.st.Ou[t * kLT + c]) = vo[it];
+                *reinterpret_cast<float4*>(&sm.st.Uu[t * kLT + c]) = vu[it];
+                *reinterpret_cast<float4*>(&sm.st.Yu[t * kLT + c]) = vy[it];
+                *reinterpret_cast<float4*>(&sm.st.O[t * kLT + c]) = scaled(sm.gam[t], vo[it]);
+                *reinterpret_cast<float4*>(&sm.st.U[t * kLT + c]) = scaled(sm.f[t], vu[it]);
+                *reinterpret_cast<float4*>(&sm.st.Y[t * kLT + c]) = scaled(-sm.gam[t] * sm.beta[t], vy[it]);
             }
             __syncthreads();
-            // (each tile's 32 columns summed on their own, then added to the running totals: short
-            // fp32 chains instead of one chain over every v-head and column)
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int p = wave + 4 * j, a = p / KT, b = p % KT;
                 f32x4b tq = z4, tk = z4;
 #pragma unroll
                 for (int kk = 0; kk < kTC; kk += 4) {
-                    const float sb = sm.st.S[(16 * b + cl) * kLT + kk + gl];
-                    tq = mfma4(sm.st.O[(16 * a + cl) * kLT + kk + gl], sb, tq);
-                    tk = mfma4(sm.st.Y[(16 * a + cl) * kLT + kk + gl], sb, tk);
+                    const float sb_ = sm.st.S[(16 * b + cl) * kLT + kk + gl];
+                    tq = mfma4(sm.st.O[(16 * a + cl) * kLT + kk + gl], sb_, tq);
+                    tk = mfma4(sm.st.Y[(16 * a + cl) * kLT + kk + gl], sb_, tk);
                     tk = mfma4(sm.st.U[(16 * a + cl) * kLT + kk + gl], sm.st.D[(16 * b + cl) * kLT + kk + gl], tk);
                 }
                 aq[j] += tq;
                 ak[j] += tk;
+                __builtin_amdgcn_sched_barrier(0);   // (a tile's operand reads are not hoisted into the
+            }                                        // previous tile: registers stay within budget)
+            // dO U^T and dY U^T, tiles (j, wave) on or below the diagonal
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < wave) continue;
+                f32x4b tp = z4, ta = z4;
+#pragma unroll
+                for (int kk = 0; kk < kTC; kk += 4) {
+                    const float ub = sm.st.Uu[(16 * wave + cl) * kLT + kk + gl];
+                    tp = mfma4(sm.st.Ou[(16 * j + cl) * kLT + kk + gl], ub, tp);
+                    ta = mfma4(sm.st.Yu[(16 * j + cl) * kLT + kk + gl], ub, ta);
+                }
+                cp[j] += tp;
+                ca[j] += ta;
+                __builtin_amdgcn_sched_barrier(0);
             }
             __syncthreads();
         }
+        // ---- the C x C gradients of v-head h: E and dA o Bm to LDS, the v-head sums in registers ----
+        {
+            const float* Bmh = mats + ((size_t)slot * Hv + h) * 3 * kMat + kMat;     // (T, Bm, P)
+            const float* Ph = Bmh + kMat;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * j + 4 * gl + r, i = 16 * wave + cl;        // element (t, i)
+                    const float dP = i <= t ? cp[j][r] : 0.f;
+                    const float dA = i < t ? -ca[j][r] : 0.f;
+                    const float bm = Bmh[t * kC + i], pv = Ph[t * kC + i];
+                    const float dec = i <= t ? expf(sm.G[t] - sm.G[i]) : 0.f;
+                    const float dbm = sm.beta[t] * dA;
+                    sm.cc.E[t * kLCc + i] = dP * pv + dbm * bm;
+                    sm.cc.F[t * kLCc + i] = dA * bm;
+                    sp[j][r] += dP * dec;
+                    sb[j][r] += dbm * dec;
+                }
+        }
+        __syncthreads();
+        // rows minus columns of E (dG, as a reverse running sum) and rows of dA o Bm (dbeta), added
+        // to the slices' partials, by the first wave (lane = row t)
+        if (tid < kC) {
+            const int t = tid;
+            float re = 0.f, ce = 0.f, rb = 0.f;
+            for (int i = 0; i < kC; ++i) {
+                re += sm.cc.E[t * kLCc + i];
+                ce += sm.cc.E[i * kLCc + t];
+                rb += sm.cc.F[t * kLCc + i];
+            }
+            float xg = re - ce;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float y = __shfl_down(xg, off);
+                if (t + off < kWave) xg += y;
+            }
+            if (t < L) {
+                float ag = 0.f, ab = 0.f;
+                for (int s = 0; s < slices; ++s) {
+                    const size_t o = ((size_t)s * rows + tok0 + t) * Hv + h;
+                    ag += part_dg[o];
+                    ab += part_db[o];
+                }
+                dg[(tok0 + t) * Hv + h] = ag + xg;
+                db[(tok0 + t) * Hv + h] = ab + rb;
+            }
+        }
+        __syncthreads();                         // E, F and the gates are rewritten for the next v-head
     }
 
-    // ---- the chunk terms: K, Q, and the C x C matrices summed over v-heads and slices ----
+    // ---- the chunk terms: K, Q, and the C x C matrices summed over the v-heads ----
     stage_rows<DK, LK, kThreads>(k, tok0, Hk, kh, L, sm.ct.K, tid);
     stage_rows<DK, LK, kThreads>(q, tok0, Hk, kh, L, sm.ct.Q, tid);
-    {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * j + 4 * gl + r, i = 16 * wave + cl;
+            sm.ct.P[t * kLCc + i] = sp[j][r];
+            sm.ct.B[t * kLCc + i] = sb[j][r];
+        }
+    __syncthreads();
+    {   // B symmetrised in LDS
         constexpr int PE = kMat / kThreads;
-        float ap[PE], ab[PE];
-#pragma unroll
-        for (int it = 0; it < PE; ++it) ap[it] = ab[it] = 0.f;
-        for (int x = 0; x < G; ++x)
-            for (int s = 0; s < slices; ++s) {
-                const float* pm = pmat + (((size_t)slot * Hv + kh * G + x) * slices + s) * 2 * kMat;
-                float lp[PE], lb[PE];
-#pragma unroll
-                for (int it = 0; it < PE; ++it) {
-                    lp[it] = pm[tid + kThreads * it];
-                    lb[it] = pm[kMat + tid + kThreads * it];
-                }
-#pragma unroll
-                for (int it = 0; it < PE; ++it) {
-                    ap[it] += lp[it];
-                    ab[it] += lb[it];
-                }
-            }
+        float ab[PE];
 #pragma unroll
         for (int it = 0; it < PE; ++it) {
-            const int e = tid + kThreads * it, t = e / kC, j = e % kC;
-            sm.ct.P[t * kLCc + j] = ap[it];
-            sm.ct.B[t * kLCc + j] = ab[it];
+            const int e = tid + kThreads * it, t = e / kC, i = e % kC;
+            ab[it] = sm.ct.B[t * kLCc + i] + sm.ct.B[i * kLCc + t];
         }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < PE; ++it) {
-            const int e = tid + kThreads * it, t = e / kC, j = e % kC;
-            ab[it] = sm.ct.B[t * kLCc + j] + sm.ct.B[j * kLCc + t];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < PE; ++it) {
-            const int e = tid + kThreads * it, t = e / kC, j = e % kC;
-            sm.ct.B[t * kLCc + j] = ab[it];
+            const int e = tid + kThreads * it, t = e / kC, i = e % kC;
+            sm.ct.B[t * kLCc + i] = ab[it];
         }
     }
     __syncthreads();
@@ -815,6 +843,7 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
             }
             aq[j] += tq;
             ak[j] += tk;
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // lane (g, c) of tile (a, b), element r: row 16 a + 4 g + r, key 16 b + c
@@ -831,17 +860,6 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
             }
         }
     }
-    for (int e = tid; e < L * G; e += kThreads) {
-        const int t = e / G, h = kh * G + e % G;
-        float ag = 0.f, ab = 0.f;
-        for (int s = 0; s < slices; ++s) {
-            const size_t o = ((size_t)s * rows + tok0 + t) * Hv + h;
-            ag += part_dg[o];
-            ab += part_db[o];
-        }
-        dg[(tok0 + t) * Hv + h] = ag;
-        db[(tok0 + t) * Hv + h] = ab;
-    }
 }
 
 // dq, dk, dg, dbeta of tokens outside every packed sequence: zero (launched before the combine).
@@ -857,7 +875,7 @@ __global__ __launch_bounds__(kThreads) void bwd_zero_kernel(float* __restrict__ 
 }
 
 struct BwdLayout {
-    size_t ckpt, mats, pmat, wd, wu, wy, pg, pb, total;
+    size_t ckpt, mats, wd, wu, wy, pg, pb, total;
     int slots;
 };
 
@@ -871,7 +889,6 @@ BwdLayout bwd_layout(int B, int T, int Hv, int dk, int dv, int N) {
     size_t off = 0;
     l.ckpt = off; off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * dk * dv);
     l.mats = off; off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * 3 * kMat);
-    l.pmat = off; off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * slices * 2 * kMat);
     l.wd = off;   off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * dk * dv);
     l.wu = off;   off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * kC * dv);
     l.wy = off;   off = align256b(off + sizeof(float) * (size_t)l.slots * Hv * kC * dv);
@@ -891,7 +908,6 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
     const int slots = packed ? lay.slots : a.B * ((a.T + kC - 1) / kC);
     float* ckpt = reinterpret_cast<float*>(ws + lay.ckpt);
     float* mats = reinterpret_cast<float*>(ws + lay.mats);
-    float* pmat = reinterpret_cast<float*>(ws + lay.pmat);
     float* wd = reinterpret_cast<float*>(ws + lay.wd);
     float* wu = reinterpret_cast<float*>(ws + lay.wu);
     float* wy = reinterpret_cast<float*>(ws + lay.wy);
@@ -915,7 +931,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
                        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.v), static_cast<const TG*>(a.g),
                        static_cast<const TG*>(a.beta), a.initial_state, a.cu_seqlens, a.d_o, a.d_final,
-                       a.T, a.Hk, a.Hv, a.dv, mats, ckpt, pmat, wd, wu, wy, pg, pb, a.dv_out, a.d_initial, rows,
+                       a.T, a.Hk, a.Hv, a.dv, mats, ckpt, wd, wu, wy, pg, pb, a.dv_out, a.d_initial, rows,
                        lay.slots);
     if ((e = hipGetLastError()) != hipSuccess || rows == 0) return e;
     if (packed) {
@@ -933,7 +949,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
         hipLaunchKernelGGL(ck, dim3((unsigned)slots, (unsigned)a.Hk), dim3(kThreads), cbytes, a.stream,
                            static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), static_cast<const TG*>(a.g),
                            static_cast<const TG*>(a.beta), a.d_o, a.cu_seqlens, a.N, a.T, a.Hk, a.Hv, a.dv, slices,
-                           rows, pmat, ckpt, wd, wu, wy, pg, pb, a.dq, a.dk_out, a.dg, a.dbeta);
+                           rows, mats, ckpt, wd, wu, wy, pg, pb, a.dq, a.dk_out, a.dg, a.dbeta);
     }
     return hipGetLastError();
 }

@@ -295,8 +295,7 @@ gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v,
  * [N, Hv, dk, dv] or NULL (not computed).  Tokens outside every packed sequence get zero d_q, d_k,
  * d_g, d_beta and an untouched d_v.
  * Workspace: gdn_chunk_bwd_workspace_size bytes, 256-byte aligned (per chunk: the state at its start,
- * the state gradient at its end, U and dY, and each 16-column slice's partial sums of the chunk's
- * C x C gradient matrices, dg and dbeta).
+ * the state gradient at its end, U and dY, and each 16-column slice's partial sums of dg and dbeta).
  * Sizes and dtypes as in gdn_chunk_fwd; dk and dv 64 or 128 (others: GDN_ERROR_NOT_SUPPORTED).
  * Alignment: q and k 16 bytes, every other pointer its element size.
  * Errors: GDN_ERROR_INVALID_VALUE for null or misaligned pointers, bad sizes or dtypes;
