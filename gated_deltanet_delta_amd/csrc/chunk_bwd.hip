@@ -600,13 +600,15 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
 // added, as reverse running sums for dg, to the slices' partials; then, summed over the v-heads,
 //     dq = sum_h diag(gamma) dO S^T + (dP o Gam) K
 //     dk = sum_h [diag(f) U D^T - diag(gamma beta) dY S^T] + (dP o Gam)^T Q + ((dBm o Gam) + (dBm o Gam)^T) K
-// All products run on the fp32 matrix cores.  Wave w owns the 16 x 16 output tiles p = w, w + 4, ..
-// of dq and of dk (row tile p / KT, key tile p % KT) and the tiles (a, w) of the C x C matrices.  The
-// products over dv take it in 32-column tiles staged in LDS; each tile's (and each 16-token block's)
-// sum is formed on its own and then added to the running total, which keeps the fp32 chains short.
+// All products run on the fp32 matrix cores.  Wave w of eight owns the 16 x 16 output tiles
+// p = w, w + 8, .. of dq and of dk (row tile p / KT, key tile p % KT) and the tiles
+// ((w + 8 j) / 4, w % 4) of the C x C matrices.  The products over dv take it in 32-column tiles
+// staged in LDS; each tile's (and each 16-token block's) sum is formed on its own and then added to
+// the running total, which keeps the fp32 chains short.
 constexpr int kTC = 32;          // dv columns per staged tile of the state products
 constexpr int kLT = kTC + 4;     // pitch of those tiles: rows 16 a + c, columns k + g land in distinct banks
 constexpr int kLCc = kC + 4;     // pitch of the C x C matrices in the combine kernel
+constexpr int kCT = 512;         // combine kernel threads: 8 waves, each owning 1/8 of the output tiles
 
 template <int DK>
 struct CombineLds {
@@ -632,7 +634,7 @@ struct CombineLds {
 };
 
 template <int DK, typename TIn, typename TG>
-__global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
+__global__ __launch_bounds__(kCT) void bwd_combine_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TG* __restrict__ g,
     const TG* __restrict__ beta, const float* __restrict__ d_o, const int32_t* __restrict__ cu_seqlens,
     int N, int T, int Hk, int Hv, int dv, int slices, long long rows, const float* __restrict__ mats,
@@ -642,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     using Lds = CombineLds<DK>;
     constexpr int LK = Lds::LK;
     constexpr int KT = DK / 16;                  // key tiles
-    constexpr int NT = KT;                       // output tiles per wave (of dq, and of dk)
+    constexpr int NT = KT / 2;                   // output tiles per wave (of dq, and of dk)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Lds& sm = *reinterpret_cast<Lds*>(smem_raw);
     const int slot = blockIdx.x, kh = blockIdx.y;
@@ -657,9 +659,11 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     f32x4b aq[NT], ak[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) aq[j] = ak[j] = z4;
-    f32x4b sp[4], sb[4];                         // sum over v-heads of dP o Gam, dBm o Gam: tiles (j, wave)
+    // C x C tiles of this wave: (a, b) = ((wave + 8 j) / 4, wave % 4), j = 0, 1
+    const int cb = wave & 3, ca0 = wave >> 2;
+    f32x4b sp[2], sb[2];                         // sum over v-heads of dP o Gam, dBm o Gam
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sp[j] = sb[j] = z4;
+    for (int j = 0; j < 2; ++j) sp[j] = sb[j] = z4;
 
     for (int x = 0; x < G; ++x) {
         const int h = kh * G + x;
@@ -675,24 +679,24 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
         const float* Dg = ws_d + ((size_t)slot * Hv + h) * DK * dv;
         const float* Ug = ws_u + ((size_t)slot * Hv + h) * kC * dv;
         const float* Yg = ws_y + ((size_t)slot * Hv + h) * kC * dv;
-        f32x4b cp[4], ca[4];                     // dO U^T and dY U^T, tiles (j, wave)
+        f32x4b cp[2], ca[2];                     // dO U^T and dY U^T on the wave's C x C tiles
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cp[j] = ca[j] = z4;
+        for (int j = 0; j < 2; ++j) cp[j] = ca[j] = z4;
         // ---- the products over dv, 32 columns at a time ----
         for (int c0 = 0; c0 < dv; c0 += kTC) {
             // stage (16-byte pieces, all loads first): S, D [DK][32]; dO, U, dY [C][32], unscaled and
             // scaled by gamma, f and -gamma beta
-            constexpr int PS = DK * kTC / 4 / kThreads, PT = kC * kTC / 4 / kThreads;
+            constexpr int PS = DK * kTC / 4 / kCT, PT = kC * kTC / 4 / kCT;
             float4 vs[PS], vd[PS], vo[PT], vu[PT], vy[PT];
 #pragma unroll
             for (int it = 0; it < PS; ++it) {
-                const int e = 4 * (tid + kThreads * it), i = e / kTC, c = e % kTC;
+                const int e = 4 * (tid + kCT * it), i = e / kTC, c = e % kTC;
                 vs[it] = *reinterpret_cast<const float4*>(Sg + (size_t)i * dv + c0 + c);
                 vd[it] = *reinterpret_cast<const float4*>(Dg + (size_t)i * dv + c0 + c);
             }
 #pragma unroll
             for (int it = 0; it < PT; ++it) {
-                const int e = 4 * (tid + kThreads * it), t = e / kTC, c = e % kTC;
+                const int e = 4 * (tid + kCT * it), t = e / kTC, c = e % kTC;
                 const float* op = d_o + ((tok0 + min(t, L - 1)) * Hv + h) * dv + c0 + c;   // (4-byte aligned)
                 const float m = t < L ? 1.f : 0.f;
                 vo[it] = make_float4(m * op[0], m * op[1], m * op[2], m * op[3]);
@@ -701,14 +705,14 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
             }
 #pragma unroll
             for (int it = 0; it < PS; ++it) {
-                const int e = 4 * (tid + kThreads * it), i = e / kTC, c = e % kTC;
+                const int e = 4 * (tid + kCT * it), i = e / kTC, c = e % kTC;
                 *reinterpret_cast<float4*>(&sm.st.S[i * kLT + c]) = vs[it];
                 *reinterpret_cast<float4*>(&sm.st.D[i * kLT + c]) = vd[it];
             }
             auto scaled = [](float s_, float4 v) { return make_float4(s_ * v.x, s_ * v.y, s_ * v.z, s_ * v.w); };
 #pragma unroll
             for (int it = 0; it < PT; ++it) {
-                const int e = 4 * (tid + kThreads * it), t = e / kTC, c = e % kTC;
+                const int e = 4 * (tid + kCT * it), t = e / kTC, c = e % kTC;
                 *reinterpret_cast<float4*>(&sm.st.Ou[t * kLT + c]) = vo[it];
                 *reinterpret_cast<float4*>(&sm.st.Uu[t * kLT + c]) = vu[it];
                 *reinterpret_cast<float4*>(&sm.st.Yu[t * kLT + c]) = vy[it];
@@ -719,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                const int p = wave + 4 * j, a = p / KT, b = p % KT;
+                const int p = wave + 8 * j, a = p / KT, b = p % KT;
                 f32x4b tq = z4, tk = z4;
 #pragma unroll
                 for (int kk = 0; kk < kTC; kk += 4) {
@@ -732,16 +736,17 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
                 ak[j] += tk;
                 __builtin_amdgcn_sched_barrier(0);   // (a tile's operand reads are not hoisted into the
             }                                        // previous tile: registers stay within budget)
-            // dO U^T and dY U^T, tiles (j, wave) on or below the diagonal
+            // dO U^T and dY U^T on the wave's C x C tiles on or below the diagonal
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < wave) continue;
+            for (int j = 0; j < 2; ++j) {
+                const int ra = ca0 + 2 * j;
+                if (ra < cb) continue;
                 f32x4b tp = z4, ta = z4;
 #pragma unroll
                 for (int kk = 0; kk < kTC; kk += 4) {
-                    const float ub = sm.st.Uu[(16 * wave + cl) * kLT + kk + gl];
-                    tp = mfma4(sm.st.Ou[(16 * j + cl) * kLT + kk + gl], ub, tp);
-                    ta = mfma4(sm.st.Yu[(16 * j + cl) * kLT + kk + gl], ub, ta);
+                    const float ub = sm.st.Uu[(16 * cb + cl) * kLT + kk + gl];
+                    tp = mfma4(sm.st.Ou[(16 * ra + cl) * kLT + kk + gl], ub, tp);
+                    ta = mfma4(sm.st.Yu[(16 * ra + cl) * kLT + kk + gl], ub, ta);
                 }
                 cp[j] += tp;
                 ca[j] += ta;
@@ -754,10 +759,10 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
             const float* Bmh = mats + ((size_t)slot * Hv + h) * 3 * kMat + kMat;     // (T, Bm, P)
             const float* Ph = Bmh + kMat;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * j + 4 * gl + r, i = 16 * wave + cl;        // element (t, i)
+                    const int t = 16 * (ca0 + 2 * j) + 4 * gl + r, i = 16 * cb + cl;   // element (t, i)
                     const float dP = i <= t ? cp[j][r] : 0.f;
                     const float dA = i < t ? -ca[j][r] : 0.f;
                     const float bm = Bmh[t * kC + i], pv = Ph[t * kC + i];
@@ -801,29 +806,29 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     }
 
     // ---- the chunk terms: K, Q, and the C x C matrices summed over the v-heads ----
-    stage_rows<DK, LK, kThreads>(k, tok0, Hk, kh, L, sm.ct.K, tid);
-    stage_rows<DK, LK, kThreads>(q, tok0, Hk, kh, L, sm.ct.Q, tid);
+    stage_rows<DK, LK, kCT>(k, tok0, Hk, kh, L, sm.ct.K, tid);
+    stage_rows<DK, LK, kCT>(q, tok0, Hk, kh, L, sm.ct.Q, tid);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * j + 4 * gl + r, i = 16 * wave + cl;
+            const int t = 16 * (ca0 + 2 * j) + 4 * gl + r, i = 16 * cb + cl;
             sm.ct.P[t * kLCc + i] = sp[j][r];
             sm.ct.B[t * kLCc + i] = sb[j][r];
         }
     __syncthreads();
     {   // B symmetrised in LDS
-        constexpr int PE = kMat / kThreads;
+        constexpr int PE = kMat / kCT;
         float ab[PE];
 #pragma unroll
         for (int it = 0; it < PE; ++it) {
-            const int e = tid + kThreads * it, t = e / kC, i = e % kC;
+            const int e = tid + kCT * it, t = e / kC, i = e % kC;
             ab[it] = sm.ct.B[t * kLCc + i] + sm.ct.B[i * kLCc + t];
         }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < PE; ++it) {
-            const int e = tid + kThreads * it, t = e / kC, i = e % kC;
+            const int e = tid + kCT * it, t = e / kC, i = e % kC;
             sm.ct.B[t * kLCc + i] = ab[it];
         }
     }
@@ -831,7 +836,7 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     // dq += P' K, dk += P'^T Q + B' K over the chunk's tokens (16-deep blocks of four products)
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int p = wave + 4 * j, a = p / KT, b = p % KT;
+        const int p = wave + 8 * j, a = p / KT, b = p % KT;
         for (int k0 = 0; k0 < kC; k0 += 16) {
             f32x4b tq = z4, tk = z4;
 #pragma unroll
@@ -849,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     // lane (g, c) of tile (a, b), element r: row 16 a + 4 g + r, key 16 b + c
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int p = wave + 4 * j, a = p / KT, b = p % KT;
+        const int p = wave + 8 * j, a = p / KT, b = p % KT;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * a + 4 * gl + r;
@@ -946,7 +951,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(ck),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)cbytes)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(ck, dim3((unsigned)slots, (unsigned)a.Hk), dim3(kThreads), cbytes, a.stream,
+        hipLaunchKernelGGL(ck, dim3((unsigned)slots, (unsigned)a.Hk), dim3(kCT), cbytes, a.stream,
                            static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), static_cast<const TG*>(a.g),
                            static_cast<const TG*>(a.beta), a.d_o, a.cu_seqlens, a.N, a.T, a.Hk, a.Hv, a.dv, slices,
                            rows, mats, ckpt, wd, wu, wy, pg, pb, a.dq, a.dk_out, a.dg, a.dbeta);
