@@ -167,8 +167,14 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     const TG* __restrict__ beta, const int32_t* __restrict__ cu_seqlens, int N, int T, int Hk, int Hv,
     float* __restrict__ mats) {
     constexpr int LK = DK + 1;
-    __shared__ float sK[kC * LK], sQ[kC * LK];
-    __shared__ float sKK[kC * kLC], sQK[kC * kLC], sBm[kC * kLC];
+    // the staged K, Q rows and the C x C products share one region (66 KB at DK = 128: two
+    // workgroups fit a CU)
+    __shared__ float smem[2 * kC * LK > 3 * kC * kLC ? 2 * kC * LK : 3 * kC * kLC];
+    float* sK = smem;
+    float* sQ = smem + kC * LK;
+    float* sKK = smem;
+    float* sQK = smem + kC * kLC;
+    float* sBm = smem + 2 * kC * kLC;
     __shared__ float sG[kC], sgam[kC], sf[kC], sb[kC];
     const int slot = blockIdx.x, kh = blockIdx.y;
     int n, row, cs, L;
@@ -198,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
                     qk[r][s] += aq[r] * b[s];
                 }
         }
+        __syncthreads();                   // K and Q are read; their region takes the products
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
