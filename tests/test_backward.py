@@ -75,6 +75,17 @@ def test_backward_head_sizes(dk, dv):
     check(x, d_o, d_final, f"bwd dk={dk} dv={dv}")
 
 
+@pytest.mark.parametrize("G", [1, 3, 4])
+def test_backward_head_groupings(G):
+    """G v-heads per q/k head other than 2: the per-chunk kernels loop over a q/k head's v-heads and
+    sum dq, dk over them."""
+    wl = with_dims(WL["prefill"], Hk=2, Hv=2 * G, init_state=True)
+    A_log = np.log(np.linspace(0.1, 0.9, wl.Hv)).astype(np.float32)
+    x = synth.make(wl, T=130, seed=92 + G, A_log=A_log)
+    d_o, d_final = grads_of_outputs(x, 95 + G)
+    check(x, d_o, d_final, f"bwd G={G}")
+
+
 def test_backward_packed_sequences():
     """Packed ragged sequences (empty ones among them, one of a single token), no gradient on the
     final state, the workloads' own strong-decay gates."""

@@ -61,6 +61,30 @@ def test_head_sizes(dk, dv, dtype):
     check_chunk(synth.make(wl, T=150, seed=7), f"dk={dk} dv={dv} {dtype}")
 
 
+@pytest.mark.parametrize("G", [1, 3, 4, 8])
+def test_head_groupings(G):
+    """G v-heads per q/k head other than the Qwen3-Next layout's 2 (each q/k head shared by G
+    v-heads, v-head h reading q/k head h // G), packed ragged sequences with a carried state and a
+    weak decay, bf16 inputs."""
+    wl = with_dims(WL["varlen"], Hk=2, Hv=2 * G, n_seqs=3)
+    A_log = np.log(np.linspace(0.1, 0.9, wl.Hv)).astype(np.float32)
+    x = synth.make(wl, lengths=np.array([150, 1, 70]), seed=60 + G, A_log=A_log)
+    check_chunk(x, f"G={G}")
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_head_groupings_decode(G):
+    wl = with_dims(WL["decode"], B=3, Hk=2, Hv=2 * G)
+    x = synth.make(wl, seed=70 + G)
+    o_ref, s_ref = oracle_of(x)
+    d = to_gpu(x)
+    state = d["initial_state"].clone()
+    o, _ = gdn_recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
+    torch.cuda.synchronize()
+    assert_close(f"decode G={G} o", o, o_ref, tol_for(torch.bfloat16))
+    assert_close(f"decode G={G} state", state, s_ref, tol_for(torch.bfloat16))
+
+
 @pytest.mark.parametrize("decay", ["zero", "linspace", "small"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_weak_decay(decay, dtype):
