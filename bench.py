@@ -55,6 +55,10 @@ TRAFFIC_SCAN = 180236148      # chunk_scan_kernel<128>, prefill B=1 T=4096
 TRAFFIC_DECODE = 1085280816    # recurrent_kernel<128,128,bf16,f32>, one decode step, B=256
 TRAFFIC_CONV = 134710246       # causal_conv1d_kernel<4,8,bf16>, T=4096, C=8192
 TRAFFIC_NORM = 134250675       # gated_rmsnorm_kernel<128,bf16,bf16>, 4096 x 32 rows
+# Matrix-core flops each launch executes, from rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops,
+# profiles/mfma_utilisation_prefill_T4096.md); None whenever the kernel changed since.
+EXEC_MFMA_BF16_SCAN = 102563840 * 512            # chunk_scan_kernel<128>, prefill B=1 T=4096
+EXEC_MFMA_F32_BWD = (69206016 + 36700160) * 512   # bwd_slice_kernel + bwd_combine_kernel, same prefill
 
 
 def prefill_algorithmic(wl, T: int, B: int, N: int, init_state: bool):
@@ -426,7 +430,13 @@ def main() -> int:
                      "call_ms_per_launch_events": round(ms_events, 5),
                      "call_achieved_gbs": round(nbytes / (ms_events / 1e3) / 1e9, 1),
                      "useful_tflops": round(useful_tflops, 2),
-                     "mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4)},
+                     "mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4),
+                     "mfma_executed_flops_per_launch": EXEC_MFMA_BF16_SCAN,
+                     "mfma_executed_tflops": (None if EXEC_MFMA_BF16_SCAN is None else
+                                              round(EXEC_MFMA_BF16_SCAN / (ms_scan / 1e3) / 1e12, 1)),
+                     "mfma_frac_executed": (None if EXEC_MFMA_BF16_SCAN is None else
+                                            round(EXEC_MFMA_BF16_SCAN / (ms_scan / 1e3) / 1e12
+                                                  / MI355X_BF16_TFLOPS, 4))},
         "prefill_long": long_res,
         "prefill_varlen": varlen_res,
         "prefill_gating": {"call": "gdn_chunk_fwd_gating (gates formed in the kernels from a, b)",
@@ -460,7 +470,11 @@ def main() -> int:
                                   "peak": MI355X_F32_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(bwd_flops / (ms_bwd / 1e3) / 1e12 / MI355X_F32_TFLOPS, 4),
                                   "flops_per_token_vhead": BWD_FLOPS_PER_TOKEN_VHEAD,
-                                  "algorithmic_flops_per_call": int(bwd_flops)},
+                                  "algorithmic_flops_per_call": int(bwd_flops),
+                                  "mfma_executed_flops_per_call": EXEC_MFMA_F32_BWD,
+                                  "mfma_frac_executed": (None if EXEC_MFMA_F32_BWD is None else
+                                                         round(EXEC_MFMA_F32_BWD / (ms_bwd / 1e3) / 1e12
+                                                               / MI355X_F32_TFLOPS, 4))},
                      "every_option": {"call": "gdn_chunk_bwd_ex (gates from a, b and q, k L2-normalised, "
                                               "both differentiated: da, db, dA_log, ddt_bias, raw dq, dk)",
                                       "ms_per_call_events": round(ms_bwd_ex, 4),
