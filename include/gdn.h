@@ -292,8 +292,7 @@ gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v,
  * and beta; no pool); d_o [B, T, Hv, dv] fp32; d_final [N, Hv, dk, dv] fp32 or NULL (zero).
  * Outputs (device, fp32, every element written): d_q, d_k [B, T, Hk, dk] (summed over the v-heads
  * that share a q/k head); d_v [B, T, Hv, dv]; d_g, d_beta [B, T, Hv]; d_initial_state
- * [N, Hv, dk, dv] or NULL (not computed).  Tokens outside every packed sequence get zero d_q, d_k,
- * d_g, d_beta and an untouched d_v.
+ * [N, Hv, dk, dv] or NULL (not computed).
  * Workspace: gdn_chunk_bwd_workspace_size bytes, 256-byte aligned (per chunk: the state at its start,
  * the state gradient at its end, U and dY, and each 16-column slice's partial sums of dg and dbeta).
  * Sizes and dtypes as in gdn_chunk_fwd; dk and dv 64 or 128 (others: GDN_ERROR_NOT_SUPPORTED).
