@@ -593,6 +593,15 @@ constexpr int kKR = 160;
 constexpr int kKDma = kC * kKR * 2 / 1024;   // 1 KiB copy instructions per K slot (20)
 // copy instructions per chunk: K, V (2 KiB), gate block (768 bytes; with L2 1 KiB + 256 bytes)
 constexpr int kDmaOps = kKDma + 2 + 1;
+// L2 prefetch: kPfAhead chunks ahead of the step that issues it, every line a workgroup group
+// reads for a chunk (Q and K rows, the N block; per v-head the M block, V rows and gate block) is
+// touched once, so that the chain's M and N loads and the output waves' Q loads (issued one step
+// before use) and the staging copies (two steps) meet L2 rather than HBM.
+constexpr int kPfAhead = 4;
+constexpr int kLinesQ = kC * kDK * 2 / 128;                  // also K's
+constexpr int kLinesN = kNFrags * kFragElems * 2 / 128;
+constexpr int kLinesM = kMFrags * kFragElems * 2 / 128;
+constexpr int kLinesG = kGRows * kC * 4 / 128;
 __host__ __device__ constexpr int kswz(int t) { return (t >> 2) & 3; }
 
 struct ScanLds {
@@ -602,7 +611,9 @@ struct ScanLds {
     __bf16 St[2][2][kWS * kSP];                // S^T at chunk start [buffer][hi, lo]
     f32x4 Ut[2][4][64];                        // U [buffer][token tile][lane], the chain's tiles
     f32x4 Yt[2][2][4][64];                     // Y in two parts [buffer][key half][tile][lane]
+    uint32_t sink[64];                         // landing row of the L2 prefetches (never read)
 };
+static_assert(sizeof(ScanLds) <= 160 * 1024, "scan LDS exceeds a CU's 160 KiB");
 
 // index (token or key) that accumulator row m of tile a stands for
 __device__ __forceinline__ int rho(int a, int m) {
@@ -1059,18 +1070,62 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 copy_to_lds(gb + 4 * min(lane, 47), sm.Gt[slot]);         // rows 0-2
             }
         };
+        // The group's lines of chunk cp, dealt out over its MB = Gq DV / 16 members: lane l of
+        // member m touches lines m + MB (l + 64 i), i < kPf.  Line order: Q rows, K rows, N, then
+        // per v-head of the group its M block, V rows and gate block.  Addresses are clamped into
+        // the chunk (a repeated line costs an L2 hit), so every instruction is issued with all
+        // lanes and the copy counts below stay exact.  Each instruction lands 64 dwords in sm.sink.
+        constexpr int kRowLines = DV / 64;                     // 128-byte lines per V row
+        constexpr int kLinesV = kC * kRowLines;
+        constexpr int kPerHead = kLinesM + kLinesV + kLinesG;
+        constexpr int kPf = DV == 64 ? 3 : 2;                  // covers Gq = 1, the widest share
+        auto prefetch = [&](int cp) {
+            const size_t tok0 = tok0_of(cp);
+            const int L = len_of(cp);
+            const int total = 2 * kLinesQ + kLinesN + Gq * kPerHead;
+#pragma unroll
+            for (int i = 0; i < kPf; ++i) {
+                const int line = min(member + MB * (lane + 64 * i), total - 1);
+                const void* src;
+                if (line < 2 * kLinesQ) {
+                    const __bf16* base = line < kLinesQ ? q : k;
+                    const int ln = line % kLinesQ;
+                    src = base + ((tok0 + min(ln >> 1, L - 1)) * Hk + kh) * kDK + 64 * (ln & 1);
+                } else if (line < 2 * kLinesQ + kLinesN) {
+                    src = ws_N + ((size_t)(slot0 + cp) * Hk + kh) * kNFrags * kFragElems +
+                          64 * (line - 2 * kLinesQ);
+                } else {
+                    const int j = line - 2 * kLinesQ - kLinesN;
+                    const int hv = kh * Gq + j / kPerHead, r = j % kPerHead;
+                    if (r < kLinesM) {
+                        src = ws_M + ((size_t)(slot0 + cp) * Hv + hv) * kMFrags * kFragElems + 64 * r;
+                    } else if (r < kLinesM + kLinesV) {
+                        const int rv = r - kLinesM;
+                        src = v + ((tok0 + min(rv / kRowLines, L - 1)) * Hv + hv) * DV + 64 * (rv % kRowLines);
+                    } else {
+                        src = ws_G + ((size_t)(slot0 + cp) * Hv + hv) * kGRows * kC + 32 * (r - kLinesM - kLinesV);
+                    }
+                }
+                __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)sm.sink, 4, 0, 0);
+            }
+        };
         dma(0);
         if (nchunks > 1) dma(1);
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();       // P: chunks 0 and 1 staged
-        if (nchunks > 2) dma(2);
+        if (nchunks > 2) {
+            dma(2);
+            prefetch(min(kPfAhead - 1, nchunks - 1));
+        }
         __builtin_amdgcn_s_barrier();       // B0
         for (int s = 0; s <= nchunks; ++s) {
             // chunk s + 3 goes into the slot chunk s - 2 left; chunk s + 2 must have landed before
-            // the step ends
+            // the step ends.  Every chunk copy from chunk 2 on is followed by one prefetch, so the
+            // copies of chunk s + 2 are older than the newest kDmaOps (+1) + 2 kPf instructions.
             if (s + 3 < nchunks) {
                 dma(s + 3);
-                wait_vmcnt<kDmaOps + (L2 ? 1 : 0)>();
+                prefetch(min(s + kPfAhead, nchunks - 1));
+                wait_vmcnt<kDmaOps + (L2 ? 1 : 0) + 2 * kPf>();
             } else {
                 wait_vmcnt<0>();
             }
