@@ -51,7 +51,7 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
 # reads on a plain copy of known size (profiles/); None whenever the kernel changed since.
-TRAFFIC_SCAN = 180236148      # chunk_scan_kernel<128>, prefill B=1 T=4096
+TRAFFIC_SCAN = 181249434      # chunk_scan_kernel<128>, prefill B=1 T=4096
 TRAFFIC_DECODE = 1085280816    # recurrent_kernel<128,128,bf16,f32>, one decode step, B=256
 TRAFFIC_CONV = 134710246       # causal_conv1d_kernel<4,8,bf16>, T=4096, C=8192
 TRAFFIC_NORM = 134250675       # gated_rmsnorm_kernel<128,bf16,bf16>, 4096 x 32 rows
@@ -122,30 +122,47 @@ def main() -> int:
         return 0
 
     # ---------------- prefill -----------------------------------------------------------------
+    # Four input sets (the workload's own draw and three more seeds), ~137 MB each with o: together
+    # larger than the GPU's 256 MB last-level cache, so that calls cycling through them read their
+    # inputs from HBM.  Repeating one set would leave most of it in that cache between calls.
     wl = synth.WORKLOADS["prefill"]
-    x = synth.make(wl)
-    d = {key: (None if x[key] is None else x[key].to(dev).contiguous())
-         for key in ("q", "k", "v", "g", "beta", "initial_state", "cu_seqlens")}
     B, T = wl.B, wl.T
     N = B
-    o = torch.empty((B, T, wl.Hv, wl.dv), dtype=torch.float32, device=dev)
-    fs = torch.empty((N, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+    NSETS = 4
+    sets = []
+    for i in range(NSETS):
+        xi = synth.make(wl) if i == 0 else synth.make(wl, seed=wl.seed + 1000 + i)
+        di = {key: (None if xi[key] is None else xi[key].to(dev).contiguous())
+              for key in ("q", "k", "v", "g", "beta", "initial_state", "cu_seqlens")}
+        raw_i = xi["raw"]
+        di["a"] = torch.from_numpy(raw_i["a"]).to(wl.gate_dtype).to(dev)
+        di["b"] = torch.from_numpy(raw_i["b"]).to(wl.gate_dtype).to(dev)
+        di["A_log"] = torch.from_numpy(raw_i["A_log"]).to(dev)
+        di["dt_bias"] = torch.from_numpy(raw_i["dt_bias"]).to(dev)
+        di["o"] = torch.empty((B, T, wl.Hv, wl.dv), dtype=torch.float32, device=dev)
+        di["fs"] = torch.empty((N, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+        sets.append(di)
+        if i == 0:
+            x = xi
+    d, o, fs = sets[0], sets[0]["o"], sets[0]["fs"]
+    ga, gb, gA, gdt = d["a"], d["b"], d["A_log"], d["dt_bias"]
     ws_bytes = workspace_size(B, T, wl.Hk, wl.Hv, wl.dk, wl.dv, N, wl.dtype)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)   # one workspace, shared
 
-    def prefill_step(stage="all"):
-        gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], None,
-                      o=o, final_state=fs, workspace=ws, stage=stage)
+    def prefill_step(stage="all", i=0):
+        s_ = sets[i % NSETS]
+        gdn_chunk_fwd(s_["q"], s_["k"], s_["v"], s_["g"], s_["beta"], s_["initial_state"], None,
+                      o=s_["o"], final_state=s_["fs"], workspace=ws, stage=stage)
 
-    for _ in range(args.warmup):
-        prefill_step()
+    for i in range(args.warmup):
+        prefill_step(i=i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record()
-    for _ in range(args.steps):
-        prefill_step()
+    for i in range(args.steps):
+        prefill_step(i=i)
     ev1.record()
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
@@ -157,59 +174,50 @@ def main() -> int:
     gate_bytes = B * T * wl.Hv * 2 * (2 if str(wl.gate_dtype).endswith("bfloat16") else 4)
     scan_bytes = nbytes - gate_bytes
 
+    def time_loop(fn):
+        """ms per call over args.steps calls, fn(i) cycling through the input sets."""
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    # for context: the same call repeated on one set of buffers (mostly last-level-cache resident)
+    ms_same_buffers = time_loop(lambda i: prefill_step())
+
     # the two halves on their own, each timed with events on the stream the kernels run on
     # (torch's current stream, which the binding passes to the library)
     def time_stage(stage):
         prefill_step("prepare")     # scan reads what prepare left in the workspace
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            prefill_step(stage)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        return time_loop(lambda i: prefill_step(stage, i))
 
     ms_prepare = time_stage("prepare")
     ms_scan = time_stage("scan")
 
     # the same prefill with the gates formed in the kernels from the raw projections a, b
-    raw = x["raw"]
-    ga = torch.from_numpy(raw["a"]).to(wl.gate_dtype).to(dev)
-    gb = torch.from_numpy(raw["b"]).to(wl.gate_dtype).to(dev)
-    gA = torch.from_numpy(raw["A_log"]).to(dev)
-    gdt = torch.from_numpy(raw["dt_bias"]).to(dev)
+    def prefill_gating(i):
+        s_ = sets[i % NSETS]
+        gdn_chunk_fwd_gating(s_["q"], s_["k"], s_["v"], s_["a"], s_["b"], s_["A_log"], s_["dt_bias"],
+                             s_["initial_state"], None, o=s_["o"], final_state=s_["fs"], workspace=ws)
 
-    def prefill_gating():
-        gdn_chunk_fwd_gating(d["q"], d["k"], d["v"], ga, gb, gA, gdt, d["initial_state"], None,
-                             o=o, final_state=fs, workspace=ws)
-
-    for _ in range(args.warmup):
-        prefill_gating()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        prefill_gating()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_gating = e0.elapsed_time(e1) / args.steps
+    for i in range(args.warmup):
+        prefill_gating(i)
+    ms_gating = time_loop(prefill_gating)
 
     # and with q, k normalised to unit length in the kernels as well (every fused input step)
-    def prefill_gating_l2():
-        gdn_chunk_fwd_ex(d["q"], d["k"], d["v"], ga, gb, A_log=gA, dt_bias=gdt,
-                         initial_state=d["initial_state"], qk_l2norm=True, o=o, final_state=fs,
+    def prefill_gating_l2(i):
+        s_ = sets[i % NSETS]
+        gdn_chunk_fwd_ex(s_["q"], s_["k"], s_["v"], s_["a"], s_["b"], A_log=s_["A_log"], dt_bias=s_["dt_bias"],
+                         initial_state=s_["initial_state"], qk_l2norm=True, o=s_["o"], final_state=s_["fs"],
                          workspace=ws)
 
-    for _ in range(args.warmup):
-        prefill_gating_l2()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        prefill_gating_l2()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_gating_l2 = e0.elapsed_time(e1) / args.steps
+    for i in range(args.warmup):
+        prefill_gating_l2(i)
+    ms_gating_l2 = time_loop(prefill_gating_l2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     achieved_gbs = scan_bytes / (ms_scan / 1e3) / 1e9
     useful_tflops = flops / (ms_events / 1e3) / 1e12
 
@@ -305,7 +313,7 @@ def main() -> int:
     # ---------------- the long-context and packed variable-length prefills ---------------------
     # (the same call on the two larger prefill workloads, each with its own initial states; reported
     # beside the headline prefill, which the value and roofline describe)
-    def time_workload(name, calls):
+    def time_workload(name, calls, warm):
         wx = synth.WORKLOADS[name]
         xx = synth.make(wx)
         dd = {key: (None if xx[key] is None else xx[key].to(dev).contiguous())
@@ -322,7 +330,10 @@ def main() -> int:
             gdn_chunk_fwd(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["initial_state"], dd["cu_seqlens"],
                           o=oo, final_state=ff, workspace=wss)
 
-        call()
+        # about 0.1 s of calls first: building the inputs on the host leaves the GPU idle and its
+        # clocks low
+        for _ in range(warm):
+            call()
         torch.cuda.synchronize()
         e0.record()
         for _ in range(calls):
@@ -343,8 +354,8 @@ def main() -> int:
         torch.cuda.empty_cache()
         return res
 
-    long_res = time_workload("long", 5)
-    varlen_res = time_workload("varlen", 3)
+    long_res = time_workload("long", 10, 100)
+    varlen_res = time_workload("varlen", 5, 12)
 
     # ---------------- decode ------------------------------------------------------------------
     wd = synth.WORKLOADS["decode"]
@@ -417,7 +428,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"prefill B={B} T={T} Hk={wl.Hk} Hv={wl.Hv} dk=dv={wl.dk} bf16 in, fp32 "
-                               f"state/out, zero initial state",
+                               f"state/out, zero initial state; calls cycle through {NSETS} input sets "
+                               f"larger together than the last-level cache",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": MI355X_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / MI355X_HBM_GBS, 4),
@@ -428,6 +440,7 @@ def main() -> int:
                      "bytes_per_token_vhead": per_tok_head - 2 * (2 if str(wl.gate_dtype).endswith("bfloat16") else 4),
                      "prepare_ms_per_launch_events": round(ms_prepare, 5),
                      "call_ms_per_launch_events": round(ms_events, 5),
+                     "call_ms_same_buffers_events": round(ms_same_buffers, 5),
                      "call_achieved_gbs": round(nbytes / (ms_events / 1e3) / 1e9, 1),
                      "useful_tflops": round(useful_tflops, 2),
                      "mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4),
