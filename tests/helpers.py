@@ -38,6 +38,30 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref))) / max(rms, 1e-300)
 
 
+def assert_close_blocked(name: str, got: torch.Tensor, ref: np.ndarray, tol: float, rows: int = 2048) -> float:
+    """assert_close for tensors of several GB: the same whole-tensor rule, max|x - x_ref| over every
+    element against tol * rms(x_ref) over every element, evaluated a block of leading-axis rows at a
+    time (after flattening the leading axes) so that no full-size temporary is made."""
+    g = got.detach().to("cpu")
+    assert tuple(g.shape) == ref.shape, (name, tuple(g.shape), ref.shape)
+    lead = int(np.prod(ref.shape[:2])) if ref.ndim > 2 else ref.shape[0]
+    gf = g.reshape(lead, -1)
+    rf = ref.reshape(lead, -1)
+    max_err, sum_sq, count = 0.0, 0.0, 0
+    for a in range(0, lead, rows):
+        gb = gf[a:a + rows].to(torch.float64).numpy()
+        rb = rf[a:a + rows]
+        assert np.all(np.isfinite(gb)), f"{name}: non-finite values in rows {a}..{a + rows}"
+        max_err = max(max_err, float(np.max(np.abs(gb - rb))) if gb.size else 0.0)
+        sum_sq += float(np.sum(np.square(rb)))
+        count += rb.size
+    rms = np.sqrt(sum_sq / max(count, 1))
+    e = max_err / max(rms, 1e-300)
+    print(f"  {name}: max err {e:.3e} x rms (tol {tol:g}, {count} elements)", flush=True)
+    assert e <= tol, f"{name}: max|err| = {e:.3e} * rms > {tol:g} * rms"
+    return e
+
+
 def assert_close(name: str, got, ref: np.ndarray, tol: float) -> float:
     g = got.detach().to("cpu", torch.float64).numpy() if isinstance(got, torch.Tensor) else got
     assert g.shape == ref.shape, (name, g.shape, ref.shape)

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from gated_deltanet_delta_amd import gdn_chunk_fwd, gdn_recurrent_step, synth
-from helpers import assert_close, oracle_of, to_gpu, tol_for
+from helpers import assert_close, assert_close_blocked, oracle_of, to_gpu, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -23,14 +23,10 @@ def run_chunk(x, initial_state="from_inputs"):
     return o, fs
 
 
-def check_chunk(x, tag, tol=None, unit_mask=None):
+def check_chunk(x, tag, tol=None):
     tol = tol_for(x["q"].dtype) if tol is None else tol
     o, fs = run_chunk(x)
-    o_ref, s_ref = oracle_of(x, unit_mask)
-    if unit_mask is not None:
-        # compare only the sampled units (the oracle leaves the others NaN)
-        o = o.cpu().double().numpy()
-        fs = fs.cpu().double().numpy()
+    o_ref, s_ref = oracle_of(x)
     assert_close(f"{tag} o", o, o_ref, tol)
     assert_close(f"{tag} final_state", fs, s_ref, tol)
 
@@ -252,27 +248,56 @@ def test_full_prefill_T4096():
     check_chunk(synth.make(WL["prefill"]), "prefill T=4096")
 
 
-def test_full_long_T32768_sampled_heads():
+def check_chunk_whole(x, tag, tol=None, per_sequence=False):
+    """check_chunk for the full-size workloads: o and every final state compared over the whole
+    tensor, a block of rows at a time (the long and packed workloads' o is several GB in fp64)."""
+    tol = tol_for(x["q"].dtype) if tol is None else tol
+    o, fs = run_chunk(x)
+    o, fs = o.cpu(), fs.cpu()
+    torch.cuda.empty_cache()
+    o_ref, s_ref = oracle_of(x)
+    assert_close_blocked(f"{tag} o", o, o_ref, tol)
+    del o_ref
+    assert_close_blocked(f"{tag} final_state", fs, s_ref, tol)
+    if per_sequence:
+        rms = float(np.sqrt(np.mean(np.square(s_ref))))
+        per = [float(np.max(np.abs(fs[n].double().numpy() - s_ref[n]))) / rms for n in range(len(s_ref))]
+        print(f"  {tag} final_state per sequence: worst {max(per):.3e} x rms (sequence {int(np.argmax(per))})",
+              flush=True)
+
+
+def test_full_long_T32768():
+    """The long-context workload as specified: T = 32768 (512 chunks) carried from a drawn initial
+    state, every v-head, o and the final state over the whole tensors."""
+    check_chunk_whole(synth.make(WL["long"]), "long T=32768")
+
+
+@pytest.mark.parametrize("decay", ["linspace", "small"])
+def test_full_long_T32768_weak_decay(decay):
+    """The long workload's shape with a slow decay, A = linspace(0.1, 0.9) or A ~ U(0.01, 0.05)
+    per v-head: the carried state then survives across hundreds of chunks, so the bf16 rounding of
+    the chunk chain accumulates over 512 carried chunks and a wrong inter-chunk carry moves the final
+    state, which the workload's own strong decay would hide."""
     wl = WL["long"]
-    mask = np.zeros((1, wl.Hv), bool)
-    mask[0, [0, 9, 22, 31]] = True
-    check_chunk(synth.make(wl), "long T=32768 (4 sampled v-heads)", unit_mask=mask)
+    if decay == "linspace":
+        A_log = np.log(np.linspace(0.1, 0.9, wl.Hv)).astype(np.float32)
+    else:
+        A_log = np.log(np.random.default_rng(5).uniform(0.01, 0.05, wl.Hv)).astype(np.float32)
+    check_chunk_whole(synth.make(wl, seed=200 + len(decay), A_log=A_log), f"long T=32768 weak decay {decay}")
 
 
-def test_full_varlen_sampled_units():
-    wl = WL["varlen"]
-    x = synth.make(wl)
-    lens = np.diff(x["cu_seqlens"].numpy())
-    rng = np.random.default_rng(99)
-    mask = np.zeros((wl.n_seqs, wl.Hv), bool)
-    picks = [int(np.argmax(lens)), int(np.argmin(lens))] + list(rng.choice(wl.n_seqs, 6, replace=False))
-    for n in picks:
-        mask[n, rng.choice(wl.Hv, 6, replace=False)] = True
-    print(f"  varlen: {int(x['cu_seqlens'][-1])} tokens, {mask.sum()} sampled units", flush=True)
-    check_chunk(x, "varlen (sampled units)", unit_mask=mask)
+@pytest.mark.timeout(600)
+def test_full_varlen():
+    """The packed workload as specified: 64 sequences of 300..8192 tokens with their own initial
+    states, o over every token and every final state, the whole tensors."""
+    x = synth.make(WL["varlen"])
+    print(f"  varlen: {int(x['cu_seqlens'][-1])} tokens", flush=True)
+    check_chunk_whole(x, "varlen", per_sequence=True)
 
 
-def test_full_decode_128_steps_sampled_sequences():
+def test_full_decode_128_steps():
+    """The decode workload as specified: 256 sequences, 128 successive one-token steps against the
+    cached state; o of every sequence at every step and the whole state after step 128."""
     wl = WL["decode"]
     x0 = synth.make(wl)
     A_log = x0["raw"]["A_log"]
@@ -284,14 +309,12 @@ def test_full_decode_128_steps_sampled_sequences():
         o, _ = gdn_recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
         outs.append(o.cpu())
     torch.cuda.synchronize()
-    picks = [0, 17, 64, 128, 200, 255]
-    cat = lambda key: torch.cat([s[key][picks] for s in steps], 1)  # noqa: E731
+    cat = lambda key: torch.cat([s[key] for s in steps], 1)  # noqa: E731
     ref_in = dict(q=cat("q"), k=cat("k"), v=cat("v"), g=cat("g"), beta=cat("beta"),
-                  initial_state=x0["initial_state"][picks], cu_seqlens=None)
+                  initial_state=x0["initial_state"], cu_seqlens=None)
     o_ref, s_ref = oracle_of(ref_in)
-    got = torch.cat([o[picks] for o in outs], 1)
-    assert_close("decode o (128 steps, sampled sequences)", got, o_ref, 2e-2)
-    assert_close("decode state after 128 steps", state[picks], s_ref, 2e-2)
+    assert_close_blocked("decode o (256 sequences x 128 steps)", torch.cat(outs, 1), o_ref, 2e-2)
+    assert_close_blocked("decode state after 128 steps", state, s_ref, 2e-2)
 
 
 @pytest.mark.parametrize("dv,T", [(128, 4096), (64, 1000)])
