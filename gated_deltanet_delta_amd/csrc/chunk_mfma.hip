@@ -53,7 +53,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kC = 64;      // chunk length
+constexpr int kC = kChunk; // chunk length
 constexpr int kGRows = 5;   // rows of a chunk's gate block (of kC floats each)
 constexpr int kDK = 128;    // key dimension handled by this file
 constexpr int kThreads = 256;
@@ -90,13 +90,12 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     const int per = (N + kThreads - 1) / kThreads;
     const int n0 = tid * per, n1 = min(N, n0 + per);
     auto len_of = [&](int n) {
-        int a = cu_seqlens[n], b = cu_seqlens[n + 1];
-        a = a < 0 ? 0 : (a > T ? T : a);
-        b = b < a ? a : (b > T ? T : b);
+        int row, a, b;
+        sequence_range(cu_seqlens, n, T, row, a, b);
         return b - a;
     };
     int sum = 0;
-    for (int n = n0; n < n1; ++n) sum += (len_of(n) + kC - 1) / kC;
+    for (int n = n0; n < n1; ++n) sum += sequence_chunks(cu_seqlens, n, T);
     part[tid] = sum;
     lds_barrier();
     for (int off = 1; off < kThreads; off <<= 1) {
@@ -108,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     int run = part[tid] - sum;  // exclusive prefix of this thread's block
     for (int n = n0; n < n1; ++n) {
         chunk_start[n] = run;
-        run += (len_of(n) + kC - 1) / kC;
+        run += sequence_chunks(cu_seqlens, n, T);
     }
     if (tid == kThreads - 1) chunk_start[N] = part[kThreads - 1];
 
@@ -124,42 +123,6 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(const int32_t* __restric
     } else {
         for (int n = tid; n < N; n += kThreads) order[n] = n;
     }
-}
-
-// Locate chunk slot `slot`: sequence n, chunk index ci, packed row, first token and length.
-struct ChunkLoc {
-    int n, ci, row, t0, len;
-};
-
-__device__ __forceinline__ bool locate_chunk(int slot, const int32_t* cu_seqlens,
-                                             const int32_t* chunk_start, int N, int T, int nct,
-                                             ChunkLoc& loc) {
-    if (cu_seqlens) {
-        if (slot >= chunk_start[N]) return false;
-        int lo = 0, hi = N;  // largest n with chunk_start[n] <= slot
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (chunk_start[mid] <= slot) lo = mid; else hi = mid;
-        }
-        // skip zero-length sequences that share the same start
-        int n = lo;
-        while (n + 1 < N && chunk_start[n + 1] <= slot) ++n;
-        int a = cu_seqlens[n], b = cu_seqlens[n + 1];
-        a = a < 0 ? 0 : (a > T ? T : a);
-        b = b < a ? a : (b > T ? T : b);
-        loc.n = n;
-        loc.ci = slot - chunk_start[n];
-        loc.row = 0;
-        loc.t0 = a + loc.ci * kC;
-        loc.len = min(kC, b - loc.t0);
-        return loc.len > 0;
-    }
-    loc.n = slot / nct;
-    loc.ci = slot % nct;
-    loc.row = loc.n;
-    loc.t0 = loc.ci * kC;
-    loc.len = min(kC, T - loc.t0);
-    return loc.len > 0;
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "seqmath.h"
+
 namespace gdn {
 
 constexpr int kWave = 64;
@@ -56,37 +58,5 @@ constexpr float kL2Eps = 1e-6f;
 // correctly rounded library exp and an IEEE division cost some 25 instructions per element, which a
 // streaming kernel cannot hide behind its memory traffic.
 __device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.f + __expf(-u)); }
-
-// State slot of sequence (or batch row) n: n itself, or state_indices[n] in a pool of num_slots
-// states.  An index outside [0, num_slots) marks a padding row, which has no state: false is
-// returned and slot is set to 0 (any in-bounds value; nothing is read or written through it).
-__device__ __forceinline__ bool state_slot(const int32_t* state_indices, int num_slots, int n, int& slot) {
-    if (!state_indices) {
-        slot = n;
-        return true;
-    }
-    const int s = state_indices[n];
-    const bool ok = s >= 0 && s < num_slots;
-    slot = ok ? s : 0;
-    return ok;
-}
-
-// Sequence n's token range [t0, t1) inside batch row `row`, clamped to [0, T] so that a malformed
-// cu_seqlens array can only produce wrong numbers, never an access outside the buffers.
-__device__ __forceinline__ void sequence_range(const int32_t* cu_seqlens, int n, int T, int& row,
-                                               int& t0, int& t1) {
-    if (cu_seqlens) {
-        int a = cu_seqlens[n], b = cu_seqlens[n + 1];
-        a = a < 0 ? 0 : (a > T ? T : a);
-        b = b < a ? a : (b > T ? T : b);
-        row = 0;
-        t0 = a;
-        t1 = b;
-    } else {
-        row = n;
-        t0 = 0;
-        t1 = T;
-    }
-}
 
 }  // namespace gdn

@@ -39,6 +39,7 @@ const char* gdn_status_string(gdn_status status) {
         case GDN_ERROR_NOT_SUPPORTED: return "GDN_ERROR_NOT_SUPPORTED";
         case GDN_ERROR_WORKSPACE: return "GDN_ERROR_WORKSPACE";
         case GDN_ERROR_LAUNCH_FAILURE: return "GDN_ERROR_LAUNCH_FAILURE";
+        default: break;
     }
     return "GDN_ERROR_UNKNOWN";
 }
@@ -49,6 +50,7 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
                                     gdn_dtype qkv_dtype) {
     if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return 0;
     if (!head_dim_ok(dk) || !head_dim_ok(dv) || !dtype_ok(qkv_dtype)) return 0;
+    if (!sizes_fit(B, T, Hv, dv > dk ? dv : dk) || !sizes_fit(N, 1, Hv, (long long)dk * dv)) return 0;
     if (!use_mfma(dk, dv, qkv_dtype)) return 0;
     return gdn::chunk_mfma_workspace_size(B, T, Hk, Hv, dk, dv, N);
 }

@@ -54,12 +54,15 @@ typedef enum {
     GDN_ERROR_INVALID_VALUE = 1,    /* a null required pointer, a bad size or a bad combination */
     GDN_ERROR_NOT_SUPPORTED = 2,    /* valid, but a head size or dtype this build has no kernel for */
     GDN_ERROR_WORKSPACE = 3,        /* workspace pointer null or smaller than the size query says */
-    GDN_ERROR_LAUNCH_FAILURE = 4    /* the HIP runtime refused a launch (hipGetLastError) */
+    GDN_ERROR_LAUNCH_FAILURE = 4,   /* the HIP runtime refused a launch (hipGetLastError) */
+    GDN_STATUS_MAX_ENUM = 0x7fffffff  /* not a status: gives the type the range of a 32-bit int, so
+                                         any int a caller passes is a valid value of it */
 } gdn_status;
 
 typedef enum {
     GDN_F32 = 0,                    /* IEEE binary32 */
-    GDN_BF16 = 1                    /* bfloat16 (upper half of binary32) */
+    GDN_BF16 = 1,                   /* bfloat16 (upper half of binary32) */
+    GDN_DTYPE_MAX_ENUM = 0x7fffffff /* not a dtype: as GDN_STATUS_MAX_ENUM (rejected by every call) */
 } gdn_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
