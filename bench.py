@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
     python bench.py --copy-calibration      (a plain 256 MiB device copy, for HBM counter scaling)
+    python bench.py --prefill-only          (the headline prefill and its halves only, for profilers)
 
 Prints ONE JSON line.  The timed step is one gdn_chunk_fwd call over the Qwen3-Next-shaped prefill
 workload (B=1, T=4096, 16 q/k heads, 32 v heads, head dim 128, bf16 inputs, fp32 state and output),
@@ -49,16 +50,36 @@ CHUNK = 64
 
 METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next shape, 1 GPU"
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
-# reads on a plain copy of known size (profiles/); None whenever the kernel changed since.
-TRAFFIC_SCAN = 181249434      # chunk_scan_kernel<128>, prefill B=1 T=4096
-TRAFFIC_DECODE = 1085280816    # recurrent_kernel<128,128,bf16,f32>, one decode step, B=256
-TRAFFIC_CONV = 134710246       # causal_conv1d_kernel<4,8,bf16>, T=4096, C=8192
-TRAFFIC_NORM = 134250675       # gated_rmsnorm_kernel<128,bf16,bf16>, 4096 x 32 rows
-# Matrix-core flops each launch executes, from rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops,
-# profiles/mfma_utilisation_prefill_T4096.md); None whenever the kernel changed since.
-EXEC_MFMA_BF16_SCAN = 102563840 * 512            # chunk_scan_kernel<128>, prefill B=1 T=4096
-EXEC_MFMA_F32_BWD = (69206016 + 36700160) * 512   # bwd_slice_kernel + bwd_combine_kernel, same prefill
+# Counter readings per launch from rocprofv3 (profiles/): HBM bytes from FETCH_SIZE and WRITE_SIZE, each
+# scaled by what the same counter reads on a plain copy of known size, and the matrix-core work from
+# SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
+# kernel's source file whose hash it names; when the file has changed since, it is reported as null.
+COUNTERS = {
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": None,
+             "traffic": None, "mfma_exec_flops": None},
+    "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
+               "traffic": 1085280816},
+    "conv": {"source": "gated_deltanet_delta_amd/csrc/conv1d.hip", "sha16": "592040b86d906439",
+             "traffic": 134710246},
+    "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
+             "traffic": 134250675},
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "eb9461988c0ef06b",
+            "mfma_exec_flops": (69206016 + 36700160) * 512},
+}
+
+
+def source_sha16(rel: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def counter(kernel: str, key: str):
+    """A counter reading if it was taken at the kernel's current source, else None."""
+    c = COUNTERS[kernel]
+    if c.get(key) is None or c["sha16"] != source_sha16(c["source"]):
+        return None
+    return c[key]
 
 
 def prefill_algorithmic(wl, T: int, B: int, N: int, init_state: bool):
@@ -87,6 +108,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the headline prefill and its two halves (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (HBM counter scaling)")
     args = ap.parse_args()
@@ -154,8 +177,14 @@ def main() -> int:
         gdn_chunk_fwd(s_["q"], s_["k"], s_["v"], s_["g"], s_["beta"], s_["initial_state"], None,
                       o=s_["o"], final_state=s_["fs"], workspace=ws, stage=stage)
 
-    for i in range(args.warmup):
-        prefill_step(i=i)
+    # Warm-up: at least --warmup calls and at least 0.3 s of them, whatever --warmup says (the
+    # GPU's clocks take a few milliseconds of sustained work to settle; a cold stretch reads slow).
+    warm0, warm_calls = time.perf_counter(), 0
+    while warm_calls < args.warmup or time.perf_counter() - warm0 < 0.3:
+        prefill_step(i=warm_calls)
+        warm_calls += 1
+        if warm_calls % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -196,6 +225,15 @@ def main() -> int:
 
     ms_prepare = time_stage("prepare")
     ms_scan = time_stage("scan")
+    if args.prefill_only:
+        print(json.dumps({"workload": "prefill B=1 T=4096 Hk=16 Hv=32 dk=dv=128 bf16 in",
+                          "tokens_per_s": round(tokens / (ms_wall / 1e3), 1), "ms_per_call_wall": round(ms_wall, 5),
+                          "ms_per_call_events": round(ms_events, 5), "ms_scan_events": round(ms_scan, 5),
+                          "ms_prepare_events": round(ms_prepare, 5),
+                          "scan_useful_mfma_frac": round(flops / (ms_scan / 1e3) / 1e12 / MI355X_BF16_TFLOPS, 4),
+                          "scan_hbm_frac": round(scan_bytes / (ms_scan / 1e3) / 1e9 / MI355X_HBM_GBS, 4)}),
+              flush=True)
+        return 0
 
     # the same prefill with the gates formed in the kernels from the raw projections a, b
     def prefill_gating(i):
@@ -220,6 +258,87 @@ def main() -> int:
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     achieved_gbs = scan_bytes / (ms_scan / 1e3) / 1e9
     useful_tflops = flops / (ms_events / 1e3) / 1e12
+    scan_useful_tflops = flops / (ms_scan / 1e3) / 1e12
+    scan_traffic = counter("scan", "traffic")
+    scan_exec = counter("scan", "mfma_exec_flops")
+
+    # ---------------- ceilings measured on this GPU in the same run ----------------------------
+    # bf16 GEMM through torch.matmul (the vendor library), 8192^3, and a plain 1 GiB device copy
+    ga_ = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gb_ = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    for _ in range(5):
+        gc_ = torch.matmul(ga_, gb_)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        gc_ = torch.matmul(ga_, gb_)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * 8192 ** 3 / (e0.elapsed_time(e1) / 20 / 1e3) / 1e12
+    del ga_, gb_, gc_
+    csrc_ = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst_ = torch.empty_like(csrc_)
+    for _ in range(3):
+        cdst_.copy_(csrc_)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        cdst_.copy_(csrc_)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc_.numel() * 4 / (e0.elapsed_time(e1) / 20 / 1e3) / 1e9
+    del csrc_, cdst_
+    torch.cuda.empty_cache()
+    ceilings = {"bf16_gemm_tflops": round(gemm_tflops, 1), "bf16_gemm": "torch.matmul 8192x8192x8192 bf16",
+                "copy_gbs": round(copy_gbs, 1), "copy": "torch copy_ of 1 GiB (read + write counted)"}
+
+    # ---------------- ablation: the same prefill through the token-serial (recurrent) kernel ----
+    # gdn_recurrent_step with all 4096 tokens in one call: the state stays in registers and the tokens
+    # are taken one after another, the pure-RNN mode the chunked form replaces
+    st_r = torch.zeros((B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+    o_r = torch.empty_like(o)
+    gdn_recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st_r, o=o_r)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        gdn_recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st_r, o=o_r)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_recurrent = e0.elapsed_time(e1) / 3
+    del st_r, o_r
+    ablation = {"workload": "the prefill above", "recurrent_call": "gdn_recurrent_step, T=4096 in one call",
+                "ms_recurrent": round(ms_recurrent, 4), "ms_chunked": round(ms_events, 5),
+                "chunked_speedup": round(ms_recurrent / ms_events, 2),
+                "pages_claim": "chunk mode 4-6x faster than a pure RNN in training (Qwen3-Next article, "
+                               "jsqmd.com, section 2.2; hardware unstated)"}
+
+    # ---------------- head size 64 with bf16 inputs --------------------------------------------
+    w64 = synth.Workload(**{**wl.__dict__, "dk": 64, "dv": 64})
+    x64 = synth.make(w64, seed=wl.seed + 64)
+    d64 = {key: (None if x64[key] is None else x64[key].to(dev).contiguous())
+           for key in ("q", "k", "v", "g", "beta")}
+    del x64
+    o64 = torch.empty((B, T, wl.Hv, 64), dtype=torch.float32, device=dev)
+    f64_ = torch.empty((N, wl.Hv, 64, 64), dtype=torch.float32, device=dev)
+    ws64 = torch.empty(max(workspace_size(B, T, wl.Hk, wl.Hv, 64, 64, N, wl.dtype), 1), dtype=torch.uint8,
+                       device=dev)
+    call64 = lambda: gdn_chunk_fwd(d64["q"], d64["k"], d64["v"], d64["g"], d64["beta"], None, None,  # noqa: E731
+                                   o=o64, final_state=f64_, workspace=ws64)
+    for _ in range(10):
+        call64()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        call64()
+    e1.record()
+    torch.cuda.synchronize()
+    ms64 = e0.elapsed_time(e1) / 20
+    nb64, fl64, _ = prefill_algorithmic(w64, T, B, N, False)
+    dk64_res = {"workload": f"prefill B=1 T={T} Hk={wl.Hk} Hv={wl.Hv} dk=dv=64 bf16 in, fp32 state/out",
+                "ms_per_call_events": round(ms64, 5), "tokens_per_s": round(tokens / (ms64 / 1e3), 1),
+                "useful_tflops": round(fl64 / (ms64 / 1e3) / 1e12, 2),
+                "achieved_gbs": round(nb64 / (ms64 / 1e3) / 1e9, 1)}
+    del d64, o64, f64_, ws64
 
     clib = _lib.load()
 
@@ -288,6 +407,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_bwd = e0.elapsed_time(e1) / bwd_calls
     bwd_flops = BWD_FLOPS_PER_TOKEN_VHEAD * tokens * wl.Hv
+    bwd_exec = counter("bwd", "mfma_exec_flops")
     del bws
 
     # the same through every input option (gates from a, b and q, k normalised, both differentiated)
@@ -406,13 +526,34 @@ def main() -> int:
         f = synth.to_f64
         arrs = [f(x[key]) for key in ("q", "k", "v", "g", "beta")]
         threads = O.default_threads()
+        runs = []
+        for _ in range(3):
+            c0 = time.perf_counter()
+            O.forward(*arrs, None, None, threads=threads)
+            runs.append(time.perf_counter() - c0)
+        sec = sorted(runs)[1]
+        # one thread on 4 of the 32 v-heads, scaled to the whole workload
+        mask = np.zeros((N, wl.Hv), dtype=bool)
+        mask[:, :4] = True
         c0 = time.perf_counter()
-        O.forward(*arrs, None, None, threads=threads)
-        c1 = time.perf_counter()
-        cpu = {"value": round(tokens / (c1 - c0), 1), "unit": "tokens/s", "cores": threads,
+        O.forward(*arrs, None, None, unit_mask=mask, threads=1)
+        sec1 = (time.perf_counter() - c0) * wl.Hv / 4
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as fh:
+                for ln in fh:
+                    if ln.startswith("model name"):
+                        cpu_model = ln.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+        cpu = {"value": round(tokens / sec, 1), "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
                "sample": f"the whole prefill workload (T={T}, {wl.Hv} v-heads), fp64 token-by-token, "
-                         f"{c1 - c0:.2f} s"}
+                         f"median of 3 runs of {sec:.2f} s",
+               "cpu_model": cpu_model,
+               "threads_1": {"value": round(tokens / sec1, 1), "unit": "tokens/s",
+                             "sample": "4 of the 32 v-heads on one thread, scaled to all 32"}}
 
     line = {
         "metric": METRIC,
@@ -431,25 +572,33 @@ def main() -> int:
                                f"state/out, zero initial state; calls cycle through {NSETS} input sets "
                                f"larger together than the last-level cache",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": MI355X_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved_gbs / MI355X_HBM_GBS, 4),
-                     "traffic": TRAFFIC_SCAN,
+        "roofline": {"bound": "mfma", "achieved": round(scan_useful_tflops, 2), "peak": MI355X_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(scan_useful_tflops / MI355X_BF16_TFLOPS, 4),
+                     "traffic": scan_traffic,
                      "kernel": "chunk_scan_kernel<128> (gdn_chunk_fwd_scan)",
                      "ms_per_launch_events": round(ms_scan, 5),
-                     "algorithmic_bytes_per_launch": int(scan_bytes),
-                     "bytes_per_token_vhead": per_tok_head - 2 * (2 if str(wl.gate_dtype).endswith("bfloat16") else 4),
+                     "flops_per_token_vhead": flops // (tokens * wl.Hv),
+                     "algorithmic_flops_per_launch": int(flops),
+                     "mfma_executed_flops_per_launch": scan_exec,
+                     "mfma_executed_tflops": (None if scan_exec is None else
+                                              round(scan_exec / (ms_scan / 1e3) / 1e12, 1)),
+                     "mfma_frac_executed": (None if scan_exec is None else
+                                            round(scan_exec / (ms_scan / 1e3) / 1e12 / MI355X_BF16_TFLOPS, 4)),
+                     "hbm": {"achieved": round(achieved_gbs, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                             "frac": round(achieved_gbs / MI355X_HBM_GBS, 4),
+                             "algorithmic_bytes_per_launch": int(scan_bytes),
+                             "bytes_per_token_vhead": per_tok_head - 2 * (2 if str(wl.gate_dtype).endswith("bfloat16") else 4)},
+                     "measured_ceilings": ceilings,
+                     "frac_of_measured_gemm": round(scan_useful_tflops / ceilings["bf16_gemm_tflops"], 4),
+                     "hbm_frac_of_measured_copy": round(achieved_gbs / ceilings["copy_gbs"], 4),
                      "prepare_ms_per_launch_events": round(ms_prepare, 5),
                      "call_ms_per_launch_events": round(ms_events, 5),
                      "call_ms_same_buffers_events": round(ms_same_buffers, 5),
                      "call_achieved_gbs": round(nbytes / (ms_events / 1e3) / 1e9, 1),
-                     "useful_tflops": round(useful_tflops, 2),
-                     "mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4),
-                     "mfma_executed_flops_per_launch": EXEC_MFMA_BF16_SCAN,
-                     "mfma_executed_tflops": (None if EXEC_MFMA_BF16_SCAN is None else
-                                              round(EXEC_MFMA_BF16_SCAN / (ms_scan / 1e3) / 1e12, 1)),
-                     "mfma_frac_executed": (None if EXEC_MFMA_BF16_SCAN is None else
-                                            round(EXEC_MFMA_BF16_SCAN / (ms_scan / 1e3) / 1e12
-                                                  / MI355X_BF16_TFLOPS, 4))},
+                     "call_useful_tflops": round(useful_tflops, 2),
+                     "call_mfma_frac_useful": round(useful_tflops / MI355X_BF16_TFLOPS, 4)},
+        "chunk_vs_recurrent": ablation,
+        "prefill_dk64": dk64_res,
         "prefill_long": long_res,
         "prefill_varlen": varlen_res,
         "prefill_gating": {"call": "gdn_chunk_fwd_gating (gates formed in the kernels from a, b)",
@@ -465,7 +614,7 @@ def main() -> int:
                           "roofline": {"bound": "hbm", "achieved": round(conv_bytes / (ms_conv / 1e3) / 1e9, 1),
                                        "peak": MI355X_HBM_GBS, "unit": "GB/s",
                                        "frac": round(conv_bytes / (ms_conv / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
-                                       "traffic": TRAFFIC_CONV,
+                                       "traffic": counter("conv", "traffic"),
                                        "algorithmic_bytes_per_launch": int(conv_bytes)}},
         "gated_rmsnorm": {"call": "gdn_gated_rmsnorm on the prefill's o (fp32 in, bf16 z and out)",
                           "rows": o.numel() // wl.dv, "d": wl.dv,
@@ -473,7 +622,7 @@ def main() -> int:
                           "roofline": {"bound": "hbm", "achieved": round(norm_bytes / (ms_norm / 1e3) / 1e9, 1),
                                        "peak": MI355X_HBM_GBS, "unit": "GB/s",
                                        "frac": round(norm_bytes / (ms_norm / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
-                                       "traffic": TRAFFIC_NORM,
+                                       "traffic": counter("norm", "traffic"),
                                        "algorithmic_bytes_per_launch": int(norm_bytes)}},
         "backward": {"call": "gdn_chunk_bwd (dq, dk, dv, dg, dbeta, d_initial of the prefill; fp32 "
                              "arithmetic, the slice kernel on fp32 matrix cores)",
@@ -484,22 +633,29 @@ def main() -> int:
                                   "frac": round(bwd_flops / (ms_bwd / 1e3) / 1e12 / MI355X_F32_TFLOPS, 4),
                                   "flops_per_token_vhead": BWD_FLOPS_PER_TOKEN_VHEAD,
                                   "algorithmic_flops_per_call": int(bwd_flops),
-                                  "mfma_executed_flops_per_call": EXEC_MFMA_F32_BWD,
-                                  "mfma_frac_executed": (None if EXEC_MFMA_F32_BWD is None else
-                                                         round(EXEC_MFMA_F32_BWD / (ms_bwd / 1e3) / 1e12
+                                  "mfma_executed_flops_per_call": bwd_exec,
+                                  "mfma_frac_executed": (None if bwd_exec is None else
+                                                         round(bwd_exec / (ms_bwd / 1e3) / 1e12
                                                                / MI355X_F32_TFLOPS, 4))},
                      "every_option": {"call": "gdn_chunk_bwd_ex (gates from a, b and q, k L2-normalised, "
                                               "both differentiated: da, db, dA_log, ddt_bias, raw dq, dk)",
                                       "ms_per_call_events": round(ms_bwd_ex, 4),
                                       "tokens_per_s": round(tokens / (ms_bwd_ex / 1e3), 1)}},
         "cpu_baseline": cpu,
+        "pages_context": {
+            "note": "layer- or model-level claims of the pages, hardware unstated: context, not targets",
+            "vs_standard_attention_32k": "9.3x throughput, 1/8 memory (Qwen3-Next architecture write-up, "
+                                         "intelliparadigm.com, section 2.2)",
+            "vs_transformer_8192": "3.8x speed, 48G -> 12G memory (Gated DeltaNet deployment article, "
+                                   "kwkr.cn, section 2.3)",
+            "chunk_vs_rnn_training": "4-6x (Qwen3-Next Gated DeltaNet article, jsqmd.com, section 2.2)"},
         "decode": {"metric": "decode state GB/s", "value": round(state_gbs, 1), "unit": "GB/s",
                    "workload": f"decode B={wd.B} Hk={wd.Hk} Hv={wd.Hv} dk=dv={wd.dk}, {nd} one-token "
                                f"steps, fp32 state {wd.B * wd.Hv * wd.dk * wd.dv * 4 / 2**20:.0f} MiB",
                    "ms_per_step": round(ms_decode, 5),
                    "roofline": {"bound": "hbm", "achieved": round(total_gbs, 1), "peak": MI355X_HBM_GBS,
                                 "unit": "GB/s", "frac": round(total_gbs / MI355X_HBM_GBS, 4),
-                                "traffic": TRAFFIC_DECODE, "kernel": "recurrent_kernel<128,128,bf16,f32>",
+                                "traffic": counter("decode", "traffic"), "kernel": "recurrent_kernel<128,128,bf16,f32>",
                                 "algorithmic_bytes_per_launch": int(total_bytes)},
                    "gating": {"call": "gdn_recurrent_step_gating (gates formed in the kernel from a, b)",
                               "ms_per_step": round(ms_decode_gating, 5),
