@@ -21,7 +21,8 @@ EXPORTED = ("gdn_status_string", "gdn_version", "gdn_chunk_fwd_workspace_size", 
             "gdn_chunk_fwd_gating", "gdn_recurrent_step_gating", "gdn_chunk_fwd_indexed",
             "gdn_recurrent_step_indexed", "gdn_gated_rmsnorm", "gdn_causal_conv1d",
             "gdn_chunk_fwd_ex", "gdn_recurrent_step_ex", "gdn_chunk_bwd_workspace_size",
-            "gdn_chunk_bwd", "gdn_chunk_bwd_ex_workspace_size", "gdn_chunk_bwd_ex")
+            "gdn_chunk_bwd", "gdn_chunk_bwd_ex_workspace_size", "gdn_chunk_bwd_ex",
+            "gdn_chunk_fwd_noalloc_max_bytes", "gdn_chunk_fwd_noalloc")
 
 GDN_FLAG_QK_L2NORM = 1
 
@@ -54,6 +55,10 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = i32
         fn.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp, vp, sz, vp]
+    lib.gdn_chunk_fwd_noalloc_max_bytes.restype = sz
+    lib.gdn_chunk_fwd_noalloc_max_bytes.argtypes = []
+    lib.gdn_chunk_fwd_noalloc.restype = i32
+    lib.gdn_chunk_fwd_noalloc.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp, vp]
     lib.gdn_recurrent_step.restype = i32
     lib.gdn_recurrent_step.argtypes = [vp] * 6 + [i32] * 6 + [i32, i32] + [vp, vp]
     lib.gdn_chunk_fwd_gating.restype = i32

@@ -122,6 +122,37 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                        workspace, gating=False)
 
 
+def gdn_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None, *, o: torch.Tensor,
+                          final_state: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gdn_chunk_fwd with its scratch in the library's static device array (no workspace, nothing
+    allocated by the library; the caller passes o and final_state).  Raises GdnError
+    (GDN_ERROR_WORKSPACE) when the call needs more scratch than the array holds."""
+    lib = _lib.load()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, H, d]")
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    for t, shape, what in ((k, (B, T, Hk, dk), "k"), (v, (B, T, Hv, dv), "v"), (g, (B, T, Hv), "g"),
+                           (beta, (B, T, Hv), "beta"), (o, (B, T, Hv, dv), "o"),
+                           (final_state, (N, Hv, dk, dv), "final_state")):
+        _check(t, shape, what, dev)
+    _check(q, (B, T, Hk, dk), "q", dev)
+    if initial_state is not None:
+        _check(initial_state, (N, Hv, dk, dv), "initial_state", dev, torch.float32)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, (N + 1,), "cu_seqlens", dev, torch.int32)
+    st = lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                   _ptr(cu_seqlens), B, T, Hk, Hv, dk, dv, N, _code(q, "q"), _code(g, "g"),
+                                   _ptr(o), _ptr(final_state), _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_chunk_fwd_noalloc")
+    return o, final_state
+
+
 def gdn_chunk_fwd_gating(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor,
                          b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
                          initial_state: Optional[torch.Tensor] = None,

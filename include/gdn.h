@@ -119,6 +119,34 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          hipStream_t stream);
 
 /*
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ *
+ * Arguments, checks and results are those of gdn_chunk_fwd on the same stream; the scratch between the
+ * call's two phases comes from a static device array of GDN_NOALLOC_SCRATCH_BYTES (64 MiB) inside the
+ * library instead of a caller's workspace.  Each GPU the library runs on holds its own copy of that
+ * array until the process ends; nothing is allocated or freed by the call.  The array's address on a
+ * device is looked up on the first call there (the stream must belong to the calling thread's current
+ * device, else GDN_ERROR_INVALID_VALUE).
+ *   - GDN_ERROR_WORKSPACE when gdn_chunk_fwd_workspace_size(...) for these sizes exceeds
+ *     GDN_NOALLOC_SCRATCH_BYTES (e.g. more than about 6000 tokens at 16 q/k and 32 v heads of 128).
+ *   - Every call on one GPU shares that GPU's array, so two calls that overlap in time on one GPU
+ *     (on different streams, or from different threads) race and give undefined results; calls
+ *     ordered on one stream are safe.  The array keeps the last call's contents; no call depends on
+ *     them.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+size_t gdn_chunk_fwd_noalloc_max_bytes(void);    /* GDN_NOALLOC_SCRATCH_BYTES, as built */
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 const float* initial_state, const int32_t* cu_seqlens,
+                                 int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                 gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                                 float* o, float* final_state,
+                                 hipStream_t stream);
+
+/*
  * gdn_chunk_fwd_prepare, gdn_chunk_fwd_scan -- the two halves of gdn_chunk_fwd.
  *
  * gdn_chunk_fwd(args) is exactly gdn_chunk_fwd_prepare(args) followed by gdn_chunk_fwd_scan(args)
