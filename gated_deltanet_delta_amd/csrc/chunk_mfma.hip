@@ -1,4 +1,4 @@
-// chunk_mfma.hip -- chunked gated delta rule on gfx950 bf16 matrix cores (dk = 128).
+// chunk_mfma.hip -- chunked gated delta rule on gfx950 bf16 matrix cores (dk = 64 or 128).
 //
 // Notation (one chunk of C = 64 tokens of one sequence and v-head, start state S (dk x dv), G_t the
 // running sum of g inside the chunk, Gam_tj = e^(G_t - G_j) for j <= t):
@@ -55,7 +55,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = kChunk; // chunk length
 constexpr int kGRows = 5;   // rows of a chunk's gate block (of kC floats each)
-constexpr int kDK = 128;    // key dimension handled by this file
+// Key dimension DK (64 or 128) is a template parameter of both kernels; KB = DK / 32 is the number of
+// 32-key steps of one matrix-core product over the keys.
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -225,7 +226,7 @@ __device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }
 
 // (at most 128 registers per lane: four waves per SIMD, so a whole 4096-token prefill's chunk
 // workgroups are resident at once)
-template <typename TG, bool L2>
+template <int DK, typename TG, bool L2>
 __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const TG* __restrict__ g,
     const TG* __restrict__ beta, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
@@ -236,6 +237,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     __shared__ float sT[10][16 * kBP];     // blocks (a, b), a >= b, of T = (I + A)^-1
     __shared__ float sB[kC];
 
+    constexpr int KB = DK / 32;
     const int slot = blockIdx.x, kh = blockIdx.y;
     ChunkLoc loc;
     if (!locate_chunk(slot, cu_seqlens, chunk_start, N, T, nct, loc)) return;
@@ -253,34 +255,34 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     // the chunk's end repeat its last row: they only meet rows with beta = 0.
     auto kfrag = [&](int t, int kb) {
         const int r = min(16 * t + c, L - 1);
-        return *reinterpret_cast<const bf16x8*>(k + ((tok0 + r) * Hk + kh) * kDK + 32 * kb + 8 * gq);
+        return *reinterpret_cast<const bf16x8*>(k + ((tok0 + r) * Hk + kh) * DK + 32 * kb + 8 * gq);
     };
     // token tiles of the K rows: wave 0 {0, 1}, wave 1 {1, 2, 0}, wave 2 {2, 3}, wave 3 {3, 0, 1}
     const int tt0 = wave, tt1 = (wave + 1) & 3, tt2 = wave == 1 ? 0 : 1;
-    bf16x8 k0[4], k1[4], k2[4];
+    bf16x8 k0[KB], k1[KB], k2[KB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
         k0[kb] = kfrag(tt0, kb);
         k1[kb] = kfrag(tt1, kb);
     }
     if (wave & 1) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) k2[kb] = kfrag(tt2, kb);
+        for (int kb = 0; kb < KB; ++kb) k2[kb] = kfrag(tt2, kb);
     }
     // the previous chunk's K rows 16 b + c, b = 0..3, for N
-    bf16x8 kp[4][4];
+    bf16x8 kp[4][KB];
     if (has_prev) {
-        const __bf16* pb = k + ((tok0 - kC + c) * Hk + kh) * kDK + 8 * gq;
+        const __bf16* pb = k + ((tok0 - kC + c) * Hk + kh) * DK + 8 * gq;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                kp[b][kb] = *reinterpret_cast<const bf16x8*>(pb + (size_t)16 * b * Hk * kDK + 32 * kb);
+            for (int kb = 0; kb < KB; ++kb)
+                kp[b][kb] = *reinterpret_cast<const bf16x8*>(pb + (size_t)16 * b * Hk * DK + 32 * kb);
     }
     auto kkt = [&](const bf16x8* ka, const bf16x8* kb_) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mma(ka[kb], kb_[kb], acc);
+        for (int kb = 0; kb < KB; ++kb) acc = mma(ka[kb], kb_[kb], acc);
         return acc;
     };
     // lane (g, c) element r of tile (ta, tb) holds (K K^T)[16 ta + 4 g + r][16 tb + c]
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         auto rnorm = [&](const bf16x8* kf) {
             float ss = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float x = (float)kf[kb][e];
@@ -474,13 +476,13 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         // rq_t = 1 / sqrt(|q_t|^2 + eps) for token tile `wave` (lane (g, c): 32 of row 16 wave + c's
         // keys), into every v-head's gate block; read last, when the solve's registers are free
         const int qrow = min(16 * wave + c, L - 1);
-        const __bf16* qr = q + ((tok0 + qrow) * Hk + kh) * kDK + 8 * gq;
-        bf16x8 qf[4];
+        const __bf16* qr = q + ((tok0 + qrow) * Hk + kh) * DK + 8 * gq;
+        bf16x8 qf[KB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qf[kb] = *reinterpret_cast<const bf16x8*>(qr + 32 * kb);
+        for (int kb = 0; kb < KB; ++kb) qf[kb] = *reinterpret_cast<const bf16x8*>(qr + 32 * kb);
         float ss = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = (float)qf[kb][e];
@@ -546,37 +548,49 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
 // s + 3's copy and waits for chunk s + 2's.
 constexpr int kScanThreads = 384;
 constexpr int kWS = 16;          // state columns per workgroup
-constexpr int kSP = kDK + 8;     // row pitch of the S^T copies [column][key]
 constexpr int kRing = 5;         // chunks in the staging ring
-// K ring rows: pitch kKR elements (320 bytes, 20 sixteen-byte chunks, the last 4 unused), and the
-// 16-byte chunk q of row t stored at chunk q ^ ((t >> 2) & 3).  With 64 four-byte banks, both ways
-// the rows are read then touch 16 different chunk positions per 16 lanes: a row fragment (16
-// rows, one chunk each) and a transposed fragment (4 consecutive rows x 4 consecutive chunks).
-constexpr int kKR = 160;
-constexpr int kKDma = kC * kKR * 2 / 1024;   // 1 KiB copy instructions per K slot (20)
-// copy instructions per chunk: K, V (2 KiB), gate block (768 bytes; with L2 1 KiB + 256 bytes)
-constexpr int kDmaOps = kKDma + 2 + 1;
+// Geometry that depends on the key dimension DK.
+// K ring rows: pitch KR elements, and the 16-byte chunk q of row t stored at chunk q ^ ((t >> 2) & 3).
+// DK = 128: 320 bytes (20 sixteen-byte chunks, the last 4 unused); DK = 64: 192 bytes (12 chunks, 8
+// used).  Either way row t starts 16 (mod 64) banks after row t - 1 up to a permutation of
+// {0, 16, 32, 48}, so with 64 four-byte banks both ways the rows are read touch 16 different chunk
+// positions per 16 lanes: a row fragment (16 rows, one chunk each) and a transposed fragment (4
+// consecutive rows x 4 consecutive chunks).
+template <int DK>
+struct Geom {
+    static constexpr int KB = DK / 32;                  // 32-key steps of a product over the keys
+    static constexpr int KR = DK == 128 ? 160 : 96;     // K ring row pitch (elements)
+    static constexpr int SP = DK + 8;                   // row pitch of the S^T copies [column][key]
+    static constexpr int KDma = kC * KR * 2 / 1024;     // 1 KiB copy instructions per K slot (20, 12)
+    static constexpr int DmaOps = KDma + 2 + 1;         // per chunk: K, V (2 KiB), gate block
+    static constexpr int TPH = DK / 32;                 // 16-key state tiles per key half
+    static constexpr int UPH = DK / 64;                 // 32-key blocks per key half
+    static constexpr int LinesQ = kC * DK * 2 / 128;    // 128-byte lines of a chunk's Q (also K) rows
+    static constexpr int RowLines = DK / 64;            // 128-byte lines per Q or K row
+    static_assert(DK == 64 || DK == 128, "key dimension");
+    static_assert(kC * KR * 2 % 1024 == 0, "K slot is a whole number of copy instructions");
+};
 // L2 prefetch: kPfAhead chunks ahead of the step that issues it, every line a workgroup group
 // reads for a chunk (Q and K rows, the N block; per v-head the M block, V rows and gate block) is
 // touched once, so that the chain's M and N loads and the output waves' Q loads (issued one step
 // before use) and the staging copies (two steps) meet L2 rather than HBM.
 constexpr int kPfAhead = 4;
-constexpr int kLinesQ = kC * kDK * 2 / 128;                  // also K's
 constexpr int kLinesN = kNFrags * kFragElems * 2 / 128;
 constexpr int kLinesM = kMFrags * kFragElems * 2 / 128;
 constexpr int kLinesG = kGRows * kC * 4 / 128;
 __host__ __device__ constexpr int kswz(int t) { return (t >> 2) & 3; }
 
+template <int DK>
 struct ScanLds {
-    __bf16 Kr[kRing][kC * kKR];                // K rows [token][key]
+    __bf16 Kr[kRing][kC * Geom<DK>::KR];       // K rows [token][key]
     __bf16 Vr[kRing][kC * kWS];                // V [token][this slice's 16 columns]
     float Gt[kRing][kGRows * kC];              // gate block: G2, 2^G2, 2^(G2_C - G2), (r, rq)
-    __bf16 St[2][2][kWS * kSP];                // S^T at chunk start [buffer][hi, lo]
+    __bf16 St[2][2][kWS * Geom<DK>::SP];       // S^T at chunk start [buffer][hi, lo]
     f32x4 Ut[2][4][64];                        // U [buffer][token tile][lane], the chain's tiles
     f32x4 Yt[2][2][4][64];                     // Y in two parts [buffer][key half][tile][lane]
     uint32_t sink[64];                         // landing row of the L2 prefetches (never read)
 };
-static_assert(sizeof(ScanLds) <= 160 * 1024, "scan LDS exceeds a CU's 160 KiB");
+static_assert(sizeof(ScanLds<128>) <= 160 * 1024, "scan LDS exceeds a CU's 160 KiB");
 
 // index (token or key) that accumulator row m of tile a stands for
 __device__ __forceinline__ int rho(int a, int m) {
@@ -588,9 +602,10 @@ __device__ __forceinline__ int rho(int a, int m) {
 // as in the chain's D fragments.  Each half is a transposed read of row 32 kb + 4 g (+ 16) + c / 4
 // at logical chunk 4 (kt / 2) + c % 4, half kt % 2 of the chunk; `k0` holds the ring slot plus the
 // lane's part of the address (the chunk swizzle of those rows is g).
+template <int KR>
 __device__ __forceinline__ bf16x8 kt_frag(lds_u8* k0, int kt, int kb) {
-    const int off = 2 * (32 * kb * kKR + 32 * (kt >> 1) + 4 * (kt & 1));
-    return cat44(read_tr(k0, off), read_tr(k0, off + 2 * 16 * kKR));
+    const int off = 2 * (32 * kb * KR + 32 * (kt >> 1) + 4 * (kt & 1));
+    return cat44(read_tr(k0, off), read_tr(k0, off + 2 * 16 * KR));
 }
 
 typedef __attribute__((address_space(1))) void glb_void;
@@ -608,11 +623,12 @@ __device__ __forceinline__ void copy_to_lds(const void* src, void* dst) {
     __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)dst, 16, 0, 0);
 }
 
+template <int KB>
 struct OutIn {                     // one chunk's Q fragments for an output wave (registers)
-    bf16x8 q[2][4];                // Q rows 16 a + c of its two tiles, columns 32 kb + 8 g ..
+    bf16x8 q[2][KB];               // Q rows 16 a + c of its two tiles, columns 32 kb + 8 g ..
 };
 
-template <int DV, bool L2>
+template <int DK, int DV, bool L2>
 __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
@@ -622,8 +638,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const __bf16* __restrict__ ws_M, const __bf16* __restrict__ ws_N, float* __restrict__ o,
     float* final_state) {
     constexpr int NS = DV / kWS;  // slices per v-head
+    using GM = Geom<DK>;
+    constexpr int KB = GM::KB, KR = GM::KR, SP = GM::SP, TPH = GM::TPH, UPH = GM::UPH;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    ScanLds& sm = *reinterpret_cast<ScanLds*>(smem_raw);
+    ScanLds<DK>& sm = *reinterpret_cast<ScanLds<DK>*>(smem_raw);
 
     // blockIdx -> (group, member): a group is one (sequence, q/k head); its members are the
     // (v-head, slice) workgroups that read the same q and k.  All members of a group share
@@ -648,7 +666,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     const bool has_slot = state_slot(state_indices, num_slots, n, sslot);
     const float* s_in = has_slot ? initial_state : nullptr;
     float* s_out = has_slot ? final_state : nullptr;
-    const size_t sbase = ((size_t)sslot * Hv + h) * kDK * DV;
+    const size_t sbase = ((size_t)sslot * Hv + h) * DK * DV;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -755,14 +773,14 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
     } else if (wave == 1 || wave == 4) {
         // ------------------------------------------------ state waves -------------------------
         auto state_role = [&](auto hc) {
-            constexpr int hh = decltype(hc)::value;   // key half: state tiles 4 hh .. 4 hh + 3
+            constexpr int hh = decltype(hc)::value;   // key half: state tiles TPH hh .. TPH hh + TPH - 1
             auto state_idx = [&](int t, int r) {
-                return sbase + (size_t)rho(4 * hh + t, 4 * g + r) * DV + c0 + c;
+                return sbase + (size_t)rho(TPH * hh + t, 4 * g + r) * DV + c0 + c;
             };
             if (nchunks == 0) {  // zero-length sequence: the state passes through
                 if (s_out) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                    for (int t = 0; t < TPH; ++t)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             s_out[state_idx(t, r)] = s_in ? s_in[state_idx(t, r)] : 0.f;
@@ -770,21 +788,21 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 return;
             }
             __builtin_amdgcn_s_setprio(2);
-            f32x4 S[4];
+            f32x4 S[TPH];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < TPH; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[t][r] = s_in ? s_in[state_idx(t, r)] : 0.f;
             // lane parts of the LDS addresses (the rest are compile-time offsets)
-            const int l_kf = c * kKR + 8 * (g ^ kswz(c));                 // K row c, logical chunk g
-            const int l_kt = (4 * g + (c >> 2)) * kKR + 8 * ((c & 3) ^ g);
+            const int l_kf = c * KR + 8 * (g ^ kswz(c));                  // K row c, logical chunk g
+            const int l_kt = (4 * g + (c >> 2)) * KR + 8 * ((c & 3) ^ g);
             const int l_v = (4 * g + (c >> 2)) * kWS + 4 * (c & 3);
-            const int l_st = c * kSP + 8 * g;
-            bf16x8 sh[2], sl[2];             // this half of S as hi + lo B fragments
-                                             // (keys 32 (2 hh + u) + 8 g + e)
+            const int l_st = c * SP + 8 * g;
+            bf16x8 sh[UPH], sl[UPH];         // this half of S as hi + lo B fragments
+                                             // (keys 32 (UPH hh + u) + 8 g + e)
             auto split_s = [&]() {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) split8(S[2 * u], S[2 * u + 1], sh[u], sl[u]);
+                for (int u = 0; u < UPH; ++u) split8(S[2 * u], S[2 * u + 1], sh[u], sl[u]);
             };
             // this half's part of Y for chunk ci: -diag(e^G) e^(G_C, ci - 1) K S over its keys,
             // plus V in half 0 (ec = that decay factor)
@@ -795,12 +813,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 f32x4 ks[4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    bf16x8 kf[2];
+                    bf16x8 kf[UPH];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) kf[u] = ld<bf16x8>(kfl, 2 * (16 * a * kKR + 32 * (2 * hh + u)));
+                    for (int u = 0; u < UPH; ++u) kf[u] = ld<bf16x8>(kfl, 2 * (16 * a * KR + 32 * (UPH * hh + u)));
                     ks[a] = zero4();
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
+                    for (int u = 0; u < UPH; ++u) {
                         ks[a] = mma(kf[u], sh[u], ks[a]);
                         ks[a] = mma(kf[u], sl[u], ks[a]);
                     }
@@ -843,10 +861,10 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     split8(ds[2], ds[3], dh[1], dlo[1]);
                     lds_u8* ktl = lds_at(sm.Kr[ps] + l_kt);
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
+                    for (int t = 0; t < TPH; ++t) {
                         bf16x8 kt[2];
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) kt[kb] = kt_frag(ktl, 4 * hh + t, kb);
+                        for (int kb = 0; kb < 2; ++kb) kt[kb] = kt_frag<KR>(ktl, TPH * hh + t, kb);
                         f32x4 acc = S[t] * ec;
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb) {
@@ -861,9 +879,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     split_s();
                     lds_u8* stb = lds_at(sm.St[s & 1][0] + l_st);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        st(stb, 2 * 32 * (2 * hh + u), sh[u]);
-                        st(stb, 2 * (kWS * kSP + 32 * (2 * hh + u)), sl[u]);
+                    for (int u = 0; u < UPH; ++u) {
+                        st(stb, 2 * 32 * (UPH * hh + u), sh[u]);
+                        st(stb, 2 * (kWS * SP + 32 * (UPH * hh + u)), sl[u]);
                     }
                     if (s + 1 < nchunks) make_y(s + 1, sm.Gt[s % kRing][2 * kC - 1]);
                 }
@@ -871,7 +889,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             }
             if (s_out) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < TPH; ++t)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) s_out[state_idx(t, r)] = S[t][r];
             }
@@ -884,9 +902,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         auto run = [&](auto oc) {
             constexpr int ow = decltype(oc)::value;      // 0: tiles {0, 3}; 1: tiles {1, 2}
             constexpr int tiles[2] = {ow, 3 - ow};
-            const int l_kf = c * kKR + 8 * (g ^ kswz(c));                 // K row c, logical chunk g
-            const int l_st = c * kSP + 8 * g;
-            auto fetch_out = [&](OutIn& f, int ci) {
+            const int l_kf = c * KR + 8 * (g ^ kswz(c));                  // K row c, logical chunk g
+            const int l_st = c * SP + 8 * g;
+            auto fetch_out = [&](OutIn<KB>& f, int ci) {
                 const size_t tok0 = tok0_of(ci);
                 const int L = len_of(ci);
 #pragma unroll
@@ -894,12 +912,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     // rows past a partial chunk's end repeat its last row: their outputs are never
                     // stored, and they enter no other row's output
                     const int t = min(16 * tiles[x] + c, L - 1);
-                    const __bf16* qr = q + ((tok0 + t) * Hk + kh) * kDK + 8 * g;
+                    const __bf16* qr = q + ((tok0 + t) * Hk + kh) * DK + 8 * g;
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) f.q[x][kb] = *reinterpret_cast<const bf16x8*>(qr + 32 * kb);
+                    for (int kb = 0; kb < KB; ++kb) f.q[x][kb] = *reinterpret_cast<const bf16x8*>(qr + 32 * kb);
                 }
             };
-            auto step = [&](int s, const OutIn& cur, OutIn& nxt) {
+            auto step = [&](int s, const OutIn<KB>& cur, OutIn<KB>& nxt) {
                 fetch_out(nxt, min(s, nchunks - 1));             // chunk s's Q rows, for the next step
                 const int ci = s - 1;                            // the chunk finished in this step
                 const int slot = ci % kRing;
@@ -916,12 +934,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     eq[x] = gt[kC + 16 * tiles[x] + c];
                     if constexpr (L2) rq[x] = gt[4 * kC + 16 * tiles[x] + c];
                 }
-                bf16x8 sf[2][4], uf[2][2];
+                bf16x8 sf[2][KB], uf[2][2];
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl) {
                     lds_u8* sp = lds_at(sm.St[buf][hl] + l_st);
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) sf[hl][kb] = ld<bf16x8>(sp, 2 * 32 * kb);
+                    for (int kb = 0; kb < KB; ++kb) sf[hl][kb] = ld<bf16x8>(sp, 2 * 32 * kb);
                 }
                 // U^T fragments: lane (g, c) of the chain's tiles 2 kb, 2 kb + 1 holds U at
                 // tokens 32 kb + 4 g + r and 32 kb + 16 + 4 g + r, column c: the P^T row order
@@ -936,18 +954,18 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     const int a = tiles[x];
                     const int t = 16 * a + c;
                     // P^T tiles (b, a) = K Q^T for b <= a: rows t' = 16 b + m, masked to t' <= t
-                    bf16x8 kf[4][4];
+                    bf16x8 kf[4][KB];
 #pragma unroll
                     for (int b = 0; b <= a; ++b)
 #pragma unroll
-                        for (int kb = 0; kb < 4; ++kb) kf[b][kb] = ld<bf16x8>(kfl, 2 * (16 * b * kKR + 32 * kb));
+                        for (int kb = 0; kb < KB; ++kb) kf[b][kb] = ld<bf16x8>(kfl, 2 * (16 * b * KR + 32 * kb));
                     f32x4 pt[4];
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         pt[b] = zero4();
                         if (b > a) continue;
 #pragma unroll
-                        for (int kb = 0; kb < 4; ++kb) pt[b] = mma(kf[b][kb], cur.q[x][kb], pt[b]);
+                        for (int kb = 0; kb < KB; ++kb) pt[b] = mma(kf[b][kb], cur.q[x][kb], pt[b]);
                         const f32x4 gp = ld<f32x4>(gl, 4 * 16 * b);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
@@ -961,7 +979,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     split8(pt[2], pt[3], ph[1], pl[1]);
                     f32x4 qs = zero4(), qs2 = zero4();
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) {
+                    for (int kb = 0; kb < KB; ++kb) {
                         qs = mma(sf[0][kb], cur.q[x][kb], qs);
                         qs2 = mma(sf[1][kb], cur.q[x][kb], qs2);
                     }
@@ -985,7 +1003,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 }
                 lds_barrier();
             };
-            OutIn fa, fb;
+            OutIn<KB> fa, fb;
             fetch_out(fa, 0);
             lds_barrier();  // P
             lds_barrier();  // B0
@@ -1004,22 +1022,23 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         if (nchunks == 0) return;
         // K piece of copy instruction ii: byte 1024 ii + 16 lane of the slot, i.e. row t, physical
         // chunk pc (pc >= 16 is row padding: any in-bounds source will do)
-        int krow[kKDma], kcol[kKDma];
+        constexpr int KDma = GM::KDma;
+        int krow[KDma], kcol[KDma];
 #pragma unroll
-        for (int ii = 0; ii < kKDma; ++ii) {
+        for (int ii = 0; ii < KDma; ++ii) {
             const int ob = 1024 * ii + 16 * lane;
-            const int t = ob / (2 * kKR), pc = (ob % (2 * kKR)) / 16;
+            const int t = ob / (2 * KR), pc = (ob % (2 * KR)) / 16;
             krow[ii] = t;
-            kcol[ii] = 8 * (pc < 16 ? (pc ^ kswz(t)) : 0);
+            kcol[ii] = 8 * (pc < DK / 8 ? (pc ^ kswz(t)) : 0);
         }
         auto dma = [&](int ci) {
             const int slot = ci % kRing;
             const size_t tok0 = tok0_of(ci);
             const int L = len_of(ci);
-            const __bf16* kb = k + (tok0 * Hk + kh) * kDK;
+            const __bf16* kb = k + (tok0 * Hk + kh) * DK;
 #pragma unroll
-            for (int ii = 0; ii < kKDma; ++ii)
-                copy_to_lds(kb + (size_t)min(krow[ii], L - 1) * Hk * kDK + kcol[ii], sm.Kr[slot] + 512 * ii);
+            for (int ii = 0; ii < KDma; ++ii)
+                copy_to_lds(kb + (size_t)min(krow[ii], L - 1) * Hk * DK + kcol[ii], sm.Kr[slot] + 512 * ii);
             const __bf16* vb = v + (tok0 * Hv + h) * DV + c0;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)          // rows 32 jj + lane / 2, columns 8 (lane % 2)
@@ -1045,6 +1064,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         auto prefetch = [&](int cp) {
             const size_t tok0 = tok0_of(cp);
             const int L = len_of(cp);
+            constexpr int kLinesQ = GM::LinesQ, kQRow = GM::RowLines;
             const int total = 2 * kLinesQ + kLinesN + Gq * kPerHead;
 #pragma unroll
             for (int i = 0; i < kPf; ++i) {
@@ -1053,7 +1073,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 if (line < 2 * kLinesQ) {
                     const __bf16* base = line < kLinesQ ? q : k;
                     const int ln = line % kLinesQ;
-                    src = base + ((tok0 + min(ln >> 1, L - 1)) * Hk + kh) * kDK + 64 * (ln & 1);
+                    src = base + ((tok0 + min(ln / kQRow, L - 1)) * Hk + kh) * DK + 64 * (ln % kQRow);
                 } else if (line < 2 * kLinesQ + kLinesN) {
                     src = ws_N + ((size_t)(slot0 + cp) * Hk + kh) * kNFrags * kFragElems +
                           64 * (line - 2 * kLinesQ);
@@ -1084,11 +1104,11 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         for (int s = 0; s <= nchunks; ++s) {
             // chunk s + 3 goes into the slot chunk s - 2 left; chunk s + 2 must have landed before
             // the step ends.  Every chunk copy from chunk 2 on is followed by one prefetch, so the
-            // copies of chunk s + 2 are older than the newest kDmaOps (+1) + 2 kPf instructions.
+            // copies of chunk s + 2 are older than the newest DmaOps (+1) + 2 kPf instructions.
             if (s + 3 < nchunks) {
                 dma(s + 3);
                 prefetch(min(s + kPfAhead, nchunks - 1));
-                wait_vmcnt<kDmaOps + (L2 ? 1 : 0) + 2 * kPf>();
+                wait_vmcnt<GM::DmaOps + (L2 ? 1 : 0) + 2 * kPf>();
             } else {
                 wait_vmcnt<0>();
             }
@@ -1121,7 +1141,7 @@ Layout layout(int B, int T, int Hk, int Hv, int N) {
     return l;
 }
 
-template <int DV, typename TG, bool L2>
+template <int DK, int DV, typename TG, bool L2>
 hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
     const Layout lay = layout(a.B, a.T, a.Hk, a.Hv, a.N);
     char* ws = static_cast<char*>(a.workspace);
@@ -1141,7 +1161,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((stages & kStagePrepare) && slots > 0) {
-        hipLaunchKernelGGL((chunk_solve_kernel<TG, L2>), dim3((unsigned)slots, (unsigned)a.Hk),
+        hipLaunchKernelGGL((chunk_solve_kernel<DK, TG, L2>), dim3((unsigned)slots, (unsigned)a.Hk),
                            dim3(kThreads), 0, a.stream, static_cast<const __bf16*>(a.q),
                            static_cast<const __bf16*>(a.k),
                            static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta), a.A_log,
@@ -1150,8 +1170,8 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (!(stages & kStageScan)) return hipSuccess;
-    const auto kern = chunk_scan_kernel<DV, L2>;
-    const size_t bytes = sizeof(ScanLds);
+    const auto kern = chunk_scan_kernel<DK, DV, L2>;
+    const size_t bytes = sizeof(ScanLds<DK>);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)) != hipSuccess)
         return e;
@@ -1170,7 +1190,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
 }  // namespace
 
 bool chunk_mfma_supported(int dk, int dv, gdn_dtype qkv_dtype) {
-    return qkv_dtype == GDN_BF16 && dk == kDK && (dv == 64 || dv == 128);
+    return qkv_dtype == GDN_BF16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
 }
 
 size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N) {
@@ -1179,11 +1199,17 @@ size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, i
     return layout(B, T, Hk, Hv, N).total;
 }
 
+template <int DK, bool L2>
+hipError_t launch_dk(const ChunkArgs& a, unsigned stages) {
+    const bool g_bf16 = a.gate_dtype == GDN_BF16;
+    if (a.dv == 128)
+        return g_bf16 ? launch_dv<DK, 128, bf16_t, L2>(a, stages) : launch_dv<DK, 128, float, L2>(a, stages);
+    return g_bf16 ? launch_dv<DK, 64, bf16_t, L2>(a, stages) : launch_dv<DK, 64, float, L2>(a, stages);
+}
+
 template <bool L2>
 hipError_t launch_l2(const ChunkArgs& a, unsigned stages) {
-    const bool g_bf16 = a.gate_dtype == GDN_BF16;
-    if (a.dv == 128) return g_bf16 ? launch_dv<128, bf16_t, L2>(a, stages) : launch_dv<128, float, L2>(a, stages);
-    return g_bf16 ? launch_dv<64, bf16_t, L2>(a, stages) : launch_dv<64, float, L2>(a, stages);
+    return a.dk == 128 ? launch_dk<128, L2>(a, stages) : launch_dk<64, L2>(a, stages);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, unsigned stages) {

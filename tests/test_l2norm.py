@@ -58,14 +58,16 @@ def run_ex(x, **kw):
     return o, fs
 
 
-@pytest.mark.parametrize("dtype,dv", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 128)])
-def test_l2norm_prefill_ragged(dtype, dv):
-    wl = with_dims(WL["prefill"], Hk=2, Hv=4, dv=dv, dtype=dtype, gate_dtype=dtype, init_state=True)
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.bfloat16, 128, 128), (torch.bfloat16, 128, 64),
+                                         (torch.bfloat16, 64, 64), (torch.bfloat16, 64, 128),
+                                         (torch.float32, 128, 128)])
+def test_l2norm_prefill_ragged(dtype, dk, dv):
+    wl = with_dims(WL["prefill"], Hk=2, Hv=4, dk=dk, dv=dv, dtype=dtype, gate_dtype=dtype, init_state=True)
     x = unnormalise(synth.make(wl, T=300, seed=61), 62)
     o, fs = run_ex(x, qk_l2norm=True)
     o_ref, s_ref = oracle_l2(x)
-    assert_close(f"l2norm prefill {dtype} dv={dv} o", o, o_ref, tol_for(dtype))
-    assert_close(f"l2norm prefill {dtype} dv={dv} final_state", fs, s_ref, tol_for(dtype))
+    assert_close(f"l2norm prefill {dtype} dk={dk} dv={dv} o", o, o_ref, tol_for(dtype))
+    assert_close(f"l2norm prefill {dtype} dk={dk} dv={dv} final_state", fs, s_ref, tol_for(dtype))
 
 
 def test_l2norm_with_gating_pool_and_packed_sequences():

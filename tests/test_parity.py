@@ -57,6 +57,18 @@ def test_head_sizes(dk, dv, dtype):
     check_chunk(synth.make(wl, T=150, seed=7), f"dk={dk} dv={dv} {dtype}")
 
 
+@pytest.mark.parametrize("dv", [64, 128])
+def test_dk64_bf16_matrix_core_path(dv):
+    """Head size 64 on the bf16 matrix-core path: the 4096-token prefill with the Qwen3-Next head
+    counts, then packed ragged sequences with a carried state and a weak decay (512 + 4 chunks)."""
+    wl = with_dims(WL["prefill"], dk=64, dv=dv)
+    check_chunk(synth.make(wl, seed=140 + dv), f"dk=64 dv={dv} T=4096")
+    wv = with_dims(WL["varlen"], dk=64, dv=dv, Hk=4, Hv=8, n_seqs=4)
+    A_log = np.log(np.linspace(0.1, 0.9, wv.Hv)).astype(np.float32)
+    x = synth.make(wv, lengths=np.array([2000, 0, 65, 63]), seed=150 + dv, A_log=A_log)
+    check_chunk(x, f"dk=64 dv={dv} packed weak decay")
+
+
 @pytest.mark.parametrize("G", [1, 3, 4, 8])
 def test_head_groupings(G):
     """G v-heads per q/k head other than the Qwen3-Next layout's 2 (each q/k head shared by G
