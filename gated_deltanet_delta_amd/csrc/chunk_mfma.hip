@@ -1,4 +1,4 @@
-// chunk_mfma.hip -- chunked gated delta rule on gfx950 bf16 matrix cores (dk = 64 or 128).
+// chunk_mfma.hip -- chunked gated delta rule on gfx950 matrix cores (bf16 inputs, dk = 64 or 128).
 //
 // Notation (one chunk of C = 64 tokens of one sequence and v-head, start state S (dk x dv), G_t the
 // running sum of g inside the chunk, Gam_tj = e^(G_t - G_j) for j <= t):
@@ -18,17 +18,22 @@
 //                       a serial dependence inside a chunk.  Cumsum, A on the matrix cores, T by a
 //                       blocked forward substitution (16 x 16 diagonal blocks by substitution,
 //                       off-diagonal blocks by fp32 matrix-core products), M = T diag(beta) as
-//                       hi + lo bf16 into the workspace (12 KiB per chunk and v-head), the chunk's
-//                       decay factors, and N = K K_prev^T (16 KiB per chunk and q/k head).
+//                       fp16 into the workspace (6 KiB per chunk and v-head), the chunk's decay
+//                       factors, and N = K K_prev^T (8 KiB per chunk and q/k head).
 //   chunk_scan_kernel   one workgroup per (sequence, v-head, 16 columns of S), walking the chunks
 //                       in order with chain, state and output waves (see there).  With M, the
 //                       chunk's deltas are U = Ut - W S = M (V - diag(e^G) K S), so W and Ut are
 //                       never formed; everything else comes from q, k, v on the fly.
 //
-// Precision: q, k, v enter the matrix cores as exact bf16 values.  Quantities that feed the output
-// with full weight (S, X, U, D, P, M, N) enter as two bf16 terms hi + lo (hi = bf16(x),
-// lo = bf16(x - hi)), so their products carry ~16 significant bits.  Accumulation is fp32
-// everywhere; decay factors are applied on the fp32 side.
+// Precision: q, k, v enter the matrix cores as exact bf16 values.  S, U, P and the state update's D
+// enter as two bf16 terms hi + lo (hi = bf16(x), lo = bf16(x - hi)), so their products carry ~16
+// significant bits.  The chunk-to-chunk chain (N D and M X, see the scan kernel) runs on fp16
+// operands (11 significant bits, 8x finer than one bf16 term): a single product per tile instead of
+// three.  Their entries are bounded by the inputs' scale: |M| and |N| by the keys' norms (the
+// normalised keys' N is stored for the L2 option), |X| and |D| by |v| and |S|; fp16 holds them
+// while those stay below ~6e4 and keeps full relative precision above ~6e-5 (smaller entries keep
+// an absolute precision of 6e-8).  Accumulation is fp32 everywhere; decay factors are applied on
+// the fp32 side.
 //
 // Lane layouts used (wave64, checked on the device):
 //   v_mfma_f32_16x16x32_bf16: lane l = 16 g + c holds A[c][8g..8g+7] and B[8g..8g+7][c]; the 16x16
@@ -67,8 +72,6 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, const f32x4& c) {
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-__device__ __forceinline__ __bf16 hi_of(float x) { return (__bf16)x; }
-__device__ __forceinline__ __bf16 lo_of(float x, __bf16 hi) { return (__bf16)(x - (float)hi); }
 
 __device__ __forceinline__ bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -158,7 +161,7 @@ __device__ __forceinline__ bf16x4 read_tr(lds_u8* b, int off) {
 // ------------------------------------------------------------------------------------------------
 // Fragment layouts shared by the solve kernel (writer) and the scan kernel (reader).
 //
-// A "fragment" is the A operand of one v_mfma_f32_16x16x32_bf16 as the 64 lanes hold it: lane
+// A "fragment" is the A operand of one v_mfma_f32_16x16x32 (bf16 or fp16) as the 64 lanes hold it: lane
 // (g, c) has eight bf16 values, 16 bytes; a fragment is stored as 64 x 16 = 1 KiB with lane l at
 // byte 16 l, so that one wave loads it with one fully coalesced instruction.
 //
@@ -168,14 +171,22 @@ __device__ __forceinline__ bf16x4 read_tr(lds_u8* b, int off) {
 // column 32 j + colperm(g, e) of its row, colperm(g, e) = 4 g + (e & 3) + 16 (e >> 2).
 //
 //   M (per chunk and v-head): the nonzero pairs (row tile a, k-step j) of the lower-triangular
-//     M = T diag(beta), in the order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), each as hi then lo:
-//     12 fragments.  Lane (g, c) of pair (a, j) holds row 16 a + c.
+//     M = T diag(beta), in the order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), fp16: 6 fragments.  Lane
+//     (g, c) of pair (a, j) holds row 16 a + c.
 //   N (per chunk and q/k head, chunks with a predecessor in the same sequence only): N = K K_p^T,
 //     rows the chunk's tokens, columns the previous chunk's, all pairs (a, j) in the order
-//     (0,0) (0,1) (1,0) ... (3,1), each as hi then lo: 16 fragments.
-constexpr int kFragElems = 512;  // bf16 per fragment
-constexpr int kMFrags = 12;
-constexpr int kNFrags = 16;
+//     (0,0) (0,1) (1,0) ... (3,1), fp16: 8 fragments.
+constexpr int kFragElems = 512;  // 16-bit values per fragment
+constexpr int kMFrags = 6;
+constexpr int kNFrags = 8;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 pack_f16(const f32x4& a, const f32x4& b) {
+    return __builtin_convertvector((f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}, f16x8);
+}
+__device__ __forceinline__ f32x4 mma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 __host__ __device__ constexpr int m_pair_row(int p) { return p < 2 ? p : (p < 4 ? 2 : 3); }
 __host__ __device__ constexpr int m_pair_step(int p) { return (p == 3 || p == 5) ? 1 : 0; }
 __device__ __forceinline__ int colperm(int g, int e) { return 4 * g + (e & 3) + 16 * (e >> 2); }
@@ -294,43 +305,28 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     const int xa = wave == 3 ? 3 : wave + 1, xb = wave == 3 ? 0 : wave;
     const int ya = wave == 1 ? 2 : 3, yb = wave == 1 ? 0 : 1;
 
-    // N: wave w forms the tiles (b, w) of N^T = K_p K^T, whose lane (g, c) element r is
-    // N[16 w + c][16 b + 4 g + r]; tiles 2j and 2j + 1 together are exactly fragment (w, j)
-    if (has_prev) {
-        f32x4 nt[4];
+    // L2: r_t = 1 / sqrt(|k_t|^2 + eps) for K rows held as matrix-core fragments (lane (g, c) holds 32
+    // of row 16 t + c's keys; the sum over g leaves every lane with its row's r)
+    auto rnorm = [&](const bf16x8* kf) {
+        float ss = 0.f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) nt[b] = kkt(kp[b], k0);
-        __bf16* nb = ws_N + ((size_t)slot * Hk + kh) * kNFrags * kFragElems + 8 * lane;
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            bf16x8 hv, lv;
-            split8(nt[2 * j], nt[2 * j + 1], hv, lv);
-            *reinterpret_cast<bf16x8*>(nb + (2 * (2 * wave + j)) * kFragElems) = hv;
-            *reinterpret_cast<bf16x8*>(nb + (2 * (2 * wave + j) + 1) * kFragElems) = lv;
-        }
-    }
-
-
+            for (int e = 0; e < 8; ++e) {
+                const float x = (float)kf[kb][e];
+                ss += x * x;
+            }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        return 1.f / sqrtf(ss + kL2Eps);
+    };
+    float r0 = 1.f;
     if constexpr (L2) {
-        // r_t = 1 / sqrt(|k_t|^2 + eps) for the rows of the wave's K tiles (lane (g, c) holds 32 of
-        // row 16 tt + c's keys; the sum over g leaves every lane with its column's r), then
         // K K^T -> diag(r) K K^T diag(r) tile by tile: a tile's column factor is the lane's own, its
         // row factors come from lanes 4 g + r.  Each wave writes r of its own tile `wave` to the gate
         // blocks of every v-head.
-        auto rnorm = [&](const bf16x8* kf) {
-            float ss = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = (float)kf[kb][e];
-                    ss += x * x;
-                }
-            ss += __shfl_xor(ss, 16);
-            ss += __shfl_xor(ss, 32);
-            return 1.f / sqrtf(ss + kL2Eps);
-        };
-        const float r0 = rnorm(k0), r1 = rnorm(k1), r2 = (wave & 1) ? rnorm(k2) : 1.f;
+        r0 = rnorm(k0);
+        const float r1 = rnorm(k1), r2 = (wave & 1) ? rnorm(k2) : 1.f;
         auto scale_tile = [&](f32x4& acc, float rrow, float rcol) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] *= __shfl(rrow, 4 * gq + r) * rcol;
@@ -343,6 +339,28 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         if (gq == 0)
             for (int qh = 0; qh < Gq; ++qh)
                 ws_G[((size_t)slot * Hv + kh * Gq + qh) * kGRows * kC + 3 * kC + 16 * wave + c] = r0;
+    }
+
+    // N: wave w forms the tiles (b, w) of N^T = K_p K^T, whose lane (g, c) element r is
+    // N[16 w + c][16 b + 4 g + r]; tiles 2j and 2j + 1 together are exactly fragment (w, j), stored as
+    // single fp16 values.  With L2 it is the normalised keys' N: each entry times r of its row (the
+    // lane's own r0) and r_p of its column (previous chunk's row 16 b + 4 g + r), so that its entries
+    // stay within |N| <= 1 whatever the raw keys' scale.
+    if (has_prev) {
+        f32x4 nt[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            nt[b] = kkt(kp[b], k0);
+            if constexpr (L2) {
+                const float rp = rnorm(kp[b]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) nt[b][r] *= r0 * __shfl(rp, 4 * gq + r);
+            }
+        }
+        __bf16* nb = ws_N + ((size_t)slot * Hk + kh) * kNFrags * kFragElems + 8 * lane;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<f16x8*>(nb + (2 * wave + j) * kFragElems) = pack_f16(nt[2 * j], nt[2 * j + 1]);
     }
     // the gates of the first kPre v-heads are loaded together with K (one memory round trip)
     constexpr int kPre = 4;
@@ -457,18 +475,15 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
             if (e >= 6 * 64) break;
             const int p = e >> 6, ln = e & 63, lg = ln >> 4;
             const int t = 16 * m_pair_row(p) + (ln & 15), j0 = 32 * m_pair_step(p);
-            bf16x8 hv, lv;
+            f16x8 hv;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int col = j0 + colperm(lg, j);
                 const int ba = t >> 4, bb = col >> 4;
                 const float tv = bb <= ba ? sT[blk(ba, bb)][(t & 15) * kBP + (col & 15)] : 0.f;
-                const float x = tv * sB[col];
-                hv[j] = hi_of(x);
-                lv[j] = lo_of(x, hv[j]);
+                hv[j] = (_Float16)(tv * sB[col]);
             }
-            *reinterpret_cast<bf16x8*>(Mb + (2 * p) * kFragElems + 8 * ln) = hv;
-            *reinterpret_cast<bf16x8*>(Mb + (2 * p + 1) * kFragElems + 8 * ln) = lv;
+            *reinterpret_cast<f16x8*>(Mb + p * kFragElems + 8 * ln) = hv;
         }
         lds_barrier();                 // sT and sB are rewritten for the next v-head
     }
@@ -512,8 +527,9 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
 //
 //   chain wave (0)   per chunk: N_s D_{s-1}, X_s = Y_s - diag(e^G) N_s D_{s-1}, U_s = M_s X_s and
 //                    D_s, with Y_s = V_s - diag(e^G) e^(G_C,s-1) K_s S_{s-2} from the state waves.
-//                    64 x 16 quantities, four 16 x 16 fp32 accumulator tiles each; N and M from
-//                    the solve kernel, loaded into registers a chunk ahead.
+//                    64 x 16 quantities, four 16 x 16 fp32 accumulator tiles each, fed to fp16
+//                    products; N and M (fp16) from the solve kernel, loaded into registers two
+//                    chunks ahead (two buffers).
 //   state waves (1, 4)  one per half of the keys (64 keys x 16 columns, four tiles): one chunk
 //                    behind the chain, S <- e^(G_C) S + K^T D from the chain's U; then the half's
 //                    part of Y for the next chunk (half 0 adds V), and S^T (hi + lo) in LDS for
@@ -522,7 +538,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
 //                    O^T = S^T Q^T diag(e^G) + U^T P^T, P^T tiles = K Q^T masked and decayed in
 //                    registers, Q from memory a chunk ahead.
 //   staging wave (5) copies each chunk's K rows, V columns and gate block straight from memory into
-//                    a five-chunk LDS ring (global_load_lds), three chunks ahead of the chain.
+//                    a five-chunk LDS ring (global_load_lds), three chunks ahead of the chain; for a
+//                    full chunk every lane's source is a fixed offset from one uniform base.
 //
 // L2 (q and k normalised to unit length, r = 1 / |k|, rq = 1 / |q| per token, from the solve's gate
 // block): the kernel keeps the exact bf16 K and Q and applies the scales on the fp32 side.  The
@@ -679,25 +696,34 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         // ------------------------------------------------ chain wave --------------------------
         if (nchunks == 0) return;
         __builtin_amdgcn_s_setprio(1);
-        bf16x8 mf[kMFrags];              // M_s fragments, refilled with M_{s+1}'s once used
-        bf16x8 nf[kNFrags];              // N_s fragments, likewise
-        auto fetch_m = [&](int ci) {
+        // M and N fragments of two chunks in flight: buffer ci % 2 holds chunk ci's, refilled with
+        // chunk ci + 2's as soon as the last product using them has issued
+        f16x8 mf[2][kMFrags];
+        f16x8 nf[2][kNFrags];
+        auto fetch_m = [&](int ci, auto pc) {
+            constexpr int par = decltype(pc)::value;
             const __bf16* b = ws_M + ((size_t)(slot0 + ci) * Hv + h) * kMFrags * kFragElems + 8 * lane;
 #pragma unroll
-            for (int f = 0; f < kMFrags; ++f) mf[f] = *reinterpret_cast<const bf16x8*>(b + f * kFragElems);
+            for (int f = 0; f < kMFrags; ++f) mf[par][f] = *reinterpret_cast<const f16x8*>(b + f * kFragElems);
         };
-        auto fetch_n = [&](int ci) {
+        auto fetch_n = [&](int ci, auto pc) {
+            constexpr int par = decltype(pc)::value;
             const __bf16* b = ws_N + ((size_t)(slot0 + ci) * Hk + kh) * kNFrags * kFragElems + 8 * lane;
 #pragma unroll
-            for (int f = 0; f < kNFrags; ++f) nf[f] = *reinterpret_cast<const bf16x8*>(b + f * kFragElems);
+            for (int f = 0; f < kNFrags; ++f) nf[par][f] = *reinterpret_cast<const f16x8*>(b + f * kFragElems);
         };
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
         f32x4 u[4];                      // U of the previous chunk
-        fetch_m(0);
-        if (nchunks > 1) fetch_n(1);
+        fetch_m(0, P0{});
+        fetch_m(min(1, nchunks - 1), P1{});
+        fetch_n(min(1, nchunks - 1), P1{});
+        fetch_n(min(2, nchunks - 1), P0{});
         lds_barrier();  // P: chunks 0 and 1 staged
         lds_barrier();  // B0: Y_0 ready
-        auto step = [&](int s, auto first) {
+        auto step = [&](int s, auto first, auto pc) {
             constexpr bool kFirst = decltype(first)::value;
+            constexpr int par = decltype(pc)::value;
             const float* gt = sm.Gt[s % kRing];
             lds_u8* yl = lds_at(&sm.Yt[s & 1][0][0][lane]);
             lds_u8* gl = lds_at(gt + kC + 4 * g);                    // 2^G2 at rows 16 a + 4 g + r
@@ -706,69 +732,62 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             for (int a = 0; a < 4; ++a) {
                 y[a] = ld<f32x4>(yl, 16 * 64 * a) + ld<f32x4>(yl, 16 * 64 * (4 + a));
                 eg[a] = ld<f32x4>(gl, 4 * 16 * a);
-                if constexpr (L2) {
-                    rk[a] = ld<f32x4>(gl, 4 * 16 * a + 4 * 2 * kC);                     // r_s
-                    eg[a] *= rk[a];
-                }
+                if constexpr (L2) rk[a] = ld<f32x4>(gl, 4 * 16 * a + 4 * 2 * kC);          // r_s
             }
             f32x4 x[4];
             if constexpr (kFirst) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a) x[a] = y[a];
             } else {
-                // D_{s-1} = diag(e^(G_C - G)) U_{s-1} as hi + lo B fragments
+                // D_{s-1} = diag(e^(G_C - G)) U_{s-1} as fp16 B fragments
                 lds_u8* dl_ = lds_at(sm.Gt[(s - 1) % kRing] + 2 * kC + 4 * g);
                 f32x4 ds[4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) ds[a] = u[a] * ld<f32x4>(dl_, 4 * 16 * a);
-                bf16x8 dh[2], dlo[2];
-                split8(ds[0], ds[1], dh[0], dlo[0]);
-                split8(ds[2], ds[3], dh[1], dlo[1]);
+                const f16x8 d16[2] = {pack_f16(ds[0], ds[1]), pack_f16(ds[2], ds[3])};
                 // N_s D_{s-1}
                 f32x4 nd[4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     nd[a] = zero4();
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        nd[a] = mma(nf[2 * (2 * a + j)], dh[j], nd[a]);
-                        nd[a] = mma(nf[2 * (2 * a + j)], dlo[j], nd[a]);
-                        nd[a] = mma(nf[2 * (2 * a + j) + 1], dh[j], nd[a]);
-                    }
+                    for (int j = 0; j < 2; ++j) nd[a] = mma16(nf[par][2 * a + j], d16[j], nd[a]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                fetch_n(min(s + 1, nchunks - 1));   // unconditional: see fetch_m
+                fetch_n(min(s + 2, nchunks - 1), pc);   // unconditional: see fetch_m
 #pragma unroll
                 for (int a = 0; a < 4; ++a) x[a] = y[a] - eg[a] * nd[a];
             }
-            bf16x8 xh[2], xl[2];
-            split8(x[0], x[1], xh[0], xl[0]);
-            split8(x[2], x[3], xh[1], xl[1]);
+            const f16x8 x16[2] = {pack_f16(x[0], x[1]), pack_f16(x[2], x[3])};
             // U = M X (M lower triangular: pairs (a, j) with 2 j <= a)
 #pragma unroll
             for (int a = 0; a < 4; ++a) u[a] = zero4();
 #pragma unroll
             for (int p = 0; p < 6; ++p) {
                 const int a = m_pair_row(p), j = m_pair_step(p);
-                u[a] = mma(mf[2 * p], xh[j], u[a]);
-                u[a] = mma(mf[2 * p], xl[j], u[a]);
-                u[a] = mma(mf[2 * p + 1], xh[j], u[a]);
+                u[a] = mma16(mf[par][p], x16[j], u[a]);
             }
-            if constexpr (L2) {
+
+            // the other roles get diag(r) U with L2 (the raw keys then act as normalised ones)
+            lds_u8* ul = lds_at(&sm.Ut[s & 1][0][lane]);
 #pragma unroll
-                for (int a = 0; a < 4; ++a) u[a] *= rk[a];         // diag(r) U
+            for (int a = 0; a < 4; ++a) {
+                if constexpr (L2) st(ul, 16 * 64 * a, u[a] * rk[a]);
+                else st(ul, 16 * 64 * a, u[a]);
             }
             __builtin_amdgcn_sched_barrier(0);
             // unconditional (the last chunk refetches itself): a conditional fetch makes the
             // compiler's wait before the next use also wait for every load issued after it
-            fetch_m(min(s + 1, nchunks - 1));
-            lds_u8* ul = lds_at(&sm.Ut[s & 1][0][lane]);
-#pragma unroll
-            for (int a = 0; a < 4; ++a) st(ul, 16 * 64 * a, u[a]);
+            fetch_m(min(s + 2, nchunks - 1), pc);
             lds_barrier();
         };
-        step(0, std::true_type{});
-        for (int s = 1; s < nchunks; ++s) step(s, std::false_type{});
+        step(0, std::true_type{}, P0{});
+        int s = 1;
+        for (; s + 1 < nchunks; s += 2) {
+            step(s, std::false_type{}, P1{});
+            step(s + 1, std::false_type{}, P0{});
+        }
+        if (s < nchunks) step(s, std::false_type{}, P1{});
         lds_barrier();  // the other roles' last step
     } else if (wave == 1 || wave == 4) {
         // ------------------------------------------------ state waves -------------------------
@@ -1031,19 +1050,34 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             krow[ii] = t;
             kcol[ii] = 8 * (pc < DK / 8 ? (pc ^ kswz(t)) : 0);
         }
+        // byte offsets of each lane's pieces inside a full chunk (the same for every chunk)
+        uint32_t koff[KDma], voff[2];
+#pragma unroll
+        for (int ii = 0; ii < KDma; ++ii) koff[ii] = 2u * ((uint32_t)krow[ii] * Hk * DK + kcol[ii]);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) voff[jj] = 2u * ((uint32_t)(32 * jj + (lane >> 1)) * Hv * DV + 8 * (lane & 1));
         auto dma = [&](int ci) {
             const int slot = ci % kRing;
             const size_t tok0 = tok0_of(ci);
             const int L = len_of(ci);
             const __bf16* kb = k + (tok0 * Hk + kh) * DK;
-#pragma unroll
-            for (int ii = 0; ii < KDma; ++ii)
-                copy_to_lds(kb + (size_t)min(krow[ii], L - 1) * Hk * DK + kcol[ii], sm.Kr[slot] + 512 * ii);
             const __bf16* vb = v + (tok0 * Hv + h) * DV + c0;
+            if (L == kC) {      // full chunk: uniform base plus the lane's fixed offset
+                const char* kbc = reinterpret_cast<const char*>(kb);
+                const char* vbc = reinterpret_cast<const char*>(vb);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)          // rows 32 jj + lane / 2, columns 8 (lane % 2)
-                copy_to_lds(vb + (size_t)min(32 * jj + (lane >> 1), L - 1) * Hv * DV + 8 * (lane & 1),
-                            sm.Vr[slot] + 512 * jj);
+                for (int ii = 0; ii < KDma; ++ii) copy_to_lds(kbc + koff[ii], sm.Kr[slot] + 512 * ii);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) copy_to_lds(vbc + voff[jj], sm.Vr[slot] + 512 * jj);
+            } else {
+#pragma unroll
+                for (int ii = 0; ii < KDma; ++ii)
+                    copy_to_lds(kb + (size_t)min(krow[ii], L - 1) * Hk * DK + kcol[ii], sm.Kr[slot] + 512 * ii);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)          // rows 32 jj + lane / 2, columns 8 (lane % 2)
+                    copy_to_lds(vb + (size_t)min(32 * jj + (lane >> 1), L - 1) * Hv * DV + 8 * (lane & 1),
+                                sm.Vr[slot] + 512 * jj);
+            }
             const float* gb = ws_G + ((size_t)(slot0 + ci) * Hv + h) * kGRows * kC;
             if constexpr (L2) {
                 copy_to_lds(gb + 4 * lane, sm.Gt[slot]);                  // rows 0-3
@@ -1061,11 +1095,56 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         constexpr int kLinesV = kC * kRowLines;
         constexpr int kPerHead = kLinesM + kLinesV + kLinesG;
         constexpr int kPf = DV == 64 ? 3 : 2;                  // covers Gq = 1, the widest share
+        constexpr int kLinesQ = GM::LinesQ, kQRow = GM::RowLines;
+        // per lane and prefetch instruction: the line's address in chunk 0 and its stride per chunk
+        const char* pf0[kPf];
+        uint32_t pfstride[kPf];
+        {
+            const int total = 2 * kLinesQ + kLinesN + Gq * kPerHead;
+            const size_t tok0 = tok0_of(0);
+#pragma unroll
+            for (int i = 0; i < kPf; ++i) {
+                const int line = min(member + MB * (lane + 64 * i), total - 1);
+                const void* src;
+                uint32_t stride;
+                if (line < 2 * kLinesQ) {
+                    const __bf16* base = line < kLinesQ ? q : k;
+                    const int ln = line % kLinesQ;
+                    src = base + ((tok0 + ln / kQRow) * Hk + kh) * DK + 64 * (ln % kQRow);
+                    stride = 2u * kC * Hk * DK;
+                } else if (line < 2 * kLinesQ + kLinesN) {
+                    src = ws_N + ((size_t)slot0 * Hk + kh) * kNFrags * kFragElems + 64 * (line - 2 * kLinesQ);
+                    stride = 2u * Hk * kNFrags * kFragElems;
+                } else {
+                    const int j = line - 2 * kLinesQ - kLinesN;
+                    const int hv = kh * Gq + j / kPerHead, r = j % kPerHead;
+                    if (r < kLinesM) {
+                        src = ws_M + ((size_t)slot0 * Hv + hv) * kMFrags * kFragElems + 64 * r;
+                        stride = 2u * Hv * kMFrags * kFragElems;
+                    } else if (r < kLinesM + kLinesV) {
+                        const int rv = r - kLinesM;
+                        src = v + ((tok0 + rv / kRowLines) * Hv + hv) * DV + 64 * (rv % kRowLines);
+                        stride = 2u * kC * Hv * DV;
+                    } else {
+                        src = ws_G + ((size_t)slot0 * Hv + hv) * kGRows * kC + 32 * (r - kLinesM - kLinesV);
+                        stride = 4u * Hv * kGRows * kC;
+                    }
+                }
+                pf0[i] = static_cast<const char*>(src);
+                pfstride[i] = stride;
+            }
+        }
         auto prefetch = [&](int cp) {
             const size_t tok0 = tok0_of(cp);
             const int L = len_of(cp);
-            constexpr int kLinesQ = GM::LinesQ, kQRow = GM::RowLines;
             const int total = 2 * kLinesQ + kLinesN + Gq * kPerHead;
+            if (L == kC) {     // full chunk: no clamping of rows
+#pragma unroll
+                for (int i = 0; i < kPf; ++i)
+                    __builtin_amdgcn_global_load_lds((glb_void*)(pf0[i] + (size_t)cp * pfstride[i]), (lds_void*)sm.sink,
+                                                     4, 0, 0);
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < kPf; ++i) {
                 const int line = min(member + MB * (lane + 64 * i), total - 1);

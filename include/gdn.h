@@ -130,7 +130,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
  * device is looked up on the first call there (the stream must belong to the calling thread's current
  * device, else GDN_ERROR_INVALID_VALUE).
  *   - GDN_ERROR_WORKSPACE when gdn_chunk_fwd_workspace_size(...) for these sizes exceeds
- *     GDN_NOALLOC_SCRATCH_BYTES (e.g. more than about 6000 tokens at 16 q/k and 32 v heads of 128).
+ *     GDN_NOALLOC_SCRATCH_BYTES (e.g. more than about 11,600 tokens at 16 q/k and 32 v heads of 128).
  *   - Every call on one GPU shares that GPU's array, so two calls that overlap in time on one GPU
  *     (on different streams, or from different threads) race and give undefined results; calls
  *     ordered on one stream are safe.  The array keeps the last call's contents; no call depends on

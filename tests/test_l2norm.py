@@ -70,6 +70,20 @@ def test_l2norm_prefill_ragged(dtype, dk, dv):
     assert_close(f"l2norm prefill {dtype} dk={dk} dv={dv} final_state", fs, s_ref, tol_for(dtype))
 
 
+@pytest.mark.parametrize("scale", [1e-3, 3e3])
+def test_l2norm_keys_far_from_unit_length(scale):
+    """Raw q and k with norms around 1e-3 and 3e3 (|k|^2 up to ~1e7): with the option the rule sees
+    unit vectors, so the result must match the oracle at the usual bound whatever the raw scale."""
+    wl = with_dims(WL["prefill"], Hk=2, Hv=4, init_state=True)
+    x = synth.make(wl, T=200, seed=64)
+    for key in ("q", "k"):
+        x[key] = (x[key].float() * scale).to(x[key].dtype)
+    o, fs = run_ex(x, qk_l2norm=True)
+    o_ref, s_ref = oracle_l2(x)
+    assert_close(f"l2norm |k| ~ {scale:g} o", o, o_ref, tol_for(wl.dtype))
+    assert_close(f"l2norm |k| ~ {scale:g} final_state", fs, s_ref, tol_for(wl.dtype))
+
+
 def test_l2norm_with_gating_pool_and_packed_sequences():
     """Every option at once: packed ragged sequences (an empty one, one of a single token), raw gate
     projections, a state pool with a padding row, and the normalisation."""

@@ -52,7 +52,7 @@ def test_noalloc_equals_workspace_call_on_two_calls():
 def test_noalloc_refuses_more_than_its_scratch():
     lib = _lib.load()
     wl = WL["prefill"]
-    T = 8192
+    T = 16384
     need = workspace_size(1, T, wl.Hk, wl.Hv, wl.dk, wl.dv, 1, wl.dtype)
     assert need > int(lib.gdn_chunk_fwd_noalloc_max_bytes())
     x = synth.make(wl, T=T, seed=403)
