@@ -567,18 +567,25 @@ constexpr int kScanThreads = 384;
 constexpr int kWS = 16;          // state columns per workgroup
 constexpr int kRing = 5;         // chunks in the staging ring
 // Geometry that depends on the key dimension DK.
-// K ring rows: pitch KR elements, and the 16-byte chunk q of row t stored at chunk q ^ ((t >> 2) & 3).
-// DK = 128: 320 bytes (20 sixteen-byte chunks, the last 4 unused); DK = 64: 192 bytes (12 chunks, 8
-// used).  Either way row t starts 16 (mod 64) banks after row t - 1 up to a permutation of
-// {0, 16, 32, 48}, so with 64 four-byte banks both ways the rows are read touch 16 different chunk
-// positions per 16 lanes: a row fragment (16 rows, one chunk each) and a transposed fragment (4
-// consecutive rows x 4 consecutive chunks).
+// K ring rows: unpadded (pitch DK elements: 256 or 128 bytes), the 16-byte chunk q of row t stored at
+// chunk q ^ kswz<DK>(t).  The rows are read two ways, each 16 lanes at a time, and with 64 four-byte
+// banks both are free of bank conflicts:
+//   row fragments: 16 consecutive rows (aligned), one chunk each at the same logical q -- the swizzle
+//     restricted to 16 such rows (to the 8 rows of one parity at DK = 64, whose rows alternate
+//     between the two halves of the banks) is a bijection, so the 16 chunks are distinct;
+//   transposed fragments: 4 consecutive rows (aligned) x 4 consecutive logical chunks (an aligned
+//     quad), 8 bytes each -- the swizzle's quad bits differ between those rows (between the two rows
+//     of one parity at DK = 64), so each row's quad lands on its own 4 physical chunks.
+template <int DK>
+__host__ __device__ constexpr int kswz(int t) {
+    return DK == 128 ? (((t & 3) << 2) | ((t >> 2) & 3)) : ((((t >> 1) & 1) << 2) | ((t >> 2) & 3));
+}
 template <int DK>
 struct Geom {
     static constexpr int KB = DK / 32;                  // 32-key steps of a product over the keys
-    static constexpr int KR = DK == 128 ? 160 : 96;     // K ring row pitch (elements)
+    static constexpr int KR = DK;                       // K ring row pitch (elements)
     static constexpr int SP = DK + 8;                   // row pitch of the S^T copies [column][key]
-    static constexpr int KDma = kC * KR * 2 / 1024;     // 1 KiB copy instructions per K slot (20, 12)
+    static constexpr int KDma = kC * KR * 2 / 1024;     // 1 KiB copy instructions per K slot (16, 8)
     static constexpr int DmaOps = KDma + 2 + 1;         // per chunk: K, V (2 KiB), gate block
     static constexpr int TPH = DK / 32;                 // 16-key state tiles per key half
     static constexpr int UPH = DK / 64;                 // 32-key blocks per key half
@@ -595,15 +602,14 @@ constexpr int kPfAhead = 4;
 constexpr int kLinesN = kNFrags * kFragElems * 2 / 128;
 constexpr int kLinesM = kMFrags * kFragElems * 2 / 128;
 constexpr int kLinesG = kGRows * kC * 4 / 128;
-__host__ __device__ constexpr int kswz(int t) { return (t >> 2) & 3; }
-
 template <int DK>
 struct ScanLds {
     __bf16 Kr[kRing][kC * Geom<DK>::KR];       // K rows [token][key]
     __bf16 Vr[kRing][kC * kWS];                // V [token][this slice's 16 columns]
     float Gt[kRing][kGRows * kC];              // gate block: G2, 2^G2, 2^(G2_C - G2), (r, rq)
     __bf16 St[2][2][kWS * Geom<DK>::SP];       // S^T at chunk start [buffer][hi, lo]
-    f32x4 Ut[2][4][64];                        // U [buffer][token tile][lane], the chain's tiles
+    bf16x8 Us[2][2][2][64];                    // U as B fragments [buffer][32-token step][hi, lo][lane]
+    bf16x8 Ds[2][2][2][64];                    // D = diag(e^(G_C - G)) U, likewise
     f32x4 Yt[2][2][4][64];                     // Y in two parts [buffer][key half][tile][lane]
     uint32_t sink[64];                         // landing row of the L2 prefetches (never read)
 };
@@ -614,14 +620,25 @@ __device__ __forceinline__ int rho(int a, int m) {
     return 32 * (a >> 1) + 8 * (m >> 2) + 4 * (a & 1) + (m & 3);
 }
 
+// Lane parts of the K ring addresses (elements).  Row fragment of row 16 a + c (any a) at the
+// logical chunk 4 blk + g of 32-key block blk:
+template <int DK>
+__device__ __forceinline__ int kf_lane(int c, int g, int blk) {
+    return c * DK + 8 * ((4 * blk + g) ^ kswz<DK>(c));
+}
 // K^T fragment for the state update: lane (g, c) receives K[32 kb + 4 g + e][rho(kt, c)] (e < 4)
 // and K[32 kb + 16 + 4 g + e - 4][rho(kt, c)] (e >= 4): keys in the state tiles' row order, tokens
 // as in the chain's D fragments.  Each half is a transposed read of row 32 kb + 4 g (+ 16) + c / 4
-// at logical chunk 4 (kt / 2) + c % 4, half kt % 2 of the chunk; `k0` holds the ring slot plus the
-// lane's part of the address (the chunk swizzle of those rows is g).
+// at logical chunk 4 (kt / 2) + c % 4, half kt % 2 of the chunk.  kt_lane gives the lane's part for
+// the quad kt / 2 (the rows' swizzle depends only on 4 g + c / 4); kt_frag adds the rest.
+template <int DK>
+__device__ __forceinline__ int kt_lane(int c, int g, int quad) {
+    const int r = 4 * g + (c >> 2);
+    return r * DK + 8 * ((4 * quad + (c & 3)) ^ kswz<DK>(r));
+}
 template <int KR>
-__device__ __forceinline__ bf16x8 kt_frag(lds_u8* k0, int kt, int kb) {
-    const int off = 2 * (32 * kb * KR + 32 * (kt >> 1) + 4 * (kt & 1));
+__device__ __forceinline__ bf16x8 kt_frag(lds_u8* k0, int half, int kb) {
+    const int off = 2 * (32 * kb * KR + 4 * half);
     return cat44(read_tr(k0, off), read_tr(k0, off + 2 * 16 * KR));
 }
 
@@ -714,7 +731,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         };
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
-        f32x4 u[4];                      // U of the previous chunk
+        f32x4 dprev[4];                  // D of the previous chunk, fp32
         fetch_m(0, P0{});
         fetch_m(min(1, nchunks - 1), P1{});
         fetch_n(min(1, nchunks - 1), P1{});
@@ -739,12 +756,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
                 for (int a = 0; a < 4; ++a) x[a] = y[a];
             } else {
-                // D_{s-1} = diag(e^(G_C - G)) U_{s-1} as fp16 B fragments
-                lds_u8* dl_ = lds_at(sm.Gt[(s - 1) % kRing] + 2 * kC + 4 * g);
-                f32x4 ds[4];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) ds[a] = u[a] * ld<f32x4>(dl_, 4 * 16 * a);
-                const f16x8 d16[2] = {pack_f16(ds[0], ds[1]), pack_f16(ds[2], ds[3])};
+                // D_{s-1} = diag(e^(G_C - G)) U_{s-1} (kept from the previous step) as fp16 B fragments
+                const f16x8 d16[2] = {pack_f16(dprev[0], dprev[1]), pack_f16(dprev[2], dprev[3])};
                 // N_s D_{s-1}
                 f32x4 nd[4];
 #pragma unroll
@@ -760,6 +773,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             }
             const f16x8 x16[2] = {pack_f16(x[0], x[1]), pack_f16(x[2], x[3])};
             // U = M X (M lower triangular: pairs (a, j) with 2 j <= a)
+            f32x4 u[4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) u[a] = zero4();
 #pragma unroll
@@ -768,12 +782,32 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 u[a] = mma16(mf[par][p], x16[j], u[a]);
             }
 
-            // the other roles get diag(r) U with L2 (the raw keys then act as normalised ones)
-            lds_u8* ul = lds_at(&sm.Ut[s & 1][0][lane]);
+            // D_s for the next chunk's N D, and U_s, D_s as hi + lo B fragments for the state and
+            // output waves (with L2 as diag(r) U and diag(r) D: the raw keys then act as normalised ones)
+            lds_u8* dcl = lds_at(gt + 2 * kC + 4 * g);               // 2^(G2_C - G2) at rows 16 a + 4 g + r
+#pragma unroll
+            for (int a = 0; a < 4; ++a) dprev[a] = u[a] * ld<f32x4>(dcl, 4 * 16 * a);
+            f32x4 ur[4], dr[4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                if constexpr (L2) st(ul, 16 * 64 * a, u[a] * rk[a]);
-                else st(ul, 16 * 64 * a, u[a]);
+                ur[a] = u[a];
+                dr[a] = dprev[a];
+                if constexpr (L2) {
+                    ur[a] *= rk[a];
+                    dr[a] *= rk[a];
+                }
+            }
+            lds_u8* dsl = lds_at(&sm.Ds[s & 1][0][0][lane]);
+            lds_u8* usl = lds_at(&sm.Us[s & 1][0][0][lane]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                bf16x8 hi, lo;
+                split8(dr[2 * j], dr[2 * j + 1], hi, lo);
+                st(dsl, 16 * 64 * (2 * j), hi);
+                st(dsl, 16 * 64 * (2 * j + 1), lo);
+                split8(ur[2 * j], ur[2 * j + 1], hi, lo);
+                st(usl, 16 * 64 * (2 * j), hi);
+                st(usl, 16 * 64 * (2 * j + 1), lo);
             }
             __builtin_amdgcn_sched_barrier(0);
             // unconditional (the last chunk refetches itself): a conditional fetch makes the
@@ -813,8 +847,12 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[t][r] = s_in ? s_in[state_idx(t, r)] : 0.f;
             // lane parts of the LDS addresses (the rest are compile-time offsets)
-            const int l_kf = c * KR + 8 * (g ^ kswz(c));                  // K row c, logical chunk g
-            const int l_kt = (4 * g + (c >> 2)) * KR + 8 * ((c & 3) ^ g);
+            int l_kf[UPH], l_kt[UPH];        // this half's 32-key blocks (row fragments, K^T quads)
+#pragma unroll
+            for (int u = 0; u < UPH; ++u) {
+                l_kf[u] = kf_lane<DK>(c, g, UPH * hh + u);
+                l_kt[u] = kt_lane<DK>(c, g, UPH * hh + u);
+            }
             const int l_v = (4 * g + (c >> 2)) * kWS + 4 * (c & 3);
             const int l_st = c * SP + 8 * g;
             bf16x8 sh[UPH], sl[UPH];         // this half of S as hi + lo B fragments
@@ -827,14 +865,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             // plus V in half 0 (ec = that decay factor)
             auto make_y = [&](int ci, float ec) {
                 const int slot = ci % kRing;
-                lds_u8* kfl = lds_at(sm.Kr[slot] + l_kf);
+                lds_u8* kfl[UPH];
+#pragma unroll
+                for (int u = 0; u < UPH; ++u) kfl[u] = lds_at(sm.Kr[slot] + l_kf[u]);
                 lds_u8* gl = lds_at(sm.Gt[slot] + kC + 4 * g);
                 f32x4 ks[4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     bf16x8 kf[UPH];
 #pragma unroll
-                    for (int u = 0; u < UPH; ++u) kf[u] = ld<bf16x8>(kfl, 2 * (16 * a * KR + 32 * (UPH * hh + u)));
+                    for (int u = 0; u < UPH; ++u) kf[u] = ld<bf16x8>(kfl[u], 2 * 16 * a * KR);
                     ks[a] = zero4();
 #pragma unroll
                     for (int u = 0; u < UPH; ++u) {
@@ -870,20 +910,21 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     const int ps = (s - 1) % kRing;
                     const float* gp = sm.Gt[ps];
                     const float ec = gp[2 * kC - 1];
-                    lds_u8* ul = lds_at(&sm.Ut[(s - 1) & 1][0][lane]);
-                    lds_u8* dl_ = lds_at(gp + 2 * kC + 4 * g);
-                    f32x4 ds[4];
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) ds[a] = ld<f32x4>(ul, 16 * 64 * a) * ld<f32x4>(dl_, 4 * 16 * a);
+                    lds_u8* dsl = lds_at(&sm.Ds[(s - 1) & 1][0][0][lane]);   // the chain's D, hi + lo
                     bf16x8 dh[2], dlo[2];
-                    split8(ds[0], ds[1], dh[0], dlo[0]);
-                    split8(ds[2], ds[3], dh[1], dlo[1]);
-                    lds_u8* ktl = lds_at(sm.Kr[ps] + l_kt);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        dh[j] = ld<bf16x8>(dsl, 16 * 64 * (2 * j));
+                        dlo[j] = ld<bf16x8>(dsl, 16 * 64 * (2 * j + 1));
+                    }
+                    lds_u8* ktl[UPH];
+#pragma unroll
+                    for (int u = 0; u < UPH; ++u) ktl[u] = lds_at(sm.Kr[ps] + l_kt[u]);
 #pragma unroll
                     for (int t = 0; t < TPH; ++t) {
                         bf16x8 kt[2];
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) kt[kb] = kt_frag<KR>(ktl, TPH * hh + t, kb);
+                        for (int kb = 0; kb < 2; ++kb) kt[kb] = kt_frag<KR>(ktl[t >> 1], t & 1, kb);
                         f32x4 acc = S[t] * ec;
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb) {
@@ -921,7 +962,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         auto run = [&](auto oc) {
             constexpr int ow = decltype(oc)::value;      // 0: tiles {0, 3}; 1: tiles {1, 2}
             constexpr int tiles[2] = {ow, 3 - ow};
-            const int l_kf = c * KR + 8 * (g ^ kswz(c));                  // K row c, logical chunk g
+            int l_kf[KB];                                  // K row c, logical chunk 4 kb + g
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) l_kf[kb] = kf_lane<DK>(c, g, kb);
             const int l_st = c * SP + 8 * g;
             auto fetch_out = [&](OutIn<KB>& f, int ci) {
                 const size_t tok0 = tok0_of(ci);
@@ -944,7 +987,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                 const float* gt = sm.Gt[slot];
                 const int buf = ci & 1;
                 // S^T (hi, lo), U^T (hi, lo) and the gate values of this wave's rows
-                lds_u8* kfl = lds_at(kr + l_kf);
+                lds_u8* kfl[KB];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) kfl[kb] = lds_at(kr + l_kf[kb]);
                 lds_u8* gl = lds_at(gt + 4 * g);
                 float gq[2], eq[2], rq[2];
 #pragma unroll
@@ -960,13 +1005,15 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) sf[hl][kb] = ld<bf16x8>(sp, 2 * 32 * kb);
                 }
-                // U^T fragments: lane (g, c) of the chain's tiles 2 kb, 2 kb + 1 holds U at
-                // tokens 32 kb + 4 g + r and 32 kb + 16 + 4 g + r, column c: the P^T row order
-                lds_u8* ul = lds_at(&sm.Ut[buf][0][lane]);
+                // U^T fragments (hi, lo, split by the chain): lane (g, c) of the chain's tiles 2 kb,
+                // 2 kb + 1 holds U at tokens 32 kb + 4 g + r and 32 kb + 16 + 4 g + r, column c: the
+                // P^T row order
+                lds_u8* usl = lds_at(&sm.Us[buf][0][0][lane]);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    split8(ld<f32x4>(ul, 16 * 64 * (2 * kb)), ld<f32x4>(ul, 16 * 64 * (2 * kb + 1)), uf[0][kb],
-                           uf[1][kb]);
+                for (int kb = 0; kb < 2; ++kb) {
+                    uf[0][kb] = ld<bf16x8>(usl, 16 * 64 * (2 * kb));
+                    uf[1][kb] = ld<bf16x8>(usl, 16 * 64 * (2 * kb + 1));
+                }
                 f32x4 ot[2];
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
@@ -977,7 +1024,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
                     for (int b = 0; b <= a; ++b)
 #pragma unroll
-                        for (int kb = 0; kb < KB; ++kb) kf[b][kb] = ld<bf16x8>(kfl, 2 * (16 * b * KR + 32 * kb));
+                        for (int kb = 0; kb < KB; ++kb) kf[b][kb] = ld<bf16x8>(kfl[kb], 2 * 16 * b * KR);
                     f32x4 pt[4];
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
@@ -1040,7 +1087,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         // ------------------------------------------------ staging wave ------------------------
         if (nchunks == 0) return;
         // K piece of copy instruction ii: byte 1024 ii + 16 lane of the slot, i.e. row t, physical
-        // chunk pc (pc >= 16 is row padding: any in-bounds source will do)
+        // chunk pc, which holds the row's logical chunk pc ^ kswz(t)
         constexpr int KDma = GM::KDma;
         int krow[KDma], kcol[KDma];
 #pragma unroll
@@ -1048,7 +1095,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             const int ob = 1024 * ii + 16 * lane;
             const int t = ob / (2 * KR), pc = (ob % (2 * KR)) / 16;
             krow[ii] = t;
-            kcol[ii] = 8 * (pc < DK / 8 ? (pc ^ kswz(t)) : 0);
+            kcol[ii] = 8 * (pc ^ kswz<DK>(t));
         }
         // byte offsets of each lane's pieces inside a full chunk (the same for every chunk)
         uint32_t koff[KDma], voff[2];
