@@ -63,6 +63,7 @@ constexpr int kGRows = 5;   // rows of a chunk's gate block (of kC floats each)
 // Key dimension DK (64 or 128) is a template parameter of both kernels; KB = DK / 32 is the number of
 // 32-key steps of one matrix-core product over the keys.
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;     // XCDs of an MI355X; workgroup i runs on XCD i % 8
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -235,6 +236,27 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
 constexpr int kBP = 17;          // row pitch (floats) of the 16 x 16 blocks of A and T
 __device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }   // a >= b
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 lanes inside each row of
+// 16 lanes, then lane 15's total added to rows 1 and 3 and lane 31's to rows 2 and 3 (DPP row
+// broadcasts).  Lanes whose source falls outside the row take 0.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    auto add = [&](int y) { x += __int_as_float(y); };
+    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));   // row_shr:1
+    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));   // row_shr:2
+    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));   // row_shr:4
+    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));   // row_shr:8
+    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));   // row_bcast:15
+    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));   // row_bcast:31
+    return x;
+}
+
+// Orders one wave's shared-memory writes before its later reads of what other lanes wrote.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // (at most 128 registers per lane: four waves per SIMD, so a whole 4096-token prefill's chunk
 // workgroups are resident at once)
 template <int DK, typename TG, bool L2>
@@ -247,9 +269,18 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     __shared__ float sA[10][16 * kBP];     // blocks (a, b), a > b, of A
     __shared__ float sT[10][16 * kBP];     // blocks (a, b), a >= b, of T = (I + A)^-1
     __shared__ float sB[kC];
+    // per wave: the current v-head's G2 and beta, read by address in the tile loops (instead of by
+    // cross-lane broadcasts)
+    __shared__ __attribute__((aligned(16))) float sW[4][2][kC];
 
     constexpr int KB = DK / 32;
-    const int slot = blockIdx.x, kh = blockIdx.y;
+    // Workgroups go to the XCDs round robin by linear index.  The (chunk slot, q/k head) items are
+    // dealt so that each XCD gets one contiguous run of them: a chunk and the next one, which reads
+    // its keys again as its previous chunk's, then share an L2.
+    const int nwg = gridDim.x * gridDim.y, lin = blockIdx.x + gridDim.x * blockIdx.y;
+    const int xcd = lin % kXcds, per = nwg / kXcds, extra = nwg % kXcds;
+    const int item = xcd * per + min(xcd, extra) + lin / kXcds;
+    const int slot = item % gridDim.x, kh = item / gridDim.x;
     ChunkLoc loc;
     if (!locate_chunk(slot, cu_seqlens, chunk_start, N, T, nct, loc)) return;
     const int Gq = Hv / Hk;
@@ -390,12 +421,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         gate_values(graw, braw, A_log, dt_bias, h, gv, bv);
         const float gt = lane < L ? gv * kLog2e : 0.f;
         const float bt = lane < L ? bv : 0.f;
-        float G2 = gt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(G2, off);
-            if (lane >= off) G2 += y;
-        }
+        const float G2 = wave_prefix_sum(gt);
         if (wave == 0) {
             const size_t ws_row = ((size_t)slot * Hv + h) * kGRows * kC;
             const float G2c = __shfl(G2, 63);
@@ -404,14 +430,20 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
             ws_G[ws_row + 2 * kC + lane] = exp2_fast(G2c - G2);
             sB[lane] = bt;
         }
+        float* wG = sW[wave][0];
+        float* wB = sW[wave][1];
+        wG[lane] = G2;
+        wB[lane] = bt;
+        wave_lds_sync();
         // A = diag(beta) (K K^T o Gam), strictly lower, tile by tile
         auto atile = [&](int ta, int tb, f32x4 acc) {
-            const float Gj = __shfl(G2, 16 * tb + c);
+            const f32x4 Gt = *reinterpret_cast<const f32x4*>(wG + 16 * ta + 4 * gq);
+            const f32x4 Bt = *reinterpret_cast<const f32x4*>(wB + 16 * ta + 4 * gq);
+            const float Gj = wG[16 * tb + c];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * ta + 4 * gq + r, j = 16 * tb + c;
-                const float Gt = __shfl(G2, t), Bt = __shfl(bt, t);
-                acc[r] = j < t ? Bt * acc[r] * exp2_fast(Gt - Gj) : 0.f;
+                acc[r] = j < t ? Bt[r] * acc[r] * exp2_fast(Gt[r] - Gj) : 0.f;
             }
             return acc;
         };
@@ -424,7 +456,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         if (wave & 1) store_a(ya, yb, atile(ya, yb, ky));
         // T_ww = (I + A_ww)^-1 by forward substitution, lane c computing column c, column-sweep
         // order (x_j final, then subtracted from every later row: 15 dependent steps); the entries
-        // of A_ww come out of the accumulator tile one by one, broadcast with readlane
+        // of A_ww come out of the accumulator tile one by one, broadcast with readlane (into scalar
+        // registers: the vector registers are all taken)
         {
             const f32x4 ad = atile(wave, wave, kd);
             float x[16];
