@@ -126,7 +126,7 @@ def main() -> int:
     from gated_deltanet_delta_amd import _lib
     from gated_deltanet_delta_amd import (gdn_causal_conv1d, gdn_chunk_fwd, gdn_chunk_fwd_ex,
                                           gdn_chunk_bwd, gdn_chunk_bwd_ex, gdn_chunk_fwd_gating,
-                                          gdn_gated_rmsnorm,
+                                          gdn_chunk_fwd_gated_norm, gdn_gated_rmsnorm,
                                           gdn_recurrent_step, gdn_recurrent_step_gating, synth,
                                           workspace_size)
 
@@ -374,6 +374,31 @@ def main() -> int:
     ms_norm = time_c(clib.gdn_gated_rmsnorm, norm_args)
     norm_bytes = o.numel() * (4 + 2 + 2) + wl.dv * 4
 
+    # ---------------- the prefill with the gated norm fused onto o, against prefill then norm ----
+    zsets = [zn] + [zn.clone() for _ in range(NSETS - 1)]
+    ysets = [torch.empty_like(yn) for _ in range(NSETS)]
+    fws = torch.empty(int(clib.gdn_chunk_fwd_gated_norm_workspace_size(B, T, wl.Hk, wl.Hv, wl.dk, wl.dv, N,
+                                                                       _lib.GDN_BF16)),
+                      dtype=torch.uint8, device=dev)
+
+    def fused_norm_call(i):
+        s_ = sets[i % NSETS]
+        gdn_chunk_fwd_gated_norm(s_["q"], s_["k"], s_["v"], s_["g"], s_["beta"], zsets[i % NSETS], wn, 1e-6,
+                                 initial_state=s_["initial_state"], y=ysets[i % NSETS], final_state=s_["fs"],
+                                 workspace=fws)
+
+    def prefill_then_norm(i):
+        s_ = sets[i % NSETS]
+        prefill_step(i=i)
+        gdn_gated_rmsnorm(s_["o"], zsets[i % NSETS], wn, 1e-6, out=ysets[i % NSETS])
+
+    for i in range(max(args.warmup, 20)):
+        fused_norm_call(i)
+        prefill_then_norm(i)
+    ms_fused_norm = time_loop(fused_norm_call)
+    ms_prefill_norm = time_loop(prefill_then_norm)
+    del fws
+
     # ---------------- the causal conv1d of the QKV mixture (2 Hk dk + Hv dv channels) -----------
     # (inputs drawn here with their own seed: the workloads define q, k, v after the conv)
     Cc, Wc = 2 * wl.Hk * wl.dk + wl.Hv * wl.dv, 4
@@ -616,6 +641,12 @@ def main() -> int:
                                        "frac": round(conv_bytes / (ms_conv / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
                                        "traffic": counter("conv", "traffic"),
                                        "algorithmic_bytes_per_launch": int(conv_bytes)}},
+        "prefill_fused_norm": {"call": "gdn_chunk_fwd_gated_norm (the prefill with the gated RMSNorm fused "
+                                       "onto o: bf16 y out, o never stored; bf16 z)",
+                               "ms_per_call_events": round(ms_fused_norm, 5),
+                               "tokens_per_s": round(tokens / (ms_fused_norm / 1e3), 1),
+                               "ms_prefill_then_norm_events": round(ms_prefill_norm, 5),
+                               "speedup_vs_prefill_then_norm": round(ms_prefill_norm / ms_fused_norm, 3)},
         "gated_rmsnorm": {"call": "gdn_gated_rmsnorm on the prefill's o (fp32 in, bf16 z and out)",
                           "rows": o.numel() // wl.dv, "d": wl.dv,
                           "ms_per_call_events": round(ms_norm, 5),

@@ -22,7 +22,8 @@ EXPORTED = ("gdn_status_string", "gdn_version", "gdn_chunk_fwd_workspace_size", 
             "gdn_recurrent_step_indexed", "gdn_gated_rmsnorm", "gdn_causal_conv1d",
             "gdn_chunk_fwd_ex", "gdn_recurrent_step_ex", "gdn_chunk_bwd_workspace_size",
             "gdn_chunk_bwd", "gdn_chunk_bwd_ex_workspace_size", "gdn_chunk_bwd_ex",
-            "gdn_chunk_fwd_noalloc_max_bytes", "gdn_chunk_fwd_noalloc")
+            "gdn_chunk_fwd_noalloc_max_bytes", "gdn_chunk_fwd_noalloc",
+            "gdn_chunk_fwd_gated_norm_workspace_size", "gdn_chunk_fwd_gated_norm")
 
 GDN_FLAG_QK_L2NORM = 1
 
@@ -76,6 +77,11 @@ def load() -> ctypes.CDLL:
     u32 = ctypes.c_uint
     lib.gdn_chunk_fwd_ex.restype = i32
     lib.gdn_chunk_fwd_ex.argtypes = [vp] * 10 + [i32] + [vp] + [i32] * 7 + [i32, i32] + [u32] + [vp, vp, sz, vp]
+    lib.gdn_chunk_fwd_gated_norm_workspace_size.restype = sz
+    lib.gdn_chunk_fwd_gated_norm_workspace_size.argtypes = [i32] * 7 + [i32]
+    lib.gdn_chunk_fwd_gated_norm.restype = i32
+    lib.gdn_chunk_fwd_gated_norm.argtypes = ([vp] * 10 + [i32] + [vp] + [vp, vp, ctypes.c_float] + [i32] * 7
+                                             + [i32] * 4 + [u32] + [vp, vp, sz, vp])
     lib.gdn_chunk_bwd_workspace_size.restype = sz
     lib.gdn_chunk_bwd_workspace_size.argtypes = [i32] * 7
     lib.gdn_chunk_bwd.restype = i32

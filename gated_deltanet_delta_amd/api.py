@@ -301,27 +301,17 @@ def gdn_recurrent_step_indexed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     return o
 
 
-def gdn_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                     beta: torch.Tensor, *, A_log: Optional[torch.Tensor] = None,
-                     dt_bias: Optional[torch.Tensor] = None,
-                     initial_state: Optional[torch.Tensor] = None,
-                     final_state: Optional[torch.Tensor] = None,
-                     state_indices: Optional[torch.Tensor] = None,
-                     cu_seqlens: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
-                     o: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """The chunked call with every option: A_log, dt_bias [Hv] fp32 make g, beta the raw projections
-    a, b; state_indices int32 [N] makes initial_state a pool [num_slots,Hv,dk,dv] read and written in
-    place (it is then also the returned final state); qk_l2norm normalises q and k to unit length
-    inside the kernels.  Returns (o, final_state)."""
-    lib = _lib.load()
+def _ex_args(name, q, k, v, g, beta, A_log, dt_bias, initial_state, final_state, state_indices,
+             cu_seqlens):
+    """Shape and dtype checks shared by the option-complete chunked calls; returns the sizes, the
+    pool size and the final-state tensor (allocated when not given)."""
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, T, H, d]")
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("gdn_chunk_fwd_ex runs on a GPU; tensors must be on a cuda device")
+        raise ValueError(f"{name} runs on a GPU; tensors must be on a cuda device")
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     gating = A_log is not None
     xn, yn = ("a", "b") if gating else ("g", "beta")
@@ -352,26 +342,86 @@ def gdn_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
         if final_state is None:
             final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
         _check(final_state, (N, Hv, dk, dv), "final_state", dev, torch.float32)
-    if o is None:
-        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
-    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
-    qkv, gate = _code(q, "q"), _code(g, xn)
-    ws_bytes = int(lib.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv))
+    return B, T, Hk, Hv, dk, dv, N, num_slots, final_state, dev, xn
+
+
+def _workspace(ws_bytes: int, workspace, dev):
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if workspace is not None:
         if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
             raise ValueError(f"workspace must hold {ws_bytes} bytes on {dev}")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, ctypes.c_size_t(nbytes)
+
+
+def gdn_chunk_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, *, A_log: Optional[torch.Tensor] = None,
+                     dt_bias: Optional[torch.Tensor] = None,
+                     initial_state: Optional[torch.Tensor] = None,
+                     final_state: Optional[torch.Tensor] = None,
+                     state_indices: Optional[torch.Tensor] = None,
+                     cu_seqlens: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                     o: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The chunked call with every option: A_log, dt_bias [Hv] fp32 make g, beta the raw projections
+    a, b; state_indices int32 [N] makes initial_state a pool [num_slots,Hv,dk,dv] read and written in
+    place (it is then also the returned final state); qk_l2norm normalises q and k to unit length
+    inside the kernels.  Returns (o, final_state)."""
+    lib = _lib.load()
+    B, T, Hk, Hv, dk, dv, N, num_slots, final_state, dev, xn = _ex_args(
+        "gdn_chunk_fwd_ex", q, k, v, g, beta, A_log, dt_bias, initial_state, final_state, state_indices,
+        cu_seqlens)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=torch.float32, device=dev)
+    _check(o, (B, T, Hv, dv), "o", dev, torch.float32)
+    qkv, gate = _code(q, "q"), _code(g, xn)
+    workspace, nbytes = _workspace(int(lib.gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv)),
+                                   workspace, dev)
     flags = _lib.GDN_FLAG_QK_L2NORM if qk_l2norm else 0
     st = lib.gdn_chunk_fwd_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias), _ptr(initial_state),
         _ptr(final_state), _ptr(state_indices), num_slots, _ptr(cu_seqlens), B, T, Hk, Hv, dk, dv, N,
-        qkv, gate, flags, _ptr(o), _ptr(workspace),
-        ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
-        _stream(dev))
+        qkv, gate, flags, _ptr(o), _ptr(workspace), nbytes, _stream(dev))
     if st != _lib.GDN_SUCCESS:
         raise _lib.GdnError(st, "gdn_chunk_fwd_ex")
     return o, final_state
+
+
+def gdn_chunk_fwd_gated_norm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                             beta: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6,
+                             *, A_log: Optional[torch.Tensor] = None,
+                             dt_bias: Optional[torch.Tensor] = None,
+                             initial_state: Optional[torch.Tensor] = None,
+                             final_state: Optional[torch.Tensor] = None,
+                             state_indices: Optional[torch.Tensor] = None,
+                             cu_seqlens: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                             y: Optional[torch.Tensor] = None, y_dtype: torch.dtype = torch.bfloat16,
+                             workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gdn_chunk_fwd_ex with the gated output norm fused onto o: returns (y, final_state), y [B,T,Hv,dv]
+    = o / sqrt(mean(o^2) + eps) * weight * silu(z) per (token, v-head) row, o being gdn_chunk_fwd_ex's
+    output for the same arguments.  z [B,T,Hv,dv] bf16 or fp32, weight [dv] fp32, y bf16 or fp32."""
+    lib = _lib.load()
+    B, T, Hk, Hv, dk, dv, N, num_slots, final_state, dev, xn = _ex_args(
+        "gdn_chunk_fwd_gated_norm", q, k, v, g, beta, A_log, dt_bias, initial_state, final_state,
+        state_indices, cu_seqlens)
+    _check(z, (B, T, Hv, dv), "z", dev)
+    _check(weight, (dv,), "weight", dev, torch.float32)
+    if y is None:
+        y = torch.empty((B, T, Hv, dv), dtype=y_dtype, device=dev)
+    _check(y, (B, T, Hv, dv), "y", dev)
+    qkv, gate = _code(q, "q"), _code(g, xn)
+    workspace, nbytes = _workspace(
+        int(lib.gdn_chunk_fwd_gated_norm_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv)), workspace, dev)
+    flags = _lib.GDN_FLAG_QK_L2NORM if qk_l2norm else 0
+    st = lib.gdn_chunk_fwd_gated_norm(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias), _ptr(initial_state),
+        _ptr(final_state), _ptr(state_indices), num_slots, _ptr(cu_seqlens), _ptr(z), _ptr(weight),
+        ctypes.c_float(eps), B, T, Hk, Hv, dk, dv, N, qkv, gate, _code(z, "z"), _code(y, "y"), flags,
+        _ptr(y), _ptr(workspace), nbytes, _stream(dev))
+    if st != _lib.GDN_SUCCESS:
+        raise _lib.GdnError(st, "gdn_chunk_fwd_gated_norm")
+    return y, final_state
 
 
 def gdn_recurrent_step_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

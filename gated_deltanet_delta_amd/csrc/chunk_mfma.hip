@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     const TG* __restrict__ beta, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start, int N, int T,
     int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M,
-    __bf16* __restrict__ ws_N) {
+    __bf16* __restrict__ ws_N, float* __restrict__ ws_X, int x_per_head) {
     __shared__ float sA[10][16 * kBP];     // blocks (a, b), a > b, of A
     __shared__ float sT[10][16 * kBP];     // blocks (a, b), a >= b, of T = (I + A)^-1
     __shared__ float sB[kC];
@@ -290,6 +290,14 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     const size_t tok0 = (size_t)loc.row * T + loc.t0;
     const int L = loc.len;
     const bool has_prev = loc.ci > 0;   // the previous chunk (always a full one) is in this sequence
+
+    // fused output norm: this chunk's exchange rows of the head's v-heads start out as -1, a value
+    // no sum of squares takes, so that the scan can tell a published sum from a missing one
+    if (ws_X) {
+        float* xb = ws_X + ((size_t)slot * Hv + (size_t)kh * Gq) * x_per_head;
+        for (int i = 4 * tid; i < Gq * x_per_head; i += 4 * kThreads)
+            *reinterpret_cast<f32x4*>(xb + i) = f32x4{-1.f, -1.f, -1.f, -1.f};
+    }
 
     // K K^T as 16x16 tiles; wave w owns diagonal tile (w, w) and some below it: wave 0 (0,0) (1,0);
     // wave 1 (1,1) (2,1) (2,0); wave 2 (2,2) (3,2); wave 3 (3,3) (3,0) (3,1).  The K rows of the (at
@@ -598,7 +606,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
 // s + 3's copy and waits for chunk s + 2's.
 constexpr int kScanThreads = 384;
 constexpr int kWS = 16;          // state columns per workgroup
-constexpr int kRing = 5;         // chunks in the staging ring
+constexpr int kRing = 5;         // chunks in the staging ring (K rows, gate blocks)
+constexpr int kVRing = 3;        // chunks of V in LDS (each is read in the step after it lands)
 // Geometry that depends on the key dimension DK.
 // K ring rows: unpadded (pitch DK elements: 256 or 128 bytes), the 16-byte chunk q of row t stored at
 // chunk q ^ kswz<DK>(t).  The rows are read two ways, each 16 lanes at a time, and with 64 four-byte
@@ -638,7 +647,7 @@ constexpr int kLinesG = kGRows * kC * 4 / 128;
 template <int DK>
 struct ScanLds {
     __bf16 Kr[kRing][kC * Geom<DK>::KR];       // K rows [token][key]
-    __bf16 Vr[kRing][kC * kWS];                // V [token][this slice's 16 columns]
+    __bf16 Vr[kVRing][kC * kWS];               // V [token][this slice's 16 columns]
     float Gt[kRing][kGRows * kC];              // gate block: G2, 2^G2, 2^(G2_C - G2), (r, rq)
     __bf16 St[2][2][kWS * Geom<DK>::SP];       // S^T at chunk start [buffer][hi, lo]
     bf16x8 Us[2][2][2][64];                    // U as B fragments [buffer][32-token step][hi, lo][lane]
@@ -647,6 +656,35 @@ struct ScanLds {
     uint32_t sink[64];                         // landing row of the L2 prefetches (never read)
 };
 static_assert(sizeof(ScanLds<128>) <= 160 * 1024, "scan LDS exceeds a CU's 160 KiB");
+
+// The gated output norm fused onto o, y = o / sqrt(mean(o^2) + eps) * weight * silu(z) per (token,
+// v-head) row of DV channels.  A row's channels come from the NS = DV / 16 slice workgroups of its
+// v-head.  The output waves hand each chunk's o tile to the two norm waves through a two-chunk LDS
+// ring; a norm wave (32 rows, two lanes of 8 channels per row) keeps its rows in registers, publishes
+// the row's 16 channels' sum of
+// squares of every row into the exchange block of that chunk and v-head (device-scope stores over
+// the solve kernel's -1 fill), and kNormLag steps later normalises, gates and stores its channels
+// of y, with the other slices' sums and z loaded kNormAhead steps before.  A sum still at -1 when it
+// is needed is waited for; every slice publishes each chunk kNormLag - kNormAhead steps before any
+// slice loads it, so that only happens when one slice runs behind.
+constexpr int kScanThreadsNorm = kScanThreads + 128;  // plus the norm waves (6, 7)
+constexpr int kORing = 2;                             // chunks of o in LDS
+constexpr int kNormLag = 4;                           // steps from publishing to normalising
+constexpr int kNormAhead = 2;                         // steps from loading to normalising
+constexpr int kNormSpin = 1 << 20;                    // polls of a missing sum before giving up
+struct ScanNorm {
+    const void* z;               // [rows of o] x DV, bf16 or fp32
+    const float* weight;         // [DV]
+    float eps;
+    int z_bf16, y_bf16;
+    float* xs;                   // [slots][Hv][NS][64] each slice's sum of squares of each row
+    void* y;                     // [B, T, Hv, DV], bf16 or fp32
+};
+template <int DK>
+constexpr size_t scan_lds_bytes(bool norm) {
+    return sizeof(ScanLds<DK>) + (norm ? sizeof(float) * kORing * kC * kWS : 0);
+}
+static_assert(scan_lds_bytes<128>(true) <= 160 * 1024, "fused-norm scan LDS exceeds a CU's 160 KiB");
 
 // index (token or key) that accumulator row m of tile a stands for
 __device__ __forceinline__ int rho(int a, int m) {
@@ -695,20 +733,21 @@ struct OutIn {                     // one chunk's Q fragments for an output wave
     bf16x8 q[2][KB];               // Q rows 16 a + c of its two tiles, columns 32 kb + 8 g ..
 };
 
-template <int DK, int DV, bool L2>
-__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
+template <int DK, int DV, bool L2, bool NORM>
+__global__ __launch_bounds__(NORM ? kScanThreadsNorm : kScanThreads) void chunk_scan_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ state_indices, int num_slots,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ order, int N, int T,
     int Hk, int Hv, int nct, int max_slots, const float* __restrict__ ws_G,
     const __bf16* __restrict__ ws_M, const __bf16* __restrict__ ws_N, float* __restrict__ o,
-    float* final_state) {
+    float* final_state, ScanNorm nrm) {
     constexpr int NS = DV / kWS;  // slices per v-head
     using GM = Geom<DK>;
     constexpr int KB = GM::KB, KR = GM::KR, SP = GM::SP, TPH = GM::TPH, UPH = GM::UPH;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     ScanLds<DK>& sm = *reinterpret_cast<ScanLds<DK>*>(smem_raw);
+    float* const o_ring = reinterpret_cast<float*>(smem_raw + sizeof(ScanLds<DK>));   // NORM: [kORing][kC][kWS]
 
     // blockIdx -> (group, member): a group is one (sequence, q/k head); its members are the
     // (v-head, slice) workgroups that read the same q and k.  All members of a group share
@@ -897,7 +936,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
             // this half's part of Y for chunk ci: -diag(e^G) e^(G_C, ci - 1) K S over its keys,
             // plus V in half 0 (ec = that decay factor)
             auto make_y = [&](int ci, float ec) {
-                const int slot = ci % kRing;
+                const int slot = ci % kRing, vslot = ci % kVRing;
                 lds_u8* kfl[UPH];
 #pragma unroll
                 for (int u = 0; u < UPH; ++u) kfl[u] = lds_at(sm.Kr[slot] + l_kf[u]);
@@ -922,7 +961,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     if constexpr (L2) eg *= ld<f32x4>(gl, 4 * 16 * a + 4 * 2 * kC);      // r_s
                     f32x4 y;
                     if constexpr (hh == 0) {
-                        lds_u8* vl = lds_at(sm.Vr[slot] + l_v);
+                        lds_u8* vl = lds_at(sm.Vr[vslot] + l_v);
                         const bf16x4 vv = read_tr(vl, 2 * 16 * a * kWS);        // V[16 a + 4 g + r][c]
 #pragma unroll
                         for (int r = 0; r < 4; ++r) y[r] = (float)vv[r] - eg[r] * ks[a][r];
@@ -1093,12 +1132,18 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
                     if constexpr (L2) acc *= rq[x];
                     ot[x] = acc;
                 }
-                const size_t tok0 = tok0_of(ci);
-                const int L = len_of(ci);
+                if constexpr (NORM) {      // to the norm wave's ring: row t, channels 4 g ..
+                    lds_u8* orl = lds_at(o_ring + (ci % kORing) * kC * kWS + c * kWS + 4 * g);
 #pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int t = 16 * tiles[x] + c;
-                    if (t < L) *reinterpret_cast<f32x4*>(o + ((tok0 + t) * Hv + h) * DV + c0 + 4 * g) = ot[x];
+                    for (int x = 0; x < 2; ++x) st(orl, 4 * 16 * tiles[x] * kWS, ot[x]);
+                } else {
+                    const size_t tok0 = tok0_of(ci);
+                    const int L = len_of(ci);
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        const int t = 16 * tiles[x] + c;
+                        if (t < L) *reinterpret_cast<f32x4*>(o + ((tok0 + t) * Hv + h) * DV + c0 + 4 * g) = ot[x];
+                    }
                 }
                 lds_barrier();
             };
@@ -1116,6 +1161,127 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
         };
         if (wave == 2) run(std::integral_constant<int, 0>{});
         else run(std::integral_constant<int, 1>{});
+    } else if (wave >= 6) {
+        // ------------------------------------------------ norm waves (fused output norm) ------
+        if constexpr (NORM) {
+            if (nchunks == 0) return;
+            constexpr int kCh = kWS / 2;               // channels per lane
+            const int slice = c0 / kWS;
+            const int t = 32 * (wave - 6) + (lane >> 1);   // this lane's row: token t of the chunk
+            const int ch = kCh * (lane & 1);               // and its channels ch .. ch + 7 of the slice
+            float wv[kCh];
+#pragma unroll
+            for (int j = 0; j < kCh; ++j) wv[j] = nrm.weight[c0 + ch + j];
+            // chunk ci's exchange block: [slice][row] (each slice's 64 sums one contiguous run)
+            auto xblk = [&](int ci) { return nrm.xs + ((size_t)(slot0 + ci) * Hv + h) * NS * kC; };
+            struct NIn {                               // one chunk's inputs, loaded kNormAhead steps ahead
+                float sum[NS];                         // every slice's sum of squares of row t
+                u32x4 z[2];                            // z at row t, the lane's channels (bf16: z[0])
+            };
+            auto load_sums = [&](NIn& f, int d) {
+                float* xb = xblk(d) + t;
+#pragma unroll
+                for (int e = 0; e < NS; ++e)
+                    f.sum[e] = __hip_atomic_load(xb + e * kC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
+            // the same instructions whatever the chunk and z's dtype (bf16 z loads its 16 bytes twice):
+            // every load the compiler waits for then has the same number of later ones behind it
+            auto fetch = [&](NIn& f, int d) {
+                load_sums(f, d);
+                const size_t row = ((tok0_of(d) + min(t, len_of(d) - 1)) * Hv + h) * DV + c0 + ch;
+                const u32x4* zp = nrm.z_bf16
+                                      ? reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(nrm.z) + row)
+                                      : reinterpret_cast<const u32x4*>(static_cast<const float*>(nrm.z) + row);
+                const int zhi = nrm.z_bf16 ? 0 : 1;
+                f.z[0] = zp[0];
+                f.z[1] = zp[zhi];
+            };
+            auto normalize = [&](NIn& f, const float* orow, int d) {
+                if (t >= len_of(d)) return;            // rows past a partial chunk's end
+                auto ready = [&]() {
+                    bool r = true;
+#pragma unroll
+                    for (int e = 0; e < NS; ++e) r = r && !(f.sum[e] < 0.f);
+                    return r;
+                };
+                bool ok = ready();
+                for (int it = 0; !ok && it < kNormSpin; ++it) {    // a slice running behind
+                    __builtin_amdgcn_s_sleep(2);
+                    load_sums(f, d);
+                    ok = ready();
+                }
+                float tot = 0.f;
+#pragma unroll
+                for (int e = 0; e < NS; ++e) tot += f.sum[e];
+                // (a sum that never arrived leaves the row NaN rather than wrong)
+                const float inv = ok ? 1.f / sqrtf(tot / DV + nrm.eps) : __builtin_nanf("");
+                float yv[kCh];
+#pragma unroll
+                for (int j = 0; j < kCh; ++j) {
+                    const unsigned zw = nrm.z_bf16 ? f.z[0][j >> 1] : f.z[j >> 2][j & 3];
+                    const float zf = nrm.z_bf16 ? __uint_as_float((j & 1) ? (zw & 0xffff0000u) : (zw << 16))
+                                                : __uint_as_float(zw);
+                    yv[j] = orow[j] * inv * wv[j] * silu(zf);
+                }
+                const size_t row = ((tok0_of(d) + t) * Hv + h) * DV + c0 + ch;
+                if (nrm.y_bf16) {
+                    *reinterpret_cast<u32x4*>(static_cast<__bf16*>(nrm.y) + row) =
+                        u32x4{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                              pack_bf16x2(yv[6], yv[7])};
+                } else {
+                    f32x4* yp = reinterpret_cast<f32x4*>(static_cast<float*>(nrm.y) + row);
+                    yp[0] = f32x4{yv[0], yv[1], yv[2], yv[3]};
+                    yp[1] = f32x4{yv[4], yv[5], yv[6], yv[7]};
+                }
+            };
+            // this lane's part of its row in the last kNormLag chunks (chunk p in orow[p % kNormLag])
+            // and the loaded inputs of the next kNormAhead chunks to normalise (chunk d in
+            // nin[d % kNormAhead])
+            float orow[kNormLag][kCh];
+            NIn nin[kNormAhead];
+            // step s (the other roles' step s while they run): normalise chunk d = s - 2 - kNormLag,
+            // take chunk s - 2's rows (they landed in step s - 1) into the slot d leaves and publish
+            // their sums, load the inputs of chunk d + kNormAhead into the slot d leaves
+            auto nstep = [&](int s, auto ic) {
+                constexpr int i = decltype(ic)::value;              // s % kPeriod
+                constexpr int os = ((i - 2) % kNormLag + kNormLag) % kNormLag;
+                constexpr int ns = ((i - 2 - kNormLag) % kNormAhead + kNormAhead) % kNormAhead;
+                const int d = s - 2 - kNormLag, p = s - 2;
+                if (d >= 0 && d < nchunks) normalize(nin[ns], orow[os], d);
+                if (p >= 0 && p < nchunks) {
+                    lds_u8* orl = lds_at(o_ring + (p % kORing) * kC * kWS + t * kWS + ch);
+                    float ss = 0.f;
+#pragma unroll
+                    for (int j4 = 0; j4 < 2; ++j4) {
+                        const f32x4 x = ld<f32x4>(orl, 16 * j4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            orow[os][4 * j4 + e] = x[e];
+                            ss += x[e] * x[e];
+                        }
+                    }
+                    ss += __shfl_xor(ss, 1);                // the row's other 8 channels
+                    // (both lanes of the row store the same value)
+                    __hip_atomic_store(xblk(p) + slice * kC + t, ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                fetch(nin[ns], min(max(d + kNormAhead, 0), nchunks - 1));   // unconditional: see fetch
+                if (s <= nchunks) lds_barrier();
+            };
+            lds_barrier();  // P
+            lds_barrier();  // B0
+            constexpr int kPeriod = 4;                // slot patterns repeat every kPeriod steps
+            static_assert(kPeriod % kNormLag == 0 && kPeriod % kNormAhead == 0, "slot period");
+            const int last = nchunks + 1 + kNormLag;  // the step that normalises the last chunk
+            // (whole periods, up to kPeriod - 1 idle steps past `last`: every step of an iteration
+            // then runs, so the loads the compiler waits for always have the same ones behind them)
+            for (int s = 0; s <= last; s += kPeriod) {
+                using std::integral_constant;
+                nstep(s, integral_constant<int, 0>{});
+                nstep(s + 1, integral_constant<int, 1>{});
+                nstep(s + 2, integral_constant<int, 2>{});
+                nstep(s + 3, integral_constant<int, 3>{});
+            }
+        }
     } else {
         // ------------------------------------------------ staging wave ------------------------
         if (nchunks == 0) return;
@@ -1137,7 +1303,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) voff[jj] = 2u * ((uint32_t)(32 * jj + (lane >> 1)) * Hv * DV + 8 * (lane & 1));
         auto dma = [&](int ci) {
-            const int slot = ci % kRing;
+            const int slot = ci % kRing, vslot = ci % kVRing;
             const size_t tok0 = tok0_of(ci);
             const int L = len_of(ci);
             const __bf16* kb = k + (tok0 * Hk + kh) * DK;
@@ -1148,7 +1314,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
                 for (int ii = 0; ii < KDma; ++ii) copy_to_lds(kbc + koff[ii], sm.Kr[slot] + 512 * ii);
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) copy_to_lds(vbc + voff[jj], sm.Vr[slot] + 512 * jj);
+                for (int jj = 0; jj < 2; ++jj) copy_to_lds(vbc + voff[jj], sm.Vr[vslot] + 512 * jj);
             } else {
 #pragma unroll
                 for (int ii = 0; ii < KDma; ++ii)
@@ -1156,7 +1322,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)          // rows 32 jj + lane / 2, columns 8 (lane % 2)
                     copy_to_lds(vb + (size_t)min(32 * jj + (lane >> 1), L - 1) * Hv * DV + 8 * (lane & 1),
-                                sm.Vr[slot] + 512 * jj);
+                                sm.Vr[vslot] + 512 * jj);
             }
             const float* gb = ws_G + ((size_t)(slot0 + ci) * Hv + h) * kGRows * kC;
             if constexpr (L2) {
@@ -1278,16 +1444,17 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(
 
 // ------------------------------------------------------------------------------------------------
 // workspace layout (each region 256-byte aligned):
-//   chunk_start [N+1] int32 | order [N] int32 | gates [slots][Hv][G2, 2^G2, 2^(G2_C - G2), r][64] f32
-//   | M [slots][Hv][12 fragments] bf16 | N [slots][Hk][16 fragments] bf16
+//   chunk_start [N+1] int32 | order [N] int32 | gates [slots][Hv][kGRows][64] f32
+//   | M [slots][Hv][6 fragments] fp16 | N [slots][Hk][8 fragments] fp16
+//   | with the fused norm: sums of squares [slots][Hv][dv / 16][64] f32
 struct Layout {
-    size_t chunk_start, order, G, M, Nm, total;
+    size_t chunk_start, order, G, M, Nm, X, total;
     int slots;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout layout(int B, int T, int Hk, int Hv, int N) {
+Layout layout(int B, int T, int Hk, int Hv, int N, int dv = 0, bool norm = false) {
     Layout l;
     l.slots = (int)(((long long)B * T) / kC) + N;  // bounds B*ceil(T/64) and T/64 + N (packed)
     size_t off = 0;
@@ -1296,13 +1463,15 @@ Layout layout(int B, int T, int Hk, int Hv, int N) {
     l.G = off;           off = align256(off + sizeof(float) * (size_t)l.slots * Hv * kGRows * kC);
     l.M = off;           off = align256(off + 2 * (size_t)l.slots * Hv * kMFrags * kFragElems);
     l.Nm = off;          off = align256(off + 2 * (size_t)l.slots * Hk * kNFrags * kFragElems);
+    l.X = off;           off = norm ? align256(off + sizeof(float) * (size_t)l.slots * Hv * kC * (dv / kWS)) : off;
     l.total = off;
     return l;
 }
 
 template <int DK, int DV, typename TG, bool L2>
 hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
-    const Layout lay = layout(a.B, a.T, a.Hk, a.Hv, a.N);
+    const bool norm = a.z != nullptr;
+    const Layout lay = layout(a.B, a.T, a.Hk, a.Hv, a.N, DV, norm);
     char* ws = static_cast<char*>(a.workspace);
     const bool packed = a.cu_seqlens != nullptr;
     const int nct = (a.T + kC - 1) / kC;
@@ -1312,6 +1481,7 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
     float* ws_G = reinterpret_cast<float*>(ws + lay.G);
     __bf16* ws_M = reinterpret_cast<__bf16*>(ws + lay.M);
     __bf16* ws_N = reinterpret_cast<__bf16*>(ws + lay.Nm);
+    float* ws_X = norm ? reinterpret_cast<float*>(ws + lay.X) : nullptr;
     hipError_t e;
     if ((stages & kStagePrepare) && packed) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, a.stream, a.cu_seqlens, a.N,
@@ -1325,24 +1495,25 @@ hipError_t launch_dv(const ChunkArgs& a, unsigned stages) {
                            static_cast<const __bf16*>(a.k),
                            static_cast<const TG*>(a.g), static_cast<const TG*>(a.beta), a.A_log,
                            a.dt_bias, a.cu_seqlens, chunk_start, a.N, a.T, a.Hk, a.Hv, nct, ws_G, ws_M,
-                           ws_N);
+                           ws_N, ws_X, kC * (DV / kWS));
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (!(stages & kStageScan)) return hipSuccess;
-    const auto kern = chunk_scan_kernel<DK, DV, L2>;
-    const size_t bytes = sizeof(ScanLds<DK>);
+    const auto kern = norm ? chunk_scan_kernel<DK, DV, L2, true> : chunk_scan_kernel<DK, DV, L2, false>;
+    const size_t bytes = scan_lds_bytes<DK>(norm);
+    const ScanNorm nrm{a.z, a.norm_weight, a.eps, a.z_dtype == GDN_BF16, a.y_dtype == GDN_BF16, ws_X, a.y};
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)) != hipSuccess)
         return e;
     const int groups = a.N * a.Hk;                        // (sequence, q/k head)
     const int members = (a.Hv / a.Hk) * (DV / kWS);
     const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * members);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kScanThreads), bytes,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(norm ? kScanThreadsNorm : kScanThreads), bytes,
                        a.stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), a.initial_state, a.cu_seqlens,
                        a.state_indices, a.num_slots, chunk_start,
                        order, a.N, a.T, a.Hk, a.Hv, nct, packed ? lay.slots : a.B * nct, ws_G, ws_M,
-                       ws_N, a.o, a.final_state);
+                       ws_N, a.o, a.final_state, nrm);
     return hipGetLastError();
 }
 
@@ -1352,10 +1523,9 @@ bool chunk_mfma_supported(int dk, int dv, gdn_dtype qkv_dtype) {
     return qkv_dtype == GDN_BF16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
 }
 
-size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N) {
+size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N, bool norm) {
     (void)dk;
-    (void)dv;
-    return layout(B, T, Hk, Hv, N).total;
+    return layout(B, T, Hk, Hv, N, dv, norm).total;
 }
 
 template <int DK, bool L2>

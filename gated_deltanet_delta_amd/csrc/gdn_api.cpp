@@ -15,6 +15,8 @@ bool aligned16(const void* p) { return aligned(p, 16); }
 
 size_t dtype_bytes(gdn_dtype t) { return t == GDN_BF16 ? 2 : 4; }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 bool dtype_ok(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
@@ -55,9 +57,27 @@ size_t gdn_chunk_fwd_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv
     return gdn::chunk_mfma_workspace_size(B, T, Hk, Hv, dk, dv, N);
 }
 
+size_t gdn_chunk_fwd_gated_norm_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                               gdn_dtype qkv_dtype) {
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return 0;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || !dtype_ok(qkv_dtype)) return 0;
+    if (!sizes_fit(B, T, Hv, dv > dk ? dv : dk) || !sizes_fit(N, 1, Hv, (long long)dk * dv)) return 0;
+    if (use_mfma(dk, dv, qkv_dtype)) return gdn::chunk_mfma_workspace_size(B, T, Hk, Hv, dk, dv, N, true);
+    return align256((size_t)B * T * Hv * dv * sizeof(float));   // o, between the two passes
+}
+
 }  // extern "C"
 
 namespace {
+
+// The gated output norm of gdn_chunk_fwd_gated_norm (null for the plain calls).
+struct FusedNorm {
+    const void* z;
+    const float* weight;
+    float eps;
+    gdn_dtype z_dtype, y_dtype;
+    void* y;
+};
 
 // Shared body of gdn_chunk_fwd and its two halves: checks, then the selected stages.
 // With A_log set, g and beta carry the raw projections a and b and the kernels form the gates.
@@ -67,9 +87,16 @@ gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g
                       int num_slots, const float* initial_state, const int32_t* cu_seqlens, int B, int T, int Hk,
                       int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
                       float* o, float* final_state, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream, unsigned stages, int qk_l2norm = 0) {
+                      hipStream_t stream, unsigned stages, int qk_l2norm = 0,
+                      const FusedNorm* fn = nullptr) {
     if (!final_state) return GDN_ERROR_INVALID_VALUE;
-    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERROR_INVALID_VALUE;
+    if (T > 0 && (!q || !k || !v || !g || !beta || (!fn && !o))) return GDN_ERROR_INVALID_VALUE;
+    if (fn) {
+        if (!dtype_ok(fn->z_dtype) || !dtype_ok(fn->y_dtype)) return GDN_ERROR_INVALID_VALUE;
+        if (!(fn->eps >= 0.f) || fn->eps > 3.0e38f) return GDN_ERROR_INVALID_VALUE;   // also NaN
+        if (T > 0 && (!fn->z || !fn->weight || !fn->y)) return GDN_ERROR_INVALID_VALUE;
+        if (!aligned16(fn->z) || !aligned16(fn->weight) || !aligned16(fn->y)) return GDN_ERROR_INVALID_VALUE;
+    }
     if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || N < 1 || Hv % Hk != 0) return GDN_ERROR_INVALID_VALUE;
     if (!dtype_ok(qkv_dtype) || !dtype_ok(gate_dtype)) return GDN_ERROR_INVALID_VALUE;
     if (cu_seqlens ? B != 1 : N != B) return GDN_ERROR_INVALID_VALUE;
@@ -87,15 +114,33 @@ gdn_status chunk_call(const void* q, const void* k, const void* v, const void* g
         return GDN_ERROR_INVALID_VALUE;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return GDN_ERROR_NOT_SUPPORTED;
 
-    const gdn::ChunkArgs a{q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens,
-                           state_indices, num_slots, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, o,
-                           final_state, workspace, workspace_bytes, stream, qk_l2norm};
+    gdn::ChunkArgs a{q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens,
+                     state_indices, num_slots, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, o,
+                     final_state, workspace, workspace_bytes, stream, qk_l2norm};
+    const size_t need = fn ? gdn_chunk_fwd_gated_norm_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype)
+                           : gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+        return GDN_ERROR_WORKSPACE;
     hipError_t e;
     if (use_mfma(dk, dv, qkv_dtype)) {
-        const size_t need = gdn_chunk_fwd_workspace_size(B, T, Hk, Hv, dk, dv, N, qkv_dtype);
-        if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
-            return GDN_ERROR_WORKSPACE;
+        if (fn) {
+            a.o = nullptr;
+            a.z = fn->z;
+            a.norm_weight = fn->weight;
+            a.eps = fn->eps;
+            a.z_dtype = fn->z_dtype;
+            a.y_dtype = fn->y_dtype;
+            a.y = fn->y;
+        }
         e = gdn::launch_chunk_mfma(a, stages);
+    } else if (fn) {        // fp32 inputs: the prefill's o into the workspace, then the norm over it
+        a.o = static_cast<float*>(workspace);
+        e = gdn::launch_chunk_f32(a);
+        if (e == hipSuccess && (long long)B * T > 0) {
+            const gdn::NormArgs na{a.o, fn->z, fn->weight, fn->eps, (long long)B * T * Hv, dv, fn->z_dtype,
+                                   fn->y_dtype, fn->y, stream};
+            e = gdn::launch_gated_rmsnorm(na);
+        }
     } else {
         e = (stages & gdn::kStageScan) ? gdn::launch_chunk_f32(a) : hipSuccess;
     }
@@ -281,6 +326,23 @@ gdn_status gdn_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
                       cu_seqlens, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, o, final_state,
                       workspace, workspace_bytes, stream, gdn::kStagePrepare | gdn::kStageScan,
                       (flags & GDN_FLAG_QK_L2NORM) ? 1 : 0);
+}
+
+gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v, const void* g,
+                                    const void* beta, const float* A_log, const float* dt_bias,
+                                    const float* initial_state, float* final_state,
+                                    const int32_t* state_indices, int num_slots, const int32_t* cu_seqlens,
+                                    const void* z, const float* weight, float eps, int B, int T, int Hk,
+                                    int Hv, int dk, int dv, int N, gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                                    gdn_dtype z_dtype, gdn_dtype y_dtype, unsigned flags, void* y,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if ((flags & ~GDN_FLAG_QK_L2NORM) || (dt_bias && !A_log)) return GDN_ERROR_INVALID_VALUE;
+    if (state_indices && initial_state != final_state) return GDN_ERROR_INVALID_VALUE;
+    const FusedNorm fn{z, weight, eps, z_dtype, y_dtype, y};
+    return chunk_call(q, k, v, g, beta, A_log, dt_bias, state_indices, num_slots, initial_state,
+                      cu_seqlens, B, T, Hk, Hv, dk, dv, N, qkv_dtype, gate_dtype, nullptr, final_state,
+                      workspace, workspace_bytes, stream, gdn::kStagePrepare | gdn::kStageScan,
+                      (flags & GDN_FLAG_QK_L2NORM) ? 1 : 0, &fn);
 }
 
 gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v, const void* g,

@@ -27,6 +27,13 @@ struct ChunkArgs {
     size_t workspace_bytes;
     hipStream_t stream;
     int qk_l2norm;                 // q, k normalised to unit length inside the kernels
+    // the gated output norm fused onto o (z set): y = o / sqrt(mean(o^2) + eps) * norm_weight *
+    // silu(z) per (token, v-head) row takes o's place (o is then unused)
+    const void* z = nullptr;       // [B, T, Hv, dv] z_dtype
+    const float* norm_weight = nullptr;   // [dv]
+    float eps = 0.f;
+    gdn_dtype z_dtype = GDN_BF16, y_dtype = GDN_BF16;
+    void* y = nullptr;             // [B, T, Hv, dv] y_dtype
 };
 
 struct RecurrentArgs {
@@ -131,7 +138,7 @@ hipError_t launch_chunk_f32(const ChunkArgs& a);
 
 // Chunked kernels on bf16 matrix cores (bf16 inputs).
 bool chunk_mfma_supported(int dk, int dv, gdn_dtype qkv_dtype);
-size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N);
+size_t chunk_mfma_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N, bool norm = false);
 // Stages of a chunked call: prepare (every chunk in parallel: log-decay sums and the per-chunk
 // triangular solve, into the workspace) and scan (the chunks in order).  A full call runs both.
 constexpr unsigned kStagePrepare = 1u, kStageScan = 2u;

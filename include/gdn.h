@@ -310,6 +310,48 @@ gdn_status gdn_recurrent_step_ex(const void* q, const void* k, const void* v,
                                  float* o, hipStream_t stream);
 
 /*
+ * gdn_chunk_fwd_gated_norm -- the chunked prefill with the layer's gated output norm fused onto o.
+ *
+ * The Qwen3.5 Gated DeltaNet page (wanger-sjtu.github.io, flowchart nodes "AttnOut -> Norm",
+ * "Z -> Norm" and section "Output and gated RMSNorm") feeds the rule's output straight into the
+ * gated RMSNorm.  This call computes o as gdn_chunk_fwd_ex does (same options and flags) and, per
+ * (token, v-head) row of dv channels, writes
+ *     y = o / sqrt(mean(o^2) + eps) * weight * silu(z),     silu(z) = z / (1 + exp(-z)),
+ * (gdn_gated_rmsnorm's formula, fp32 arithmetic) in place of o: o itself never reaches memory.
+ *
+ *   z       [B, T, Hv, dv] z_dtype (device), 16-byte aligned
+ *   weight  [dv] fp32 (device), 16-byte aligned
+ *   eps     >= 0 and finite
+ *   y       [B, T, Hv, dv] y_dtype (device), 16-byte aligned; must not overlap any input
+ * Everything else -- q, k, v, the gates (g, beta or the raw a, b with A_log and dt_bias), states,
+ * state_indices, cu_seqlens, flags -- as in gdn_chunk_fwd_ex.
+ * Workspace: gdn_chunk_fwd_gated_norm_workspace_size bytes, 256-byte aligned (0 only for rejected
+ * sizes).  With bf16 q, k, v it holds gdn_chunk_fwd's scratch plus each row's sums of squares per
+ * 16-channel slice; with fp32 inputs it holds o between the prefill and a separate norm pass.
+ * Scheduling (bf16 inputs): the dv / 16 workgroups of one (sequence, v-head) trade their slices'
+ * sums of squares while they run, so they must be able to run at the same time; the GPU dispatches
+ * them close together, and on an otherwise busy GPU a workgroup that waits about a second for a
+ * partner's sums gives up and writes NaN rows rather than hang.
+ * Errors: those of gdn_chunk_fwd_ex, and GDN_ERROR_INVALID_VALUE for a null z, weight or y (T > 0),
+ * a bad eps, dtype or alignment.
+ */
+size_t gdn_chunk_fwd_gated_norm_workspace_size(int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                               gdn_dtype qkv_dtype);
+gdn_status gdn_chunk_fwd_gated_norm(const void* q, const void* k, const void* v,
+                                    const void* g, const void* beta,
+                                    const float* A_log, const float* dt_bias,
+                                    const float* initial_state, float* final_state,
+                                    const int32_t* state_indices, int num_slots,
+                                    const int32_t* cu_seqlens,
+                                    const void* z, const float* weight, float eps,
+                                    int B, int T, int Hk, int Hv, int dk, int dv, int N,
+                                    gdn_dtype qkv_dtype, gdn_dtype gate_dtype,
+                                    gdn_dtype z_dtype, gdn_dtype y_dtype, unsigned flags,
+                                    void* y,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
  * gdn_chunk_bwd -- the backward pass of gdn_chunk_fwd, for training: the gradients of a scalar loss
  * with respect to q, k, v, g, beta and the initial state, given its gradients d_o with respect to
  * o and d_final with respect to the final state.

@@ -221,6 +221,44 @@ def test_ex_chunk_pool_must_be_both_states(lib):
     assert chunk_ex(lib, idx=P, num_slots=4, s0=None, fs=P) == INVALID
 
 
+def fused(lib, z=P, w=P, eps=1e-6, y=P, zt=BF16, yt=BF16, A_log=None, dt_bias=None, s0=None, fs=P,
+          idx=None, num_slots=0, flags=0, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=None, B=1, T=64, Hk=1, Hv=1, dk=64, dv=64, N=1, qkv=BF16,
+             gate=F32, ws=P, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.gdn_chunk_fwd_gated_norm(a["q"], a["k"], a["v"], a["g"], a["beta"], A_log, dt_bias, s0, fs,
+                                        idx, num_slots, a["cu"], z, w, ctypes.c_float(eps), a["B"], a["T"],
+                                        a["Hk"], a["Hv"], a["dk"], a["dv"], a["N"], a["qkv"], a["gate"], zt,
+                                        yt, flags, y, a["ws"], ctypes.c_size_t(a["ws_bytes"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(zt=5), INVALID), (dict(yt=7), INVALID),
+    (dict(z=P + 8), INVALID), (dict(y=P + 4), INVALID), (dict(w=P + 4), INVALID),   # 16-byte alignment
+    (dict(flags=2), INVALID), (dict(dt_bias=P), INVALID), (dict(q=None), INVALID),
+    (dict(idx=P, num_slots=4, s0=P, fs=P + 256), INVALID),                          # pool: one tensor
+    (dict(dk=96), UNSUPPORTED), (dict(dv=32), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=P + 16), WORKSPACE),
+    (dict(qkv=F32, ws=None), WORKSPACE),                                             # fp32: o needs room
+])
+def test_fused_norm_rejects(lib, kw, status):
+    assert fused(lib, **kw) == status
+
+
+def test_fused_norm_workspace_sizes(lib):
+    size = lib.gdn_chunk_fwd_gated_norm_workspace_size
+    plain = lib.gdn_chunk_fwd_workspace_size
+    for dk, dv in ((128, 128), (64, 64), (128, 64)):
+        # bf16: the prefill's scratch plus one fp32 sum of squares per row and 16-channel slice
+        extra = size(1, 4096, 16, 32, dk, dv, 1, BF16) - plain(1, 4096, 16, 32, dk, dv, 1, BF16)
+        assert extra == (4096 // 64 + 1) * 32 * 64 * (dv // 16) * 4, (dk, dv, extra)
+    # fp32: o between the prefill and the norm pass
+    assert size(2, 100, 2, 4, 128, 64, 2, F32) == (2 * 100 * 4 * 64 * 4 + 255) // 256 * 256
+    assert size(0, 100, 2, 4, 128, 64, 2, F32) == 0 and size(1, 100, 2, 4, 96, 64, 1, BF16) == 0
+
+
 def bwd(lib, q=P, k=P, v=P, g=P, beta=P, s0=None, cu=None, do=P, dfin=None, B=1, T=64, Hk=1, Hv=1,
         dk=64, dv=64, N=1, qkv=F32, gate=F32, dq=P, dkk=P, dvv=P, dg=P, db=P, ds0=None, ws=P,
         ws_bytes=1 << 40):

@@ -1,4 +1,4 @@
-"""Writes stay inside the memory a call owns.
+"""Writes stay inside the memory a call owns (every entry point, the fused-norm prefill included).
 
 Every output, state and workspace of a call is carved out of one device arena, each region between
 bands of a fixed NaN bit pattern that no kernel produces.  After each call every band (and the
@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 import torch
 
-from gated_deltanet_delta_amd import (_lib, gdn_causal_conv1d, gdn_chunk_fwd, gdn_gated_rmsnorm,
-                                      gdn_recurrent_step, synth, workspace_size)
+from gated_deltanet_delta_amd import (_lib, gdn_causal_conv1d, gdn_chunk_fwd, gdn_chunk_fwd_gated_norm,
+                                      gdn_gated_rmsnorm, gdn_recurrent_step, synth, workspace_size)
 from helpers import assert_close, oracle_of, to_gpu, tol_for
 
 pytestmark = pytest.mark.gpu
@@ -99,6 +99,28 @@ def test_guard_bands_and_earlier_outputs_survive_every_entry_point():
     assert_close("packed final_state", ar1["fs"], so, tol_for(wl.dtype))
     remember("packed prefill o", ar1["o"])
     remember("packed prefill final state", ar1["fs"])
+
+    # 1b. the prefill with the gated norm fused onto o, on the same inputs: y, final state and its
+    #     (larger) workspace in one arena; equal to the same call with ordinary buffers, bit for bit
+    zr = np.random.default_rng(308)
+    zf = torch.from_numpy(zr.standard_normal((B, TT, wl.Hv, wl.dv), dtype=np.float32)).to(torch.bfloat16).cuda()
+    wf = torch.from_numpy(zr.uniform(0.5, 1.5, wl.dv).astype(np.float32)).cuda()
+    fws = int(_lib.load().gdn_chunk_fwd_gated_norm_workspace_size(B, TT, wl.Hk, wl.Hv, wl.dk, wl.dv, N,
+                                                                   _lib.GDN_BF16))
+    arf = Arena([("y", (B, TT, wl.Hv, wl.dv), torch.bfloat16), ("fs", (N, wl.Hv, wl.dk, wl.dv), torch.float32),
+                 ws_region(fws)])
+    gdn_chunk_fwd_gated_norm(d["q"], d["k"], d["v"], d["g"], d["beta"], zf, wf, 1e-6,
+                             initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"], y=arf["y"],
+                             final_state=arf["fs"], workspace=arf["ws"])
+    arf.check("gdn_chunk_fwd_gated_norm")
+    ar1.check("gdn_chunk_fwd_gated_norm (earlier arena)")
+    recheck("gdn_chunk_fwd_gated_norm")
+    y_ref, s_ref2 = gdn_chunk_fwd_gated_norm(d["q"], d["k"], d["v"], d["g"], d["beta"], zf, wf, 1e-6,
+                                             initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(arf["y"], y_ref) and torch.equal(arf["fs"], s_ref2)
+    assert torch.equal(arf["fs"], ar1["fs"])
+    remember("fused norm y", arf["y"])
 
     # 2. a longer single sequence with a carried state, then a shorter one through the same call
     for T, seed in ((1000, 302), (130, 303)):
