@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
     python bench.py --copy-calibration      (a plain 256 MiB device copy, for HBM counter scaling)
     python bench.py --prefill-only          (the headline prefill and its halves only, for profilers)
+    python bench.py --fused-norm-only       (the prefill with the gated norm fused onto o, for profilers)
 
 Prints ONE JSON line.  The timed step is one gdn_chunk_fwd call over the Qwen3-Next-shaped prefill
 workload (B=1, T=4096, 16 q/k heads, 32 v heads, head dim 128, bf16 inputs, fp32 state and output),
@@ -55,8 +56,12 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
 COUNTERS = {
-    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": None,
-             "traffic": None, "mfma_exec_flops": None},
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "355bb05037670102",
+             "traffic": 160426582, "mfma_exec_flops": (80740352 + 7274496) * 512},
+    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "355bb05037670102",
+              "traffic": 43573030},
+    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "355bb05037670102",
+                  "traffic": 169139939, "prepare_traffic": 47767334},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},
     "conv": {"source": "gated_deltanet_delta_amd/csrc/conv1d.hip", "sha16": "592040b86d906439",
@@ -110,6 +115,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the headline prefill and its two halves (for profiler runs)")
+    ap.add_argument("--fused-norm-only", action="store_true",
+                    help="only the prefill with the gated norm fused onto o, on the same inputs (profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (HBM counter scaling)")
     args = ap.parse_args()
@@ -225,6 +232,27 @@ def main() -> int:
 
     ms_prepare = time_stage("prepare")
     ms_scan = time_stage("scan")
+    if args.fused_norm_only:
+        zr0 = np.random.default_rng(99).standard_normal((B, T, wl.Hv, wl.dv), dtype=np.float32)
+        zs = [torch.from_numpy(zr0).to(torch.bfloat16).to(dev) for _ in range(NSETS)]
+        ys = [torch.empty((B, T, wl.Hv, wl.dv), dtype=torch.bfloat16, device=dev) for _ in range(NSETS)]
+        w1 = torch.ones(wl.dv, dtype=torch.float32, device=dev)
+        fws_ = torch.empty(int(_lib.load().gdn_chunk_fwd_gated_norm_workspace_size(
+            B, T, wl.Hk, wl.Hv, wl.dk, wl.dv, N, _lib.GDN_BF16)), dtype=torch.uint8, device=dev)
+
+        def fused_only(i):
+            s_ = sets[i % NSETS]
+            gdn_chunk_fwd_gated_norm(s_["q"], s_["k"], s_["v"], s_["g"], s_["beta"], zs[i % NSETS], w1, 1e-6,
+                                     initial_state=s_["initial_state"], y=ys[i % NSETS], final_state=s_["fs"],
+                                     workspace=fws_)
+
+        for i in range(max(args.warmup, 20)):
+            fused_only(i)
+        ms_f = time_loop(fused_only)
+        print(json.dumps({"workload": "prefill B=1 T=4096 Hk=16 Hv=32 dk=dv=128 bf16 in, gated norm fused "
+                                      "(bf16 z, y)", "ms_per_call_events": round(ms_f, 5),
+                          "tokens_per_s": round(tokens / (ms_f / 1e3), 1)}), flush=True)
+        return 0
     if args.prefill_only:
         print(json.dumps({"workload": "prefill B=1 T=4096 Hk=16 Hv=32 dk=dv=128 bf16 in",
                           "tokens_per_s": round(tokens / (ms_wall / 1e3), 1), "ms_per_call_wall": round(ms_wall, 5),
@@ -261,6 +289,8 @@ def main() -> int:
     scan_useful_tflops = flops / (ms_scan / 1e3) / 1e12
     scan_traffic = counter("scan", "traffic")
     scan_exec = counter("scan", "mfma_exec_flops")
+    prep_traffic = counter("solve", "traffic")
+    call_traffic = None if scan_traffic is None or prep_traffic is None else scan_traffic + prep_traffic
 
     # ---------------- ceilings measured on this GPU in the same run ----------------------------
     # bf16 GEMM through torch.matmul (the vendor library), 8192^3, and a plain 1 GiB device copy
@@ -617,6 +647,11 @@ def main() -> int:
                      "frac_of_measured_gemm": round(scan_useful_tflops / ceilings["bf16_gemm_tflops"], 4),
                      "hbm_frac_of_measured_copy": round(achieved_gbs / ceilings["copy_gbs"], 4),
                      "prepare_ms_per_launch_events": round(ms_prepare, 5),
+                     "prepare_traffic": prep_traffic,
+                     "call_traffic": call_traffic,
+                     "call_algorithmic_bytes": int(nbytes),
+                     "call_traffic_vs_algorithmic": (None if call_traffic is None else
+                                                     round(call_traffic / nbytes, 3)),
                      "call_ms_per_launch_events": round(ms_events, 5),
                      "call_ms_same_buffers_events": round(ms_same_buffers, 5),
                      "call_achieved_gbs": round(nbytes / (ms_events / 1e3) / 1e9, 1),
@@ -646,6 +681,10 @@ def main() -> int:
                                "ms_per_call_events": round(ms_fused_norm, 5),
                                "tokens_per_s": round(tokens / (ms_fused_norm / 1e3), 1),
                                "ms_prefill_then_norm_events": round(ms_prefill_norm, 5),
+                               "traffic": (None if counter("scan_norm", "traffic") is None else
+                                           counter("scan_norm", "traffic") + counter("scan_norm", "prepare_traffic")),
+                               "traffic_prefill_then_norm": (None if call_traffic is None or counter("norm", "traffic") is None
+                                                             else call_traffic + counter("norm", "traffic")),
                                "speedup_vs_prefill_then_norm": round(ms_prefill_norm / ms_fused_norm, 3)},
         "gated_rmsnorm": {"call": "gdn_gated_rmsnorm on the prefill's o (fp32 in, bf16 z and out)",
                           "rows": o.numel() // wl.dv, "d": wl.dv,
