@@ -304,7 +304,11 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     L& sm = *reinterpret_cast<L*>(smem_raw);
 
     const int slices = dv / kW;
-    int unit = blockIdx.x;
+    // Workgroups go to the XCDs round robin by index (i on XCD i % 8).  Units are dealt so that each
+    // XCD gets one contiguous run of them: the slices of one v-head, which all read that v-head's
+    // T and P, then share an L2.
+    const int nwg = gridDim.x, xcd = blockIdx.x % 8, per = nwg / 8, extra = nwg % 8;
+    int unit = xcd * per + min(xcd, extra) + blockIdx.x / 8;
     const int sl = unit % slices;
     unit /= slices;
     const int h = unit % Hv, n = unit / Hv;

@@ -126,6 +126,22 @@ def test_fused_norm_packed_ragged(dk, dv):
     check_oracle(f"packed dk={dk} dv={dv}", y, o_ref, z, w, tol_for(wl.dtype), torch.bfloat16)
 
 
+def test_fused_norm_many_packed_sequences():
+    """More workgroups than the GPU holds at once (40 packed sequences at the Qwen3-Next head
+    layout: 10,240 scan workgroups): the slices of a v-head still find each other's sums."""
+    wl = WL["varlen"]
+    rng = np.random.default_rng(550)
+    lengths = rng.integers(300, 2000, size=40)
+    lengths[7] = 0
+    lengths[19] = 1
+    x = synth.make(wl, lengths=lengths, seed=551)
+    z, w = norm_inputs((1, int(lengths.sum()), wl.Hv, wl.dv), torch.bfloat16, 552)
+    y, o, _ = run(x, z, w)
+    check_fusion("40 packed sequences", y, o, z, w, torch.bfloat16)
+    o_ref, _ = oracle_of(x)
+    check_oracle("40 packed sequences", y, o_ref, z, w, tol_for(wl.dtype), torch.bfloat16)
+
+
 @pytest.mark.parametrize("z_dtype,y_dtype", [(torch.float32, torch.float32), (torch.bfloat16, torch.float32),
                                              (torch.float32, torch.bfloat16)])
 def test_fused_norm_every_option(z_dtype, y_dtype):
