@@ -726,7 +726,9 @@ def main() -> int:
                    "roofline": {"bound": "hbm", "achieved": round(total_gbs, 1), "peak": MI355X_HBM_GBS,
                                 "unit": "GB/s", "frac": round(total_gbs / MI355X_HBM_GBS, 4),
                                 "traffic": counter("decode", "traffic"), "kernel": "recurrent_kernel<128,128,bf16,f32>",
-                                "algorithmic_bytes_per_launch": int(total_bytes)},
+                                "algorithmic_bytes_per_launch": int(total_bytes),
+                                "frac_of_measured_copy": round(total_gbs / ceilings["copy_gbs"], 4),
+                                "state_frac_of_measured_copy": round(state_gbs / ceilings["copy_gbs"], 4)},
                    "gating": {"call": "gdn_recurrent_step_gating (gates formed in the kernel from a, b)",
                               "ms_per_step": round(ms_decode_gating, 5),
                               "state_gbs": round(state_bytes / (ms_decode_gating / 1e3) / 1e9, 1)}},
