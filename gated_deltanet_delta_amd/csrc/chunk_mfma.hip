@@ -163,7 +163,7 @@ __device__ __forceinline__ bf16x4 read_tr(lds_u8* b, int off) {
 // Fragment layouts shared by the solve kernel (writer) and the scan kernel (reader).
 //
 // A "fragment" is the A operand of one v_mfma_f32_16x16x32 (bf16 or fp16) as the 64 lanes hold it: lane
-// (g, c) has eight bf16 values, 16 bytes; a fragment is stored as 64 x 16 = 1 KiB with lane l at
+// (g, c) has eight 16-bit values, 16 bytes; a fragment is stored as 64 x 16 = 1 KiB with lane l at
 // byte 16 l, so that one wave loads it with one fully coalesced instruction.
 //
 // The B operands these fragments meet in the scan kernel are accumulator tiles fed straight back:
@@ -221,7 +221,7 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
 // Writes, per (chunk, v-head), the chunk's gate block [5][64] floats: G2 = running sum of
 // g log2(e), 2^G2, 2^(G2_C - G2) (G2_C = G2 at the chunk's last row; padding rows past the
 // chunk's length have g = 0) and, with L2, the key and query scales r_t = 1 / |k_t| and
-// rq_t = 1 / |q_t| (rows 3 and 4); and M = T diag(beta) as the 12 fragments described above (zero
+// rq_t = 1 / |q_t| (rows 3 and 4); and M = T diag(beta) as the 6 fp16 fragments described above (zero
 // above the diagonal and in rows/columns past the chunk's length).  Per (chunk, q/k head) it writes
 // N = K K_p^T for the scan kernel's K S recurrence.
 //
@@ -507,8 +507,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
             lds_barrier();
         }
 
-        // M = T diag(beta) as its 12 fragments: item e = (pair p, lane ln) writes the hi and lo
-        // fragment rows of that lane, one 1 KiB fragment per wave and pass
+        // M = T diag(beta) as its 6 fp16 fragments: item e = (pair p, lane ln) writes that lane's
+        // eight values of the pair's fragment, one 1 KiB fragment per wave and pass
         __bf16* Mb = ws_M + ((size_t)slot * Hv + h) * kMFrags * kFragElems;
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
@@ -579,8 +579,9 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
 //                    O^T = S^T Q^T diag(e^G) + U^T P^T, P^T tiles = K Q^T masked and decayed in
 //                    registers, Q from memory a chunk ahead.
 //   staging wave (5) copies each chunk's K rows, V columns and gate block straight from memory into
-//                    a five-chunk LDS ring (global_load_lds), three chunks ahead of the chain; for a
-//                    full chunk every lane's source is a fixed offset from one uniform base.
+//                    LDS rings (global_load_lds; five chunks of K and gates, three of V, whose
+//                    rows are read a step before their chunk's), three chunks ahead of the chain;
+//                    for a full chunk every lane's source is a fixed offset from one uniform base.
 //
 // L2 (q and k normalised to unit length, r = 1 / |k|, rq = 1 / |q| per token, from the solve's gate
 // block): the kernel keeps the exact bf16 K and Q and applies the scales on the fp32 side.  The
