@@ -57,11 +57,11 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
 COUNTERS = {
     "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7a00907359b6d21a",
-             "traffic": 160426582, "mfma_exec_flops": (80740352 + 7274496) * 512},
+             "traffic": 160426749, "mfma_exec_flops": (80740352 + 7274496) * 512},
     "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7a00907359b6d21a",
-              "traffic": 43573030},
+              "traffic": 43572288},
     "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7a00907359b6d21a",
-                  "traffic": 169139939, "prepare_traffic": 47767334},
+                  "traffic": 169136688, "prepare_traffic": 47765952},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},
     "conv": {"source": "gated_deltanet_delta_amd/csrc/conv1d.hip", "sha16": "592040b86d906439",
