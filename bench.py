@@ -56,12 +56,12 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
 COUNTERS = {
-    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7a00907359b6d21a",
-             "traffic": 160426749, "mfma_exec_flops": (80740352 + 7274496) * 512},
-    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7a00907359b6d21a",
-              "traffic": 43572288},
-    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7a00907359b6d21a",
-                  "traffic": 169136688, "prepare_traffic": 47765952},
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "415e6b6b92e5332a",
+             "traffic": 160448187, "mfma_exec_flops": (80740352 + 7274496) * 512},
+    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "415e6b6b92e5332a",
+              "traffic": 43552449},
+    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "415e6b6b92e5332a",
+                  "traffic": 169153071, "prepare_traffic": 47746497},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},
     "conv": {"source": "gated_deltanet_delta_amd/csrc/conv1d.hip", "sha16": "592040b86d906439",

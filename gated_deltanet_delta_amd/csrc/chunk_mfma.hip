@@ -46,6 +46,7 @@
 //     segment X[8g .. 8g+3][c0 + c]: a row-major tile serves directly as a transposed operand.
 
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -248,6 +249,24 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));   // row_bcast:15
     add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));   // row_bcast:31
     return x;
+}
+
+// Unit lower-triangular inverses of four 16 x 16 blocks at once, one block per row of 16 lanes:
+// lane (g, c) holds in a[t] = -A_g[t][c] (zero for t <= c) and returns in x[t] = T_g[t][c],
+// T_g = (I + A_g)^-1.  Column sweep: once x[j] is final it is subtracted from every later row, the
+// row's A_g[t][j] broadcast from lane j of the row (DPP row_newbcast:j), 15 dependent steps.
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + J, 0xf, 0xf, true));
+}
+template <int J>
+__device__ __forceinline__ void subst_step(float (&x)[16], const float (&a)[16]) {
+#pragma unroll
+    for (int t = J + 1; t < 16; ++t) x[t] = fmaf(row_bcast<J>(a[t]), x[J], x[t]);
+}
+template <int... J>
+__device__ __forceinline__ void subst_blocks(float (&x)[16], const float (&a)[16], std::integer_sequence<int, J...>) {
+    (subst_step<J>(x, a), ...);
 }
 
 // Orders one wave's shared-memory writes before its later reads of what other lanes wrote.
@@ -462,25 +481,27 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
         };
         store_a(xa, xb, atile(xa, xb, kx));
         if (wave & 1) store_a(ya, yb, atile(ya, yb, ky));
-        // T_ww = (I + A_ww)^-1 by forward substitution, lane c computing column c, column-sweep
-        // order (x_j final, then subtracted from every later row: 15 dependent steps); the entries
-        // of A_ww come out of the accumulator tile one by one, broadcast with readlane (into scalar
-        // registers: the vector registers are all taken)
+        // the diagonal blocks A_ww (zero on and above the diagonal) go where T_ww will be
         {
             const f32x4 ad = atile(wave, wave, kd);
-            float x[16];
+            float* Ad = sT[blk(wave, wave)];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) x[t] = (t == c) ? 1.f : 0.f;
+            for (int r = 0; r < 4; ++r) Ad[(4 * gq + r) * kBP + c] = ad[r];
+        }
+        lds_barrier();
+        // T_gg = (I + A_gg)^-1 for all four diagonal blocks in wave 0: lane (g, c) computes column c
+        // of block g, in place
+        if (wave == 0) {
+            float* Tg = sT[blk(gq, gq)];
+            float a[16], x[16];
 #pragma unroll
-            for (int j = 0; j < 15; ++j)
-#pragma unroll
-                for (int t = j + 1; t < 16; ++t)
-                    x[t] -= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ad[t & 3]), 16 * (t >> 2) + j)) * x[j];
-            if (lane < 16) {
-                float* Td = sT[blk(wave, wave)];
-#pragma unroll
-                for (int t = 0; t < 16; ++t) Td[t * kBP + c] = x[t];
+            for (int t = 0; t < 16; ++t) {
+                a[t] = -Tg[t * kBP + c];
+                x[t] = (t == c) ? 1.f : 0.f;
             }
+            subst_blocks(x, a, std::make_integer_sequence<int, 15>{});
+#pragma unroll
+            for (int t = 0; t < 16; ++t) Tg[t * kBP + c] = x[t];
         }
         lds_barrier();
         // off-diagonal blocks, by distance d = a - b:  T_ab = -T_aa * sum_{m=b}^{a-1} A_am T_mb
