@@ -68,7 +68,7 @@ COUNTERS = {
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "4fcf074e7757a8b4",
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "b82eb2fdf74b5efc",
             "mfma_exec_flops": (69206016 + 36700160) * 512},
 }
 

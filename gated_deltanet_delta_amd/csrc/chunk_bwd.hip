@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     // top of each chunk makes them loop-variant, so they are formed where they are used.
     auto refresh_lane = [&]() { asm volatile("" : "+v"(gl), "+v"(cl)); };
     if (tid == 0) sm.slot0 = bwd_slot0(cu_seqlens, n, T);
-    __syncthreads();
+    lds_barrier();
     const int slot0 = sm.slot0;
     // (a malformed cu_seqlens can claim more chunks than the workspace holds: stop at its end)
     const int nchunks = min((t1 - t0 + kC - 1) / kC, max(0, max_slots - slot0));
@@ -333,59 +333,111 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     const f32x4b z4 = {0.f, 0.f, 0.f, 0.f};
 
     // the chunk's inputs: K (and Q), this slice of V (and dO), the gates, G, gamma, f; T (and Bm, P)
-    auto load_chunk = [&](int ci, auto rev_c) {
+    // One chunk's inputs, fetched into registers a chunk before their use and written to LDS then:
+    // K (and Q), this slice of V (and dO), the gates, T (and P).  The registers hold the loads as
+    // they arrive (bf16 is widened only when written to LDS), so that nothing waits for them
+    // before the commit.
+    constexpr int NMX = 2, PM = kMat / 4 / kST;            // C x C matrices: T, P
+    constexpr int PV = kC * kW / kST;                      // V, dO elements per thread
+    constexpr int PR = kC * DK / 8 / kST;                  // 8-element K, Q pieces per thread
+    using Raw8 = typename std::conditional<std::is_same<TIn, float>::value, float4[2], uint4>::type;
+    struct ChunkIn {
+        float4 mv[NMX][PM];
+        TIn vv[PV];
+        float ov[PV];
+        Raw8 kr[PR], qr[PR];
+        TG gr, br;
+    };
+    auto raw_load = [&](Raw8& d, const TIn* src) {
+        if constexpr (std::is_same<TIn, float>::value) {
+            d[0] = *reinterpret_cast<const float4*>(src);
+            d[1] = *reinterpret_cast<const float4*>(src + 4);
+        } else {
+            d = *reinterpret_cast<const uint4*>(src);
+        }
+    };
+    auto raw_store = [&](const Raw8& r, float* dst, float m) {
+        if constexpr (std::is_same<TIn, float>::value) {
+            const float x[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = m * x[j];
+        } else {
+            const unsigned w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dst[2 * i] = m * __uint_as_float(w[i] << 16);
+                dst[2 * i + 1] = m * __uint_as_float(w[i] & 0xffff0000u);
+            }
+        }
+    };
+    auto fetch_chunk = [&](ChunkIn& in, int ci, auto rev_c) {
         constexpr bool rev = decltype(rev_c)::value;
         const int cs = t0 + ci * kC, Lc = min(kC, t1 - cs);
         const size_t tok0 = (size_t)row * T + cs;
-        // the three C x C matrices: 16-byte pieces, all loads first
         // (T, and in the reverse sweep P: matrices 0 and 2 of the prep kernel's T, Bm, P)
-        constexpr int NM = rev ? 2 : 1, PM = kMat / 4 / kST;
         const float* mT = mats + ((size_t)(slot0 + ci) * Hv + h) * 3 * kMat;
-        float4 mv[NM][PM];
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+        for (int m = 0; m < (rev ? 2 : 1); ++m)
 #pragma unroll
             for (int it = 0; it < PM; ++it)
-                mv[m][it] = *reinterpret_cast<const float4*>(mT + 2 * m * kMat + 4 * (tid + kST * it));
-        // this slice of V (and dO): one element per thread and row pass
-        constexpr int PV = kC * kW / kST;
-        float vv[PV], ov[PV];
+                in.mv[m][it] = *reinterpret_cast<const float4*>(mT + 2 * m * kMat + 4 * (tid + kST * it));
+        // rows past the chunk's end read its last row (in bounds) and are zeroed at the commit
 #pragma unroll
         for (int it = 0; it < PV; ++it) {
             const int e = tid + kST * it, t = e / kW, c = e % kW;
-            const int tr = t < Lc ? t : Lc - 1;
-            const size_t off = ((tok0 + tr) * Hv + h) * dv + c0 + c;
-            vv[it] = (t < Lc ? 1.f : 0.f) * to_f32(v[off]);
-            if (rev) ov[it] = (t < Lc ? 1.f : 0.f) * d_o[off];
+            const size_t off = ((tok0 + min(t, Lc - 1)) * Hv + h) * dv + c0 + c;
+            in.vv[it] = v[off];
+            if (rev) in.ov[it] = d_o[off];
         }
-        stage_rows<DK, LK, kST>(k, tok0, Hk, kh, Lc, sm.K, tid);
-        if (rev) stage_rows<DK, LK, kST>(q, tok0, Hk, kh, Lc, sm.Q, tid);
+#pragma unroll
+        for (int it = 0; it < PR; ++it) {
+            const int e = tid + kST * it, t = min(e / (DK / 8), Lc - 1), c8 = 8 * (e % (DK / 8));
+            raw_load(in.kr[it], k + ((tok0 + t) * Hk + kh) * DK + c8);
+            if (rev) raw_load(in.qr[it], q + ((tok0 + t) * Hk + kh) * DK + c8);
+        }
+        if (tid < kC) {
+            const size_t gi = (tok0 + min(tid, Lc - 1)) * Hv + h;
+            in.gr = g[gi];
+            in.br = beta[gi];
+        }
+    };
+    auto commit_chunk = [&](const ChunkIn& in, int ci, auto rev_c) {
+        constexpr bool rev = decltype(rev_c)::value;
+        const int cs = t0 + ci * kC, Lc = min(kC, t1 - cs);
 #pragma unroll
         for (int it = 0; it < PV; ++it) {
             const int e = tid + kST * it, t = e / kW, c = e % kW;
-            sm.VX[t * LW + c] = vv[it];
-            if (rev) sm.dO[t * LW + c] = ov[it];
+            const float m = t < Lc ? 1.f : 0.f;
+            sm.VX[t * LW + c] = m * to_f32(in.vv[it]);
+            if (rev) sm.dO[t * LW + c] = m * in.ov[it];
+        }
+#pragma unroll
+        for (int it = 0; it < PR; ++it) {
+            const int e = tid + kST * it, t = e / (DK / 8), c8 = 8 * (e % (DK / 8));
+            const float m = t < Lc ? 1.f : 0.f;
+            raw_store(in.kr[it], sm.K + t * LK + c8, m);
+            if (rev) raw_store(in.qr[it], sm.Q + t * LK + c8, m);
         }
         float* mdst[2] = {sm.T, sm.P};
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+        for (int m = 0; m < (rev ? 2 : 1); ++m)
 #pragma unroll
             for (int it = 0; it < PM; ++it) {
                 const int e = 4 * (tid + kST * it), t = e / kC, j = e % kC;
                 float* d = mdst[m] + t * kLC + j;
-                d[0] = mv[m][it].x;
-                d[1] = mv[m][it].y;
-                d[2] = mv[m][it].z;
-                d[3] = mv[m][it].w;
+                d[0] = in.mv[m][it].x;
+                d[1] = in.mv[m][it].y;
+                d[2] = in.mv[m][it].z;
+                d[3] = in.mv[m][it].w;
             }
         if (tid < kC) {
-            const bool in = tid < Lc;
-            sm.G[tid] = in ? to_f32(g[(tok0 + tid) * Hv + h]) : 0.f;
-            sm.beta[tid] = in ? to_f32(beta[(tok0 + tid) * Hv + h]) : 0.f;
+            const bool inside = tid < Lc;
+            sm.G[tid] = inside ? to_f32(in.gr) : 0.f;
+            sm.beta[tid] = inside ? to_f32(in.br) : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         chunk_decays(sm.G, sm.gam, sm.f, tid);
-        __syncthreads();
+        lds_barrier();
         return Lc;
     };
     // row tile a of M S (M = K or Q, C x DK, S DK x 16): A = M[16 a + c][k + g], B = S[k + g][c]
@@ -419,7 +471,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 if (cl == 0) sm.r_qsdo[t] = s;
             }
         }
-        __syncthreads();
+        lds_barrier();
     };
     // U = T diag(beta) X (waves 0-3, T lower triangular); with `kd`, K D into KD (waves 4-7)
     auto u_kd = [&](bool kd) {
@@ -438,7 +490,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.KD[(16 * a + 4 * gl + r) * LW + cl] = acc[r];
         }
-        __syncthreads();
+        lds_barrier();
     };
     // key tile b of M^T (w o Y) over the chunk (M = K or Q [C][DK], Y C x 16, w per token)
     auto keys_times = [&](const float* M, const float* Y, const float* w1, const float* w2, int b) {
@@ -460,14 +512,34 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         const int i = e / kW, c = e % kW;
         sm.S[i * LW + c] = initial_state ? initial_state[sbase + (size_t)i * dv + c0 + c] : 0.f;
     }
-    __syncthreads();
+    // the chunk-start state of this slice, prefetched a chunk ahead in the reverse sweep
+    constexpr int PS = DK * kW / kST;
+    float sck[PS];
+    auto fetch_ckpt = [&](int ci) {
+#pragma unroll
+        for (int it = 0; it < PS; ++it) {
+            const int e = tid + kST * it, i = e / kW, c = e % kW;
+            sck[it] = ck_at(ci)[(size_t)i * dv + c0 + c];
+        }
+    };
+    ChunkIn cin;
+    if (nchunks > 0) fetch_chunk(cin, 0, std::false_type{});
+    lds_barrier();
     for (int ci = 0; ci < nchunks; ++ci) {
         refresh_lane();
-        for (int e = tid; e < DK * kW; e += kST) {
-            const int i = e / kW, c = e % kW;
+        commit_chunk(cin, ci, std::false_type{});
+#pragma unroll
+        for (int it = 0; it < PS; ++it) {
+            const int e = tid + kST * it, i = e / kW, c = e % kW;
             ck_at(ci)[(size_t)i * dv + c0 + c] = sm.S[i * LW + c];
         }
-        load_chunk(ci, std::false_type{});
+        // the next chunk's inputs; after the last, the reverse sweep's first chunk (this one)
+        if (ci + 1 < nchunks) {
+            fetch_chunk(cin, ci + 1, std::false_type{});
+        } else {
+            fetch_chunk(cin, ci, std::true_type{});
+            fetch_ckpt(ci);
+        }
         ks_x(false);
         u_kd(false);
         // S <- gamma_C S + K^T diag(f) U, key tile b per wave
@@ -480,7 +552,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 *sp = gC * *sp + acc[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---------------- reverse sweep ------------------------------------------------------------
@@ -494,12 +566,17 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         const size_t tok0 = (size_t)row * T + cs;
         const int slot = slot0 + ci;
         float* wd = ws_d + ((size_t)slot * Hv + h) * SSL;
-        for (int e = tid; e < DK * kW; e += kST) {
-            const int i = e / kW, c = e % kW;
-            sm.S[i * LW + c] = ck_at(ci)[(size_t)i * dv + c0 + c];
+#pragma unroll
+        for (int it = 0; it < PS; ++it) {
+            const int e = tid + kST * it, i = e / kW, c = e % kW;
+            sm.S[i * LW + c] = sck[it];
             wd[(size_t)i * dv + c0 + c] = sm.D[i * LW + c];    // D at this chunk's end, for the combine
         }
-        const int Lc = load_chunk(ci, std::true_type{});
+        const int Lc = commit_chunk(cin, ci, std::true_type{});
+        if (ci > 0) {
+            fetch_chunk(cin, ci - 1, std::true_type{});
+            fetch_ckpt(ci - 1);
+        }
         ks_x(true);
         u_kd(true);
 
@@ -520,7 +597,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 if (cl == 0) sm.r_kdu[t] = s;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // dY = T^T dU (into KD), dX = beta dY = dV, and the row sums X.dY and (KS).dX
         if (wave < 4) {
             const int a = wave;
@@ -547,7 +624,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // <S, D> over the slice, for dG at the chunk's last row
         float sd = 0.f;
         for (int e = tid; e < DK * kW; e += kST) {
@@ -556,7 +633,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         }
         sd = sum64(sd);
         if (lane == 0) sm.red[wave] = sd;
-        __syncthreads();
+        lds_barrier();
 
         // dG (this slice's part: the terms through the state; those of the C x C matrices are the
         // combine kernel's) and its reverse running sum, by the first wave (lane = row t)
@@ -578,7 +655,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 part_db[o] = sm.r_db[t];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // dL/dS for the previous chunk: gamma_C D + Q^T diag(gamma) dO - K^T diag(gamma beta) dY
         {
             const float gC = sm.gam[kC - 1];
@@ -592,7 +669,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     if (d_initial) {
         for (int e = tid; e < DK * kW; e += kST) {
