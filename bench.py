@@ -56,20 +56,20 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
 COUNTERS = {
-    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "415e6b6b92e5332a",
-             "traffic": 160448187, "mfma_exec_flops": (80740352 + 7274496) * 512},
-    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "415e6b6b92e5332a",
-              "traffic": 43552449},
-    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "415e6b6b92e5332a",
-                  "traffic": 169153071, "prepare_traffic": 47746497},
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1d5358c9423617ee",
+             "traffic": 160448059, "mfma_exec_flops": (80740352 + 7274496) * 512},
+    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1d5358c9423617ee",
+              "traffic": 43551937},
+    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1d5358c9423617ee",
+                  "traffic": 169161518, "prepare_traffic": 47748545},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},
     "conv": {"source": "gated_deltanet_delta_amd/csrc/conv1d.hip", "sha16": "592040b86d906439",
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "b82eb2fdf74b5efc",
-            "mfma_exec_flops": (69206016 + 36700160) * 512},
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "41895fcebe33b9cd",
+            "mfma_exec_flops": (69206016 + 36700160 + 327680) * 512},
 }
 
 

@@ -32,8 +32,9 @@
 //                     dq and dk terms through the state (dO S^T, U D^T, dY S^T) and the three
 //                     C x C x dk products with the C x C matrices summed over the v-heads in a fixed
 //                     order; then dq, dk, dg and dbeta.
-// The slice kernel's products run on the fp32 matrix cores; the prepare kernel's on the vector ALU
-// with small register tiles.
+// The slice kernel's products run on the fp32 matrix cores.  The prepare kernel forms K K^T and
+// Q K^T on the vector ALU with small register tiles, and T by 16 x 16 blocks: the diagonal ones by
+// forward substitution, the others on the fp32 matrix cores.
 
 #include <type_traits>
 
@@ -161,20 +162,28 @@ __device__ __forceinline__ void chunk_decays(float* G, float* gam, float* f, int
 }
 
 // ------------------------------------------------------------------------------------------------
+// fp32 matrix-core product on 16 x 16 tiles: lane (g, c) = (lane / 16, lane % 16) feeds A[c][k + g]
+// and B[k + g][c]; element r of the result is row 4 g + r, column c
+typedef float f32x4b __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4b mfma4(float a, float b, f32x4b c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int DK, typename TIn, typename TG>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TG* __restrict__ g,
     const TG* __restrict__ beta, const int32_t* __restrict__ cu_seqlens, int N, int T, int Hk, int Hv,
     float* __restrict__ mats) {
     constexpr int LK = DK + 1;
-    // the staged K, Q rows and the C x C products share one region (66 KB at DK = 128: two
+    // the staged K, Q rows and the C x C products share one region (67 KB at DK = 128: two
     // workgroups fit a CU)
-    __shared__ float smem[2 * kC * LK > 3 * kC * kLC ? 2 * kC * LK : 3 * kC * kLC];
+    __shared__ float smem[2 * kC * LK > 4 * kC * kLC ? 2 * kC * LK : 4 * kC * kLC];
     float* sK = smem;
     float* sQ = smem + kC * LK;
     float* sKK = smem;
     float* sQK = smem + kC * kLC;
     float* sBm = smem + 2 * kC * kLC;
+    float* sTT = smem + 3 * kC * kLC;
     __shared__ float sG[kC], sgam[kC], sf[kC], sb[kC];
     const int slot = blockIdx.x, kh = blockIdx.y;
     int n, row, cs, L;
@@ -236,20 +245,56 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
             mP[e] = sQK[t * kLC + j] * dec;
         }
         __syncthreads();
-        if (tid < kC) {            // T = (I + diag(beta) Bm)^-1, lane c: column c
-            float x[kC];
+        // T = (I + A)^-1, A = diag(beta) Bm, by blocked forward substitution on 16 x 16 blocks.  Block
+        // row a of (I + A) T = I gives, for b < a,  (I + A_aa) T_ab = -sum_{m=b}^{a-1} A_am T_mb:
+        // the right-hand sides on the fp32 matrix cores, then every solve with I + A_aa in wave 0,
+        // lane (g, c) taking column c of the g-th block of a level (DPP row broadcasts of A_aa).
+        const int lane = tid & 63, wave = tid >> 6, gq = lane >> 4, c = lane & 15;
+        // wave 0: (I + A_aa) x = y for the blocks (a, b) = (g + d, g), g < 4 - d, y read from sTT
+        // (the identity for d = 0) and x written over it
+        auto solve_level = [&](int d) {
+            const int a = gq + d, b = gq;
+            if (a > 3) return;
+            float av[16], x[16];
 #pragma unroll
-            for (int t = 0; t < kC; ++t) {
-                float acc = (t == tid) ? 1.f : 0.f;
-                const float bt = sb[t];
-#pragma unroll
-                for (int j = 0; j < t; ++j) acc -= bt * sBm[t * kLC + j] * x[j];
-                x[t] = acc;
+            for (int t = 0; t < 16; ++t) {
+                const int row = 16 * a + t;
+                av[t] = -sb[row] * sBm[row * kLC + 16 * a + c];   // (zero for t <= c: Bm is strictly lower)
+                x[t] = d == 0 ? (t == c ? 1.f : 0.f) : sTT[row * kLC + 16 * b + c];
             }
+            invert_blocks16(x, av);
 #pragma unroll
-            for (int t = 0; t < kC; ++t) mT[t * kC + tid] = x[t];
+            for (int t = 0; t < 16; ++t) sTT[(16 * a + t) * kLC + 16 * b + c] = x[t];
+        };
+        if (wave == 0) {
+            solve_level(0);
+        } else {
+            for (int e = tid - kWave; e < kMat; e += kThreads - kWave) {
+                const int t = e / kC, j = e % kC;
+                if ((j >> 4) > (t >> 4)) sTT[t * kLC + j] = 0.f;
+            }
         }
-        __syncthreads();                   // sG, sb and sBm are rewritten for the next v-head
+        __syncthreads();
+        for (int d = 1; d < 4; ++d) {
+            if (wave < 4 - d) {      // right-hand side of block (w + d, w)
+                const int b = wave, a = wave + d;
+                f32x4b X = {0.f, 0.f, 0.f, 0.f};
+                for (int m = b; m < a; ++m) {
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int k = 16 * m + 4 * s4 + gq;
+                        X = mfma4(sb[16 * a + c] * sBm[(16 * a + c) * kLC + k], sTT[k * kLC + 16 * b + c], X);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sTT[(16 * a + 4 * gq + r) * kLC + 16 * b + c] = -X[r];
+            }
+            __syncthreads();
+            if (wave == 0) solve_level(d);
+            __syncthreads();
+        }
+        for (int e = tid; e < kMat; e += kThreads) mT[e] = sTT[(e / kC) * kLC + e % kC];
+        __syncthreads();                   // sG, sb, sBm and sTT are rewritten for the next v-head
     }
 }
 
@@ -262,10 +307,6 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 constexpr int kST = 512;
 constexpr int kSW = kST / kWave;                // waves
 
-typedef float f32x4b __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4b mfma4(float a, float b, f32x4b c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 template <int DK>
 struct SliceLds {

@@ -46,7 +46,6 @@
 //     segment X[8g .. 8g+3][c0 + c]: a row-major tile serves directly as a transposed operand.
 
 #include <type_traits>
-#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -249,24 +248,6 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));   // row_bcast:15
     add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));   // row_bcast:31
     return x;
-}
-
-// Unit lower-triangular inverses of four 16 x 16 blocks at once, one block per row of 16 lanes:
-// lane (g, c) holds in a[t] = -A_g[t][c] (zero for t <= c) and returns in x[t] = T_g[t][c],
-// T_g = (I + A_g)^-1.  Column sweep: once x[j] is final it is subtracted from every later row, the
-// row's A_g[t][j] broadcast from lane j of the row (DPP row_newbcast:j), 15 dependent steps.
-template <int J>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + J, 0xf, 0xf, true));
-}
-template <int J>
-__device__ __forceinline__ void subst_step(float (&x)[16], const float (&a)[16]) {
-#pragma unroll
-    for (int t = J + 1; t < 16; ++t) x[t] = fmaf(row_bcast<J>(a[t]), x[J], x[t]);
-}
-template <int... J>
-__device__ __forceinline__ void subst_blocks(float (&x)[16], const float (&a)[16], std::integer_sequence<int, J...>) {
-    (subst_step<J>(x, a), ...);
 }
 
 // Orders one wave's shared-memory writes before its later reads of what other lanes wrote.
@@ -499,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
                 a[t] = -Tg[t * kBP + c];
                 x[t] = (t == c) ? 1.f : 0.f;
             }
-            subst_blocks(x, a, std::make_integer_sequence<int, 15>{});
+            invert_blocks16(x, a);
 #pragma unroll
             for (int t = 0; t < 16; ++t) Tg[t * kBP + c] = x[t];
         }

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "seqmath.h"
 
 namespace gdn {
@@ -22,6 +24,27 @@ __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint3
 // Row/offset helpers with 64-bit arithmetic (packed sequences reach ~1e9 elements).
 __device__ __forceinline__ size_t idx3(size_t a, size_t b, size_t B_, size_t c, size_t C_) {
     return (a * B_ + b) * C_ + c;
+}
+
+// Unit lower-triangular inverses of four 16 x 16 blocks at once, one block per row of 16 lanes:
+// lane (g, c) holds in a[t] = -A_g[t][c] (zero for t <= c) and returns in x[t] = T_g[t][c],
+// T_g = (I + A_g)^-1.  Column sweep: once x[j] is final it is subtracted from every later row, the
+// row's A_g[t][j] broadcast from lane j of the row (DPP row_newbcast:j), 15 dependent steps.
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + J, 0xf, 0xf, true));
+}
+template <int J>
+__device__ __forceinline__ void subst_step(float (&x)[16], const float (&a)[16]) {
+#pragma unroll
+    for (int t = J + 1; t < 16; ++t) x[t] = fmaf(row_bcast<J>(a[t]), x[J], x[t]);
+}
+template <int... J>
+__device__ __forceinline__ void subst_blocks(float (&x)[16], const float (&a)[16], std::integer_sequence<int, J...>) {
+    (subst_step<J>(x, a), ...);
+}
+__device__ __forceinline__ void invert_blocks16(float (&x)[16], const float (&a)[16]) {
+    subst_blocks(x, a, std::make_integer_sequence<int, 15>{});
 }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global memory at
