@@ -56,12 +56,12 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
 COUNTERS = {
-    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1d5358c9423617ee",
-             "traffic": 160448059, "mfma_exec_flops": (80740352 + 7274496) * 512},
-    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1d5358c9423617ee",
-              "traffic": 43551937},
-    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1d5358c9423617ee",
-                  "traffic": 169161518, "prepare_traffic": 47748545},
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7e9ce728926d74a8",
+             "traffic": 160426941, "mfma_exec_flops": (80740352 + 7274496) * 512},
+    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7e9ce728926d74a8",
+              "traffic": 43553985},
+    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7e9ce728926d74a8",
+                  "traffic": 169139504, "prepare_traffic": 47748929},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},
     "conv": {"source": "gated_deltanet_delta_amd/csrc/conv1d.hip", "sha16": "592040b86d906439",
