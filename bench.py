@@ -68,7 +68,7 @@ COUNTERS = {
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "41895fcebe33b9cd",
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "6e94542276d6ec2e",
             "mfma_exec_flops": (69206016 + 36700160 + 327680) * 512},
 }
 

@@ -754,13 +754,34 @@ struct CombineLds {
         float K[kC * LK], Q[kC * LK];
         float P[kC * kLCc], B[kC * kLCc];
     };
-    union {
+    struct StateAndRaw {
         StateTerms st;
-        CCTerms cc;
-        ChunkTerms ct;
+        // the next tile's S, D [DK][32] and dO, U, dY [C][32] as they arrive from memory
+        // (global_load_lds), while the current tile's products run
+        float rS[DK * kTC], rD[DK * kTC], rO[kC * kTC], rU[kC * kTC], rY[kC * kTC];
+    };
+    union {
+        StateAndRaw sr;
+        CCTerms cc;                                  // (between v-heads: overlaps st only)
+        ChunkTerms ct;                               // (after the v-head loop)
     };
     float G[kC], gam[kC], f[kC], beta[kC];
 };
+
+static_assert(sizeof(CombineLds<128>) <= 160 * 1024, "combine LDS exceeds a CU's 160 KiB");
+
+typedef __attribute__((address_space(1))) void glb_void_b;
+typedef __attribute__((address_space(3))) void lds_void_b;
+// 16 (4) bytes per lane from global memory straight into LDS: lane l writes dst + 16 l (4 l); dst is
+// the same for the whole wave
+__device__ __forceinline__ void lds_copy16(const float* src, float* dst) {
+    __builtin_amdgcn_global_load_lds((glb_void_b*)src, (lds_void_b*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(const float* src, float* dst) {
+    __builtin_amdgcn_global_load_lds((glb_void_b*)src, (lds_void_b*)dst, 4, 0, 0);
+}
+// s_waitcnt vmcnt(0), the other counters left alone: the wave's copies into LDS have landed
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int DK, typename TIn, typename TG>
 __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
@@ -794,6 +815,33 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) sp[j] = sb[j] = z4;
 
+    // The 32-column tile (x, c0) of v-head kh G + x, copied from memory straight into the raw area:
+    // wave w issues the copies j = w, w + 8, ..; copy j of a [rows][32] block covers its 16-byte
+    // pieces 64 j .. 64 j + 63 (lane l: row (64 j + l) / 8, columns 4 ((64 j + l) % 8) ..), those of
+    // dO 4-byte pieces (its rows need only 4-byte alignment), rows past the chunk's end read its
+    // last row (zeroed when restaged).
+    auto prefetch_tile = [&](int x, int c0) {
+        const int h = kh * G + x;
+        const float* Sg = ckpt + ((size_t)slot * Hv + h) * DK * dv + c0;
+        const float* Dg = ws_d + ((size_t)slot * Hv + h) * DK * dv + c0;
+        const float* Ug = ws_u + ((size_t)slot * Hv + h) * kC * dv + c0;
+        const float* Yg = ws_y + ((size_t)slot * Hv + h) * kC * dv + c0;
+        constexpr int CS = DK * kTC / 4 / kWave, CT = kC * kTC / 4 / kWave, CO = kC * kTC / kWave;
+        for (int j = wave; j < CS; j += kCT / kWave) {
+            const int p = kWave * j + lane, i = p / (kTC / 4), c = 4 * (p % (kTC / 4));
+            lds_copy16(Sg + (size_t)i * dv + c, sm.sr.rS + 4 * kWave * j);
+            lds_copy16(Dg + (size_t)i * dv + c, sm.sr.rD + 4 * kWave * j);
+        }
+        for (int j = wave; j < CT; j += kCT / kWave) {
+            const int p = kWave * j + lane, t = p / (kTC / 4), c = 4 * (p % (kTC / 4));
+            lds_copy16(Ug + (size_t)t * dv + c, sm.sr.rU + 4 * kWave * j);
+            lds_copy16(Yg + (size_t)t * dv + c, sm.sr.rY + 4 * kWave * j);
+        }
+        for (int j = wave; j < CO; j += kCT / kWave) {
+            const int p = kWave * j + lane, t = p / kTC, c = p % kTC;
+            lds_copy4(d_o + ((tok0 + min(t, L - 1)) * Hv + h) * dv + c0 + c, sm.sr.rO + kWave * j);
+        }
+    };
     for (int x = 0; x < G; ++x) {
         const int h = kh * G + x;
         if (tid < kC) {
@@ -801,65 +849,58 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
             sm.G[tid] = in ? to_f32(g[(tok0 + tid) * Hv + h]) : 0.f;
             sm.beta[tid] = in ? to_f32(beta[(tok0 + tid) * Hv + h]) : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         chunk_decays(sm.G, sm.gam, sm.f, tid);
-        __syncthreads();
-        const float* Sg = ckpt + ((size_t)slot * Hv + h) * DK * dv;
-        const float* Dg = ws_d + ((size_t)slot * Hv + h) * DK * dv;
-        const float* Ug = ws_u + ((size_t)slot * Hv + h) * kC * dv;
-        const float* Yg = ws_y + ((size_t)slot * Hv + h) * kC * dv;
+        lds_barrier();
         f32x4b cp[2], ca[2];                     // dO U^T and dY U^T on the wave's C x C tiles
 #pragma unroll
         for (int j = 0; j < 2; ++j) cp[j] = ca[j] = z4;
         // ---- the products over dv, 32 columns at a time ----
         for (int c0 = 0; c0 < dv; c0 += kTC) {
-            // stage (16-byte pieces, all loads first): S, D [DK][32]; dO, U, dY [C][32], unscaled and
+            // this tile's inputs have landed in the raw area (issued during the previous tile, or
+            // just below for a v-head's first): restage them with the padded pitch, unscaled and
             // scaled by gamma, f and -gamma beta
-            constexpr int PS = DK * kTC / 4 / kCT, PT = kC * kTC / 4 / kCT;
-            float4 vs[PS], vd[PS], vo[PT], vu[PT], vy[PT];
+            if (x == 0 && c0 == 0) prefetch_tile(0, 0);
+            wait_vmcnt0();
+            lds_barrier();
+            {
+                constexpr int PS = DK * kTC / 4 / kCT, PT = kC * kTC / 4 / kCT;
 #pragma unroll
-            for (int it = 0; it < PS; ++it) {
-                const int e = 4 * (tid + kCT * it), i = e / kTC, c = e % kTC;
-                vs[it] = *reinterpret_cast<const float4*>(Sg + (size_t)i * dv + c0 + c);
-                vd[it] = *reinterpret_cast<const float4*>(Dg + (size_t)i * dv + c0 + c);
-            }
+                for (int it = 0; it < PS; ++it) {
+                    const int e = 4 * (tid + kCT * it), i = e / kTC, c = e % kTC;
+                    *reinterpret_cast<float4*>(&sm.sr.st.S[i * kLT + c]) = *reinterpret_cast<const float4*>(&sm.sr.rS[e]);
+                    *reinterpret_cast<float4*>(&sm.sr.st.D[i * kLT + c]) = *reinterpret_cast<const float4*>(&sm.sr.rD[e]);
+                }
+                auto scaled = [](float s_, float4 v) { return make_float4(s_ * v.x, s_ * v.y, s_ * v.z, s_ * v.w); };
 #pragma unroll
-            for (int it = 0; it < PT; ++it) {
-                const int e = 4 * (tid + kCT * it), t = e / kTC, c = e % kTC;
-                const float* op = d_o + ((tok0 + min(t, L - 1)) * Hv + h) * dv + c0 + c;   // (4-byte aligned)
-                const float m = t < L ? 1.f : 0.f;
-                vo[it] = make_float4(m * op[0], m * op[1], m * op[2], m * op[3]);
-                vu[it] = *reinterpret_cast<const float4*>(Ug + (size_t)t * dv + c0 + c);
-                vy[it] = *reinterpret_cast<const float4*>(Yg + (size_t)t * dv + c0 + c);
+                for (int it = 0; it < PT; ++it) {
+                    const int e = 4 * (tid + kCT * it), t = e / kTC, c = e % kTC;
+                    const float m = t < L ? 1.f : 0.f;
+                    const float4 vo = scaled(m, *reinterpret_cast<const float4*>(&sm.sr.rO[e]));
+                    const float4 vu = *reinterpret_cast<const float4*>(&sm.sr.rU[e]);
+                    const float4 vy = *reinterpret_cast<const float4*>(&sm.sr.rY[e]);
+                    *reinterpret_cast<float4*>(&sm.sr.st.Ou[t * kLT + c]) = vo;
+                    *reinterpret_cast<float4*>(&sm.sr.st.Uu[t * kLT + c]) = vu;
+                    *reinterpret_cast<float4*>(&sm.sr.st.Yu[t * kLT + c]) = vy;
+                    *reinterpret_cast<float4*>(&sm.sr.st.O[t * kLT + c]) = scaled(sm.gam[t], vo);
+                    *reinterpret_cast<float4*>(&sm.sr.st.U[t * kLT + c]) = scaled(sm.f[t], vu);
+                    *reinterpret_cast<float4*>(&sm.sr.st.Y[t * kLT + c]) = scaled(-sm.gam[t] * sm.beta[t], vy);
+                }
             }
-#pragma unroll
-            for (int it = 0; it < PS; ++it) {
-                const int e = 4 * (tid + kCT * it), i = e / kTC, c = e % kTC;
-                *reinterpret_cast<float4*>(&sm.st.S[i * kLT + c]) = vs[it];
-                *reinterpret_cast<float4*>(&sm.st.D[i * kLT + c]) = vd[it];
-            }
-            auto scaled = [](float s_, float4 v) { return make_float4(s_ * v.x, s_ * v.y, s_ * v.z, s_ * v.w); };
-#pragma unroll
-            for (int it = 0; it < PT; ++it) {
-                const int e = 4 * (tid + kCT * it), t = e / kTC, c = e % kTC;
-                *reinterpret_cast<float4*>(&sm.st.Ou[t * kLT + c]) = vo[it];
-                *reinterpret_cast<float4*>(&sm.st.Uu[t * kLT + c]) = vu[it];
-                *reinterpret_cast<float4*>(&sm.st.Yu[t * kLT + c]) = vy[it];
-                *reinterpret_cast<float4*>(&sm.st.O[t * kLT + c]) = scaled(sm.gam[t], vo[it]);
-                *reinterpret_cast<float4*>(&sm.st.U[t * kLT + c]) = scaled(sm.f[t], vu[it]);
-                *reinterpret_cast<float4*>(&sm.st.Y[t * kLT + c]) = scaled(-sm.gam[t] * sm.beta[t], vy[it]);
-            }
-            __syncthreads();
+            lds_barrier();
+            // the next tile: this v-head's, or the next v-head's first
+            if (c0 + kTC < dv) prefetch_tile(x, c0 + kTC);
+            else if (x + 1 < G) prefetch_tile(x + 1, 0);
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int p = wave + 8 * j, a = p / KT, b = p % KT;
                 f32x4b tq = z4, tk = z4;
 #pragma unroll
                 for (int kk = 0; kk < kTC; kk += 4) {
-                    const float sb_ = sm.st.S[(16 * b + cl) * kLT + kk + gl];
-                    tq = mfma4(sm.st.O[(16 * a + cl) * kLT + kk + gl], sb_, tq);
-                    tk = mfma4(sm.st.Y[(16 * a + cl) * kLT + kk + gl], sb_, tk);
-                    tk = mfma4(sm.st.U[(16 * a + cl) * kLT + kk + gl], sm.st.D[(16 * b + cl) * kLT + kk + gl], tk);
+                    const float sb_ = sm.sr.st.S[(16 * b + cl) * kLT + kk + gl];
+                    tq = mfma4(sm.sr.st.O[(16 * a + cl) * kLT + kk + gl], sb_, tq);
+                    tk = mfma4(sm.sr.st.Y[(16 * a + cl) * kLT + kk + gl], sb_, tk);
+                    tk = mfma4(sm.sr.st.U[(16 * a + cl) * kLT + kk + gl], sm.sr.st.D[(16 * b + cl) * kLT + kk + gl], tk);
                 }
                 aq[j] += tq;
                 ak[j] += tk;
@@ -873,15 +914,15 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
                 f32x4b tp = z4, ta = z4;
 #pragma unroll
                 for (int kk = 0; kk < kTC; kk += 4) {
-                    const float ub = sm.st.Uu[(16 * cb + cl) * kLT + kk + gl];
-                    tp = mfma4(sm.st.Ou[(16 * ra + cl) * kLT + kk + gl], ub, tp);
-                    ta = mfma4(sm.st.Yu[(16 * ra + cl) * kLT + kk + gl], ub, ta);
+                    const float ub = sm.sr.st.Uu[(16 * cb + cl) * kLT + kk + gl];
+                    tp = mfma4(sm.sr.st.Ou[(16 * ra + cl) * kLT + kk + gl], ub, tp);
+                    ta = mfma4(sm.sr.st.Yu[(16 * ra + cl) * kLT + kk + gl], ub, ta);
                 }
                 cp[j] += tp;
                 ca[j] += ta;
                 __builtin_amdgcn_sched_barrier(0);
             }
-            __syncthreads();
+            lds_barrier();
         }
         // ---- the C x C gradients of v-head h: E and dA o Bm to LDS, the v-head sums in registers ----
         {
@@ -903,7 +944,7 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
                     sb[j][r] += dbm * dec;
                 }
         }
-        __syncthreads();
+        lds_barrier();
         // rows minus columns of E (dG, as a reverse running sum) and rows of dA o Bm (dbeta), added
         // to the slices' partials, by the first wave (lane = row t)
         if (tid < kC) {
@@ -931,7 +972,7 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
                 db[(tok0 + t) * Hv + h] = ab + rb;
             }
         }
-        __syncthreads();                         // E, F and the gates are rewritten for the next v-head
+        lds_barrier();                         // E, F and the gates are rewritten for the next v-head
     }
 
     // ---- the chunk terms: K, Q, and the C x C matrices summed over the v-heads ----
