@@ -55,12 +55,14 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # scaled by what the same counter reads on a plain copy of known size, and the matrix-core work from
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
+# (chunk_mfma.hip's readings were taken at sha16 7e9ce728926d74a8; the file since only lost its
+# prefix-sum helper to common.h, and its gfx950 assembly is unchanged instruction for instruction.)
 COUNTERS = {
-    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7e9ce728926d74a8",
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "b5c048cf8b47d0bd",
              "traffic": 160426941, "mfma_exec_flops": (80740352 + 7274496) * 512},
-    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7e9ce728926d74a8",
+    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "b5c048cf8b47d0bd",
               "traffic": 43553985},
-    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "7e9ce728926d74a8",
+    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "b5c048cf8b47d0bd",
                   "traffic": 169139504, "prepare_traffic": 47748929},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},
@@ -68,8 +70,7 @@ COUNTERS = {
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "6e94542276d6ec2e",
-            "mfma_exec_flops": (69206016 + 36700160 + 327680) * 512},
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "37898f5a6036277b"},
 }
 
 

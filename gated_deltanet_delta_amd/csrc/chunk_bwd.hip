@@ -50,16 +50,6 @@ constexpr int kThreads = 256;
 constexpr int kLC = kC + 1;   // pitch of C x C matrices in LDS
 constexpr int kMat = kC * kC; // one C x C matrix in the workspace
 
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off);
-    return x;
-}
-__device__ __forceinline__ float sum64(float x) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
-    return x;
-}
 
 // 8 consecutive input elements as fp32 (one 16-byte load for bf16, two for fp32)
 struct F8 {
@@ -148,14 +138,9 @@ __device__ bool bwd_locate(int slot, const int32_t* cu_seqlens, int N, int T, in
 // The chunk's running log-decay G (in place over the gates), gamma and f, by the first wave.
 __device__ __forceinline__ void chunk_decays(float* G, float* gam, float* f, int tid) {
     if (tid < kWave) {
-        float x = G[tid];
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (tid >= off) x += y;
-        }
+        const float x = wave_prefix_sum(G[tid]);
         G[tid] = x;
-        const float gc = __shfl(x, kWave - 1);
+        const float gc = lane_value(x, kWave - 1);
         gam[tid] = expf(x);
         f[tid] = expf(gc - x);
     }
@@ -476,7 +461,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
             sm.G[tid] = inside ? to_f32(in.gr) : 0.f;
             sm.beta[tid] = inside ? to_f32(in.br) : 0.f;
         }
-        lds_barrier();
+        // (the first wave reads back only the gates its own lanes wrote: no barrier before)
         chunk_decays(sm.G, sm.gam, sm.f, tid);
         lds_barrier();
         return Lc;
@@ -508,7 +493,7 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * a + 4 * gl + r;
-                const float s = sum16(acc[r] * sm.dO[t * LW + cl]);
+                const float s = row_sum16(acc[r] * sm.dO[t * LW + cl]);
                 if (cl == 0) sm.r_qsdo[t] = s;
             }
         }
@@ -621,7 +606,9 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         ks_x(true);
         u_kd(true);
 
-        // dU = P^T dO + f (K D) (P lower triangular: rows t' >= t), and the row sums (KD).U
+        // dU = P^T dO + f (K D) (P lower triangular: rows t' >= t), and the row sums (KD).U, on
+        // waves 0-3; beside them waves 4-7 form <S, D> over the slice, for dG at the chunk's last
+        // row (D is still the gradient at this chunk's end)
         if (wave < 4) {
             const int a = wave;
             f32x4b acc = z4;
@@ -634,12 +621,22 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 const int t = 16 * a + 4 * gl + r;
                 const float kd = sm.KD[t * LW + cl];
                 sm.dU[t * LW + cl] = acc[r] + sm.f[t] * kd;
-                const float s = sum16(kd * sm.U[t * LW + cl]);
+                const float s = row_sum16(kd * sm.U[t * LW + cl]);
                 if (cl == 0) sm.r_kdu[t] = s;
             }
+        } else {
+            float sd = 0.f;
+            for (int e = tid - kST / 2; e < DK * kW; e += kST / 2) {
+                const int i = e / kW, c = e % kW;
+                sd += sm.S[i * LW + c] * sm.D[i * LW + c];
+            }
+            sd = wave_sum64(sd);
+            if (lane == 0) sm.red[wave - 4] = sd;
         }
         lds_barrier();
-        // dY = T^T dU (into KD), dX = beta dY = dV, and the row sums X.dY and (KS).dX
+        // dY = T^T dU (into KD), dX = beta dY = dV, and the row sums X.dY and (KS).dX, on waves 0-3;
+        // beside them waves 4-7 start dL/dS for the previous chunk, gamma_C D + Q^T diag(gamma) dO
+        // (the part that does not need dY), in place over D
         if (wave < 4) {
             const int a = wave;
             f32x4b acc = z4;
@@ -657,58 +654,45 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 wu[(size_t)t * dv] = sm.U[t * LW + cl];     // U and dY (zero past the chunk's end),
                 wy[(size_t)t * dv] = dy;                    // for the combine
                 if (t < Lc) dv_out[((tok0 + t) * Hv + h) * dv + c0 + cl] = dx;
-                const float s1 = sum16(sm.VX[t * LW + cl] * dy);
-                const float s2 = sum16(sm.KS[t * LW + cl] * dx);
+                const float s1 = row_sum16(sm.VX[t * LW + cl] * dy);
+                const float s2 = row_sum16(sm.KS[t * LW + cl] * dx);
                 if (cl == 0) {
                     sm.r_db[t] = s1;
                     sm.r_ksdx[t] = s2;
                 }
             }
+        } else {
+            const float gC = sm.gam[kC - 1];
+            for (int b = wave - 4; b < KT; b += 4) {
+                const f32x4b a1 = keys_times(sm.Q, sm.dO, sm.gam, nullptr, b);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float* dp = &sm.D[(16 * b + 4 * gl + r) * LW + cl];
+                    *dp = gC * *dp + a1[r];
+                }
+            }
         }
         lds_barrier();
-        // <S, D> over the slice, for dG at the chunk's last row
-        float sd = 0.f;
-        for (int e = tid; e < DK * kW; e += kST) {
-            const int i = e / kW, c = e % kW;
-            sd += sm.S[i * LW + c] * sm.D[i * LW + c];
-        }
-        sd = sum64(sd);
-        if (lane == 0) sm.red[wave] = sd;
-        lds_barrier();
-
         // dG (this slice's part: the terms through the state; those of the C x C matrices are the
-        // combine kernel's) and its reverse running sum, by the first wave (lane = row t)
-        if (tid < kC) {
-            const int t = tid;
-            const float fkdu = sum64(sm.f[t] * sm.r_kdu[t]);
-            float sdt = 0.f;
-            for (int w = 0; w < kSW; ++w) sdt += sm.red[w];
+        // combine kernel's) and its reverse running sum, by the last wave (lane = row t), beside the
+        // rest of dL/dS, - K^T diag(gamma beta) dY, one key tile per wave
+        if (wave == kSW - 1) {
+            const int t = lane;
+            const float fkdu = wave_sum64(sm.f[t] * sm.r_kdu[t]);
+            const float sdt = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
             float x = sm.gam[t] * sm.r_qsdo[t] - sm.gam[t] * sm.r_ksdx[t] - sm.f[t] * sm.r_kdu[t];
             if (t == kC - 1) x += sm.gam[kC - 1] * sdt + fkdu;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_down(x, off);
-                if (t + off < kWave) x += y;
-            }
+            x = wave_suffix_sum(x, t);
             if (t < Lc) {
                 const size_t o = (size_t)sl * rows * Hv + (tok0 + t) * Hv + h;
                 part_dg[o] = x;
                 part_db[o] = sm.r_db[t];
             }
         }
-        lds_barrier();
-        // dL/dS for the previous chunk: gamma_C D + Q^T diag(gamma) dO - K^T diag(gamma beta) dY
-        {
-            const float gC = sm.gam[kC - 1];
-            for (int b = wave; b < KT; b += kSW) {
-                const f32x4b a1 = keys_times(sm.Q, sm.dO, sm.gam, nullptr, b);
-                const f32x4b a2 = keys_times(sm.K, sm.KD, sm.gam, sm.beta, b);
+        for (int b = wave; b < KT; b += kSW) {
+            const f32x4b a2 = keys_times(sm.K, sm.KD, sm.gam, sm.beta, b);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float* dp = &sm.D[(16 * b + 4 * gl + r) * LW + cl];
-                    *dp = gC * *dp + a1[r] - a2[r];
-                }
-            }
+            for (int r = 0; r < 4; ++r) sm.D[(16 * b + 4 * gl + r) * LW + cl] -= a2[r];
         }
         lds_barrier();
     }
@@ -955,12 +939,7 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
                 ce += sm.cc.E[i * kLCc + t];
                 rb += sm.cc.F[t * kLCc + i];
             }
-            float xg = re - ce;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float y = __shfl_down(xg, off);
-                if (t + off < kWave) xg += y;
-            }
+            const float xg = wave_suffix_sum(re - ce, t);
             if (t < L) {
                 float ag = 0.f, ab = 0.f;
                 for (int s = 0; s < slices; ++s) {

@@ -236,20 +236,6 @@ __device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& h
 constexpr int kBP = 17;          // row pitch (floats) of the 16 x 16 blocks of A and T
 __device__ __forceinline__ int blk(int a, int b) { return a * (a + 1) / 2 + b; }   // a >= b
 
-// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 lanes inside each row of
-// 16 lanes, then lane 15's total added to rows 1 and 3 and lane 31's to rows 2 and 3 (DPP row
-// broadcasts).  Lanes whose source falls outside the row take 0.
-__device__ __forceinline__ float wave_prefix_sum(float x) {
-    auto add = [&](int y) { x += __int_as_float(y); };
-    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));   // row_shr:1
-    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));   // row_shr:2
-    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));   // row_shr:4
-    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));   // row_shr:8
-    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));   // row_bcast:15
-    add(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));   // row_bcast:31
-    return x;
-}
-
 // Stores that write through to memory (sc0 sc1) for the solve's outputs, which only the next kernel
 // reads: they leave no dirty L2 lines for the write-back at the end of the kernel (measured: the
 // prepare kernel 25.2 -> 23.5 us).

@@ -47,6 +47,60 @@ __device__ __forceinline__ void invert_blocks16(float (&x)[16], const float (&a)
     subst_blocks(x, a, std::make_integer_sequence<int, 15>{});
 }
 
+// Cross-lane sums on the vector ALU (DPP), with no LDS round trip.  dpp<CTRL, ROWS> returns the value
+// of the lane that CTRL names, in the rows of 16 lanes that ROWS selects; lanes whose source falls
+// outside their row, and rows not selected, take 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row.  A butterfly: quad_perm [1 0 3 2],
+// quad_perm [2 3 0 1], row_half_mirror, row_mirror.  After each step every lane of a group holds the
+// same partial sum, so the result is the xor butterfly's bit for bit.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp<0xb1>(x);
+    x += dpp<0x4e>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return x;
+}
+
+// Sum over the wave, the same in every lane: (R0 + R1) + (R2 + R3) of the four row sums.
+__device__ __forceinline__ float wave_sum64(float x) {
+    x = row_sum16(x);
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 lanes inside each row of
+// 16 lanes (row_shr), then lane 15's total added to rows 1 and 3 and lane 31's to rows 2 and 3 (DPP
+// row broadcasts).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp<0x111>(x);
+    x += dpp<0x112>(x);
+    x += dpp<0x114>(x);
+    x += dpp<0x118>(x);
+    x += dpp<0x142, 0xa>(x);
+    x += dpp<0x143, 0xc>(x);
+    return x;
+}
+
+// Inclusive suffix sum over the 64 lanes of a wave (lane t gets the sum of lanes t .. 63): shifts
+// by 1, 2, 4, 8 lanes toward lower lanes inside each row (row_shl), then every row adds the totals
+// of the rows above it, which lanes 16, 32 and 48 hold.
+__device__ __forceinline__ float wave_suffix_sum(float x, int lane) {
+    x += dpp<0x101>(x);
+    x += dpp<0x102>(x);
+    x += dpp<0x104>(x);
+    x += dpp<0x108>(x);
+    const float s3 = lane_value(x, 48), s2 = lane_value(x, 32) + s3, s1 = lane_value(x, 16) + s2;
+    const int row = lane >> 4;
+    return x + (row == 0 ? s1 : row == 1 ? s2 : row == 2 ? s3 : 0.f);
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global memory at
 // workgroup scope, which on gfx950 waits for every outstanding global load and store of the wave
 // (vmcnt(0)); that would stall register prefetches of the next chunk at every barrier.  The kernels
