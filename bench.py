@@ -56,13 +56,14 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
 # (chunk_mfma.hip's readings were taken at sha16 7e9ce728926d74a8; the file since only lost its
-# prefix-sum helper to common.h, and its gfx950 assembly is unchanged instruction for instruction.)
+# prefix-sum helper to common.h and its fragment helpers to mfma_frag.h, and its gfx950 assembly is
+# unchanged instruction for instruction.)
 COUNTERS = {
-    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "b5c048cf8b47d0bd",
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1126536af6b02ce9",
              "traffic": 160426941, "mfma_exec_flops": (80740352 + 7274496) * 512},
-    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "b5c048cf8b47d0bd",
+    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1126536af6b02ce9",
               "traffic": 43553985},
-    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "b5c048cf8b47d0bd",
+    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1126536af6b02ce9",
                   "traffic": 169139504, "prepare_traffic": 47748929},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},
@@ -70,7 +71,7 @@ COUNTERS = {
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "37898f5a6036277b"},
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "e46dd0b348bb1587"},
 }
 
 

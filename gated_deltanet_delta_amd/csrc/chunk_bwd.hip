@@ -40,6 +40,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "mfma_frag.h"
 
 namespace gdn {
 namespace {
@@ -291,13 +292,34 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 // wave, the dq / dk terms four.  Operands come straight from LDS, two reads per 1024 multiply-adds.
 constexpr int kST = 512;
 constexpr int kSW = kST / kWave;                // waves
+constexpr int kPieces = 3;                      // bf16 pieces of an fp32 operand (put_frag)
 
 
+// K and Q of the chunk: fp32 rows (fp32 inputs), or for bf16 inputs the exact bf16 rows in the
+// swizzled layout of mfma_frag.h, with the products' other operands as three-piece B fragments of
+// v_mfma_f32_16x16x32_bf16 (put_frag), each written by the phase that forms the values:
+//   Sf, Df   S and D over the keys: [32-key step kb][piece][lane (g, c)], element e = row 32 kb + 8 g + e
+//   Yf, Zf   token-weighted operands over the chunk: [32-token step kb][piece][lane (g, c)], element
+//            e = token 32 kb + 4 g + e (e < 4) or 32 kb + 16 + 4 g + e - 4 (e >= 4), the token order of
+//            kt_frag; Yf holds f U (forward sweep) or gamma dO (reverse), Zf gamma beta dY
+template <int DK, bool BF>
+struct SliceKQ {
+    float K[kC * (DK + 1)];
+    float Q[kC * (DK + 1)];
+};
 template <int DK>
-struct SliceLds {
+struct SliceKQ<DK, true> {
+    __bf16 Kb[kC * DK];
+    __bf16 Qb[kC * DK];
+    bf16x8 Sf[DK / 32][kPieces][kWave];
+    bf16x8 Df[DK / 32][kPieces][kWave];
+    bf16x8 Yf[kC / 32][kPieces][kWave];
+    bf16x8 Zf[kC / 32][kPieces][kWave];
+};
+
+template <int DK, bool BF>
+struct SliceLds : SliceKQ<DK, BF> {
     static constexpr int LK = DK + 1, LW = kW + 1;
-    float K[kC * LK];
-    float Q[kC * LK];
     float S[DK * LW];        // chunk-start state, this slice
     float D[DK * LW];        // dL/dS at the chunk end, this slice
     float T[kC * kLC];       // T
@@ -314,6 +336,36 @@ struct SliceLds {
     int slot0;
 };
 
+// Three bf16 pieces of fp32 values, x = hi + mid + lo to within 2^-27 |x| (each residual is exact in
+// fp32; each rounding to bf16 leaves at most 2^-9 of what it rounds), into a B fragment array
+// F[kb][piece][lane]: N = 4 or 2 consecutive elements of lane `ln`'s 8, from element e0 (a multiple
+// of N).  Against exact bf16 K and Q, three products then carry the fp32 operand in full.
+template <int N>
+__device__ __forceinline__ void put_frag(bf16x8 (*F)[kPieces][kWave], int kb, int ln, int e0, const float* x) {
+    unsigned w[kPieces][N / 2];
+#pragma unroll
+    for (int p = 0; p < N / 2; ++p) {
+        float r0 = x[2 * p], r1 = x[2 * p + 1];
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) {
+            const unsigned h = pack_bf16x2(r0, r1);
+            w[k][p] = h;
+            r0 -= __uint_as_float(h << 16);
+            r1 -= __uint_as_float(h & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+        char* f = reinterpret_cast<char*>(&F[kb][k][ln]) + 2 * e0;
+        if constexpr (N == 4) *reinterpret_cast<uint2*>(f) = uint2{w[k][0], w[k][1]};
+        else *reinterpret_cast<unsigned*>(f) = w[k][0];
+    }
+}
+__device__ __forceinline__ void put_frag4(bf16x8 (*F)[kPieces][kWave], int kb, int ln, int e0, const f32x4b& v) {
+    const float x[4] = {v[0], v[1], v[2], v[3]};
+    put_frag<4>(F, kb, ln, e0, x);
+}
+
 template <int DK, typename TIn, typename TG>
 __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
@@ -323,7 +375,8 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     float* __restrict__ ckpt, float* __restrict__ ws_d,
     float* __restrict__ ws_u, float* __restrict__ ws_y, float* __restrict__ part_dg, float* __restrict__ part_db,
     float* __restrict__ dv_out, float* __restrict__ d_initial, long long rows, int max_slots) {
-    using L = SliceLds<DK>;
+    constexpr bool BF = std::is_same<TIn, bf16_t>::value;   // exact bf16 K and Q: bf16 matrix cores
+    using L = SliceLds<DK, BF>;
     constexpr int LK = L::LK, LW = L::LW;
     constexpr int KT = DK / 16;                  // key tiles
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -440,9 +493,22 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
 #pragma unroll
         for (int it = 0; it < PR; ++it) {
             const int e = tid + kST * it, t = e / (DK / 8), c8 = 8 * (e % (DK / 8));
-            const float m = t < Lc ? 1.f : 0.f;
-            raw_store(in.kr[it], sm.K + t * LK + c8, m);
-            if (rev) raw_store(in.qr[it], sm.Q + t * LK + c8, m);
+            if constexpr (BF) {
+                // 16-byte chunk c8 / 8 of row t at its swizzled place; rows past the chunk's end zero
+                // (component by component: a select of whole vectors becomes one of their addresses,
+                // which puts the register prefetch on the stack)
+                const int off = t * DK + 8 * ((c8 / 8) ^ kswz<DK>(t));
+                const bool in_chunk = t < Lc;
+                auto keep = [&](const uint4& x) {
+                    return uint4{in_chunk ? x.x : 0u, in_chunk ? x.y : 0u, in_chunk ? x.z : 0u, in_chunk ? x.w : 0u};
+                };
+                *reinterpret_cast<uint4*>(sm.Kb + off) = keep(in.kr[it]);
+                if (rev) *reinterpret_cast<uint4*>(sm.Qb + off) = keep(in.qr[it]);
+            } else {
+                const float m = t < Lc ? 1.f : 0.f;
+                raw_store(in.kr[it], sm.K + t * LK + c8, m);
+                if (rev) raw_store(in.qr[it], sm.Q + t * LK + c8, m);
+            }
         }
         float* mdst[2] = {sm.T, sm.P};
 #pragma unroll
@@ -476,11 +542,43 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                 acc = mfma4(M[(16 * a + cl) * LK + kk + gl], Sx[(kk + gl) * LW + cl], acc);
         return acc;
     };
-    // K S and X = V - gamma K S (waves 0-3); with `qs`, also the row sums (QS).dO (waves 4-7)
+    // bf16 inputs: row tile a of M X over the keys, M = K or Q (exact bf16 rows), X = S or D as
+    // three-piece fragments; three products per 32-key step
+    auto rows_bf = [&](const __bf16* Mb, bf16x8 (*Xf)[kPieces][kWave], int a) {
+        f32x4b acc = z4;
+        const __bf16* mrow = Mb + 16 * a * DK;
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            const bf16x8 am = *reinterpret_cast<const bf16x8*>(mrow + kf_lane<DK>(cl, gl, kb));
+#pragma unroll
+            for (int k = 0; k < kPieces; ++k) acc = mma(am, Xf[kb][k][lane], acc);
+        }
+        return acc;
+    };
+    // bf16 inputs: key tile kt of M^T Y over the chunk's tokens (Y a token-weighted operand as
+    // three-piece fragments); element r of lane (g, c) is key rho(kt, 4 g + r), column c
+    auto keys_bf = [&](const __bf16* Mb, bf16x8 (*Yw)[kPieces][kWave], int kt) {
+        f32x4b acc = z4;
+        lds_u8* base = lds_at(Mb + kt_lane<DK>(cl, gl, kt >> 1));
+#pragma unroll
+        for (int kb = 0; kb < kC / 32; ++kb) {
+            const bf16x8 at = kt_frag<DK>(base, kt & 1, kb);
+#pragma unroll
+            for (int k = 0; k < kPieces; ++k) acc = mma(at, Yw[kb][k][lane], acc);
+        }
+        return acc;
+    };
+    // the key that element r of a key tile b's result stands for
+    auto key_of = [&](int b, int r) { return BF ? rho(b, 4 * gl + r) : 16 * b + 4 * gl + r; };
+
+    // K S and X = V - gamma K S (waves 0-3); with `qs`, also the row sums (QS).dO and, for bf16
+    // inputs, gamma dO as fragments for the state gradient (waves 4-7)
     auto ks_x = [&](bool qs) {
         if (wave < 4) {
             const int a = wave;
-            const f32x4b acc = rows_times_state(sm.K, sm.S, a);
+            f32x4b acc;
+            if constexpr (BF) acc = rows_bf(sm.Kb, sm.Sf, a);
+            else acc = rows_times_state(sm.K, sm.S, a);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * a + 4 * gl + r;
@@ -489,13 +587,18 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
             }
         } else if (qs) {
             const int a = wave - 4;
-            const f32x4b acc = rows_times_state(sm.Q, sm.S, a);
+            f32x4b acc, gdo;
+            if constexpr (BF) acc = rows_bf(sm.Qb, sm.Sf, a);
+            else acc = rows_times_state(sm.Q, sm.S, a);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * a + 4 * gl + r;
-                const float s = row_sum16(acc[r] * sm.dO[t * LW + cl]);
+                const float o = sm.dO[t * LW + cl];
+                const float s = row_sum16(acc[r] * o);
                 if (cl == 0) sm.r_qsdo[t] = s;
+                gdo[r] = sm.gam[t] * o;
             }
+            if constexpr (BF) put_frag4(sm.Yf, a >> 1, lane, 4 * (a & 1), gdo);
         }
         lds_barrier();
     };
@@ -510,9 +613,19 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                     acc = mfma4(sm.T[(16 * a + cl) * kLC + kk + gl], sm.beta[kk + gl] * sm.VX[(kk + gl) * LW + cl], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.U[(16 * a + 4 * gl + r) * LW + cl] = acc[r];
+            if constexpr (BF) {
+                if (!kd) {                     // forward sweep: f U as fragments for the state update
+                    f32x4b fu;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) fu[r] = sm.f[16 * a + 4 * gl + r] * acc[r];
+                    put_frag4(sm.Yf, a >> 1, lane, 4 * (a & 1), fu);
+                }
+            }
         } else if (kd) {
             const int a = wave - 4;
-            const f32x4b acc = rows_times_state(sm.K, sm.D, a);
+            f32x4b acc;
+            if constexpr (BF) acc = rows_bf(sm.Kb, sm.Df, a);
+            else acc = rows_times_state(sm.K, sm.D, a);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm.KD[(16 * a + 4 * gl + r) * LW + cl] = acc[r];
         }
@@ -534,19 +647,32 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
 
     // ---------------- forward sweep: the state at every chunk start ----------------------------
     const size_t sbase = ((size_t)n * Hv + h) * SSL;
-    for (int e = tid; e < DK * kW; e += kST) {
-        const int i = e / kW, c = e % kW;
-        sm.S[i * LW + c] = initial_state ? initial_state[sbase + (size_t)i * dv + c0 + c] : 0.f;
+    // Per-thread elements of a slice state: column tid % 16, the PS consecutive keys PS (tid / 16) + j
+    // (4 or 2 consecutive elements of one lane of a key fragment)
+    constexpr int PS = DK * kW / kST;
+    const int st_c = tid % kW, st_i = PS * (tid / kW);
+    // X (fp32, pitch LW) and, for bf16 inputs, its fragments Xf from the thread's elements x
+    auto put_state = [&](float* X, bf16x8 (*Xf)[kPieces][kWave], const float* x) {
+#pragma unroll
+        for (int j = 0; j < PS; ++j) X[(st_i + j) * LW + st_c] = x[j];
+        if constexpr (BF) {
+            const int i = st_i % 32;
+            put_frag<PS>(Xf, st_i / 32, 16 * (i / 8) + st_c, i % 8, x);
+        }
+    };
+    {
+        float x[PS];
+#pragma unroll
+        for (int j = 0; j < PS; ++j)
+            x[j] = initial_state ? initial_state[sbase + (size_t)(st_i + j) * dv + c0 + st_c] : 0.f;
+        if constexpr (BF) put_state(sm.S, sm.Sf, x);
+        else put_state(sm.S, nullptr, x);
     }
     // the chunk-start state of this slice, prefetched a chunk ahead in the reverse sweep
-    constexpr int PS = DK * kW / kST;
     float sck[PS];
     auto fetch_ckpt = [&](int ci) {
 #pragma unroll
-        for (int it = 0; it < PS; ++it) {
-            const int e = tid + kST * it, i = e / kW, c = e % kW;
-            sck[it] = ck_at(ci)[(size_t)i * dv + c0 + c];
-        }
+        for (int j = 0; j < PS; ++j) sck[j] = ck_at(ci)[(size_t)(st_i + j) * dv + c0 + st_c];
     };
     ChunkIn cin;
     if (nchunks > 0) fetch_chunk(cin, 0, std::false_type{});
@@ -554,11 +680,11 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
     for (int ci = 0; ci < nchunks; ++ci) {
         refresh_lane();
         commit_chunk(cin, ci, std::false_type{});
+        // (each thread stores the elements it reads back with fetch_ckpt: the last chunk's are read
+        // right away, with no barrier between)
 #pragma unroll
-        for (int it = 0; it < PS; ++it) {
-            const int e = tid + kST * it, i = e / kW, c = e % kW;
-            ck_at(ci)[(size_t)i * dv + c0 + c] = sm.S[i * LW + c];
-        }
+        for (int j = 0; j < PS; ++j)
+            ck_at(ci)[(size_t)(st_i + j) * dv + c0 + st_c] = sm.S[(st_i + j) * LW + st_c];
         // the next chunk's inputs; after the last, the reverse sweep's first chunk (this one)
         if (ci + 1 < nchunks) {
             fetch_chunk(cin, ci + 1, std::false_type{});
@@ -571,20 +697,28 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         // S <- gamma_C S + K^T diag(f) U, key tile b per wave
         const float gC = sm.gam[kC - 1];
         for (int b = wave; b < KT; b += kSW) {
-            const f32x4b acc = keys_times(sm.K, sm.U, sm.f, nullptr, b);
+            f32x4b acc, sn;
+            if constexpr (BF) acc = keys_bf(sm.Kb, sm.Yf, b);
+            else acc = keys_times(sm.K, sm.U, sm.f, nullptr, b);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float* sp = &sm.S[(16 * b + 4 * gl + r) * LW + cl];
+                float* sp = &sm.S[key_of(b, r) * LW + cl];
                 *sp = gC * *sp + acc[r];
+                sn[r] = *sp;
             }
+            if constexpr (BF) put_frag4(sm.Sf, b >> 1, lane, 4 * (b & 1), sn);
         }
         lds_barrier();
     }
 
     // ---------------- reverse sweep ------------------------------------------------------------
-    for (int e = tid; e < DK * kW; e += kST) {
-        const int i = e / kW, c = e % kW;
-        sm.D[i * LW + c] = d_final ? d_final[sbase + (size_t)i * dv + c0 + c] : 0.f;
+    {
+        float x[PS];
+#pragma unroll
+        for (int j = 0; j < PS; ++j)
+            x[j] = d_final ? d_final[sbase + (size_t)(st_i + j) * dv + c0 + st_c] : 0.f;
+        if constexpr (BF) put_state(sm.D, sm.Df, x);
+        else put_state(sm.D, nullptr, x);
     }
     for (int ci = nchunks - 1; ci >= 0; --ci) {
         refresh_lane();
@@ -592,12 +726,11 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
         const size_t tok0 = (size_t)row * T + cs;
         const int slot = slot0 + ci;
         float* wd = ws_d + ((size_t)slot * Hv + h) * SSL;
+        if constexpr (BF) put_state(sm.S, sm.Sf, sck);
+        else put_state(sm.S, nullptr, sck);
 #pragma unroll
-        for (int it = 0; it < PS; ++it) {
-            const int e = tid + kST * it, i = e / kW, c = e % kW;
-            sm.S[i * LW + c] = sck[it];
-            wd[(size_t)i * dv + c0 + c] = sm.D[i * LW + c];    // D at this chunk's end, for the combine
-        }
+        for (int j = 0; j < PS; ++j)                            // D at this chunk's end, for the combine
+            wd[(size_t)(st_i + j) * dv + c0 + st_c] = sm.D[(st_i + j) * LW + st_c];
         const int Lc = commit_chunk(cin, ci, std::true_type{});
         if (ci > 0) {
             fetch_chunk(cin, ci - 1, std::true_type{});
@@ -646,10 +779,12 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                     acc = mfma4(sm.T[(kk + gl) * kLC + 16 * a + cl], sm.dU[(kk + gl) * LW + cl], acc);
             float* wu = ws_u + ((size_t)slot * Hv + h) * kC * dv + c0 + cl;
             float* wy = ws_y + ((size_t)slot * Hv + h) * kC * dv + c0 + cl;
+            f32x4b zd;                                  // gamma beta dY, for bf16 inputs as fragments
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * a + 4 * gl + r;
                 const float dy = acc[r], dx = sm.beta[t] * dy;
+                zd[r] = sm.gam[t] * dx;
                 sm.KD[t * LW + cl] = dy;
                 wu[(size_t)t * dv] = sm.U[t * LW + cl];     // U and dY (zero past the chunk's end),
                 wy[(size_t)t * dv] = dy;                    // for the combine
@@ -661,13 +796,16 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
                     sm.r_ksdx[t] = s2;
                 }
             }
+            if constexpr (BF) put_frag4(sm.Zf, a >> 1, lane, 4 * (a & 1), zd);
         } else {
             const float gC = sm.gam[kC - 1];
             for (int b = wave - 4; b < KT; b += 4) {
-                const f32x4b a1 = keys_times(sm.Q, sm.dO, sm.gam, nullptr, b);
+                f32x4b a1;
+                if constexpr (BF) a1 = keys_bf(sm.Qb, sm.Yf, b);
+                else a1 = keys_times(sm.Q, sm.dO, sm.gam, nullptr, b);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float* dp = &sm.D[(16 * b + 4 * gl + r) * LW + cl];
+                    float* dp = &sm.D[key_of(b, r) * LW + cl];
                     *dp = gC * *dp + a1[r];
                 }
             }
@@ -690,17 +828,23 @@ __global__ __launch_bounds__(kST) void bwd_slice_kernel(
             }
         }
         for (int b = wave; b < KT; b += kSW) {
-            const f32x4b a2 = keys_times(sm.K, sm.KD, sm.gam, sm.beta, b);
+            f32x4b a2, dn;
+            if constexpr (BF) a2 = keys_bf(sm.Kb, sm.Zf, b);
+            else a2 = keys_times(sm.K, sm.KD, sm.gam, sm.beta, b);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.D[(16 * b + 4 * gl + r) * LW + cl] -= a2[r];
+            for (int r = 0; r < 4; ++r) {
+                float* dp = &sm.D[key_of(b, r) * LW + cl];
+                *dp -= a2[r];
+                dn[r] = *dp;
+            }
+            if constexpr (BF) put_frag4(sm.Df, b >> 1, lane, 4 * (b & 1), dn);
         }
         lds_barrier();
     }
-    if (d_initial) {
-        for (int e = tid; e < DK * kW; e += kST) {
-            const int i = e / kW, c = e % kW;
-            d_initial[sbase + (size_t)i * dv + c0 + c] = sm.D[i * LW + c];
-        }
+    if (d_initial) {   // (the thread's own elements of D: with no chunk there is no barrier since they were written)
+#pragma unroll
+        for (int j = 0; j < PS; ++j)
+            d_initial[sbase + (size_t)(st_i + j) * dv + c0 + st_c] = sm.D[(st_i + j) * LW + st_c];
     }
 }
 
@@ -1076,7 +1220,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const auto kern = bwd_slice_kernel<DK, TIn, TG>;
-    const size_t bytes = sizeof(SliceLds<DK>);
+    const size_t bytes = sizeof(SliceLds<DK, std::is_same<TIn, bf16_t>::value>);
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes)) != hipSuccess)
         return e;
