@@ -71,7 +71,11 @@ COUNTERS = {
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "e46dd0b348bb1587"},
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "e46dd0b348bb1587",
+            "mfma_exec_f32_flops": (10485760 + 36700160 + 327680) * 512,
+            "mfma_exec_bf16_flops": 176160768 * 512,
+            "traffic": round((207864.5625 + 314180.25 + 16958.0) * 1.9998 * 1024
+                             + (479251.6875 + 69698.4375 + 98304.0) * 1024)},
 }
 
 
@@ -464,7 +468,8 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_bwd = e0.elapsed_time(e1) / bwd_calls
     bwd_flops = BWD_FLOPS_PER_TOKEN_VHEAD * tokens * wl.Hv
-    bwd_exec = counter("bwd", "mfma_exec_flops")
+    bwd_exec32 = counter("bwd", "mfma_exec_f32_flops")
+    bwd_exec16 = counter("bwd", "mfma_exec_bf16_flops")
     del bws
 
     # the same through every input option (gates from a, b and q, k normalised, both differentiated)
@@ -696,19 +701,25 @@ def main() -> int:
                                        "frac": round(norm_bytes / (ms_norm / 1e3) / 1e9 / MI355X_HBM_GBS, 4),
                                        "traffic": counter("norm", "traffic"),
                                        "algorithmic_bytes_per_launch": int(norm_bytes)}},
-        "backward": {"call": "gdn_chunk_bwd (dq, dk, dv, dg, dbeta, d_initial of the prefill; fp32 "
-                             "arithmetic, the slice kernel on fp32 matrix cores)",
+        "backward": {"call": "gdn_chunk_bwd (dq, dk, dv, dg, dbeta, d_initial of the prefill; fp32-accurate "
+                             "arithmetic: the slice kernel's products against K and Q on bf16 matrix cores with "
+                             "three-piece operands, the others on fp32 matrix cores)",
                      "calls": bwd_calls, "ms_per_call_events": round(ms_bwd, 4),
                      "tokens_per_s": round(tokens / (ms_bwd / 1e3), 1),
                      "roofline": {"bound": "mfma", "achieved": round(bwd_flops / (ms_bwd / 1e3) / 1e12, 3),
                                   "peak": MI355X_F32_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(bwd_flops / (ms_bwd / 1e3) / 1e12 / MI355X_F32_TFLOPS, 4),
+                                  "traffic": counter("bwd", "traffic"),
                                   "flops_per_token_vhead": BWD_FLOPS_PER_TOKEN_VHEAD,
                                   "algorithmic_flops_per_call": int(bwd_flops),
-                                  "mfma_executed_flops_per_call": bwd_exec,
-                                  "mfma_frac_executed": (None if bwd_exec is None else
-                                                         round(bwd_exec / (ms_bwd / 1e3) / 1e12
-                                                               / MI355X_F32_TFLOPS, 4))},
+                                  "mfma_executed_f32_flops_per_call": bwd_exec32,
+                                  "mfma_executed_bf16_flops_per_call": bwd_exec16,
+                                  # the share of the call the matrix units would need at their peaks for
+                                  # the work they executed (fp32 and bf16 parts each at its own peak)
+                                  "mfma_time_frac_executed": (None if bwd_exec32 is None or bwd_exec16 is None else
+                                                              round((bwd_exec32 / MI355X_F32_TFLOPS
+                                                                     + bwd_exec16 / MI355X_BF16_TFLOPS)
+                                                                    / 1e12 / (ms_bwd / 1e3), 4))},
                      "every_option": {"call": "gdn_chunk_bwd_ex (gates from a, b and q, k L2-normalised, "
                                               "both differentiated: da, db, dA_log, ddt_bias, raw dq, dk)",
                                       "ms_per_call_events": round(ms_bwd_ex, 4),
