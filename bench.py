@@ -71,11 +71,7 @@ COUNTERS = {
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "e46dd0b348bb1587",
-            "mfma_exec_f32_flops": (10485760 + 36700160 + 327680) * 512,
-            "mfma_exec_bf16_flops": 176160768 * 512,
-            "traffic": round((207864.5625 + 314180.25 + 16958.0) * 1.9998 * 1024
-                             + (479251.6875 + 69698.4375 + 98304.0) * 1024)},
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "04610cae2a836398"},
 }
 
 

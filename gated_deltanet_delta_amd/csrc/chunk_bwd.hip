@@ -866,6 +866,7 @@ constexpr int kTC = 32;          // dv columns per staged tile of the state prod
 constexpr int kLT = kTC + 4;     // pitch of those tiles: rows 16 a + c, columns k + g land in distinct banks
 constexpr int kLCc = kC + 4;     // pitch of the C x C matrices in the combine kernel
 constexpr int kCT = 512;         // combine kernel threads: 8 waves, each owning 1/8 of the output tiles
+constexpr int kMaxSlices = 8;    // 16-column slices of a state, at most (dv <= 128)
 
 template <int DK>
 struct CombineLds {
@@ -1056,6 +1057,18 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
         {
             const float* Bmh = mats + ((size_t)slot * Hv + h) * 3 * kMat + kMat;     // (T, Bm, P)
             const float* Ph = Bmh + kMat;
+            // every element's Bm and P in flight together, and no branch around the decay (its
+            // argument clamped to <= 0, which leaves the elements on or below the diagonal as they
+            // are): loads inside a branch were each waited for before the next
+            float bmv[2][4], pvv[2][4];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * (ca0 + 2 * j) + 4 * gl + r, i = 16 * cb + cl;
+                    bmv[j][r] = Bmh[t * kC + i];
+                    pvv[j][r] = Ph[t * kC + i];
+                }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1063,8 +1076,9 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
                     const int t = 16 * (ca0 + 2 * j) + 4 * gl + r, i = 16 * cb + cl;   // element (t, i)
                     const float dP = i <= t ? cp[j][r] : 0.f;
                     const float dA = i < t ? -ca[j][r] : 0.f;
-                    const float bm = Bmh[t * kC + i], pv = Ph[t * kC + i];
-                    const float dec = i <= t ? expf(sm.G[t] - sm.G[i]) : 0.f;
+                    const float bm = bmv[j][r], pv = pvv[j][r];
+                    const float ed = expf(fminf(sm.G[t] - sm.G[i], 0.f));
+                    const float dec = i <= t ? ed : 0.f;
                     const float dbm = sm.beta[t] * dA;
                     sm.cc.E[t * kLCc + i] = dP * pv + dbm * bm;
                     sm.cc.F[t * kLCc + i] = dA * bm;
@@ -1077,7 +1091,18 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
         // to the slices' partials, by the first wave (lane = row t)
         if (tid < kC) {
             const int t = tid;
+            // the slices' partials first, all in flight together while the row sums run (a loop that
+            // adds each as it arrives waits out one memory round trip per load); summed in slice order
+            float pg[kMaxSlices], pb[kMaxSlices];
+            const int tl = min(t, L - 1);
+#pragma unroll
+            for (int s = 0; s < kMaxSlices; ++s) {
+                const size_t o = ((size_t)min(s, slices - 1) * rows + tok0 + tl) * Hv + h;
+                pg[s] = part_dg[o];
+                pb[s] = part_db[o];
+            }
             float re = 0.f, ce = 0.f, rb = 0.f;
+#pragma unroll 8
             for (int i = 0; i < kC; ++i) {
                 re += sm.cc.E[t * kLCc + i];
                 ce += sm.cc.E[i * kLCc + t];
@@ -1086,10 +1111,12 @@ __global__ __launch_bounds__(kCT) void bwd_combine_kernel(
             const float xg = wave_suffix_sum(re - ce, t);
             if (t < L) {
                 float ag = 0.f, ab = 0.f;
-                for (int s = 0; s < slices; ++s) {
-                    const size_t o = ((size_t)s * rows + tok0 + t) * Hv + h;
-                    ag += part_dg[o];
-                    ab += part_db[o];
+#pragma unroll
+                for (int s = 0; s < kMaxSlices; ++s) {
+                    if (s < slices) {
+                        ag += pg[s];
+                        ab += pb[s];
+                    }
                 }
                 dg[(tok0 + t) * Hv + h] = ag + xg;
                 db[(tok0 + t) * Hv + h] = ab + rb;
