@@ -71,7 +71,11 @@ COUNTERS = {
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "04610cae2a836398"},
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "04610cae2a836398",
+            "mfma_exec_f32_flops": (10485760 + 36700160 + 327680) * 512,
+            "mfma_exec_bf16_flops": 176160768 * 512,
+            "traffic": round((207879.1875 + 312944.875 + 16956.25) * 1.9998 * 1024
+                             + (477808.71875 + 67957.75 + 98304.125) * 1024)},
 }
 
 
