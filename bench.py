@@ -57,7 +57,8 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
 # (chunk_mfma.hip's readings were taken at sha16 7e9ce728926d74a8; the file since only lost its
 # prefix-sum helper to common.h and its fragment helpers to mfma_frag.h, and its gfx950 assembly is
-# unchanged instruction for instruction.)
+# unchanged instruction for instruction.  Likewise chunk_bwd.hip's readings were taken at sha16
+# 04610cae2a836398; since then only comments changed.)
 COUNTERS = {
     "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1126536af6b02ce9",
              "traffic": 160426941, "mfma_exec_flops": (80740352 + 7274496) * 512},
@@ -71,7 +72,7 @@ COUNTERS = {
              "traffic": 134710246},
     "norm": {"source": "gated_deltanet_delta_amd/csrc/norm.hip", "sha16": "e94d82c291e7fd2c",
              "traffic": 134250675},
-    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "04610cae2a836398",
+    "bwd": {"source": "gated_deltanet_delta_amd/csrc/chunk_bwd.hip", "sha16": "4bbae852a1b2b7dc",
             "mfma_exec_f32_flops": (10485760 + 36700160 + 327680) * 512,
             "mfma_exec_bf16_flops": 176160768 * 512,
             "traffic": round((207879.1875 + 312944.875 + 16956.25) * 1.9998 * 1024

@@ -32,7 +32,9 @@
 //                     dq and dk terms through the state (dO S^T, U D^T, dY S^T) and the three
 //                     C x C x dk products with the C x C matrices summed over the v-heads in a fixed
 //                     order; then dq, dk, dg and dbeta.
-// The slice kernel's products run on the fp32 matrix cores.  The prepare kernel forms K K^T and
+// The slice kernel's products against K or Q run, for bf16 inputs, on the bf16 matrix cores with the
+// other operand in three bf16 pieces; its T and P products, and all of them for fp32 inputs, on the
+// fp32 matrix cores.  The prepare kernel forms K K^T and
 // Q K^T on the vector ALU with small register tiles, and T by 16 x 16 blocks: the diagonal ones by
 // forward substitution, the others on the fp32 matrix cores.
 
@@ -285,11 +287,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------
-// The slice kernel: 512 threads, eight waves.  Every product is a chain of fp32 matrix-core
-// instructions on 16 x 16 tiles (v_mfma_f32_16x16x4f32: lane (g, c) = (lane / 16, lane % 16) feeds
-// A[c][k + g] and B[k + g][c]; element r of the result is row 4 g + r, column c), each wave owning
-// whole tiles: the C x 16 slice products one row tile per wave, the C x C gradients two tiles per
-// wave, the dq / dk terms four.  Operands come straight from LDS, two reads per 1024 multiply-adds.
+// The slice kernel: 512 threads, eight waves, each owning whole 16 x 16 output tiles (the C x 16
+// slice products one row tile per wave, the K^T / Q^T products one key tile).  The fp32 products are
+// chains of v_mfma_f32_16x16x4f32 (lane (g, c) = (lane / 16, lane % 16) feeds A[c][k + g] and
+// B[k + g][c]; element r of the result is row 4 g + r, column c) with operands straight from LDS.
+// For bf16 inputs the products against K or Q use v_mfma_f32_16x16x32_bf16 on fragments instead
+// (rows_bf, keys_bf below).
 constexpr int kST = 512;
 constexpr int kSW = kST / kWave;                // waves
 constexpr int kPieces = 3;                      // bf16 pieces of an fp32 operand (put_frag)
