@@ -55,17 +55,16 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # scaled by what the same counter reads on a plain copy of known size, and the matrix-core work from
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
-# (chunk_mfma.hip's readings were taken at sha16 7e9ce728926d74a8; the file since only lost its
-# prefix-sum helper to common.h and its fragment helpers to mfma_frag.h, and its gfx950 assembly is
-# unchanged instruction for instruction.  Likewise chunk_bwd.hip's readings were taken at sha16
-# 04610cae2a836398; since then only comments changed.)
+# (chunk_mfma.hip's HBM readings were taken at sha16 538da900da46eea7, its matrix-core reading at
+# 7e9ce728926d74a8: since then the solve kernel changed and the scan kernel's gfx950 assembly did not.
+# chunk_bwd.hip's readings were taken at sha16 04610cae2a836398; since then only comments changed.)
 COUNTERS = {
-    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1126536af6b02ce9",
-             "traffic": 160426941, "mfma_exec_flops": (80740352 + 7274496) * 512},
-    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1126536af6b02ce9",
-              "traffic": 43553985},
-    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "1126536af6b02ce9",
-                  "traffic": 169139504, "prepare_traffic": 47748929},
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "538da900da46eea7",
+             "traffic": 160440667, "mfma_exec_flops": (80740352 + 7274496) * 512},
+    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "538da900da46eea7",
+              "traffic": 43558845},
+    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "538da900da46eea7",
+                  "traffic": 169155707, "prepare_traffic": 47753149},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},
     "conv": {"source": "gated_deltanet_delta_amd/csrc/conv1d.hip", "sha16": "592040b86d906439",
@@ -689,7 +688,8 @@ def main() -> int:
                                "ms_per_call_events": round(ms_fused_norm, 5),
                                "tokens_per_s": round(tokens / (ms_fused_norm / 1e3), 1),
                                "ms_prefill_then_norm_events": round(ms_prefill_norm, 5),
-                               "traffic": (None if counter("scan_norm", "traffic") is None else
+                               "traffic": (None if counter("scan_norm", "traffic") is None
+                                           or counter("scan_norm", "prepare_traffic") is None else
                                            counter("scan_norm", "traffic") + counter("scan_norm", "prepare_traffic")),
                                "traffic_prefill_then_norm": (None if call_traffic is None or counter("norm", "traffic") is None
                                                              else call_traffic + counter("norm", "traffic")),

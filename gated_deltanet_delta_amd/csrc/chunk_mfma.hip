@@ -205,8 +205,18 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_start, int N, int T,
     int Hk, int Hv, int nct, float* __restrict__ ws_G, __bf16* __restrict__ ws_M,
     __bf16* __restrict__ ws_N, float* __restrict__ ws_X, int x_per_head) {
-    __shared__ float sA[10][16 * kBP];     // blocks (a, b), a > b, of A
-    __shared__ float sT[10][16 * kBP];     // blocks (a, b), a >= b, of T = (I + A)^-1
+    // The chunk's K rows and the previous chunk's, staged once in the swizzled row layout of
+    // mfma_frag.h (whole-row copies straight into shared memory) and read from there as matrix-core
+    // fragments by all four waves; the blocks of A and T reuse the same space afterwards.
+    constexpr bool kStageK = DK == 128;
+    constexpr int kKBytes = kC * DK * 2;
+    constexpr int kATBytes = 2 * 10 * 16 * kBP * 4;
+    constexpr int kRawBytes = 2 * kKBytes > kATBytes ? 2 * kKBytes : kATBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char s_raw[kRawBytes];
+    float (*sA)[16 * kBP] = reinterpret_cast<float (*)[16 * kBP]>(s_raw);                 // blocks (a, b), a > b, of A
+    float (*sT)[16 * kBP] = reinterpret_cast<float (*)[16 * kBP]>(s_raw + kATBytes / 2);  // (a, b), a >= b, of T = (I + A)^-1
+    __bf16* const sKc = reinterpret_cast<__bf16*>(s_raw);              // this chunk's K rows
+    __bf16* const sKp = reinterpret_cast<__bf16*>(s_raw + kKBytes);    // the previous chunk's
     __shared__ float sB[kC];
     // per wave: the current v-head's G2 and beta, read by address in the tile loops (instead of by
     // cross-lane broadcasts)
@@ -238,11 +248,31 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
             *reinterpret_cast<f32x4*>(xb + i) = f32x4{-1.f, -1.f, -1.f, -1.f};
     }
 
+    // Stage K: each 1 KiB copy instruction writes four rows; lane l lands at byte 16 l of the copy,
+    // row t, physical chunk p, and so fetches logical chunk p ^ kswz(t) of row t.  Rows past the
+    // chunk's end repeat its last row: they only meet rows with beta = 0.
+    {
+        constexpr int kCopies = kKBytes / 1024;          // per chunk of K rows
+        auto stage = [&](__bf16* dst, size_t row0, int rows, int j) {
+            const int byte = j * 1024 + 16 * lane;
+            const int t = byte / (2 * DK), pch = (byte % (2 * DK)) / 16;
+            const __bf16* src = k + ((row0 + min(t, rows - 1)) * Hk + kh) * DK + 8 * (pch ^ kswz<DK>(t));
+            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(reinterpret_cast<unsigned char*>(dst) + j * 1024),
+                                             16, 0, 0);
+        };
+        if constexpr (kStageK) {
+            for (int j = wave; j < kCopies; j += 4) stage(sKc, tok0, L, j);
+            if (has_prev)
+                for (int j = wave; j < kCopies; j += 4) stage(sKp, tok0 - kC, kC, j);
+            __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this wave's copies have landed
+            __syncthreads();                             // and every other wave's
+        }
+    }
     // K K^T as 16x16 tiles; wave w owns diagonal tile (w, w) and some below it: wave 0 (0,0) (1,0);
     // wave 1 (1,1) (2,1) (2,0); wave 2 (2,2) (3,2); wave 3 (3,3) (3,0) (3,1).  The K rows of the (at
-    // most three) token tiles a wave needs are all loaded before the first product.  K rows past
-    // the chunk's end repeat its last row: they only meet rows with beta = 0.
+    // most three) token tiles a wave needs are all read before the first product.
     auto kfrag = [&](int t, int kb) {
+        if constexpr (kStageK) return *reinterpret_cast<const bf16x8*>(sKc + 16 * t * DK + kf_lane<DK>(c, gq, kb));
         const int r = min(16 * t + c, L - 1);
         return *reinterpret_cast<const bf16x8*>(k + ((tok0 + r) * Hk + kh) * DK + 32 * kb + 8 * gq);
     };
@@ -261,13 +291,16 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     // the previous chunk's K rows 16 b + c, b = 0..3, for N
     bf16x8 kp[4][KB];
     if (has_prev) {
-        const __bf16* pb = k + ((tok0 - kC + c) * Hk + kh) * DK + 8 * gq;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                kp[b][kb] = *reinterpret_cast<const bf16x8*>(pb + (size_t)16 * b * Hk * DK + 32 * kb);
+                kp[b][kb] = kStageK ? *reinterpret_cast<const bf16x8*>(sKp + 16 * b * DK + kf_lane<DK>(c, gq, kb))
+                                    : *reinterpret_cast<const bf16x8*>(k + ((tok0 - kC + 16 * b + c) * Hk + kh) * DK
+                                                                       + 32 * kb + 8 * gq);
     }
+    // every wave holds its fragments before any writes the blocks of A and T over the staged rows
+    if constexpr (kStageK) __syncthreads();
     auto kkt = [&](const bf16x8* ka, const bf16x8* kb_) {
         f32x4 acc = zero4();
 #pragma unroll
@@ -615,8 +648,6 @@ constexpr size_t scan_lds_bytes(bool norm) {
 }
 static_assert(scan_lds_bytes<128>(true) <= 160 * 1024, "fused-norm scan LDS exceeds a CU's 160 KiB");
 
-typedef __attribute__((address_space(1))) void glb_void;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
 template <int n>

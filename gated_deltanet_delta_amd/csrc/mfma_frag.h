@@ -26,6 +26,8 @@ __device__ __forceinline__ bf16x8 cat44(const bf16x4& a, const bf16x4& b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+typedef __attribute__((address_space(1))) void glb_void;   // for global_load_lds (memory -> LDS)
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
