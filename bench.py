@@ -55,15 +55,16 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # scaled by what the same counter reads on a plain copy of known size, and the matrix-core work from
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
-# (chunk_mfma.hip's HBM readings were taken at sha16 538da900da46eea7, its matrix-core reading at
-# 7e9ce728926d74a8: since then the solve kernel changed and the scan kernel's gfx950 assembly did not.
+# (chunk_mfma.hip's HBM readings were taken at sha16 538da900da46eea7, since when only a comment
+# changed; its matrix-core reading at 7e9ce728926d74a8, since when the solve kernel changed and the
+# scan kernel's gfx950 assembly did not.
 # chunk_bwd.hip's readings were taken at sha16 04610cae2a836398; since then only comments changed.)
 COUNTERS = {
-    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "538da900da46eea7",
+    "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "f5f86e9959c219d4",
              "traffic": 160440667, "mfma_exec_flops": (80740352 + 7274496) * 512},
-    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "538da900da46eea7",
+    "solve": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "f5f86e9959c219d4",
               "traffic": 43558845},
-    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "538da900da46eea7",
+    "scan_norm": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "f5f86e9959c219d4",
                   "traffic": 169155707, "prepare_traffic": 47753149},
     "decode": {"source": "gated_deltanet_delta_amd/csrc/recurrent.hip", "sha16": "df00f8ca898a19e2",
                "traffic": 1085280816},

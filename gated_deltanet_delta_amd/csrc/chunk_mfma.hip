@@ -208,6 +208,8 @@ __global__ __launch_bounds__(kThreads, 4) void chunk_solve_kernel(
     // The chunk's K rows and the previous chunk's, staged once in the swizzled row layout of
     // mfma_frag.h (whole-row copies straight into shared memory) and read from there as matrix-core
     // fragments by all four waves; the blocks of A and T reuse the same space afterwards.
+    // (head size 64 keeps its fragment loads from memory: a staged build failed its parity tests there
+    // with non-finite final states, for a cause not found)
     constexpr bool kStageK = DK == 128;
     constexpr int kKBytes = kC * DK * 2;
     constexpr int kATBytes = 2 * 10 * 16 * kBP * 4;
