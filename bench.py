@@ -56,8 +56,7 @@ METRIC = "prefill tokens/s + decode state GB/s, gated delta rule, Qwen3-Next sha
 # SQ_INSTS_VALU_MFMA_MOPS_* (units of 512 flops).  Each reading was taken at the version of its
 # kernel's source file whose hash it names; when the file has changed since, it is reported as null.
 # (chunk_mfma.hip's HBM readings were taken at sha16 538da900da46eea7, since when only a comment
-# changed; its matrix-core reading at 7e9ce728926d74a8, since when the solve kernel changed and the
-# scan kernel's gfx950 assembly did not.
+# changed; its matrix-core reading at the current source.
 # chunk_bwd.hip's readings were taken at sha16 04610cae2a836398; since then only comments changed.)
 COUNTERS = {
     "scan": {"source": "gated_deltanet_delta_amd/csrc/chunk_mfma.hip", "sha16": "f5f86e9959c219d4",
